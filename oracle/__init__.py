@@ -1,0 +1,23 @@
+"""CPU oracle for exact softmax attention: TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import anything from here. The GPU library and its Python
+binding never do, and this package imports nothing from them.
+
+Contents
+  core        ctypes front end of ``fa_oracle.c``: fp64 three-pass safe-softmax
+              attention (the definition written out).
+  recurrence  the online-softmax recurrence for one query in fp64, block by
+              block, in any block partition and order, with switches that plant
+              the four classic implementation mistakes (used only to show that
+              the pins catch them).
+  brute       50-digit decimal evaluation of the definition with no
+              max-subtraction, for tiny inputs.
+
+Pins (tests/test_oracle_*.py): the two worked examples printed on the pages
+(tests/golden/), closed forms (uniform keys, a single key, causal row 0),
+softmax rows summing to 1, shift invariance, block order/size invariance and
+the brute force. Every function here is pinned; none is "parity unpinned"
+except the second worked example's output vector, whose value vectors the
+page does not print.
+"""

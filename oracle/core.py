@@ -1,0 +1,76 @@
+"""ctypes front end of the fp64 three-pass attention oracle (``fa_oracle.c``).
+
+Test infrastructure only. See ``fa_oracle.c`` for the definition it computes
+and the passages it follows ("FlashAttention tiles exact softmax without
+materializing the score matrix", opening definition; "transformer math: flash
+attention math", sections "What we must compute..." and "Safe softmax").
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        lib.fa_oracle_fwd.restype = ctypes.c_int
+        lib.fa_oracle_fwd.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+        ]
+        lib.fa_oracle_threads.restype = ctypes.c_int
+        lib.fa_oracle_threads.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle runs on."""
+    return int(_load().fa_oracle_threads())
+
+
+def attention(q, k, v, scale, causal=False, rows=None):
+    """Exact attention in fp64.
+
+    q, k, v : array-likes of shape [B, H, N, d] (converted to contiguous fp64;
+              fp16/bf16 inputs convert exactly).
+    scale   : the logit multiplier, as a Python float (pass the exact value the
+              GPU receives, e.g. ``float(np.float32(1/sqrt(d)))``).
+    causal  : key j is excluded for j > i.
+    rows    : None for every query row, else an int array [B*H, R] of row
+              indices per (batch, head).
+    Returns (o, lse): o [B,H,N,d] and lse [B,H,N] (rows=None), or
+    o [B*H,R,d] and lse [B*H,R].
+    """
+    q = np.ascontiguousarray(np.asarray(q, dtype=np.float64))
+    k = np.ascontiguousarray(np.asarray(k, dtype=np.float64))
+    v = np.ascontiguousarray(np.asarray(v, dtype=np.float64))
+    if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError(f"q, k, v must share one [B,H,N,d] shape, got {q.shape} {k.shape} {v.shape}")
+    B, H, N, d = q.shape
+    if rows is None:
+        o = np.empty((B, H, N, d), dtype=np.float64)
+        lse = np.empty((B, H, N), dtype=np.float64)
+        rows_p, n_rows = None, 0
+    else:
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        if rows.ndim != 2 or rows.shape[0] != B * H:
+            raise ValueError(f"rows must be [B*H, R], got {rows.shape}")
+        n_rows = rows.shape[1]
+        o = np.empty((B * H, n_rows, d), dtype=np.float64)
+        lse = np.empty((B * H, n_rows), dtype=np.float64)
+        rows_p = rows.ctypes.data
+    rc = _load().fa_oracle_fwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, o.ctypes.data, lse.ctypes.data,
+                               B, H, N, d, float(scale), int(bool(causal)), rows_p, n_rows)
+    if rc != 0:
+        raise RuntimeError(f"fa_oracle_fwd failed with code {rc}")
+    return o, lse

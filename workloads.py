@@ -1,0 +1,102 @@
+"""Seeded synthetic attention inputs, shared by the tests, the smoke check and the benchmark.
+
+This module draws random numbers and rounds them to the storage dtype; it holds
+none of the attention arithmetic, so both the GPU path's callers and the CPU
+oracle's callers can use it without sharing any of the computation.
+
+Each workload is a forward-attention problem [B, H, N, d]:
+  q, k, v ~ iid N(0, 1) drawn in fp32 from a CPU torch.Generator seeded with
+  the workload's seed, in the order q, k, v; q and k are multiplied by
+  ``sigma_qk`` (4 for the wide-logit case); then each is rounded to fp16 or
+  bf16 (round to nearest even). The sizing follows the pages' own example
+  ("Decoding flash attention", bibekananda.in: N = 8192 tokens, head dim 128,
+  fp16) and the head counts / lengths listed below.
+  ``scale`` is the fp32 value of 1/sqrt(d).
+  For the large problems parity is checked on a sampled subset of query rows:
+  per (b, h), in order, a generator seeded with ``seed + 1000`` draws
+  randperm(N)[:rows_per_head]; rows 0 and N-1 are forced in (replacing the last
+  draws if absent) and the set is sorted.
+"""
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str          # "f16" or "bf16"
+    causal: bool
+    sigma_qk: float
+    seed: int
+    rows_per_head: Optional[int]   # None: every row is checked
+
+    @property
+    def torch_dtype(self):
+        return torch.float16 if self.dtype == "f16" else torch.bfloat16
+
+    @property
+    def scale(self) -> float:
+        """fp32 value of 1/sqrt(d), returned as a Python float (exact)."""
+        return float(np.float32(1.0 / np.sqrt(self.d)))
+
+    def flops(self) -> float:
+        """Conventional forward flop count 4*B*H*N^2*d, halved when causal."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+
+WORKLOADS = [
+    Workload("B1-H1-N256-d64-f16", 1, 1, 256, 64, "f16", False, 1.0, 1, None),
+    Workload("B4-H16-N2047-d64-bf16", 4, 16, 2047, 64, "bf16", False, 1.0, 2, None),
+    Workload("B1-H32-N8192-d128-f16", 1, 32, 8192, 128, "f16", False, 1.0, 3, 1024),
+    Workload("B2-H16-N8192-d128-bf16-causal", 2, 16, 8192, 128, "bf16", True, 1.0, 4, 1024),
+    Workload("B1-H8-N32768-d128-bf16-causal-qk4", 1, 8, 32768, 128, "bf16", True, 4.0, 5, 1024),
+]
+
+BY_NAME = {w.name: w for w in WORKLOADS}
+
+# The configuration the headline throughput is quoted on.
+HEADLINE = BY_NAME["B1-H32-N8192-d128-f16"]
+
+
+def make_inputs(w: Workload):
+    """(q, k, v) as CPU tensors [B, H, N, d] of the workload's dtype."""
+    g = torch.Generator(device="cpu").manual_seed(w.seed)
+    shape = (w.B, w.H, w.N, w.d)
+    q = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(shape, generator=g, dtype=torch.float32)
+    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    if w.sigma_qk != 1.0:
+        q = q * w.sigma_qk
+        k = k * w.sigma_qk
+    return q.to(w.torch_dtype), k.to(w.torch_dtype), v.to(w.torch_dtype)
+
+
+def custom_inputs(B, H, N, d, dtype, seed, sigma_qk=1.0):
+    """Same recipe as ``make_inputs`` for an arbitrary shape (tests of edge sizes)."""
+    w = Workload("custom", B, H, N, d, dtype, False, sigma_qk, seed, None)
+    return make_inputs(w)
+
+
+def sample_rows(w: Workload):
+    """int64 array [B*H, R] of query rows to check, or None for every row."""
+    if w.rows_per_head is None or w.rows_per_head >= w.N:
+        return None
+    g = torch.Generator(device="cpu").manual_seed(w.seed + 1000)
+    r = w.rows_per_head
+    out = np.empty((w.B * w.H, r), dtype=np.int64)
+    for bh in range(w.B * w.H):
+        rows = torch.randperm(w.N, generator=g)[:r].numpy().copy()
+        if not (rows == 0).any():
+            rows[r - 1] = 0
+        if not (rows == w.N - 1).any():
+            rows[r - 2 if rows[r - 1] == 0 else r - 1] = w.N - 1
+        out[bh] = np.sort(rows)
+    return out
