@@ -1,0 +1,162 @@
+"""Throughput of the attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one fa_fwd call over the whole workload (every query row of every
+head), with q, k, v already resident in device memory. The default workload is
+B=1, H=32, N=8192, d=128, non-causal, fp16. Prints one JSON line.
+
+Algorithmic work per launch: 4*B*H*N^2*d flops (the two products QK^T and PV;
+halved when causal), i.e. 1.0995e12 for the default workload. The roofline
+object prices it against the dense fp16/bf16 matrix-core peak of MI355X
+(256 CUs x 2.4 GHz x 4096 flop/clk = 2516.6 TFLOP/s). ``traffic`` is the
+device-memory bytes per launch measured with rocprofv3 counters (FETCH_SIZE +
+WRITE_SIZE, scaled by the factor a plain copy kernel of known size reads),
+taken from the committed summary in profiles/ when it was measured on the
+current kernel source, else null.
+
+cpu_baseline: the fp64 CPU oracle (test infrastructure) timed on this host on a
+bounded sample of the same workload (the 1024 seeded query rows per head the
+parity test checks), converted to TFLOP/s with the same flop convention.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+PEAK_MFMA_F16_TFLOPS = 2516.6  # 256 CU * 2.4 GHz * 4096 flop/clk/CU, dense fp16/bf16
+KERNEL_SRC = os.path.join(ROOT, "exact_tiled_softmax_fa_amd", "csrc", "fa_fwd.hip")
+KERNEL_NAME = "fa_fwd_kernel"
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload_name: str):
+    """Bytes per launch from the committed counter summary, if it matches this kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{KERNEL_NAME}_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sha256") != kernel_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w):
+    import numpy as np
+    from oracle import core
+
+    q, k, v = workloads.make_inputs(w)
+    rows = workloads.sample_rows(w)
+    if rows is None:
+        rows = np.tile(np.arange(w.N, dtype=np.int64), (w.B * w.H, 1))
+    qd, kd, vd = q.double().numpy(), k.double().numpy(), v.double().numpy()
+    t0 = time.perf_counter()
+    core.attention(qd, kd, vd, w.scale, w.causal, rows)
+    dt = time.perf_counter() - t0
+    keys = (rows + 1).sum() if w.causal else rows.size * w.N
+    flops = 4.0 * w.d * float(keys)
+    # the conventional count halves the causal pair count; scale the sample the same way
+    conv = flops * (w.flops() / (4.0 * w.d * (w.B * w.H * w.N * (w.N + 1) / 2 if w.causal else w.B * w.H * w.N * w.N)))
+    return {
+        "value": conv / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": core.threads(),
+        "kind": "oracle",
+        "sample": f"{rows.shape[1]} seeded query rows per head x {rows.shape[0]} heads of {w.name} "
+                  f"({rows.size} rows, {dt:.2f} s, fp64 three-pass)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=workloads.HEADLINE.name, choices=sorted(workloads.BY_NAME))
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the forward pass shards over heads with no communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_tiled_softmax_fa_amd as fa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = workloads.BY_NAME[args.workload]
+    q, k, v = (t.cuda() for t in workloads.make_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+
+    def step():
+        fa.forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = e0.elapsed_time(e1) / args.steps  # average launch duration on the kernel's stream
+
+    flops = w.flops()
+    value = flops / (wall / args.steps) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    out = {
+        "metric": "fwd attention TFLOP/s and % MFMA peak at B1 H32 N8192 d128 (fp16)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "pct_mfma_peak": round(100.0 * value / PEAK_MFMA_F16_TFLOPS, 2),
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "global_batch": w.B, "seq_len": w.N, "parallelism": "none"},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_MFMA_F16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_MFMA_F16_TFLOPS, 4),
+            "traffic": measured_traffic(w.name),
+            "kernel": KERNEL_NAME,
+            "kernel_ms": round(kernel_ms, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,116 @@
+"""Exact tiled-softmax attention forward on MI355X (gfx950): Python binding.
+
+A thin ctypes layer over the C ABI declared in ``include/fa_fwd.h``
+(``libfa_fwd.so``, built from ``csrc/fa_fwd.hip``). It only marshals
+arguments: shapes, dtypes, device pointers and torch's current HIP stream.
+Every step of the computation runs in the HIP kernel. PyTorch supplies device
+memory and streams.
+
+    o, lse = forward(q, k, v, causal=False, scale=None)
+
+q, k, v: contiguous CUDA (HIP) tensors [B, H, N, d], float16 or bfloat16,
+d in {64, 128}. Returns o (same shape and dtype) and lse ([B, H, N] float32,
+natural log of each row's softmax denominator). There is no CPU fallback: if
+the library is missing or the tensors are not on the GPU, the call raises.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+from . import build as _build
+
+FA_F16 = 0
+FA_BF16 = 1
+_DTYPES = {torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    """A non-zero status returned by the C library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"fa_fwd failed with status {status}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _build.LIB
+
+
+def lib():
+    """The loaded C library. Loaded after torch so that it binds to the HIP runtime
+    torch already has in the process (both carry the soname libamdhip64.so.7)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            raise ImportError(
+                f"{_build.LIB} is not built; run `python -m exact_tiled_softmax_fa_amd.build` "
+                "(or __graft_entry__.build()) first. There is no fallback path.")
+        L = ctypes.CDLL(_build.LIB)
+        L.fa_fwd.restype = ctypes.c_int
+        L.fa_fwd.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+        ]
+        L.fa_status_string.restype = ctypes.c_char_p
+        L.fa_status_string.argtypes = [ctypes.c_int]
+        L.fa_version.restype = ctypes.c_int
+        L.fa_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().fa_status_string(int(status)).decode()
+
+
+def default_scale(d: int) -> float:
+    """fp32 value of 1/sqrt(d)."""
+    return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype) -> int:
+    """Raw call of the C entry point with integer pointers; returns the status code."""
+    return int(lib().fa_fwd(q, k, v, o, lse, B, H, N, d, float(scale), int(causal), stream, int(dtype)))
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale=None,
+            out: torch.Tensor = None, lse: torch.Tensor = None, return_lse: bool = True):
+    """Attention forward on the current stream of q's device. See the module docstring."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, N, d], got shape {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.shape != k.shape or q.shape != v.shape:
+        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+    if q.dtype != k.dtype or q.dtype != v.dtype or q.dtype not in _DTYPES:
+        raise ValueError(f"q, k, v must all be float16 or all bfloat16, got {q.dtype} {k.dtype} {v.dtype}")
+    if q.device != k.device or q.device != v.device:
+        raise ValueError("q, k, v must be on one device")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = default_scale(d)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, N] on q's device")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                    lse.data_ptr() if lse is not None else None,
+                    B, H, N, d, scale, causal, stream, _DTYPES[q.dtype])
+    if st != 0:
+        raise FaError(st, status_string(st))
+    return (out, lse) if return_lse else out

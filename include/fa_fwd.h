@@ -1,0 +1,94 @@
+/*
+ * fa_fwd.h -- exact tiled-softmax attention forward pass on MI355X (gfx950).
+ *
+ * The operation: for every batch b, head h and query row i,
+ *     s_ij   = scale * (q_i . k_j)                 over the allowed keys j
+ *     o_i    = sum_j softmax_j(s_i) v_j
+ *     lse_i  = ln sum_j exp(s_ij)                  (the per-row log-sum-exp)
+ * i.e. O = softmax(Q K^T * scale) V, as defined on "FlashAttention tiles exact
+ * softmax without materializing the score matrix" (nalar.dev, opening
+ * definition) and, per query, on "transformer math: flash attention math"
+ * (aicassindra.com, section "What we must compute, and why storage is the
+ * problem"). The library evaluates it tile by tile with the online-softmax
+ * recurrence (running max, running denominator, unnormalised accumulator,
+ * rescale factor exp(m_old - m_new)) so the N x N score and probability
+ * matrices never reach device memory (same aicassindra.com page, "The
+ * block-wise update, and the full algorithm"). lse is the compact per-row
+ * statistic a backward pass recomputes from ("Decoding flash attention",
+ * bibekananda.in, section "The backward pass").
+ *
+ * Allowed keys: every j in [0, N), or only j <= i when causal != 0 (square,
+ * top-left aligned; nalar.dev, "Causal masking fits inside the tiled
+ * computation"). Every row keeps at least key 0, so no row is empty.
+ */
+#ifndef FA_FWD_H
+#define FA_FWD_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and o. */
+typedef enum fa_dtype {
+    FA_F16 = 0,  /* IEEE binary16 */
+    FA_BF16 = 1  /* bfloat16 */
+} fa_dtype;
+
+/* Return codes. Every code except FA_ERR_LAUNCH is returned before any device
+ * work is enqueued, and nothing is written. */
+typedef enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,      /* q, k, v or o is NULL */
+    FA_ERR_SHAPE = 2,     /* B, H or N < 1, or a size beyond the limits below */
+    FA_ERR_HEAD_DIM = 3,  /* d is not 64 or 128 */
+    FA_ERR_DTYPE = 4,     /* dtype is not FA_F16 or FA_BF16 */
+    FA_ERR_ALIGN = 5,     /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
+    FA_ERR_SCALE = 6,     /* scale is not finite and > 0 */
+    FA_ERR_ALIAS = 7,     /* o or lse overlaps an input, or o overlaps lse */
+    FA_ERR_LAUNCH = 8     /* the kernel launch failed (hipGetLastError) */
+} fa_status;
+
+/*
+ * fa_fwd -- enqueue the attention forward pass on `stream`.
+ *
+ * q, k, v : device pointers, contiguous row-major [B, H, N, d] of `dtype`.
+ * o       : device pointer, contiguous [B, H, N, d] of `dtype`; receives the
+ *           output rounded to nearest-even from fp32.
+ * lse     : device pointer, contiguous [B, H, N] fp32, or NULL to skip it;
+ *           receives ln sum_j exp(s_ij) in natural-log units.
+ * B, H, N : batch, heads, sequence length (queries = keys = N). Each >= 1,
+ *           B*H*ceil(N/128) <= 2^31 - 1 and N <= 2^30.
+ * d       : head dimension, 64 or 128.
+ * scale   : logit multiplier (1/sqrt(d) is the usual choice); finite, > 0.
+ * causal  : non-zero excludes key j from query i when j > i.
+ * stream  : HIP stream (0 = the null stream). The call only enqueues work and
+ *           returns; the caller synchronises.
+ * dtype   : an fa_dtype value (the element type cannot be read off a void*).
+ *
+ * Ownership: the caller allocates and frees every buffer; the library
+ * allocates nothing, keeps no state between calls and uses no workspace, so
+ * calls are re-entrant and thread-safe. o and lse must not overlap q, k, v
+ * or each other. Numerics: products accumulate in fp32 on the matrix cores;
+ * the probabilities are rounded to `dtype` as the second product's operand;
+ * the running statistics are fp32.
+ * Errors: see fa_status. Device faults surface at the caller's next
+ * synchronisation.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int64_t B, int64_t H, int64_t N, int64_t d,
+           float scale, int causal, hipStream_t stream, int dtype);
+
+/* Static, NUL-terminated description of a return code (never NULL). */
+const char* fa_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_FWD_H */

@@ -1,0 +1,103 @@
+"""The C-ABI library without a GPU: it loads, exports what include/fa_fwd.h declares,
+and rejects bad arguments synchronously, before any device work.
+
+Pointers passed here are never dereferenced: each call fails validation first.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_fwd.h")
+PKG = os.path.join(ROOT, "exact_tiled_softmax_fa_amd")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import exact_tiled_softmax_fa_amd as fa
+    return fa.lib()
+
+
+def test_header_declares_the_entry_points():
+    assert _declared_functions() == ["fa_fwd", "fa_status_string", "fa_version"]
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_exported_symbols_match_with_nm():
+    import subprocess
+    import exact_tiled_softmax_fa_amd as fa
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (fa_\w+)$", out, flags=re.M))
+    assert set(_declared_functions()) <= exported
+
+
+def test_status_strings(L):
+    for st in range(0, 9):
+        s = L.fa_status_string(st)
+        assert s and s != b"unknown status"
+    assert L.fa_status_string(99) == b"unknown status"
+    assert L.fa_status_string(0) == b"ok"
+    assert L.fa_version() >= 100
+
+
+# Fake, well-aligned device addresses; validation fails before any of them is used.
+QA, KA, VA, OA, LA = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+GOOD = dict(q=QA, k=KA, v=VA, o=OA, lse=LA, B=1, H=2, N=64, d=64, scale=0.125, causal=0, stream=None, dtype=0)
+
+
+def _call(L, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    import exact_tiled_softmax_fa_amd as fa
+    return fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                     a["causal"], a["stream"], a["dtype"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1),
+    (dict(B=0), 2), (dict(H=0), 2), (dict(N=0), 2), (dict(N=-5), 2), (dict(N=(1 << 30) + 1), 2),
+    (dict(B=1 << 20, H=1 << 20, N=1 << 20), 2),
+    (dict(d=0), 3), (dict(d=32), 3), (dict(d=96), 3), (dict(d=256), 3),
+    (dict(dtype=2), 4), (dict(dtype=-1), 4),
+    (dict(q=QA + 8), 5), (dict(k=KA + 2), 5), (dict(v=VA + 4), 5), (dict(o=OA + 12), 5), (dict(lse=LA + 2), 5),
+    (dict(scale=0.0), 6), (dict(scale=-0.125), 6), (dict(scale=float("inf")), 6), (dict(scale=float("nan")), 6),
+    (dict(o=QA), 7), (dict(o=KA + 16), 7), (dict(lse=VA + 64), 7), (dict(lse=OA), 7),
+])
+def test_argument_errors(L, kw, code):
+    assert _call(L, **kw) == code
+
+
+def test_product_path_never_touches_the_oracle():
+    """The GPU library and its binding share no code with the oracle and never load it."""
+    for dirpath, _, files in os.walk(PKG):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp", ".c")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"\boracle\b", text), f"{f} mentions the oracle"
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        assert "oracle" not in open(os.path.join(ROOT, "include", f)).read()
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith((".py", ".c")):
+            text = open(os.path.join(ROOT, "oracle", f)).read()
+            assert "exact_tiled_softmax_fa_amd" not in text and "fa_fwd.h" not in text, f
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    import exact_tiled_softmax_fa_amd as fa
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q)
