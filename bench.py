@@ -87,6 +87,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=workloads.HEADLINE.name, choices=sorted(workloads.BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--copy-ref-mib", type=int, default=0,
+                    help="before timing, run 3 plain device copies of this many MiB (a known-size "
+                         "reference for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -104,6 +107,14 @@ def main():
     q, k, v = (t.cuda() for t in workloads.make_inputs(w))
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+
+    if args.copy_ref_mib > 0:
+        src = torch.empty(args.copy_ref_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         fa.forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
