@@ -43,6 +43,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -124,20 +125,38 @@ __device__ __forceinline__ void map_block(int bid, int G, int n_qt, bool causal,
     qt = causal ? n_qt - 1 - bid % n_qt : bid % n_qt;
 }
 
+// K and V tiles live in LDS as kBlockN rows of D elements (no padding); the 16-byte chunk c of
+// row r is stored at chunk position c ^ swz(r). Both read patterns are then free of bank
+// conflicts: the K operand reads one chunk from each of 16 consecutive rows, and the V^T
+// transpose read takes 4 consecutive chunks from each of 4 consecutive rows.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);  // 16 chunks per row
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);              // 8 chunks per row
+}
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int c) {  // element offset of (row, chunk)
+    return r * D + ((c ^ swz<D>(r)) << 3);
+}
+
 template <int D, bool BF16, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void fa_fwd_kernel(
+__global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qt, int G, float c, float tau_raw) {
-    constexpr int KS = D + 8;            // K row stride in LDS (elements)
-    constexpr int VS = D + 16;           // V row stride in LDS (elements)
-    constexpr int DK = D / 16;           // k-steps of the first product
-    constexpr int DB = D / 32;           // 32-column blocks of the output
-    constexpr int CH = D / 8;            // 16-byte chunks per row
-    constexpr int LD = kBlockN * CH / kThreads;  // 16-byte loads per thread per K (or V) tile
-    static_assert(LD * kThreads == kBlockN * CH, "tile must split evenly over the threads");
+    constexpr int DK = D / 16;                 // k-steps of the first product
+    constexpr int DB = D / 32;                 // 32-column blocks of the output
+    constexpr int CPR = D / 8;                 // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;              // rows one wave-wide 1 KiB load covers
+    constexpr int IPW = kBlockN / RPI / kWaves;  // such loads per wave per tile (each of K, V)
+    constexpr int TILE = kBlockN * D;          // elements per tile
+    static_assert(IPW * RPI * kWaves == kBlockN, "tile must split evenly over the waves");
 
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[kBlockN * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[kBlockN * VS];
+    // Two buffers each for K and V: tile j is read from buffer j % 2 while tile j + 1 streams
+    // into the other one straight from global memory (global_load_lds, no register staging).
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -155,6 +174,27 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(
     const int wq0 = q0 + 32 * wave;  // first query row of this wave
     const int qrow = wq0 + lq;       // this lane's query row
 
+    const int kv_end = CAUSAL ? min(N, q0 + kBlockM) : N;
+    const int n_kv = (kv_end + kBlockN - 1) / kBlockN;
+
+    // Wave w fills loads w*IPW .. w*IPW+IPW-1 of a tile; load g covers rows RPI*g .. RPI*g+RPI-1
+    // and lane l writes LDS bytes [1024 g + 16 l, +16), i.e. row RPI*g + l/CPR at chunk position
+    // l % CPR, which holds global chunk (l % CPR) ^ swz(row). Rows past the end of the sequence
+    // repeat row N-1 (finite data; those keys are masked before they can carry weight).
+    auto issue = [&](int j, uint16_t* kdst, uint16_t* vdst) {
+        const int k0 = j * kBlockN;
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const int g = wave * IPW + i;
+            const int r = RPI * g + lane / CPR;
+            const int ch = (lane % CPR) ^ swz<D>(r);
+            const int64_t src = (int64_t)min(k0 + r, N - 1) * D + 8 * ch;
+            __builtin_amdgcn_global_load_lds((const void*)(Kh + src), (lds_void*)(kdst + g * 512), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(Vh + src), (lds_void*)(vdst + g * 512), 16, 0, 0);
+        }
+    };
+    issue(0, k_lds0, v_lds0);
+
     // Q^T fragment (B operand of the first product): lane holds row qrow, columns
     // 16t + 8h .. 16t + 8h + 7 for every k-step t. Rows past N are zero.
     u32x4 qf[DK];
@@ -164,54 +204,25 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(
         if (qrow < N) qf[t] = *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow * D + 16 * t + 8 * h);
     }
 
-    const int kv_end = CAUSAL ? min(N, q0 + kBlockM) : N;
-    const int n_kv = (kv_end + kBlockN - 1) / kBlockN;
-
-    u32x4 kpre[LD], vpre[LD];
-    auto gload = [&](int j) {
-#pragma unroll
-        for (int r = 0; r < LD; ++r) {
-            const int ch = tid + kThreads * r;
-            const int row = ch / CH, col = ch % CH;
-            const int key = j * kBlockN + row;
-            kpre[r] = (u32x4){0u, 0u, 0u, 0u};
-            vpre[r] = (u32x4){0u, 0u, 0u, 0u};
-            if (key < N) {
-                kpre[r] = *reinterpret_cast<const u32x4*>(Kh + (int64_t)key * D + col * 8);
-                vpre[r] = *reinterpret_cast<const u32x4*>(Vh + (int64_t)key * D + col * 8);
-            }
-        }
-    };
-    gload(0);
-
     f32x16 oacc[DB];
 #pragma unroll
     for (int b = 0; b < DB; ++b) oacc[b] = (f32x16){};
-    float m_run = -INFINITY;  // running max of raw dot products (reference of l and oacc)
+    float m_run = -INFINITY;  // reference max of raw dot products for l and oacc
     float l_run = 0.f;        // this lane's half of the running denominator (rounded p)
     float l_f32 = 0.f;        // the same sum of unrounded p: bf16 keeps 8 mantissa bits, too few
                               // for lse to 1e-3 on rows with few keys, so lse uses this one
 
-    // ds_read_b64_tr_b16 source address pattern: within each 16-lane group, lane s reads
-    // 4 consecutive columns 4*(s%4).. of key row s/4; the instruction hands lane i element e
-    // of the 4x16 block as (key row e, column i), i.e. one V^T row of 4 keys per lane.
-    const int tr_row = 4 * h + ((lane & 15) >> 2);
-    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // ds_read_b64_tr_b16 source pattern: within each 16-lane group, lane s reads 4 consecutive
+    // columns 4*(s%4).. of key row s/4; the instruction hands lane i element e of that 4x16
+    // block as (key row e, column i), i.e. one V^T row of 4 keys per lane.
+    const int s16 = lane & 15;
+    const int tr_row = 4 * h + (s16 >> 2);                       // + key0 (+8 for the upper 4)
+    const int tr_chunk = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);  // + 4*b
+    const int tr_half = 4 * (s16 & 1);                          // element offset in the chunk
 
-    for (int j = 0; j < n_kv; ++j) {
-        __syncthreads();  // every wave is done reading the previous tile
-#pragma unroll
-        for (int r = 0; r < LD; ++r) {
-            const int ch = tid + kThreads * r;
-            const int row = ch / CH, col = ch % CH;
-            *reinterpret_cast<u32x4*>(&k_lds[row * KS + col * 8]) = kpre[r];
-            *reinterpret_cast<u32x4*>(&v_lds[row * VS + col * 8]) = vpre[r];
-        }
-        __syncthreads();
-        if (j + 1 < n_kv) gload(j + 1);
-
+    auto compute = [&](int j, const uint16_t* kt, const uint16_t* vt) {
         const int k0 = j * kBlockN;
-        if (CAUSAL && k0 > wq0 + 31) continue;  // tile lies wholly above the diagonal for this wave
+        if (CAUSAL && k0 > wq0 + 31) return;  // tile lies wholly above the diagonal for this wave
 
         // ---- S^T = K . Q^T (raw dot products) ----
         f32x16 sacc[2];
@@ -220,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(
             sacc[kb] = (f32x16){};
 #pragma unroll
             for (int t = 0; t < DK; ++t) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(&k_lds[(kb * 32 + lq) * KS + 16 * t + 8 * h]);
+                const u32x4 a = *reinterpret_cast<const u32x4*>(kt + tile_off<D>(kb * 32 + lq, 2 * t + h));
                 sacc[kb] = mfma32<BF16>(a, qf[t], sacc[kb]);
             }
         }
@@ -237,16 +248,16 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(
                 }
         }
 
-        // ---- running max; rescale only when some row of the wave needs it ----
-        float mx = sacc[0][0];
+        // ---- reference max: move it (and rescale l, o~ by alpha) only when some row of the
+        //      wave has a score more than tau above it; otherwise p <= 2^tau_log2 ----
+        float mx = fmaxf(sacc[0][0], sacc[0][1]);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
         mx = max_with_partner(mx);
-        const bool upd = mx > m_run + tau_raw;
-        if (__builtin_amdgcn_ballot_w64(upd)) {
-            const float m_new = upd ? mx : m_run;
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + tau_raw)) {
+            const float m_new = fmaxf(m_run, mx);
             const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
             l_run *= alpha;
             if constexpr (BF16) l_f32 *= alpha;
@@ -279,8 +290,9 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(
             const int key0 = kb * 32 + 16 * hf;
 #pragma unroll
             for (int b = 0; b < DB; ++b) {
-                const uint16_t* p_lo = &v_lds[(key0 + tr_row) * VS + b * 32 + tr_col];
-                const uint16_t* p_hi = p_lo + 8 * VS;
+                const int r_lo = key0 + tr_row, r_hi = r_lo + 8;
+                const uint16_t* p_lo = vt + tile_off<D>(r_lo, 4 * b + tr_chunk) + tr_half;
+                const uint16_t* p_hi = vt + tile_off<D>(r_hi, 4 * b + tr_chunk) + tr_half;
                 const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p_lo));
                 const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p_hi));
                 const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
@@ -289,6 +301,20 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(
                 oacc[b] = mfma32<BF16>(aop, bop, oacc[b]);
             }
         }
+    };
+
+    // One barrier per tile: after it, tile j is in LDS for every wave and every wave has finished
+    // tile j - 1, so the buffer tile j - 1 used can take tile j + 1.
+    for (int j = 0; j < n_kv; j += 2) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (j + 1 < n_kv) issue(j + 1, k_lds1, v_lds1);
+        compute(j, k_lds0, v_lds0);
+        if (j + 1 >= n_kv) break;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (j + 2 < n_kv) issue(j + 2, k_lds0, v_lds0);
+        compute(j + 1, k_lds1, v_lds1);
     }
 
     // ---- epilogue: O = o~ / l, lse = m*scale + ln l ----
@@ -371,7 +397,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
         return FA_ERR_ALIAS;
 
     const float c = scale * 1.4426950408889634f;  // scale * log2(e)
-    const float tau_raw = 0.f;                    // rescale whenever a row's max rises
+    // The reference max moves only when a score exceeds it by more than 8 in log2 units, so the
+    // unnormalised p stay <= 2^8 (exact in f16/bf16 range) and most tiles skip the rescale.
+    const float tau_raw = 8.f / c;
     const int n = static_cast<int>(N), nq = static_cast<int>(n_qt), g = static_cast<int>(G);
     const bool bf = dtype == FA_BF16;
     hipError_t e;
