@@ -45,9 +45,9 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;             // two groups of 4; each SIMD runs one wave of each group
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBlockM = 32 * kWaves;  // query rows per workgroup
+constexpr int kBlockM = 32 * kWaves;  // query rows per workgroup (32 per wave)
 constexpr int kBlockN = 64;           // keys per tile
 constexpr int kXcds = 8;              // MI355X: workgroups are dealt round-robin to 8 XCDs
 
@@ -140,7 +140,7 @@ __device__ __forceinline__ int tile_off(int r, int c) {  // element offset of (r
 }
 
 template <int D, bool BF16, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qt, int G, float c, float tau_raw) {
     constexpr int DK = D / 16;                 // k-steps of the first product
@@ -149,14 +149,19 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(
     constexpr int RPI = 64 / CPR;              // rows one wave-wide 1 KiB load covers
     constexpr int IPW = kBlockN / RPI / kWaves;  // such loads per wave per tile (each of K, V)
     constexpr int TILE = kBlockN * D;          // elements per tile
-    static_assert(IPW * RPI * kWaves == kBlockN, "tile must split evenly over the waves");
+    static_assert(IPW >= 1 && IPW * RPI * kWaves == kBlockN, "tile must split evenly over the waves");
 
-    // Two buffers each for K and V: tile j is read from buffer j % 2 while tile j + 1 streams
-    // into the other one straight from global memory (global_load_lds, no register staging).
-    __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[TILE];
+    // Two buffers each for K and V, and the Q rows of the workgroup (each wave's 32 rows), all
+    // filled straight from global memory (global_load_lds) in the same swizzled layout. The
+    // K and V buffers come first so that every K/V operand address is a per-lane register plus
+    // an immediate below 64 KiB (the ds_read offset field).
+    // (Separate arrays let the compiler see that the loads into one buffer never alias the
+    // reads of another; the larger alignment of the K/V buffers places them first.)
+    __shared__ __attribute__((aligned(4096))) uint16_t k_lds0[TILE];
+    __shared__ __attribute__((aligned(4096))) uint16_t k_lds1[TILE];
+    __shared__ __attribute__((aligned(4096))) uint16_t v_lds0[TILE];
+    __shared__ __attribute__((aligned(4096))) uint16_t v_lds1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t q_lds[kBlockM * D];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -175,87 +180,137 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(
     const int qrow = wq0 + lq;       // this lane's query row
 
     const int kv_end = CAUSAL ? min(N, q0 + kBlockM) : N;
-    const int n_kv = (kv_end + kBlockN - 1) / kBlockN;
+    const int T = (kv_end + kBlockN - 1) / kBlockN;  // key tiles this workgroup visits
+    // tiles this wave computes: causal waves stop at the tile holding their last row
+    const int T_w = CAUSAL ? min(T, (min(wq0 + 32, N) + kBlockN - 1) / kBlockN) : T;
 
-    // Wave w fills loads w*IPW .. w*IPW+IPW-1 of a tile; load g covers rows RPI*g .. RPI*g+RPI-1
-    // and lane l writes LDS bytes [1024 g + 16 l, +16), i.e. row RPI*g + l/CPR at chunk position
-    // l % CPR, which holds global chunk (l % CPR) ^ swz(row). Rows past the end of the sequence
-    // repeat row N-1 (finite data; those keys are masked before they can carry weight).
-    auto issue = [&](int j, uint16_t* kdst, uint16_t* vdst) {
+    // Load g of a tile covers rows RPI*g .. RPI*g+RPI-1; lane l writes LDS bytes [1024 g + 16 l,
+    // +16), i.e. row RPI*g + l/CPR at chunk position l % CPR, which holds global chunk
+    // (l % CPR) ^ swz(row). Rows past the end of the sequence repeat row N-1 (finite data; those
+    // keys are masked before they can carry weight).
+    // Offsets inside one head fit in 32 bits (the host limits N * d * 2 bytes to < 2^31).
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // scalar copy for LDS destinations
+    auto issue = [&](const uint16_t* src_head, int j, uint16_t* dst) __attribute__((always_inline)) {
         const int k0 = j * kBlockN;
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
-            const int g = wave * IPW + i;
+            const int g = wave_s * IPW + i;
             const int r = RPI * g + lane / CPR;
             const int ch = (lane % CPR) ^ swz<D>(r);
-            const int64_t src = (int64_t)min(k0 + r, N - 1) * D + 8 * ch;
-            __builtin_amdgcn_global_load_lds((const void*)(Kh + src), (lds_void*)(kdst + g * 512), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(Vh + src), (lds_void*)(vdst + g * 512), 16, 0, 0);
+            const unsigned src = (unsigned)min(k0 + r, N - 1) * D + 8 * ch;
+            __builtin_amdgcn_global_load_lds((const void*)(src_head + src), (lds_void*)(dst + g * 512), 16, 0, 0);
         }
     };
-    issue(0, k_lds0, v_lds0);
 
-    // Q^T fragment (B operand of the first product): lane holds row qrow, columns
-    // 16t + 8h .. 16t + 8h + 7 for every k-step t. Rows past N are zero.
-    u32x4 qf[DK];
+    // This wave's 32 query rows go to q_lds rows 32*wave.. (the B operand of the first product
+    // is read from there each tile, which keeps 32 VGPRs free). Rows past N repeat row N-1;
+    // they are never stored.
+    {
+        constexpr int QPW = 32 / RPI;  // 1 KiB loads per wave for 32 rows
 #pragma unroll
-    for (int t = 0; t < DK; ++t) {
-        qf[t] = (u32x4){0u, 0u, 0u, 0u};
-        if (qrow < N) qf[t] = *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow * D + 16 * t + 8 * h);
+        for (int i = 0; i < QPW; ++i) {
+            const int r = RPI * i + lane / CPR;  // row within the wave's 32
+            const int ch = (lane % CPR) ^ swz<D>(r);
+            const unsigned src = (unsigned)min(wq0 + r, N - 1) * D + 8 * ch;
+            __builtin_amdgcn_global_load_lds((const void*)(Qh + src), (lds_void*)(q_lds + (32 * wave + RPI * i) * D), 16, 0, 0);
+        }
     }
+    const uint16_t* q_wave = q_lds + 32 * wave * D;
 
     f32x16 oacc[DB];
 #pragma unroll
     for (int b = 0; b < DB; ++b) oacc[b] = (f32x16){};
+    unsigned pk[2][8];        // P^T of the tile between its softmax and its product with V
     float m_run = -INFINITY;  // reference max of raw dot products for l and oacc
     float l_run = 0.f;        // this lane's half of the running denominator (rounded p)
     float l_f32 = 0.f;        // the same sum of unrounded p: bf16 keeps 8 mantissa bits, too few
                               // for lse to 1e-3 on rows with few keys, so lse uses this one
 
+    // LDS operand addresses (elements). The swizzle depends on row & 15 only, so moving 16 rows
+    // down a tile is the constant offset 16*D: one address per k-step serves both 32-key halves
+    // of the K tile, and one per column block serves all four 16-key steps of the V tile.
+    int koff[DK];
+#pragma unroll
+    for (int t = 0; t < DK; ++t) koff[t] = tile_off<D>(lq, 2 * t + h);
     // ds_read_b64_tr_b16 source pattern: within each 16-lane group, lane s reads 4 consecutive
     // columns 4*(s%4).. of key row s/4; the instruction hands lane i element e of that 4x16
-    // block as (key row e, column i), i.e. one V^T row of 4 keys per lane.
-    const int s16 = lane & 15;
-    const int tr_row = 4 * h + (s16 >> 2);                       // + key0 (+8 for the upper 4)
-    const int tr_chunk = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);  // + 4*b
-    const int tr_half = 4 * (s16 & 1);                          // element offset in the chunk
-
-    auto compute = [&](int j, const uint16_t* kt, const uint16_t* vt) {
-        const int k0 = j * kBlockN;
-        if (CAUSAL && k0 > wq0 + 31) return;  // tile lies wholly above the diagonal for this wave
-
-        // ---- S^T = K . Q^T (raw dot products) ----
-        f32x16 sacc[2];
+    // block as (key row e, column i), i.e. one V^T row of 4 keys per lane. The upper 4 keys of
+    // each 8 come from rows + 8.
+    int voff_lo[DB], voff_hi[DB];
+    {
+        const int s16 = lane & 15;
+        const int tr_row = 4 * h + (s16 >> 2);
+        const int tr_chunk = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
+        const int tr_half = 4 * (s16 & 1);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            sacc[kb] = (f32x16){};
-#pragma unroll
-            for (int t = 0; t < DK; ++t) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(kt + tile_off<D>(kb * 32 + lq, 2 * t + h));
-                sacc[kb] = mfma32<BF16>(a, qf[t], sacc[kb]);
-            }
+        for (int b = 0; b < DB; ++b) {
+            voff_lo[b] = tile_off<D>(tr_row, 4 * b + tr_chunk) + tr_half;
+            voff_hi[b] = tile_off<D>(tr_row + 8, 4 * b + tr_chunk) + tr_half;
         }
+    }
+    auto k_operand = [&](const uint16_t* kt, int t, int kb) __attribute__((always_inline)) {
+        return *reinterpret_cast<const u32x4*>(kt + koff[t] + kb * 32 * D);
+    };
+    auto v_operand = [&](const uint16_t* vt, int kk, int b) __attribute__((always_inline)) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + voff_lo[b] + kk * 16 * D));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + voff_hi[b] + kk * 16 * D));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+        return (u32x4){lo2[0], lo2[1], hi2[0], hi2[1]};
+    };
+    // Q^T (B operand of the first product): lane holds row qrow, columns 16t + 8h .. +7.
+    auto q_operand = [&](int t) __attribute__((always_inline)) {
+        return *reinterpret_cast<const u32x4*>(q_wave + koff[t]);
+    };
+    auto p_operand = [&](int kk) __attribute__((always_inline)) {
+        const int kb = kk >> 1, hf = kk & 1;
+        return (u32x4){pk[kb][4 * hf + 0], pk[kb][4 * hf + 1], pk[kb][4 * hf + 2], pk[kb][4 * hf + 3]};
+    };
 
-        // ---- mask: keys past the end, and (causal) keys after the query ----
-        const bool need_mask = (k0 + kBlockN > N) || (CAUSAL && k0 + kBlockN - 1 > wq0);
-        if (need_mask) {
+    // ---- the pieces of one tile's work ----
+    f32x16 s0[2], s1[2];  // S^T of two consecutive tiles: one being produced, one being consumed
+    float mc = 0.f;       // m_run * c with m_run the current reference (0 while m_run = -inf)
+
+    // S^T(t) = K(t) . Q^T into s (16 MFMAs for D = 128; K and Q operands from LDS)
+    auto qk = [&](const uint16_t* kt, f32x16 (&sd)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 2 * DK; ++i) {
+            const int t = i >> 1, kb = i & 1;
+            sd[kb] = mfma32<BF16>(k_operand(kt, t, kb), q_operand(t), t == 0 ? (f32x16){} : sd[kb]);
+        }
+    };
+    // O^T += V(t)^T . P^T (16 MFMAs for D = 128; V^T operand from LDS transpose reads)
+    auto pv = [&](const uint16_t* vt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4 * DB; ++i) {
+            const int kk = i / DB, b = i % DB;
+            oacc[b] = mfma32<BF16>(v_operand(vt, kk, b), p_operand(kk), oacc[b]);
+        }
+    };
+    // keys past the end, and (causal) keys after the query, become -inf before the max
+    auto mask = [&](int t, f32x16 (&sd)[2]) __attribute__((always_inline)) {
+        const int k0 = t * kBlockN;
+        if ((k0 + kBlockN > N) || (CAUSAL && k0 + kBlockN - 1 > wq0)) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    if (key >= N || (CAUSAL && key > qrow)) sacc[kb][r] = -INFINITY;
+                    if (key >= N || (CAUSAL && key > qrow)) sd[kb][r] = -INFINITY;
                 }
         }
-
-        // ---- reference max: move it (and rescale l, o~ by alpha) only when some row of the
-        //      wave has a score more than tau above it; otherwise p <= 2^tau_log2 ----
-        float mx = fmaxf(sacc[0][0], sacc[0][1]);
+    };
+    auto row_max = [&](const f32x16 (&sd)[2]) __attribute__((always_inline)) {
+        float mx = fmaxf(sd[0][0], sd[0][1]);
 #pragma unroll
-        for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
+        for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sd[0][r]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
-        mx = max_with_partner(mx);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sd[1][r]);
+        return max_with_partner(mx);
+    };
+    // Move the reference max (and rescale l, o~ by alpha = exp(m_old - m_new)) only when some row
+    // of the wave has a score more than tau above it; otherwise p stays <= 2^tau_log2.
+    auto rebase = [&](float mx) __attribute__((always_inline)) {
         if (__builtin_amdgcn_ballot_w64(mx > m_run + tau_raw)) {
             const float m_new = fmaxf(m_run, mx);
             const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
@@ -266,55 +321,125 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
             m_run = m_new;
+            mc = (m_run == -INFINITY) ? 0.f : m_run * c;
         }
-        const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-
-        // ---- p = exp2(s*c - m*c), rounded to the operand type; row sum of the rounded values ----
-        unsigned pk[2][8];
+    };
+    // p = exp2(s*c - m*c), rounded to the operand type; row sum of the rounded values
+    auto expo = [&](const f32x16 (&sd)[2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c, -mc));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], c, -mc));
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(sd[kb][r], c, -mc));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(sd[kb][r + 1], c, -mc));
                 pk[kb][r >> 1] = pack2<BF16>(p0, p1);
                 l_run = add_pair<BF16>(pk[kb][r >> 1], l_run);
                 if constexpr (BF16) l_f32 += p0 + p1;
             }
-
-        // ---- O^T += V^T . P^T ----
-#pragma unroll
-        for (int kk = 0; kk < kBlockN / 16; ++kk) {
-            const int kb = kk >> 1, hf = kk & 1;
-            const u32x4 bop = {pk[kb][4 * hf + 0], pk[kb][4 * hf + 1], pk[kb][4 * hf + 2], pk[kb][4 * hf + 3]};
-            const int key0 = kb * 32 + 16 * hf;
-#pragma unroll
-            for (int b = 0; b < DB; ++b) {
-                const int r_lo = key0 + tr_row, r_hi = r_lo + 8;
-                const uint16_t* p_lo = vt + tile_off<D>(r_lo, 4 * b + tr_chunk) + tr_half;
-                const uint16_t* p_hi = vt + tile_off<D>(r_hi, 4 * b + tr_chunk) + tr_half;
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p_lo));
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p_hi));
-                const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
-                const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
-                const u32x4 aop = {lo2[0], lo2[1], hi2[0], hi2[1]};
-                oacc[b] = mfma32<BF16>(aop, bop, oacc[b]);
-            }
-        }
     };
 
-    // One barrier per tile: after it, tile j is in LDS for every wave and every wave has finished
-    // tile j - 1, so the buffer tile j - 1 used can take tile j + 1.
-    for (int j = 0; j < n_kv; j += 2) {
+    // ---- schedule ----
+    // Tile t's K sits in buffer t % 2 and so does its V. Iteration j runs, in each wave:
+    //   region 1: S^T(j+1) = K(j+1) . Q^T on the matrix cores, with the exponentials of tile j
+    //             (S^T(j) -> P^T(j)) interleaved between the MFMAs on the vector ALU;
+    //   region 2: O^T += V(j)^T . P^T(j), with the row max of S^T(j+1) interleaved;
+    //   then the (rare) move of the reference max for tile j+1, after P(j) has been used.
+    // So each wave overlaps its own softmax with its own products, one tile apart. At the top of
+    // iteration j a barrier makes K(j+1) and V(j) visible (loaded during iteration j - 1) and
+    // frees the buffers of K(j) and V(j-1), which then take K(j+2) and V(j+1).
+    issue(Kh, 0, k_lds0);
+    issue(Vh, 0, v_lds0);
+    if (T > 1) issue(Kh, 1, k_lds1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (0 < T_w) {
+        qk(k_lds0, s0);
+        mask(0, s0);
+        rebase(row_max(s0));
+    }
+    auto iteration = [&](int j, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], const uint16_t* k_nxt,
+                         const uint16_t* v_cur, uint16_t* k_load, uint16_t* v_load) __attribute__((always_inline)) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (j + 1 < n_kv) issue(j + 1, k_lds1, v_lds1);
-        compute(j, k_lds0, v_lds0);
-        if (j + 1 >= n_kv) break;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (j + 2 < n_kv) issue(j + 2, k_lds0, v_lds0);
-        compute(j + 1, k_lds1, v_lds1);
+        if (j + 2 < T) issue(Kh, j + 2, k_load);
+        if (j + 1 < T) issue(Vh, j + 1, v_load);
+        if (j + 1 < T_w) {
+            // region 1: S^T(j+1) = K(j+1) . Q^T with the exponentials of tile j in between.
+            // Explicit software pipeline: the LDS operands of MFMA i + 2 are read before MFMA i
+            // issues, and one pair of exponentials follows each MFMA; sched_barrier(0) pins that
+            // order so the LDS latency stays behind two MFMAs instead of stalling every one.
+            constexpr int NQ = 2 * DK;  // 16 MFMAs for D = 128, 8 for D = 64
+            u32x4 ka[NQ], qa[DK];
+            qa[0] = q_operand(0);
+            ka[0] = k_operand(k_nxt, 0, 0);
+            ka[1] = k_operand(k_nxt, 0, 1);
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const int t = i >> 1, kb = i & 1;
+                if (i + 2 < NQ) {
+                    const int t2 = (i + 2) >> 1, kb2 = (i + 2) & 1;
+                    if (kb2 == 0) qa[t2] = q_operand(t2);
+                    ka[i + 2] = k_operand(k_nxt, t2, kb2);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                s_nxt[kb] = mfma32<BF16>(ka[i], qa[t], t == 0 ? (f32x16){} : s_nxt[kb]);
+                __builtin_amdgcn_sched_barrier(0);
+                // exponentials: pair i of the 16 pairs of S^T(j) held by this lane (NQ == 16),
+                // or pairs 2i, 2i+1 when D = 64 (NQ == 8)
+#pragma unroll
+                for (int u = 0; u < 16 / NQ; ++u) {
+                    const int pr = i * (16 / NQ) + u;  // pair index 0..15
+                    const int kbp = pr >> 3, r = 2 * (pr & 7);
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[kbp][r], c, -mc));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[kbp][r + 1], c, -mc));
+                    pk[kbp][r >> 1] = pack2<BF16>(p0, p1);
+                    l_run = add_pair<BF16>(pk[kbp][r >> 1], l_run);
+                    if constexpr (BF16) l_f32 += p0 + p1;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // Keep the exponentials in region 1: without this the compiler sinks them past the
+            // mask branch into region 2, next to their only consumer.
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 8; ++r) asm volatile("" : "+v"(pk[kb][r]));
+            asm volatile("" : "+v"(l_run));
+            if constexpr (BF16) asm volatile("" : "+v"(l_f32));
+            mask(j + 1, s_nxt);
+            // region 2: O^T += V(j)^T . P^T(j) with the row max of S^T(j+1) in between, V^T
+            // operands read two MFMAs ahead.
+            constexpr int NP = 4 * DB;  // 16 MFMAs for D = 128, 8 for D = 64
+            u32x4 va[NP];
+            va[0] = v_operand(v_cur, 0, 0);
+            va[1] = v_operand(v_cur, 1 / DB, 1 % DB);
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const int kk = i / DB, b = i % DB;
+                if (i + 2 < NP) va[i + 2] = v_operand(v_cur, (i + 2) / DB, (i + 2) % DB);
+                __builtin_amdgcn_sched_barrier(0);
+                oacc[b] = mfma32<BF16>(va[i], p_operand(kk), oacc[b]);
+                __builtin_amdgcn_sched_barrier(0);
+                // row max: the 32 scores of this lane, 32 / NP per MFMA
+#pragma unroll
+                for (int u = 0; u < 32 / NP; ++u) {
+                    const int e = i * (32 / NP) + u;
+                    mx = fmaxf(mx, s_nxt[e >> 4][e & 15]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            rebase(max_with_partner(mx));
+        } else if (j < T_w) {
+            expo(s_cur);
+            pv(v_cur);
+        }
+    };
+    for (int j = 0; j < T; j += 2) {
+        // even j: K(j+1) in buffer 1, V(j) in buffer 0; K(j+2) -> buffer 0, V(j+1) -> buffer 1
+        iteration(j, s0, s1, k_lds1, v_lds0, k_lds0, v_lds1);
+        if (j + 1 >= T) break;
+        iteration(j + 1, s1, s0, k_lds0, v_lds1, k_lds1, v_lds0);
     }
 
     // ---- epilogue: O = o~ / l, lse = m*scale + ln l ----
@@ -376,8 +501,9 @@ const char* fa_status_string(int status) {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
            int64_t d, float scale, int causal, hipStream_t stream, int dtype) {
     if (!q || !k || !v || !o) return FA_ERR_NULL;
-    if (B < 1 || H < 1 || N < 1 || N > (int64_t(1) << 30)) return FA_ERR_SHAPE;
+    if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+    if (N * d * 2 > INT32_MAX) return FA_ERR_SHAPE;  // one head of q, k or v stays under 2 GiB
     if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
     const int64_t n_qt = (N + kBlockM - 1) / kBlockM;
     if (B > INT32_MAX || H > INT32_MAX || B * H > INT32_MAX / n_qt) return FA_ERR_SHAPE;

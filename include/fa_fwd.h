@@ -60,7 +60,8 @@ typedef enum fa_status {
  * lse     : device pointer, contiguous [B, H, N] fp32, or NULL to skip it;
  *           receives ln sum_j exp(s_ij) in natural-log units.
  * B, H, N : batch, heads, sequence length (queries = keys = N). Each >= 1,
- *           B*H*ceil(N/128) <= 2^31 - 1 and N <= 2^30.
+ *           B*H*ceil(N/256) <= 2^31 - 1 and N*d*2 < 2^31 (one head of one
+ *           tensor under 2 GiB; N <= 8388607 at d = 128).
  * d       : head dimension, 64 or 128.
  * scale   : logit multiplier (1/sqrt(d) is the usual choice); finite, > 0.
  * causal  : non-zero excludes key j from query i when j > i.

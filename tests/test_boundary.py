@@ -68,7 +68,7 @@ def _call(L, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1),
-    (dict(B=0), 2), (dict(H=0), 2), (dict(N=0), 2), (dict(N=-5), 2), (dict(N=(1 << 30) + 1), 2),
+    (dict(B=0), 2), (dict(H=0), 2), (dict(N=0), 2), (dict(N=-5), 2), (dict(N=(1 << 24), d=128), 2), (dict(N=(1 << 25), d=64), 2),
     (dict(B=1 << 20, H=1 << 20, N=1 << 20), 2),
     (dict(d=0), 3), (dict(d=32), 3), (dict(d=96), 3), (dict(d=256), 3),
     (dict(dtype=2), 4), (dict(dtype=-1), 4),
