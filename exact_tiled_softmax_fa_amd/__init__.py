@@ -28,6 +28,11 @@ _DTYPES = {torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 _lib = None
 
 
+class FaOptions(ctypes.Structure):
+    """Mirror of fa_fwd_options in include/fa_fwd.h."""
+    _fields_ = [("rescale_threshold_log2", ctypes.c_float), ("variant", ctypes.c_int)]
+
+
 class FaError(RuntimeError):
     """A non-zero status returned by the C library."""
 
@@ -56,6 +61,8 @@ def lib():
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
         ]
+        L.fa_fwd_ex.restype = ctypes.c_int
+        L.fa_fwd_ex.argtypes = L.fa_fwd.argtypes + [ctypes.POINTER(FaOptions)]
         L.fa_status_string.restype = ctypes.c_char_p
         L.fa_status_string.argtypes = [ctypes.c_int]
         L.fa_version.restype = ctypes.c_int
@@ -73,14 +80,22 @@ def default_scale(d: int) -> float:
     return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())
 
 
-def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype) -> int:
-    """Raw call of the C entry point with integer pointers; returns the status code."""
-    return int(lib().fa_fwd(q, k, v, o, lse, B, H, N, d, float(scale), int(causal), stream, int(dtype)))
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype, options=None) -> int:
+    """Raw call of the C entry point with integer pointers; returns the status code.
+    options: None (fa_fwd) or an FaOptions (fa_fwd_ex)."""
+    if options is None:
+        return int(lib().fa_fwd(q, k, v, o, lse, B, H, N, d, float(scale), int(causal), stream, int(dtype)))
+    return int(lib().fa_fwd_ex(q, k, v, o, lse, B, H, N, d, float(scale), int(causal), stream, int(dtype),
+                               ctypes.byref(options)))
 
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale=None,
-            out: torch.Tensor = None, lse: torch.Tensor = None, return_lse: bool = True):
-    """Attention forward on the current stream of q's device. See the module docstring."""
+            out: torch.Tensor = None, lse: torch.Tensor = None, return_lse: bool = True,
+            rescale_threshold_log2=None, variant: int = 0):
+    """Attention forward on the current stream of q's device. See the module docstring.
+
+    rescale_threshold_log2 / variant: the fa_fwd_options of include/fa_fwd.h (None and 0 keep the
+    library defaults, i.e. plain fa_fwd)."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
@@ -106,11 +121,14 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
     if lse is not None and (lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous()
                             or lse.device != q.device):
         raise ValueError("lse must be a contiguous float32 tensor [B, H, N] on q's device")
+    options = None
+    if rescale_threshold_log2 is not None or variant != 0:
+        options = FaOptions(8.0 if rescale_threshold_log2 is None else float(rescale_threshold_log2), int(variant))
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                     lse.data_ptr() if lse is not None else None,
-                    B, H, N, d, scale, causal, stream, _DTYPES[q.dtype])
+                    B, H, N, d, scale, causal, stream, _DTYPES[q.dtype], options)
     if st != 0:
         raise FaError(st, status_string(st))
     return (out, lse) if return_lse else out

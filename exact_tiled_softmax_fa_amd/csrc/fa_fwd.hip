@@ -50,6 +50,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBlockM = 32 * kWaves;  // query rows per workgroup (32 per wave)
 constexpr int kBlockN = 64;           // keys per tile
 constexpr int kXcds = 8;              // MI355X: workgroups are dealt round-robin to 8 XCDs
+constexpr float kDefaultRescaleLog2 = 8.f;  // default reference-max threshold (log2 units)
 
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -494,12 +495,13 @@ const char* fa_status_string(int status) {
         case FA_ERR_SCALE: return "scale must be finite and > 0";
         case FA_ERR_ALIAS: return "o and lse must not overlap the inputs or each other";
         case FA_ERR_LAUNCH: return "kernel launch failed";
+        case FA_ERR_OPTION: return "fa_fwd_options out of range (rescale threshold 0..15, variant 0)";
         default: return "unknown status";
     }
 }
 
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
-           int64_t d, float scale, int causal, hipStream_t stream, int dtype) {
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
+              int64_t d, float scale, int causal, hipStream_t stream, int dtype, const fa_fwd_options* opts) {
     if (!q || !k || !v || !o) return FA_ERR_NULL;
     if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
@@ -521,11 +523,18 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     if (lse && (overlaps(lse, lbytes, q, nbytes) || overlaps(lse, lbytes, k, nbytes) ||
                 overlaps(lse, lbytes, v, nbytes) || overlaps(lse, lbytes, o, nbytes)))
         return FA_ERR_ALIAS;
+    // The reference max moves only when a score exceeds it by more than tau (log2 units), so the
+    // unnormalised p stay <= 2^tau and most tiles skip the rescale; tau = 0 moves it on every
+    // increase, the loop exactly as the pages write it.
+    float tau = kDefaultRescaleLog2;
+    if (opts) {
+        if (!(opts->rescale_threshold_log2 >= 0.f && opts->rescale_threshold_log2 <= 15.f)) return FA_ERR_OPTION;
+        if (opts->variant != 0) return FA_ERR_OPTION;
+        tau = opts->rescale_threshold_log2;
+    }
 
     const float c = scale * 1.4426950408889634f;  // scale * log2(e)
-    // The reference max moves only when a score exceeds it by more than 8 in log2 units, so the
-    // unnormalised p stay <= 2^8 (exact in f16/bf16 range) and most tiles skip the rescale.
-    const float tau_raw = 8.f / c;
+    const float tau_raw = tau / c;
     const int n = static_cast<int>(N), nq = static_cast<int>(n_qt), g = static_cast<int>(G);
     const bool bf = dtype == FA_BF16;
     hipError_t e;
@@ -541,6 +550,11 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
                         : launch<128, false, false>(q, k, v, o, lse, n, nq, g, c, tau_raw, stream);
     }
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
+           int64_t d, float scale, int causal, hipStream_t stream, int dtype) {
+    return fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype, nullptr);
 }
 
 }  // extern "C"

@@ -48,8 +48,31 @@ typedef enum fa_status {
     FA_ERR_ALIGN = 5,     /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
     FA_ERR_SCALE = 6,     /* scale is not finite and > 0 */
     FA_ERR_ALIAS = 7,     /* o or lse overlaps an input, or o overlaps lse */
-    FA_ERR_LAUNCH = 8     /* the kernel launch failed (hipGetLastError) */
+    FA_ERR_LAUNCH = 8,    /* the kernel launch failed (hipGetLastError) */
+    FA_ERR_OPTION = 9     /* an fa_fwd_options field is out of range */
 } fa_status;
+
+/*
+ * Tuning options for fa_fwd_ex. They change how the result is reached, never
+ * what it is (the same exact softmax attention, up to rounding).
+ *
+ * rescale_threshold_log2: the online recurrence keeps every partial sum
+ *   relative to a reference maximum m and rescales them by
+ *   alpha = exp(m_old - m_new) when m moves ("transformer math: flash
+ *   attention math", aicassindra.com, "The rescaling identity, derived").
+ *   With 0 the reference moves whenever a row's running maximum rises, the
+ *   loop exactly as that page writes it ("The block-wise update, and the full
+ *   algorithm"). With t > 0 a wave moves it (to the exact running maximum)
+ *   only when some score exceeds it by more than t in log2 units, so the
+ *   unnormalised probabilities stay <= 2^t and most tiles skip the rescale
+ *   ("fewer rescaling operations", "Decoding flash attention",
+ *   bibekananda.in, "Later versions"). Range [0, 15]; fa_fwd uses 8.
+ * variant: kernel variant; 0 (the default kernel) is the only one.
+ */
+typedef struct fa_fwd_options {
+    float rescale_threshold_log2;
+    int variant;
+} fa_fwd_options;
 
 /*
  * fa_fwd -- enqueue the attention forward pass on `stream`.
@@ -81,6 +104,16 @@ typedef enum fa_status {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int64_t B, int64_t H, int64_t N, int64_t d,
            float scale, int causal, hipStream_t stream, int dtype);
+
+/*
+ * fa_fwd_ex -- fa_fwd with tuning options (see fa_fwd_options). opts == NULL
+ * gives exactly fa_fwd. Same arguments, layouts, ownership, synchronisation
+ * and errors as fa_fwd, plus FA_ERR_OPTION for an out-of-range option.
+ */
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+              int64_t B, int64_t H, int64_t N, int64_t d,
+              float scale, int causal, hipStream_t stream, int dtype,
+              const fa_fwd_options* opts);
 
 /* Static, NUL-terminated description of a return code (never NULL). */
 const char* fa_status_string(int status);

@@ -27,7 +27,7 @@ def L():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_fwd", "fa_status_string", "fa_version"]
+    assert _declared_functions() == ["fa_fwd", "fa_fwd_ex", "fa_status_string", "fa_version"]
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -45,7 +45,7 @@ def test_exported_symbols_match_with_nm():
 
 
 def test_status_strings(L):
-    for st in range(0, 9):
+    for st in range(0, 10):
         s = L.fa_status_string(st)
         assert s and s != b"unknown status"
     assert L.fa_status_string(99) == b"unknown status"
@@ -101,3 +101,20 @@ def test_binding_fails_loudly_without_gpu_tensors():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
     with pytest.raises(ValueError):
         fa.forward(q, q, q)
+
+
+@pytest.mark.parametrize("thr,variant", [(-1.0, 0), (15.5, 0), (float("nan"), 0), (float("inf"), 0), (8.0, 1), (8.0, -1)])
+def test_option_errors(L, thr, variant):
+    import exact_tiled_softmax_fa_amd as fa
+    a = dict(GOOD)
+    st = fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                   a["causal"], a["stream"], a["dtype"], fa.FaOptions(thr, variant))
+    assert st == 9
+
+
+def test_argument_errors_precede_option_errors(L):
+    import exact_tiled_softmax_fa_amd as fa
+    a = dict(GOOD)
+    st = fa.fa_fwd(None, a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                   a["causal"], a["stream"], a["dtype"], fa.FaOptions(-1.0, 0))
+    assert st == 1
