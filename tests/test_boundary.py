@@ -103,7 +103,7 @@ def test_binding_fails_loudly_without_gpu_tensors():
         fa.forward(q, q, q)
 
 
-@pytest.mark.parametrize("thr,variant", [(-1.0, 0), (15.5, 0), (float("nan"), 0), (float("inf"), 0), (8.0, 1), (8.0, -1)])
+@pytest.mark.parametrize("thr,variant", [(-1.0, 0), (15.5, 0), (float("nan"), 0), (float("inf"), 0), (8.0, 3), (8.0, -1)])
 def test_option_errors(L, thr, variant):
     import exact_tiled_softmax_fa_amd as fa
     a = dict(GOOD)

@@ -32,12 +32,12 @@ def _canaries_intact(buf, n):
     return bool((head == CANARY).all().item() and (tail == CANARY).all().item())
 
 
-def run_gpu(q, k, v, causal, scale):
+def run_gpu(q, k, v, causal, scale, variant=0):
     import exact_tiled_softmax_fa_amd as fa
     B, H, N, d = q.shape
     obuf, o = _guarded((B, H, N, d), q.dtype)
     lbuf, lse = _guarded((B, H, N), torch.float32)
-    fa.forward(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale, out=o, lse=lse)
+    fa.forward(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale, out=o, lse=lse, variant=variant)
     torch.cuda.synchronize()
     assert _canaries_intact(obuf, B * H * N * d), "write outside o"
     assert _canaries_intact(lbuf, B * H * N), "write outside lse"
@@ -48,13 +48,15 @@ def oracle_rows(q, k, v, causal, scale, rows):
     return core.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), scale, causal, rows)
 
 
+# variant 0 is the library default (plain fa_fwd); 1 and 2 select each kernel through fa_fwd_ex
+@pytest.mark.parametrize("variant", [0, 1, 2])
 @pytest.mark.parametrize("name", [w.name for w in workloads.WORKLOADS])
-def test_workload_parity(name):
+def test_workload_parity(name, variant):
     w = workloads.BY_NAME[name]
-    print(f"\n[parity] {w.name} seed={w.seed} shape=({w.B},{w.H},{w.N},{w.d}) causal={w.causal} entry=fa_fwd",
-          flush=True)
+    print(f"\n[parity] {w.name} seed={w.seed} shape=({w.B},{w.H},{w.N},{w.d}) causal={w.causal} "
+          f"entry={'fa_fwd' if variant == 0 else 'fa_fwd_ex variant %d' % variant}", flush=True)
     q, k, v = workloads.make_inputs(w)
-    o_gpu, lse_gpu = run_gpu(q, k, v, w.causal, w.scale)
+    o_gpu, lse_gpu = run_gpu(q, k, v, w.causal, w.scale, variant)
     rows = workloads.sample_rows(w)
     o_ref, lse_ref = oracle_rows(q, k, v, w.causal, w.scale, rows)
     BH = w.B * w.H

@@ -30,8 +30,8 @@ def fa():
     return m
 
 
-def gpu(q, k, v, causal=False, scale=None):
-    o, lse = fa().forward(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale)
+def gpu(q, k, v, causal=False, scale=None, variant=0):
+    o, lse = fa().forward(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale, variant=variant)
     torch.cuda.synchronize()
     return o.float().cpu().double().numpy(), lse.cpu().double().numpy()
 
@@ -44,15 +44,16 @@ def say(msg):
     print(f"\n[prop] {msg}", flush=True)
 
 
+@pytest.mark.parametrize("variant", [1, 2])
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 2, 3, 4, 63, 64, 65, 127, 128, 129, 255, 256, 257, 2047])
-def test_tail_sweep(N, causal, d, dt):
-    say(f"tail N={N} causal={causal} d={d} {dt}")
+def test_tail_sweep(N, causal, d, dt, variant):
+    say(f"tail N={N} causal={causal} d={d} {dt} variant={variant}")
     q, k, v = workloads.custom_inputs(2, 3, N, d, dt, seed=100 + N)
     scale = float(np.float32(1 / math.sqrt(d)))
-    o, lse = gpu(q, k, v, causal, scale)
+    o, lse = gpu(q, k, v, causal, scale, variant)
     o_ref, lse_ref = ref(q, k, v, causal, scale)
     ok, rep = check_o(o, o_ref, dt)
     assert ok, rep
