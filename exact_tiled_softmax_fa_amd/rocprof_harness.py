@@ -1,0 +1,192 @@
+"""rocprofv3 harness: kernel time, matrix-core utilisation and device-memory traffic of fa_fwd.
+
+    python -m exact_tiled_softmax_fa_amd.rocprof_harness [--workload NAME] [--out DIR]
+                                                         [--summary-dir DIR] [--parse-only]
+
+Runs four rocprofv3 passes over ``bench.py`` as child processes (this process
+never touches the GPU, so the profiler's preload stays in its own process):
+
+1. ``--kernel-trace --stats``: per-dispatch kernel durations.
+2. ``--pmc FETCH_SIZE`` and 3. ``--pmc WRITE_SIZE``, one counter per pass, with a
+   plain 256 MiB device copy run first (``bench.py --copy-ref-mib 256``). The copy's
+   known size calibrates both counters (bytes read and written by a copy of known
+   size / counter value), and the same factors scale the kernel's counts.
+4. ``--pmc SQ_INSTS_VALU_MFMA_MOPS_{F16,BF16} SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES
+   GRBM_GUI_ACTIVE``: matrix-core work and busy cycles against elapsed cycles.
+
+It then writes a Markdown summary (``<summary-dir>/fa_fwd_kernel_<workload>.md``)
+and ``traffic_fa_fwd_kernel_<workload>.json``. The JSON holds the bytes per launch
+and the SHA-256 of the kernel source it was measured on; ``bench.py`` reports
+the traffic only while that hash matches. Reported figures:
+- the mean kernel time over the timed dispatches;
+- MFMA busy fraction = busy cycles / SIMDs / (GUI-active cycles / XCDs);
+- device-memory bytes per launch and the achieved GB/s (bytes / mean kernel time);
+- the ratio of measured to unavoidable bytes (Q, K, V read once; O, lse written once).
+"""
+import argparse
+import csv
+import hashlib
+import json
+import os
+import shlex
+import statistics
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+KERNEL_SRC = os.path.join(HERE, "csrc", "fa_fwd.hip")
+N_SIMD = 1024   # MI355X: 256 CUs x 4 SIMDs
+N_XCD = 8
+COPY_MIB = 256
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def passes(workload: str, out: str, steps: int, warmup: int):
+    bench = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload, "--no-cpu-baseline"]
+    timed = bench + ["--steps", str(steps), "--warmup", str(warmup)]
+    short = bench + ["--steps", "2", "--warmup", "1"]
+    copy = ["--copy-ref-mib", str(COPY_MIB)]
+    dtype_mops = "SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU_MFMA_MOPS_BF16".split()
+    return [
+        ("kt", ["--kernel-trace", "--stats"], timed),
+        ("fetch", ["--pmc", "FETCH_SIZE"], short + copy),
+        ("write", ["--pmc", "WRITE_SIZE"], short + copy),
+        ("mfma", ["--pmc", *dtype_mops, "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"], short),
+    ]
+
+
+def run(workload: str, out: str, steps: int, warmup: int, timeout: int) -> list:
+    cmds = []
+    for name, prof_args, prog in passes(workload, out, steps, warmup):
+        cmd = ["rocprofv3", *prof_args, "--output-format", "csv", "-d", os.path.join(out, name), "-o", name,
+               "--", *prog]
+        cmds.append(" ".join(shlex.quote(c) for c in cmd))
+        print(f"[rocprof] {name}: {cmds[-1]}", flush=True)
+        env = dict(os.environ, TMPDIR=os.environ.get("TMPDIR", "/tmp"))
+        res = subprocess.run(cmd, env=env, timeout=timeout)
+        if res.returncode != 0:
+            raise RuntimeError(f"rocprofv3 pass {name} failed with exit code {res.returncode}")
+    return cmds
+
+
+def _rows(path):
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(out, name, suffix):
+    d = os.path.join(out, name)
+    for dirpath, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(dirpath, f)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def _counter(out, name, counter, kernel):
+    return [float(r["Counter_Value"]) for r in _rows(_find(out, name, "counter_collection.csv"))
+            if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]]
+
+
+def summarize(workload: str, out: str, steps: int, cmds=None) -> dict:
+    sys.path.insert(0, ROOT)
+    import workloads
+
+    w = workloads.BY_NAME[workload]
+    trace = [r for r in _rows(_find(out, "kt", "kernel_trace.csv")) if "fa_fwd_kernel" in r["Kernel_Name"]]
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in trace]
+    timed = durs[-steps:]
+    ms = statistics.mean(timed)
+    fetch_copy = _counter(out, "fetch", "FETCH_SIZE", "copyBuffer")
+    write_copy = _counter(out, "write", "WRITE_SIZE", "copyBuffer")
+    fetch_k = _counter(out, "fetch", "FETCH_SIZE", "fa_fwd_kernel")
+    write_k = _counter(out, "write", "WRITE_SIZE", "fa_fwd_kernel")
+    f_fac = COPY_MIB * 1024.0 / statistics.mean(fetch_copy)
+    w_fac = COPY_MIB * 1024.0 / statistics.mean(write_copy)
+    fetch_b = statistics.mean(fetch_k) * f_fac * 1024
+    write_b = statistics.mean(write_k) * w_fac * 1024
+    gui = statistics.mean(_counter(out, "mfma", "GRBM_GUI_ACTIVE", "fa_fwd_kernel"))
+    busy = statistics.mean(_counter(out, "mfma", "SQ_VALU_MFMA_BUSY_CYCLES", "fa_fwd_kernel"))
+    mops = sum(statistics.mean(v) for v in (_counter(out, "mfma", "SQ_INSTS_VALU_MFMA_MOPS_F16", "fa_fwd_kernel"),
+                                            _counter(out, "mfma", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "fa_fwd_kernel")) if v)
+    util = busy / N_SIMD / (gui / N_XCD)
+    unavoidable = w.B * w.H * (4 * w.N * w.d * 2 + 4 * w.N)
+    rec = {
+        "kernel_sha256": kernel_sha(),
+        "workload": workload,
+        "kernel_ms_mean_timed": ms,
+        "dispatch_ms": durs,
+        "bytes_per_launch": fetch_b + write_b,
+        "fetch_bytes": fetch_b,
+        "write_bytes": write_b,
+        "fetch_scale": f_fac,
+        "write_scale": w_fac,
+        "achieved_gb_per_s": (fetch_b + write_b) / (ms * 1e-3) / 1e9,
+        "unavoidable_bytes": unavoidable,
+        "traffic_over_unavoidable": (fetch_b + write_b) / unavoidable,
+        "mfma_flop_per_launch": mops * 512,
+        "mfma_busy_fraction": util,
+        "tflops_from_trace": w.flops() / (ms * 1e-3) / 1e12,
+        "commands": cmds or [],
+    }
+    return rec
+
+
+def write_summary(rec: dict, summary_dir: str):
+    os.makedirs(summary_dir, exist_ok=True)
+    name = f"fa_fwd_kernel_{rec['workload']}"
+    lines = [f"# fa_fwd_kernel — {rec['workload']}", ""]
+    if rec["commands"]:
+        lines += ["Made by `python -m exact_tiled_softmax_fa_amd.rocprof_harness --workload "
+                  f"{rec['workload']}` (repository root, GPU box), which ran:", "", "```",
+                  *rec["commands"], "```", ""]
+    d = rec["dispatch_ms"]
+    lines += [
+        "## Kernel time (rocprofv3 --kernel-trace --stats)", "",
+        f"- dispatches (ms): {', '.join(f'{x:.3f}' for x in d)}",
+        f"- mean of the timed dispatches: **{rec['kernel_ms_mean_timed']:.4f} ms** "
+        f"= {rec['tflops_from_trace']:.1f} TFLOP/s (conventional flop count)", "",
+        "## Device-memory traffic (FETCH_SIZE, WRITE_SIZE; one counter per pass)", "",
+        f"- scale factors from a {COPY_MIB} MiB device copy: fetch x{rec['fetch_scale']:.3f}, "
+        f"write x{rec['write_scale']:.3f}",
+        f"- per launch: {rec['fetch_bytes'] / 2**20:.1f} MiB read + {rec['write_bytes'] / 2**20:.1f} MiB written "
+        f"= {rec['bytes_per_launch'] / 2**20:.1f} MiB; unavoidable (Q, K, V once; O, lse once) "
+        f"{rec['unavoidable_bytes'] / 2**20:.1f} MiB; ratio {rec['traffic_over_unavoidable']:.3f}",
+        f"- achieved device-memory bandwidth: {rec['achieved_gb_per_s']:.1f} GB/s (of about 8000)", "",
+        "## Matrix cores (SQ_INSTS_VALU_MFMA_MOPS_*, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE)", "",
+        f"- MFMA work per launch: {rec['mfma_flop_per_launch']:.4e} flop",
+        f"- MFMA busy: **{100 * rec['mfma_busy_fraction']:.1f} %** of elapsed cycles", "",
+    ]
+    with open(os.path.join(summary_dir, name + ".md"), "w") as f:
+        f.write("\n".join(lines))
+    slim = {k: v for k, v in rec.items() if k != "dispatch_ms"}
+    with open(os.path.join(summary_dir, "traffic_" + name + ".json"), "w") as f:
+        json.dump(slim, f, indent=1)
+    print("\n".join(lines), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", default="B1-H32-N8192-d128-f16")
+    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "rocprof"))
+    ap.add_argument("--summary-dir", default=os.path.join(ROOT, "gpurun_out", "rocprof"))
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--timeout", type=int, default=240, help="seconds per rocprofv3 pass")
+    ap.add_argument("--parse-only", action="store_true", help="summarise existing outputs under --out")
+    args = ap.parse_args()
+    out = os.path.join(args.out, args.workload)
+    cmds = None
+    if not args.parse_only:
+        cmds = run(args.workload, out, args.steps, args.warmup, args.timeout)
+    rec = summarize(args.workload, out, args.steps, cmds)
+    write_summary(rec, args.summary_dir)
+
+
+if __name__ == "__main__":
+    main()

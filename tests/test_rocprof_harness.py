@@ -1,0 +1,77 @@
+"""The rocprof harness's parsing and arithmetic, on synthetic rocprofv3 CSV files (no GPU)."""
+import csv
+import json
+import os
+
+import pytest
+
+from exact_tiled_softmax_fa_amd import rocprof_harness as rh
+
+KERNEL = "void (anonymous namespace)::fa_fwd_kernel<128, false, false>(...)"
+COPY = "__amd_rocclr_copyBuffer"
+TRACE_FIELDS = ["Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+PMC_FIELDS = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def _write(path, fields, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+@pytest.fixture
+def fake_run(tmp_path):
+    out = str(tmp_path / "run")
+    # 3 warm-up dispatches at 2 ms, then 20 timed ones at 1 ms
+    durs_ns = [2_000_000] * 3 + [1_000_000] * 20
+    t, rows = 0, []
+    for d in durs_ns:
+        rows.append({"Kernel_Name": KERNEL, "Start_Timestamp": t, "End_Timestamp": t + d})
+        t += d + 1000
+    _write(os.path.join(out, "kt", "h", "kt_kernel_trace.csv"), TRACE_FIELDS, rows)
+    # the copy reference reads half its size in FETCH_SIZE units and writes its full size
+    _write(os.path.join(out, "fetch", "h", "fetch_counter_collection.csv"), PMC_FIELDS, [
+        {"Kernel_Name": COPY, "Counter_Name": "FETCH_SIZE", "Counter_Value": 131072.0},
+        {"Kernel_Name": KERNEL, "Counter_Name": "FETCH_SIZE", "Counter_Value": 100000.0}])
+    _write(os.path.join(out, "write", "h", "write_counter_collection.csv"), PMC_FIELDS, [
+        {"Kernel_Name": COPY, "Counter_Name": "WRITE_SIZE", "Counter_Value": 262144.0},
+        {"Kernel_Name": KERNEL, "Counter_Name": "WRITE_SIZE", "Counter_Value": 66560.0}])
+    _write(os.path.join(out, "mfma", "h", "mfma_counter_collection.csv"), PMC_FIELDS, [
+        {"Kernel_Name": KERNEL, "Counter_Name": "SQ_INSTS_VALU_MFMA_MOPS_F16", "Counter_Value": 2 ** 31},
+        {"Kernel_Name": KERNEL, "Counter_Name": "SQ_VALU_MFMA_BUSY_CYCLES", "Counter_Value": 1024 * 1e6},
+        {"Kernel_Name": KERNEL, "Counter_Name": "GRBM_GUI_ACTIVE", "Counter_Value": 8 * 2e6}])
+    return out
+
+
+def test_summarize_arithmetic(fake_run, tmp_path):
+    rec = rh.summarize("B1-H32-N8192-d128-f16", fake_run, steps=20, cmds=["rocprofv3 ..."])
+    assert rec["kernel_ms_mean_timed"] == pytest.approx(1.0)
+    assert rec["fetch_scale"] == pytest.approx(2.0)
+    assert rec["write_scale"] == pytest.approx(1.0)
+    assert rec["fetch_bytes"] == pytest.approx(100000.0 * 2 * 1024)
+    assert rec["write_bytes"] == pytest.approx(66560.0 * 1024)
+    assert rec["achieved_gb_per_s"] == pytest.approx(rec["bytes_per_launch"] / 1e-3 / 1e9)
+    assert rec["mfma_flop_per_launch"] == pytest.approx(2 ** 40)
+    assert rec["mfma_busy_fraction"] == pytest.approx(0.5)
+    assert rec["unavoidable_bytes"] == 32 * (4 * 8192 * 128 * 2 + 4 * 8192)
+    assert rec["tflops_from_trace"] == pytest.approx(2 ** 40 / 1e-3 / 1e12)
+    assert rec["kernel_sha256"] == rh.kernel_sha()
+    rh.write_summary(rec, str(tmp_path / "summ"))
+    j = json.load(open(tmp_path / "summ" / "traffic_fa_fwd_kernel_B1-H32-N8192-d128-f16.json"))
+    assert j["bytes_per_launch"] == pytest.approx(rec["bytes_per_launch"])
+    assert "dispatch_ms" not in j
+    md = open(tmp_path / "summ" / "fa_fwd_kernel_B1-H32-N8192-d128-f16.md").read()
+    assert "MFMA busy: **50.0 %**" in md
+
+
+def test_passes_keep_counters_within_one_pass_limits():
+    for name, prof_args, prog in rh.passes("B1-H32-N8192-d128-f16", "/tmp/x", 20, 10):
+        if "--pmc" in prof_args:
+            counters = prof_args[prof_args.index("--pmc") + 1:]
+            assert sum(c.startswith("SQ_") for c in counters) <= 8
+            assert sum(c.startswith("GRBM_") for c in counters) <= 2
+            assert len([c for c in counters if c in ("FETCH_SIZE", "WRITE_SIZE")]) <= 1
+        assert "--no-cpu-baseline" in prog
