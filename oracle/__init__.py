@@ -6,18 +6,22 @@ binding never do, and this package imports nothing from them.
 
 Contents
   core        ctypes front end of ``fa_oracle.c``: fp64 three-pass safe-softmax
-              attention (the definition written out).
+              attention (the definition written out), and its gradients with
+              respect to q, k, v by the chain rule (``attention_backward``).
   recurrence  the online-softmax recurrence for one query in fp64, block by
               block, in any block partition and order, with switches that plant
               the four classic implementation mistakes (used only to show that
               the pins catch them).
   brute       50-digit decimal evaluation of the definition with no
-              max-subtraction, for tiny inputs.
+              max-subtraction, for tiny inputs, and gradients of the loss
+              sum(dO * O) by 50-digit central differences of it.
 
 Pins (tests/test_oracle_*.py): the two worked examples printed on the pages
 (tests/golden/), closed forms (uniform keys, a single key, causal row 0),
 softmax rows summing to 1, shift invariance, block order/size invariance and
-the brute force. Every function here is pinned; none is "parity unpinned"
+the brute force. The gradients (tests/test_oracle_bwd_pins.py): decimal
+finite differences, fp64 autograd, sum rules, translation invariance,
+linearity and closed forms. Every function here is pinned; none is "parity unpinned"
 except the second worked example's output vector, whose value vectors the
 page does not print.
 """

@@ -1,4 +1,5 @@
-"""ctypes front end of the fp64 three-pass attention oracle (``fa_oracle.c``).
+"""ctypes front end of the fp64 attention oracle (``fa_oracle.c``): the three-pass forward and the
+chain-rule gradients.
 
 Test infrastructure only. See ``fa_oracle.c`` for the definition it computes
 and the passages it follows ("FlashAttention tiles exact softmax without
@@ -26,6 +27,13 @@ def _load():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+        ]
+        lib.fa_oracle_bwd.restype = ctypes.c_int
+        lib.fa_oracle_bwd.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
         ]
         lib.fa_oracle_threads.restype = ctypes.c_int
         lib.fa_oracle_threads.argtypes = []
@@ -74,3 +82,44 @@ def attention(q, k, v, scale, causal=False, rows=None):
     if rc != 0:
         raise RuntimeError(f"fa_oracle_fwd failed with code {rc}")
     return o, lse
+
+
+def _index_list(idx, G, name):
+    if idx is None:
+        return None, 0, None
+    idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int64))
+    if idx.ndim != 2 or idx.shape[0] != G:
+        raise ValueError(f"{name} must be [G, R] with G = {G} heads, got {idx.shape}")
+    return idx, idx.shape[1], idx.ctypes.data
+
+
+def attention_backward(q, k, v, dout, scale, causal=False, rows=None, keys=None):
+    """Gradients of L = sum(dout * o) with respect to q, k, v, in fp64 (``fa_oracle_bwd``).
+
+    q, k, v, dout : array-likes of one shape [..., N, d]; the leading axes are flattened into G
+                    heads (fp16/bf16 inputs convert exactly).
+    rows          : None for dq of every row, else int [G, R] row indices per head.
+    keys          : None for dk, dv of every key, else int [G, C] key indices per head.
+    Returns (dq, dk, dv, lse, delta): dq [G, R or N, d], dk and dv [G, C or N, d], lse and delta
+    [G, N] (the log-sum-exp of each row's logits and D_i = sum_j a_ij (dout_i . v_j)).
+    """
+    arrs = [np.ascontiguousarray(np.asarray(t, dtype=np.float64)) for t in (q, k, v, dout)]
+    shape = arrs[0].shape
+    if len(shape) < 2 or any(a.shape != shape for a in arrs):
+        raise ValueError(f"q, k, v, dout must share one [..., N, d] shape, got {[a.shape for a in arrs]}")
+    N, d = shape[-2], shape[-1]
+    G = int(np.prod(shape[:-2])) if len(shape) > 2 else 1
+    q, k, v, dout = (a.reshape(G, N, d) for a in arrs)
+    rows, n_rows, rows_p = _index_list(rows, G, "rows")
+    keys, n_keys, keys_p = _index_list(keys, G, "keys")
+    dq = np.empty((G, n_rows if rows is not None else N, d), dtype=np.float64)
+    dk = np.empty((G, n_keys if keys is not None else N, d), dtype=np.float64)
+    dv = np.empty_like(dk)
+    lse = np.empty((G, N), dtype=np.float64)
+    delta = np.empty((G, N), dtype=np.float64)
+    rc = _load().fa_oracle_bwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+                               dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, lse.ctypes.data, delta.ctypes.data,
+                               G, N, d, float(scale), int(bool(causal)), rows_p, n_rows, keys_p, n_keys)
+    if rc != 0:
+        raise RuntimeError(f"fa_oracle_bwd failed with code {rc}")
+    return dq, dk, dv, lse, delta

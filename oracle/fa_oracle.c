@@ -27,6 +27,9 @@
  * the query is excluded, nalar.dev section "Causal masking fits inside the
  * tiled computation"). There is no tiling, blocking or reordering here: one
  * N-length fp64 score buffer per row, summed in ascending key order.
+ *
+ * fa_oracle_bwd, at the end of the file, gives the gradients of the same
+ * definition with respect to q, k and v by the chain rule.
  */
 #include <math.h>
 #include <stdint.h>
@@ -120,5 +123,154 @@ int fa_oracle_fwd(const double* q, const double* k, const double* v, double* o, 
     }
     free(s_all);
     free(acc_all);
+    return 0;
+}
+
+/*
+ * Gradients of the loss L = sum_i dO_i . o_i with respect to q, k and v (fp64).
+ *
+ * The pages give the backward pass only as a dataflow: keep the per-row
+ * softmax statistics and recompute score tiles rather than store them
+ * ("Decoding flash attention" (bibekananda.in), section "The backward pass";
+ * nalar.dev, section "Backward computation can trade recomputation for stored
+ * intermediates"). The values are the chain rule applied to the definition at
+ * the top of this file, written out with no tiling:
+ *   a_ij  = softmax weights of row i (three-pass route, as above)
+ *   dP_ij = dO_i . v_j
+ *   D_i   = sum_j a_ij dP_ij                 (the row's weighted mean of dP)
+ *   dS_ij = a_ij (dP_ij - D_i)               (Jacobian of softmax applied to dP)
+ *   dV_j  = sum_i a_ij dO_i
+ *   dQ_i  = scale * sum_j dS_ij k_j
+ *   dK_j  = scale * sum_i dS_ij q_i
+ * Sums over i run over the rows that allow key j (all rows, or i >= j when
+ * causal); sums over j over the keys row i allows.
+ *
+ * q, k, v, dout : [G, N, d] fp64 (G heads), contiguous.
+ * rows          : NULL for every row, else [G, n_rows] row indices; dq is [G, n_rows or N, d].
+ * keys          : NULL for every key, else [G, n_keys] key indices; dk, dv are [G, n_keys or N, d].
+ * lse, delta    : NULL or [G, N]; receive m_i + ln l_i and D_i of every row.
+ * Returns 0 on success, 1 on a bad argument, 2 on allocation failure.
+ */
+int fa_oracle_bwd(const double* q, const double* k, const double* v, const double* dout,
+                  double* dq, double* dk, double* dv, double* lse, double* delta,
+                  int64_t G, int64_t N, int64_t d, double scale, int causal,
+                  const int64_t* rows, int64_t n_rows, const int64_t* keys, int64_t n_keys) {
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || G < 1 || N < 1 || d < 1) return 1;
+    int64_t R = rows ? n_rows : N;
+    int64_t C = keys ? n_keys : N;
+    if (R < 1 || C < 1) return 1;
+    for (int64_t t = 0; rows && t < G * n_rows; ++t)
+        if (rows[t] < 0 || rows[t] >= N) return 1;
+    for (int64_t t = 0; keys && t < G * n_keys; ++t)
+        if (keys[t] < 0 || keys[t] >= N) return 1;
+    int nthreads = fa_oracle_threads();
+    double* m_all = (double*)malloc((size_t)(G * N) * sizeof(double));
+    double* l_all = (double*)malloc((size_t)(G * N) * sizeof(double));
+    double* D_all = (double*)malloc((size_t)(G * N) * sizeof(double));
+    double* s_all = (double*)malloc((size_t)nthreads * (size_t)N * sizeof(double));
+    double* dp_all = (double*)malloc((size_t)nthreads * (size_t)N * sizeof(double));
+    if (!m_all || !l_all || !D_all || !s_all || !dp_all) {
+        free(m_all); free(l_all); free(D_all); free(s_all); free(dp_all);
+        return 2;
+    }
+
+    /* pass 1, every row: m_i, l_i (three-pass route) and D_i */
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nthreads)
+    for (int64_t t = 0; t < G * N; ++t) {
+#ifdef _OPENMP
+        int tid = omp_get_thread_num();
+#else
+        int tid = 0;
+#endif
+        double* s = s_all + (size_t)tid * (size_t)N;
+        int64_t g = t / N, i = t % N;
+        const double* qi = q + t * d;
+        const double* doi = dout + t * d;
+        const double* kh = k + g * N * d;
+        const double* vh = v + g * N * d;
+        int64_t n_allowed = causal ? i + 1 : N;
+        for (int64_t j = 0; j < n_allowed; ++j) {
+            double dot = 0.0;
+            for (int64_t c = 0; c < d; ++c) dot += qi[c] * kh[j * d + c];
+            s[j] = scale * dot;
+        }
+        double m = -INFINITY;
+        for (int64_t j = 0; j < n_allowed; ++j)
+            if (s[j] > m) m = s[j];
+        double l = 0.0;
+        for (int64_t j = 0; j < n_allowed; ++j) l += exp(s[j] - m);
+        double D = 0.0;
+        for (int64_t j = 0; j < n_allowed; ++j) {
+            double dp = 0.0;
+            for (int64_t c = 0; c < d; ++c) dp += doi[c] * vh[j * d + c];
+            D += (exp(s[j] - m) / l) * dp;
+        }
+        m_all[t] = m;
+        l_all[t] = l;
+        D_all[t] = D;
+        if (lse) lse[t] = m + log(l);
+        if (delta) delta[t] = D;
+    }
+
+    /* pass 2, requested rows: dQ_i = scale * sum_j a_ij (dP_ij - D_i) k_j */
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nthreads)
+    for (int64_t t = 0; t < G * R; ++t) {
+#ifdef _OPENMP
+        int tid = omp_get_thread_num();
+#else
+        int tid = 0;
+#endif
+        double* s = s_all + (size_t)tid * (size_t)N;
+        double* dp = dp_all + (size_t)tid * (size_t)N;
+        int64_t g = t / R, r = t % R;
+        int64_t i = rows ? rows[g * n_rows + r] : r;
+        const double* qi = q + (g * N + i) * d;
+        const double* doi = dout + (g * N + i) * d;
+        const double* kh = k + g * N * d;
+        const double* vh = v + g * N * d;
+        int64_t n_allowed = causal ? i + 1 : N;
+        double m = m_all[g * N + i], l = l_all[g * N + i], D = D_all[g * N + i];
+        for (int64_t j = 0; j < n_allowed; ++j) {
+            double dot = 0.0, dpv = 0.0;
+            for (int64_t c = 0; c < d; ++c) dot += qi[c] * kh[j * d + c];
+            for (int64_t c = 0; c < d; ++c) dpv += doi[c] * vh[j * d + c];
+            s[j] = exp(scale * dot - m) / l;
+            dp[j] = dpv;
+        }
+        double* out = dq + t * d;
+        for (int64_t c = 0; c < d; ++c) out[c] = 0.0;
+        for (int64_t j = 0; j < n_allowed; ++j) {
+            double ds = s[j] * (dp[j] - D);
+            for (int64_t c = 0; c < d; ++c) out[c] += ds * kh[j * d + c];
+        }
+        for (int64_t c = 0; c < d; ++c) out[c] *= scale;
+    }
+
+    /* pass 3, requested keys: dV_j = sum_i a_ij dO_i, dK_j = scale * sum_i a_ij (dP_ij - D_i) q_i */
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads)
+    for (int64_t t = 0; t < G * C; ++t) {
+        int64_t g = t / C, r = t % C;
+        int64_t j = keys ? keys[g * n_keys + r] : r;
+        const double* kj = k + (g * N + j) * d;
+        const double* vj = v + (g * N + j) * d;
+        double* ok = dk + t * d;
+        double* ov = dv + t * d;
+        for (int64_t c = 0; c < d; ++c) ok[c] = ov[c] = 0.0;
+        for (int64_t i = causal ? j : 0; i < N; ++i) {
+            const double* qi = q + (g * N + i) * d;
+            const double* doi = dout + (g * N + i) * d;
+            double dot = 0.0, dpv = 0.0;
+            for (int64_t c = 0; c < d; ++c) dot += qi[c] * kj[c];
+            for (int64_t c = 0; c < d; ++c) dpv += doi[c] * vj[c];
+            double a = exp(scale * dot - m_all[g * N + i]) / l_all[g * N + i];
+            double ds = a * (dpv - D_all[g * N + i]);
+            for (int64_t c = 0; c < d; ++c) {
+                ov[c] += a * doi[c];
+                ok[c] += ds * qi[c];
+            }
+        }
+        for (int64_t c = 0; c < d; ++c) ok[c] *= scale;
+    }
+    free(m_all); free(l_all); free(D_all); free(s_all); free(dp_all);
     return 0;
 }
