@@ -1,10 +1,18 @@
-"""Throughput of the attention forward pass on one MI355X.
+"""Throughput of the attention forward (or backward) pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd]
+                    [--no-cpu-baseline]
 
 A step is one fa_fwd call over the whole workload (every query row of every
 head), with q, k, v already resident in device memory. The default workload is
 B=1, H=32, N=8192, d=128, non-causal, fp16. Prints one JSON line.
+
+--pass bwd times one fa_bwd call instead (dq, dk, dv from q, k, v, o, lse and a
+seeded dout, all resident), priced by the conventional backward count of 2.5x
+the forward flops (the five products dP = dO V^T, dV = P^T dO, dQ = dS K,
+dK = dS^T Q and the recomputed S = Q K^T); the kernels run two more (S and dP
+once in each of the two kernels). The roofline object then covers the whole
+call (both kernels).
 
 Algorithmic work per launch: 4*B*H*N^2*d flops (the two products QK^T and PV;
 halved when causal), i.e. 1.0995e12 for the default workload. The roofline
@@ -20,7 +28,6 @@ bounded sample of the same workload (the 1024 seeded query rows per head the
 parity test checks), converted to TFLOP/s with the same flop convention.
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -33,14 +40,13 @@ if ROOT not in sys.path:
 import workloads  # noqa: E402
 
 PEAK_MFMA_F16_TFLOPS = 2516.6  # 256 CU * 2.4 GHz * 4096 flop/clk/CU, dense fp16/bf16
-KERNEL_SRC = os.path.join(ROOT, "exact_tiled_softmax_fa_amd", "csrc", "fa_fwd.hip")
 KERNEL_NAME = "fa_fwd_kernel"
 HEADLINE_METRIC = "fwd attention TFLOP/s and % MFMA peak at B1 H32 N8192 d128 (fp16)"
 
 
 def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    from exact_tiled_softmax_fa_amd.rocprof_harness import kernel_sha as sha
+    return sha()
 
 
 def measured_traffic(workload_name: str):
@@ -81,12 +87,45 @@ def cpu_baseline(w):
     }
 
 
+def cpu_baseline_bwd(w):
+    """The fp64 backward oracle on one head of the workload (1024 sampled rows of dq and 1024
+    sampled keys of dk, dv when the workload samples rows, else everything), in conventional
+    backward TFLOP/s: 10 * d flops per (row, key) pair of the parts it computes."""
+    import numpy as np
+    from oracle import core
+
+    q, k, v = workloads.make_inputs(w)
+    dout = workloads.make_dout(w)
+    head = lambda t: t.reshape(w.B * w.H, w.N, w.d)[:1].double().numpy()  # noqa: E731
+    rows, keys = workloads.sample_rows(w), workloads.sample_keys(w)
+    rows = None if rows is None else rows[:1]
+    keys = None if keys is None else keys[:1]
+    t0 = time.perf_counter()
+    core.attention_backward(head(q), head(k), head(v), head(dout), w.scale, w.causal, rows=rows, keys=keys)
+    dt = time.perf_counter() - t0
+    pairs = w.N * (w.N + 1) / 2 if w.causal else float(w.N) * w.N
+    # every row's statistics cost a full pass; dq and dk/dv are computed for the sampled part only
+    frac = 1.0 if rows is None else (rows.shape[1] + keys.shape[1]) / (2.0 * w.N)
+    flops = 10.0 * w.d * pairs * (0.4 + 0.6 * frac)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": core.threads(),
+        "kind": "oracle",
+        "sample": f"one head of {w.name}: every row's softmax statistics and D, dq of "
+                  f"{'all' if rows is None else rows.shape[1]} rows, dk and dv of "
+                  f"{'all' if keys is None else keys.shape[1]} keys ({dt:.2f} s, fp64 chain rule)",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=workloads.HEADLINE.name, choices=sorted(workloads.BY_NAME))
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
+                    help="time the forward pass (default) or the backward pass")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="before timing, run 3 plain device copies of this many MiB (a known-size "
@@ -120,6 +159,15 @@ def main():
     def step():
         fa.forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
 
+    if args.which == "bwd":
+        step()
+        dout = workloads.make_dout(w).cuda()
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        delta = torch.empty_like(lse)
+
+        def step():  # noqa: F811
+            fa.backward(q, k, v, o, lse, dout, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, delta=delta)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -135,11 +183,12 @@ def main():
     wall = time.perf_counter() - t0
     kernel_ms = e0.elapsed_time(e1) / args.steps  # average launch duration on the kernel's stream
 
-    flops = w.flops()
+    flops = w.flops() * (2.5 if args.which == "bwd" else 1.0)
     value = flops / (wall / args.steps) / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     out = {
-        "metric": HEADLINE_METRIC if w.name == workloads.HEADLINE.name else f"fwd attention TFLOP/s ({w.name})",
+        "metric": (HEADLINE_METRIC if w.name == workloads.HEADLINE.name and args.which == "fwd"
+                   else f"{args.which} attention TFLOP/s ({w.name})"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -160,13 +209,13 @@ def main():
             "peak": PEAK_MFMA_F16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_MFMA_F16_TFLOPS, 4),
-            "traffic": measured_traffic(w.name),
-            "kernel": KERNEL_NAME,
+            "traffic": measured_traffic(w.name) if args.which == "fwd" else None,
+            "kernel": KERNEL_NAME if args.which == "fwd" else "fa_bwd_dq_kernel + fa_bwd_dkdv_kernel",
             "kernel_ms": round(kernel_ms, 4),
         },
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"] = cpu_baseline(w) if args.which == "fwd" else cpu_baseline_bwd(w)
     print(json.dumps(out), flush=True)
 
 

@@ -1,17 +1,20 @@
-"""Exact tiled-softmax attention forward on MI355X (gfx950): Python binding.
+"""Exact tiled-softmax attention on MI355X (gfx950): Python binding.
 
-A thin ctypes layer over the C ABI declared in ``include/fa_fwd.h``
-(``libfa_fwd.so``, built from ``csrc/fa_fwd.hip``). It only marshals
-arguments: shapes, dtypes, device pointers and torch's current HIP stream.
-Every step of the computation runs in the HIP kernel. PyTorch supplies device
-memory and streams.
+A thin ctypes layer over the C ABI declared in ``include/fa_fwd.h`` and
+``include/fa_bwd.h`` (``libfa_fwd.so``, built from ``csrc/fa_fwd.hip`` and
+``csrc/fa_bwd.hip``). It only marshals arguments: shapes, dtypes, device
+pointers and torch's current HIP stream. Every step of the computation runs in
+the HIP kernels. PyTorch supplies device memory and streams.
 
     o, lse = forward(q, k, v, causal=False, scale=None)
+    dq, dk, dv = backward(q, k, v, o, lse, dout, causal=False, scale=None)
 
 q, k, v: contiguous CUDA (HIP) tensors [B, H, N, d], float16 or bfloat16,
-d in {64, 128}. Returns o (same shape and dtype) and lse ([B, H, N] float32,
-natural log of each row's softmax denominator). There is no CPU fallback: if
-the library is missing or the tensors are not on the GPU, the call raises.
+d in {64, 128}. forward returns o (same shape and dtype) and lse ([B, H, N]
+float32, natural log of each row's softmax denominator); backward returns the
+gradients of a loss L with respect to q, k, v given dout = dL/do. There is no
+CPU fallback: if the library is missing or the tensors are not on the GPU, the
+call raises.
 """
 import ctypes
 import math
@@ -37,7 +40,7 @@ class FaError(RuntimeError):
     """A non-zero status returned by the C library."""
 
     def __init__(self, status: int, message: str):
-        super().__init__(f"fa_fwd failed with status {status}: {message}")
+        super().__init__(f"fa call failed with status {status}: {message}")
         self.status = status
 
 
@@ -63,6 +66,11 @@ def lib():
         ]
         L.fa_fwd_ex.restype = ctypes.c_int
         L.fa_fwd_ex.argtypes = L.fa_fwd.argtypes + [ctypes.POINTER(FaOptions)]
+        L.fa_bwd.restype = ctypes.c_int
+        L.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+        ]
         L.fa_status_string.restype = ctypes.c_char_p
         L.fa_status_string.argtypes = [ctypes.c_int]
         L.fa_version.restype = ctypes.c_int
@@ -132,3 +140,58 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
     if st != 0:
         raise FaError(st, status_string(st))
     return (out, lse) if return_lse else out
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, causal, stream, dtype) -> int:
+    """Raw call of the C entry point fa_bwd with integer pointers; returns the status code."""
+    return int(lib().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, float(scale), int(causal),
+                            stream, int(dtype)))
+
+
+def _check_like(name, t, ref, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.shape != (ref.shape if shape is None else shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(ref.shape if shape is None else shape)}")
+    if t.dtype != (ref.dtype if dtype is None else dtype):
+        raise ValueError(f"{name} has dtype {t.dtype}")
+    if not t.is_contiguous() or t.device != ref.device:
+        raise ValueError(f"{name} must be contiguous and on {ref.device}")
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+             dout: torch.Tensor, causal: bool = False, scale=None, dq=None, dk=None, dv=None, delta=None,
+             return_delta: bool = False):
+    """Gradients (dq, dk, dv) of a loss L with respect to q, k, v, given dout = dL/do and the
+    forward's o and lse (same q, k, v, causal and scale). Runs on the current stream of q's device.
+    delta ([B, H, N] float32, receives dout_i . o_i) is allocated if not given; with
+    return_delta=True it is returned as a fourth value."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, N, d], got shape {tuple(t.shape)}")
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"q must be float16 or bfloat16, got {q.dtype}")
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_like(name, t, q)
+    _check_like("q", q, q)
+    _check_like("lse", lse, q, torch.float32, (B, H, N))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_like(name, t, q)
+    _check_like("delta", delta, q, torch.float32, (B, H, N))
+    if scale is None:
+        scale = default_scale(d)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, scale, causal,
+                    stream, _DTYPES[q.dtype])
+    if st != 0:
+        raise FaError(st, status_string(st))
+    return (dq, dk, dv, delta) if return_delta else (dq, dk, dv)

@@ -1,4 +1,4 @@
-"""Compile the HIP library (``csrc/fa_fwd.hip`` -> ``libfa_fwd.so``) for gfx950 with hipcc.
+"""Compile the HIP library (``csrc/fa_fwd.hip`` + ``csrc/fa_bwd.hip`` -> ``libfa_fwd.so``) for gfx950.
 
 The library is built in-tree, next to this file, so it travels with the source
 tree. ``build()`` always recompiles.
@@ -9,7 +9,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "fa_fwd.hip")
+SRCS = [os.path.join(HERE, "csrc", "fa_fwd.hip"), os.path.join(HERE, "csrc", "fa_bwd.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfa_fwd.so")
 ARCH = "gfx950"
@@ -35,7 +35,7 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, SRC, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, *SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,0 +1,539 @@
+// Backward pass of exact attention for gfx950 (CDNA4), behind the C ABI of fa_bwd.h.
+//
+// The forward pass keeps one statistic per query row, lse_i = m_i + ln l_i. The backward pass
+// recomputes each score tile from Q, K and that statistic instead of reading a stored probability
+// matrix ("Decoding flash attention" (bibekananda.in), section "The backward pass"; nalar.dev,
+// section "Backward computation can trade recomputation for stored intermediates"). With
+// p_ij = exp(s_ij - lse_i), the gradients of L = sum(dO * O) are the chain rule through softmax:
+//   dP_ij = dO_i . v_j,   D_i = dO_i . o_i (= sum_j p_ij dP_ij),   dS_ij = p_ij (dP_ij - D_i)
+//   dV_j = sum_i p_ij dO_i,   dK_j = scale * sum_i dS_ij q_i,   dQ_i = scale * sum_j dS_ij k_j
+// Two kernels, no atomics, every output written once by one lane (deterministic):
+//
+// fa_bwd_dq_kernel   one workgroup = 8 waves x 32 query rows (the forward's query tiles and grid).
+//                    First D_i = dO_i . o_i for its rows (written to delta), then a walk over the
+//                    key tiles (64 keys, double-buffered in LDS as in the forward):
+//                      S^T  = K . Q^T,  dP^T = V . dO^T   (Q^T, dO^T held in registers)
+//                      dS^T = P^T (dP^T - D)              (one query row per lane)
+//                      dQ^T += K^T . dS^T                 (K^T by the LDS transpose read)
+// fa_bwd_dkdv_kernel one workgroup = 128 keys in 4 groups of 32, each group taken by two waves
+//                    that split every query tile of 64 rows in halves; the K and V rows sit in
+//                    LDS for the whole kernel, the Q and dO tiles (with lse and D of their rows)
+//                    are double-buffered; at the end the two partial sums of each key group are
+//                    added through LDS:
+//                      S  = Q . K^T,  dP = dO . V^T       (one key per lane)
+//                      dS = P (dP - D)
+//                      dV^T += dO^T . P,  dK^T += Q^T . dS (dO^T, Q^T by the LDS transpose read)
+// P and dS are rounded to f16/bf16 as operands of the second products, with fp32 accumulation;
+// masked entries (a key after the query, rows or keys past the end) get s = -inf, so p = 0 and
+// dS = 0 before they touch any sum.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include "fa_bwd.h"
+#include "fa_device.h"
+
+namespace {
+
+using namespace fa_detail;
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 32 * kWaves;  // query rows per workgroup in the dq kernel
+constexpr int kKeyTile = 64;        // keys per tile in the dq kernel
+constexpr int kKeys = 128;          // keys per workgroup in the dkdv kernel (4 groups of 32)
+constexpr int kQueryTile = 64;      // query rows per tile in the dkdv kernel (two halves of 32)
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __attribute__((address_space(3))) const uint16_t lds_u16;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+
+// ds_read_b64_tr_b16 offsets: lane s of each 16-lane group reads 4 consecutive columns 4*(s%4).. of
+// tile row s/4 (+4h); the instruction returns, per lane, one column of 4 rows. With the second read
+// 8 rows further down, a lane holds 8 rows in the order of the C-layout registers of a 32x32 MFMA
+// result (rows 4h..4h+3, 8+4h..8+4h+3 of each 16), so a product whose B operand comes straight
+// from such registers contracts over matching rows.
+template <int D>
+__device__ __forceinline__ void transpose_offsets(int lane, int (&lo)[D / 32], int (&hi)[D / 32]) {
+    const int h = lane >> 5;
+    const int s16 = lane & 15;
+    const int tr_row = 4 * h + (s16 >> 2);
+    const int tr_chunk = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
+    const int tr_half = 4 * (s16 & 1);
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) {
+        lo[b] = tile_off<D>(tr_row, 4 * b + tr_chunk) + tr_half;
+        hi[b] = tile_off<D>(tr_row + 8, 4 * b + tr_chunk) + tr_half;
+    }
+}
+
+// A operand (32 columns of block b x 16 rows of step kk, transposed) from a row-major LDS tile.
+template <int D>
+__device__ __forceinline__ u32x4 transposed_operand(const uint16_t* tile, const int (&lo)[D / 32],
+                                                    const int (&hi)[D / 32], int kk, int b) {
+    const i16x4 l4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + lo[b] + kk * 16 * D));
+    const i16x4 h4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + hi[b] + kk * 16 * D));
+    const u32x2 a = __builtin_bit_cast(u32x2, l4);
+    const u32x2 c = __builtin_bit_cast(u32x2, h4);
+    return (u32x4){a[0], a[1], c[0], c[1]};
+}
+
+// Sum of the 8 products of two packed 8-element rows, in fp32. (Each element is copied to a
+// scalar before the bit cast: __builtin_bit_cast applied to a vector element reads element 0.)
+template <bool BF16>
+__device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const unsigned x = a[i], y = b[i];
+        if constexpr (BF16)
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, y), acc,
+                                                  false);
+        else
+            acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x), __builtin_bit_cast(f16x2, y), acc, false);
+    }
+    return acc;
+}
+
+// Store rows of a transposed accumulator (lane = row, registers = 4 columns per group) times f.
+template <int D, bool BF16>
+__device__ __forceinline__ void store_rows(uint16_t* row, const f32x16 (&acc)[D / 32], float f, int h) {
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const u32x2 st = {pack2<BF16>(acc[b][4 * g + 0] * f, acc[b][4 * g + 1] * f),
+                              pack2<BF16>(acc[b][4 * g + 2] * f, acc[b][4 * g + 3] * f)};
+            *reinterpret_cast<u32x2*>(row + b * 32 + 8 * g + 4 * h) = st;
+        }
+}
+
+// Stage `rows` rows starting at r0 of one head into a swizzled LDS tile with global_load_lds
+// (rows past the end repeat row N-1); each of the kWaves waves issues its share of 1 KiB loads.
+template <int D>
+__device__ __forceinline__ void stage_rows(const uint16_t* src_head, int r0, int rows, int N, uint16_t* dst,
+                                           int wave_s, int lane) {
+    constexpr int CPR = D / 8;
+    constexpr int RPI = 64 / CPR;
+    const int per_wave = rows / RPI / kWaves;
+    for (int i = 0; i < per_wave; ++i) {
+        const int g = wave_s * per_wave + i;
+        const int r = RPI * g + lane / CPR;
+        const int ch = (lane % CPR) ^ swz<D>(r);
+        const unsigned src = (unsigned)min(r0 + r, N - 1) * D + 8 * ch;
+        __builtin_amdgcn_global_load_lds((const void*)(src_head + src), (lds_void*)(dst + g * 512), 16, 0, 0);
+    }
+}
+
+template <int D, bool BF16, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
+    float* __restrict__ DELTA, uint16_t* __restrict__ dQ, int N, int n_qt, int G, float c, float scale) {
+    constexpr int DK = D / 16;
+    constexpr int DB = D / 32;
+    constexpr int TILE = kKeyTile * D;
+    static_assert(kKeyTile * D / (64 * 8) % kWaves == 0, "tile loads must split evenly over the waves");
+
+    __shared__ __attribute__((aligned(4096))) uint16_t k_lds0[TILE];
+    __shared__ __attribute__((aligned(4096))) uint16_t k_lds1[TILE];
+    __shared__ __attribute__((aligned(4096))) uint16_t v_lds0[TILE];
+    __shared__ __attribute__((aligned(4096))) uint16_t v_lds1[TILE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int h = lane >> 5;
+    const int lq = lane & 31;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+
+    int bh, qt;
+    map_block(blockIdx.x, G, n_qt, CAUSAL, bh, qt);
+    const int q0 = qt * kRows;
+    const int64_t head = (int64_t)bh * N * D;
+    const uint16_t* Kh = K + head;
+    const uint16_t* Vh = V + head;
+    const int wq0 = q0 + 32 * wave;
+    const int qrow = wq0 + lq;
+    const int qr = min(qrow, N - 1);  // row the lane loads (rows past N repeat N-1, never stored)
+
+    // This lane's query row as the B operand of the first two products: columns 16t + 8h .. +7.
+    // The same columns of o give the lane's half of D = dO . o.
+    u32x4 qreg[DK], dreg[DK];
+    float dsum = 0.f;
+    {
+        const uint16_t* qrp = Q + head + (int64_t)qr * D + 8 * h;
+        const uint16_t* drp = dO + head + (int64_t)qr * D + 8 * h;
+        const uint16_t* orp = O + head + (int64_t)qr * D + 8 * h;
+#pragma unroll
+        for (int t = 0; t < DK; ++t) {
+            qreg[t] = *reinterpret_cast<const u32x4*>(qrp + 16 * t);
+            dreg[t] = *reinterpret_cast<const u32x4*>(drp + 16 * t);
+            dsum = dot8<BF16>(dreg[t], *reinterpret_cast<const u32x4*>(orp + 16 * t), dsum);
+        }
+    }
+    const float Dq = sum_with_partner(dsum);
+    if (h == 0 && qrow < N) DELTA[(int64_t)bh * N + qrow] = Dq;
+    const float lse2 = LSE[(int64_t)bh * N + qr] * kLog2e;  // lse in log2 units
+
+    const int kv_end = CAUSAL ? min(N, q0 + kRows) : N;
+    const int T = (kv_end + kKeyTile - 1) / kKeyTile;
+    const int T_w = CAUSAL ? min(T, (min(wq0 + 32, N) + kKeyTile - 1) / kKeyTile) : T;
+
+    int koff[DK];
+#pragma unroll
+    for (int t = 0; t < DK; ++t) koff[t] = tile_off<D>(lq, 2 * t + h);
+    int tlo[DB], thi[DB];
+    transpose_offsets<D>(lane, tlo, thi);
+
+    f32x16 acc[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) acc[b] = (f32x16){};
+
+    auto tile = [&](int j, const uint16_t* kt, const uint16_t* vt) __attribute__((always_inline)) {
+        const int k0 = j * kKeyTile;
+        const bool masked = (k0 + kKeyTile > N) || (CAUSAL && k0 + kKeyTile - 1 > wq0);
+        // keep the constant parts of the LDS addresses in the instructions (see the dkdv kernel)
+#pragma unroll
+        for (int t = 0; t < DK; ++t) asm volatile("" : "+v"(koff[t]));
+#pragma unroll
+        for (int b = 0; b < DB; ++b) asm volatile("" : "+v"(tlo[b]), "+v"(thi[b]));
+        unsigned dsk[2][8];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            __builtin_amdgcn_sched_barrier(0);  // one 32-key block at a time
+            f32x16 s = {}, dp = {};
+#pragma unroll
+            for (int t = 0; t < DK; ++t) {
+                s = mfma32<BF16>(*reinterpret_cast<const u32x4*>(kt + koff[t] + kb * 32 * D), qreg[t], s);
+                dp = mfma32<BF16>(*reinterpret_cast<const u32x4*>(vt + koff[t] + kb * 32 * D), dreg[t], dp);
+            }
+            if (masked) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    if (key >= N || (CAUSAL && key > qrow)) s[r] = -INFINITY;
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c, -lse2));
+                dsk[kb][r >> 1] = pack2<BF16>(p0 * (dp[r] - Dq), p1 * (dp[r + 1] - Dq));
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // dQ^T += K^T . dS^T over the 64 keys (4 steps of 16)
+#pragma unroll
+        for (int i = 0; i < 4 * DB; ++i) {
+            const int kk = i / DB, b = i % DB;
+            const int kb = kk >> 1, hf = kk & 1;
+            const u32x4 ds = {dsk[kb][4 * hf], dsk[kb][4 * hf + 1], dsk[kb][4 * hf + 2], dsk[kb][4 * hf + 3]};
+            acc[b] = mfma32<BF16>(transposed_operand<D>(kt, tlo, thi, kk, b), ds, acc[b]);
+        }
+    };
+
+    // K(j), V(j) sit in buffer j % 2; the loads of tile j + 1 go out right after the barrier that
+    // makes tile j visible (and frees the buffers of tile j - 1).
+    // T_w as an opaque scalar: with the test j < T_w folded away (non-causal) the compiler keeps
+    // the accumulators of the two unrolled tiles in two register sets and spills.
+    int T_ws = __builtin_amdgcn_readfirstlane(T_w);
+    asm volatile("" : "+s"(T_ws));
+    stage_rows<D>(Kh, 0, kKeyTile, N, k_lds0, wave_s, lane);
+    stage_rows<D>(Vh, 0, kKeyTile, N, v_lds0, wave_s, lane);
+    for (int j = 0; j < T; j += 2) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (j + 1 < T) {
+            stage_rows<D>(Kh, (j + 1) * kKeyTile, kKeyTile, N, k_lds1, wave_s, lane);
+            stage_rows<D>(Vh, (j + 1) * kKeyTile, kKeyTile, N, v_lds1, wave_s, lane);
+        }
+        if (j < T_ws) tile(j, k_lds0, v_lds0);
+        if (j + 1 >= T) break;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (j + 2 < T) {
+            stage_rows<D>(Kh, (j + 2) * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
+            stage_rows<D>(Vh, (j + 2) * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
+        }
+        if (j + 1 < T_ws) tile(j + 1, k_lds1, v_lds1);
+    }
+
+    if (qrow < N) store_rows<D, BF16>(dQ + head + (int64_t)qrow * D, acc, scale, h);
+}
+
+template <int D, bool BF16, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ DELTA,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_kt, int G, float c, float scale) {
+    constexpr int DK = D / 16;
+    constexpr int DB = D / 32;
+    constexpr int TILE = kQueryTile * D;
+    static_assert(kQueryTile * D / (64 * 8) % kWaves == 0, "tile loads must split evenly over the waves");
+
+    // The Q and dO tiles (most reads, several buffers) get the larger alignment so they are placed
+    // in the first 64 KiB, where a constant offset fits the LDS instructions' offset field. K and
+    // V rows follow in one array (V = K + kKeys * D), addressed from one register per k-step.
+    __shared__ __attribute__((aligned(8192))) uint16_t q_lds0[TILE];
+    __shared__ __attribute__((aligned(8192))) uint16_t q_lds1[TILE];
+    __shared__ __attribute__((aligned(8192))) uint16_t do_lds0[TILE];
+    __shared__ __attribute__((aligned(8192))) uint16_t do_lds1[TILE];
+    __shared__ __attribute__((aligned(4096))) uint16_t kv_lds[2 * kKeys * D];  // K rows, then V rows
+    __shared__ __attribute__((aligned(16))) float st_lds[2][2][kQueryTile];    // [buffer][lse2, D][row]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int h = lane >> 5;
+    const int lq = lane & 31;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const int kg = wave & 3;     // key group: keys 32 kg .. 32 kg + 31 of the workgroup
+    const int half = wave >> 2;  // the 32-row half of every query tile this wave takes
+
+    // Causal: key tile 0 meets every query row, so the reversed order of map_block puts the
+    // longest key tiles first.
+    int bh, kt;
+    map_block(blockIdx.x, G, n_kt, CAUSAL, bh, kt);
+    if (CAUSAL) kt = n_kt - 1 - kt;
+    const int k0 = kt * kKeys;
+    const int64_t head = (int64_t)bh * N * D;
+    const uint16_t* Qh = Q + head;
+    const uint16_t* dOh = dO + head;
+    const float* lse_h = LSE + (int64_t)bh * N;
+    const float* del_h = DELTA + (int64_t)bh * N;
+    const int kw0 = k0 + 32 * kg;
+    const int key = kw0 + lq;
+
+    stage_rows<D>(K + head, k0, kKeys, N, kv_lds, wave_s, lane);
+    stage_rows<D>(V + head, k0, kKeys, N, kv_lds + kKeys * D, wave_s, lane);
+
+    // Per-lane element offsets with this wave's row block folded in (the swizzle depends on
+    // row % 16 only, so moving whole 32-row blocks is a plain offset): qoff into a Q or dO tile
+    // (this wave's 32-row half), tlo/thi for the transpose reads of the same rows, and kvp = the
+    // LDS address of this lane's K chunk per k-step (its V chunk is kKeys * D elements further).
+    int qoff[DK], tlo[DB], thi[DB];
+    const lds_u16* kvp[DK];
+    transpose_offsets<D>(lane, tlo, thi);
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+        tlo[b] += 32 * half * D;
+        thi[b] += 32 * half * D;
+    }
+#pragma unroll
+    for (int t = 0; t < DK; ++t) {
+        qoff[t] = tile_off<D>(lq, 2 * t + h) + 32 * half * D;
+        kvp[t] = (const lds_u16*)kv_lds + tile_off<D>(lq, 2 * t + h) + 32 * kg * D;
+    }
+
+    f32x16 dv[DB], dk[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) dv[b] = dk[b] = (f32x16){};
+
+    const int n_steps = (N + kQueryTile - 1) / kQueryTile;
+    const int j0 = CAUSAL ? k0 / kQueryTile : 0;
+
+    // lse (log2 units) and D of the rows of query tile j, staged by wave 0 through registers
+    float st_l = 0.f, st_d = 0.f;
+    auto stats_load = [&](int j) __attribute__((always_inline)) {
+        const int r = min(j * kQueryTile + lane, N - 1);
+        st_l = lse_h[r] * kLog2e;
+        st_d = del_h[r];
+    };
+    auto stats_store = [&](int buf) __attribute__((always_inline)) {
+        st_lds[buf][0][lane] = st_l;
+        st_lds[buf][1][lane] = st_d;
+    };
+
+    // Query rows below skip_below meet none of this wave's keys (causal). The bound is a scalar
+    // the compiler cannot see through: with the test folded away (non-causal) it keeps the
+    // accumulators of the two unrolled steps in two register sets and spills.
+    int skip_below = __builtin_amdgcn_readfirstlane(CAUSAL ? kw0 : -1);
+    asm volatile("" : "+s"(skip_below));
+    // One 32-row half of query tile j against this wave's 32 keys: 32 MFMAs at D = 128.
+    auto step = [&](int j, const uint16_t* qt_, const uint16_t* dot_, int buf) __attribute__((always_inline)) {
+        const int qs = j * kQueryTile + 32 * half;  // first query row of this wave's half
+        if (qs + 31 < skip_below) return;           // every key of this wave is after these rows
+        // Redefining the per-lane offsets each step keeps the compiler from hoisting every
+        // (offset + constant) LDS address of the unrolled loop into a register of its own.
+#pragma unroll
+        for (int t = 0; t < DK; ++t) asm volatile("" : "+v"(qoff[t]), "+v"(kvp[t]));
+#pragma unroll
+        for (int b = 0; b < DB; ++b) asm volatile("" : "+v"(tlo[b]), "+v"(thi[b]));
+        f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int t = 0; t < DK; ++t) {
+            s = mfma32<BF16>(*reinterpret_cast<const u32x4*>(qt_ + qoff[t]), *(const lds_u32x4*)kvp[t], s);
+            dp = mfma32<BF16>(*reinterpret_cast<const u32x4*>(dot_ + qoff[t]),
+                              *(const lds_u32x4*)(kvp[t] + kKeys * D), dp);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // C layout: register r holds query row qs + 8(r/4) + 4h + r%4 of key `key`
+        if (qs + 32 > N || (CAUSAL && qs < kw0 + 31)) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int qrow = qs + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (qrow >= N || (CAUSAL && key > qrow)) s[r] = -INFINITY;
+            }
+        }
+        unsigned pk[8], dsk[8];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int o = 32 * half + 8 * g + 4 * h;
+            const float4 l4 = *reinterpret_cast<const float4*>(&st_lds[buf][0][o]);
+            const float4 d4 = *reinterpret_cast<const float4*>(&st_lds[buf][1][o]);
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[4 * g + 0], c, -l4.x));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[4 * g + 1], c, -l4.y));
+            const float p2 = __builtin_amdgcn_exp2f(fmaf(s[4 * g + 2], c, -l4.z));
+            const float p3 = __builtin_amdgcn_exp2f(fmaf(s[4 * g + 3], c, -l4.w));
+            pk[2 * g] = pack2<BF16>(p0, p1);
+            pk[2 * g + 1] = pack2<BF16>(p2, p3);
+            dsk[2 * g] = pack2<BF16>(p0 * (dp[4 * g + 0] - d4.x), p1 * (dp[4 * g + 1] - d4.y));
+            dsk[2 * g + 1] = pack2<BF16>(p2 * (dp[4 * g + 2] - d4.z), p3 * (dp[4 * g + 3] - d4.w));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // dV^T += dO^T . P and dK^T += Q^T . dS over these 32 rows (2 steps of 16)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const u32x4 pop = {pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]};
+            const u32x4 dop = {dsk[4 * kk], dsk[4 * kk + 1], dsk[4 * kk + 2], dsk[4 * kk + 3]};
+#pragma unroll
+            for (int b = 0; b < DB; ++b) {
+                dv[b] = mfma32<BF16>(transposed_operand<D>(dot_, tlo, thi, kk, b), pop, dv[b]);
+                dk[b] = mfma32<BF16>(transposed_operand<D>(qt_, tlo, thi, kk, b), dop, dk[b]);
+            }
+        }
+    };
+
+    // Q(j), dO(j) and the statistics of tile j sit in buffer (j - j0) % 2. The tensor tiles of
+    // j + 1 are requested right after the barrier that publishes tile j; wave 0 fetches the
+    // statistics of j + 1 into registers at the same time and writes them to LDS at the end of
+    // the step (the buffer they go to was last read in step j - 1, before that barrier).
+    if (wave == 0) stats_load(j0);
+    stage_rows<D>(Qh, j0 * kQueryTile, kQueryTile, N, q_lds0, wave_s, lane);
+    stage_rows<D>(dOh, j0 * kQueryTile, kQueryTile, N, do_lds0, wave_s, lane);
+    if (wave == 0) stats_store(0);
+    for (int j = j0; j < n_steps; j += 2) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (j + 1 < n_steps) {
+            if (wave == 0) stats_load(j + 1);
+            stage_rows<D>(Qh, (j + 1) * kQueryTile, kQueryTile, N, q_lds1, wave_s, lane);
+            stage_rows<D>(dOh, (j + 1) * kQueryTile, kQueryTile, N, do_lds1, wave_s, lane);
+        }
+        step(j, q_lds0, do_lds0, 0);
+        if (j + 1 >= n_steps) break;
+        if (wave == 0) stats_store(1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (j + 2 < n_steps) {
+            if (wave == 0) stats_load(j + 2);
+            stage_rows<D>(Qh, (j + 2) * kQueryTile, kQueryTile, N, q_lds0, wave_s, lane);
+            stage_rows<D>(dOh, (j + 2) * kQueryTile, kQueryTile, N, do_lds0, wave_s, lane);
+        }
+        step(j + 1, q_lds1, do_lds1, 1);
+        if (j + 2 < n_steps && wave == 0) stats_store(0);
+    }
+
+    // The two waves of a key group summed over different query rows: the second half hands its
+    // partial sums over through LDS (the tiles are no longer needed) and the first half stores.
+    // Layout [register][lane]: consecutive lanes hit consecutive banks.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    float* dv_x = reinterpret_cast<float*>(kv_lds + kg * (kKeys / 2) * D);
+    float* dk_x = reinterpret_cast<float*>(kg == 0 ? q_lds0 : kg == 1 ? q_lds1 : kg == 2 ? do_lds0 : do_lds1);
+    if (half == 1) {
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                dv_x[(b * 16 + r) * 64 + lane] = dv[b][r];
+                dk_x[(b * 16 + r) * 64 + lane] = dk[b][r];
+            }
+    }
+    __syncthreads();
+    if (half == 0 && key < N) {
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                dv[b][r] += dv_x[(b * 16 + r) * 64 + lane];
+                dk[b][r] += dk_x[(b * 16 + r) * 64 + lane];
+            }
+        store_rows<D, BF16>(dV + head + (int64_t)key * D, dv, 1.f, h);
+        store_rows<D, BF16>(dK + head + (int64_t)key * D, dk, scale, h);
+    }
+}
+
+template <int D, bool BF16, bool CAUSAL>
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                      void* dq, void* dk, void* dv, float* delta, int N, int BH, float c, float scale,
+                      hipStream_t stream) {
+    const int n_qt = (N + kRows - 1) / kRows, n_kt = (N + kKeys - 1) / kKeys;
+    const int Gq = BH * n_qt, Gk = BH * n_kt;
+    const auto* Q = static_cast<const uint16_t*>(q);
+    const auto* K = static_cast<const uint16_t*>(k);
+    const auto* V = static_cast<const uint16_t*>(v);
+    const auto* dO = static_cast<const uint16_t*>(dout);
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, CAUSAL>), dim3(Gq), dim3(kThreads), 0, stream, Q, K, V,
+                       static_cast<const uint16_t*>(o), dO, lse, delta, static_cast<uint16_t*>(dq), N, n_qt, Gq, c,
+                       scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, CAUSAL>), dim3(Gk), dim3(kThreads), 0, stream, Q, K, V, dO, lse,
+                       delta, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), N, n_kt, Gk, c, scale);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+           void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+           int causal, hipStream_t stream, int dtype) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return FA_ERR_NULL;
+    if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+    if (N * d * 2 > INT32_MAX) return FA_ERR_SHAPE;
+    if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+    const int64_t n_t = (N + kKeys - 1) / kKeys;  // the larger of the two grids
+    if (B > INT32_MAX || H > INT32_MAX || B * H > INT32_MAX / n_t) return FA_ERR_SHAPE;
+    if (B * H * N > INT64_MAX / (d * 2)) return FA_ERR_SHAPE;
+    auto misaligned = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; };
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(dout, 16) ||
+        misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16) || misaligned(lse, 4) || misaligned(delta, 4))
+        return FA_ERR_ALIGN;
+    if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+    const size_t nb = static_cast<size_t>(B * H * N * d * 2);
+    const size_t lb = static_cast<size_t>(B * H * N * 4);
+    const void* ins[6] = {q, k, v, o, dout, lse};
+    const size_t in_sz[6] = {nb, nb, nb, nb, nb, lb};
+    const void* outs[4] = {dq, dk, dv, delta};
+    const size_t out_sz[4] = {nb, nb, nb, lb};
+    for (int a = 0; a < 4; ++a) {
+        for (int i = 0; i < 6; ++i)
+            if (overlaps(outs[a], out_sz[a], ins[i], in_sz[i])) return FA_ERR_ALIAS;
+        for (int b = a + 1; b < 4; ++b)
+            if (overlaps(outs[a], out_sz[a], outs[b], out_sz[b])) return FA_ERR_ALIAS;
+    }
+
+    const float c = scale * kLog2e;
+    const int n = static_cast<int>(N), BH = static_cast<int>(B * H);
+    const bool bf = dtype == FA_BF16;
+    hipError_t e;
+    if (d == 64) {
+        if (bf) e = causal ? launch_bwd<64, true, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, n, BH, c, scale, stream)
+                           : launch_bwd<64, true, false>(q, k, v, o, dout, lse, dq, dk, dv, delta, n, BH, c, scale, stream);
+        else e = causal ? launch_bwd<64, false, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, n, BH, c, scale, stream)
+                        : launch_bwd<64, false, false>(q, k, v, o, dout, lse, dq, dk, dv, delta, n, BH, c, scale, stream);
+    } else {
+        if (bf) e = causal ? launch_bwd<128, true, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, n, BH, c, scale, stream)
+                           : launch_bwd<128, true, false>(q, k, v, o, dout, lse, dq, dk, dv, delta, n, BH, c, scale, stream);
+        else e = causal ? launch_bwd<128, false, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, n, BH, c, scale, stream)
+                        : launch_bwd<128, false, false>(q, k, v, o, dout, lse, dq, dk, dv, delta, n, BH, c, scale, stream);
+    }
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,6 +1,6 @@
 // Exact tiled-softmax attention forward for gfx950 (CDNA4), behind the C ABI of fa_fwd.h.
 //
-// One workgroup = 4 waves = 128 query rows of one (batch, head); each wave owns 32 rows.
+// One workgroup = 8 waves = 256 query rows of one (batch, head); each wave owns 32 rows.
 // The workgroup walks the keys in tiles of 64 (ascending), staging each K and V tile in LDS
 // with coalesced 16-byte global loads that are issued one tile ahead. Per tile and wave:
 //
@@ -31,115 +31,18 @@
 #include <math.h>
 
 #include "fa_fwd.h"
+#include "fa_device.h"
 
 namespace {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
+using namespace fa_detail;
 
 constexpr int kWaves = 8;             // two groups of 4; each SIMD runs one wave of each group
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlockM = 32 * kWaves;  // query rows per workgroup (32 per wave)
 constexpr int kBlockN = 64;           // keys per tile
-constexpr int kXcds = 8;              // MI355X: workgroups are dealt round-robin to 8 XCDs
 constexpr float kDefaultRescaleLog2 = 8.f;  // default reference-max threshold (log2 units)
 constexpr int kDefaultVariant = 1;          // kernel fa_fwd runs: 1 = 32 rows per wave, 2 = 64
-
-template <bool BF16>
-__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
-    if constexpr (BF16) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-    } else {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-    }
-}
-
-// Two fp32 values -> one packed pair, each rounded to nearest even.
-template <bool BF16>
-__device__ __forceinline__ unsigned pack2(float lo, float hi) {
-    if constexpr (BF16) {
-        bf16x2 v = {(__bf16)lo, (__bf16)hi};
-        return __builtin_bit_cast(unsigned, v);
-    } else {
-        f16x2 v = {(_Float16)lo, (_Float16)hi};
-        return __builtin_bit_cast(unsigned, v);
-    }
-}
-
-// acc + lo + hi of a packed pair (the rounded probabilities, so the denominator sums exactly
-// the weights the second product uses).
-template <bool BF16>
-__device__ __forceinline__ float add_pair(unsigned packed, float acc) {
-    if constexpr (BF16) {
-        const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
-    } else {
-        const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), one, acc, false);
-    }
-}
-
-// Value held by the lane 32 positions away (same query row, other half of the keys).
-__device__ __forceinline__ float max_with_partner(float x) {
-    unsigned u = __float_as_uint(x);
-    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_with_partner(float x) {
-    unsigned u = __float_as_uint(x);
-    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Workgroup -> (head, query tile). Workgroups are dealt to XCDs round-robin, so block b runs on
-// XCD b % 8. Non-causal: give each XCD a contiguous range of (head, tile) pairs, so the
-// workgroups resident on one XCD at a time share one head's K/V in that XCD's L2. Causal: each
-// XCD owns whole heads and starts with their longest query tiles (most keys) so the short ones
-// fill in at the end.
-__device__ __forceinline__ void map_block(int bid, int G, int n_qt, bool causal, int& bh, int& qt) {
-    if (G % kXcds == 0) {
-        const int per = G / kXcds;
-        const int x = bid % kXcds, s = bid / kXcds;
-        if (!causal) {
-            const int w = x * per + s;
-            bh = w / n_qt;
-            qt = w % n_qt;
-            return;
-        }
-        if (per % n_qt == 0) {
-            const int hpx = per / n_qt;
-            qt = n_qt - 1 - s / hpx;
-            bh = x * hpx + s % hpx;
-            return;
-        }
-    }
-    bh = bid / n_qt;
-    qt = causal ? n_qt - 1 - bid % n_qt : bid % n_qt;
-}
-
-// K and V tiles live in LDS as kBlockN rows of D elements (no padding); the 16-byte chunk c of
-// row r is stored at chunk position c ^ swz(r). Both read patterns are then free of bank
-// conflicts: the K operand reads one chunk from each of 16 consecutive rows, and the V^T
-// transpose read takes 4 consecutive chunks from each of 4 consecutive rows.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);  // 16 chunks per row
-    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);              // 8 chunks per row
-}
-template <int D>
-__device__ __forceinline__ int tile_off(int r, int c) {  // element offset of (row, chunk)
-    return r * D + ((c ^ swz<D>(r)) << 3);
-}
 
 template <int D, bool BF16, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(
@@ -800,11 +703,6 @@ hipError_t launch_w64(const void* q, const void* k, const void* v, void* o, floa
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qt, G, c, tau_raw);
     return hipGetLastError();
-}
-
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-    return x < y + nb && y < x + na;
 }
 
 }  // namespace

@@ -1,7 +1,10 @@
-"""rocprofv3 harness: kernel time, matrix-core utilisation and device-memory traffic of fa_fwd.
+"""rocprofv3 harness: kernel time, matrix-core utilisation and device-memory traffic.
 
-    python -m exact_tiled_softmax_fa_amd.rocprof_harness [--workload NAME] [--out DIR]
-                                                         [--summary-dir DIR] [--parse-only]
+    python -m exact_tiled_softmax_fa_amd.rocprof_harness [--workload NAME] [--pass fwd|bwd]
+                                                         [--out DIR] [--summary-dir DIR] [--parse-only]
+
+--pass fwd (default) profiles fa_fwd's kernel; --pass bwd profiles the two kernels of fa_bwd
+(fa_bwd_dq_kernel, fa_bwd_dkdv_kernel), each summarised on its own.
 
 Runs four rocprofv3 passes over ``bench.py`` as child processes (this process
 never touches the GPU, so the profiler's preload stays in its own process):
@@ -35,19 +38,27 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-KERNEL_SRC = os.path.join(HERE, "csrc", "fa_fwd.hip")
+# each pass's kernel sources: its own file and the device helpers it includes
+KERNEL_SRCS = {
+    "fwd": [os.path.join(HERE, "csrc", "fa_fwd.hip"), os.path.join(HERE, "csrc", "fa_device.h")],
+    "bwd": [os.path.join(HERE, "csrc", "fa_bwd.hip"), os.path.join(HERE, "csrc", "fa_device.h")],
+}
 N_SIMD = 1024   # MI355X: 256 CUs x 4 SIMDs
 N_XCD = 8
 COPY_MIB = 256
 
 
-def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def kernel_sha(which: str = "fwd") -> str:
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS[which]:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
-def passes(workload: str, out: str, steps: int, warmup: int):
-    bench = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload, "--no-cpu-baseline"]
+def passes(workload: str, out: str, steps: int, warmup: int, which: str = "fwd"):
+    bench = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload, "--pass", which,
+             "--no-cpu-baseline"]
     timed = bench + ["--steps", str(steps), "--warmup", str(warmup)]
     short = bench + ["--steps", "2", "--warmup", "1"]
     copy = ["--copy-ref-mib", str(COPY_MIB)]
@@ -60,9 +71,9 @@ def passes(workload: str, out: str, steps: int, warmup: int):
     ]
 
 
-def run(workload: str, out: str, steps: int, warmup: int, timeout: int) -> list:
+def run(workload: str, out: str, steps: int, warmup: int, timeout: int, which: str = "fwd") -> list:
     cmds = []
-    for name, prof_args, prog in passes(workload, out, steps, warmup):
+    for name, prof_args, prog in passes(workload, out, steps, warmup, which):
         cmd = ["rocprofv3", *prof_args, "--output-format", "csv", "-d", os.path.join(out, name), "-o", name,
                "--", *prog]
         cmds.append(" ".join(shlex.quote(c) for c in cmd))
@@ -93,69 +104,87 @@ def _counter(out, name, counter, kernel):
             if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]]
 
 
-def summarize(workload: str, out: str, steps: int, cmds=None) -> dict:
+def kernels(workload: str, which: str = "fwd"):
+    """(kernel name, matrix-product flops per launch, unavoidable bytes per launch) of a pass.
+    Flops: 2 N^2 d per product per head (halved when causal); forward: the two products of the
+    conventional count; backward: the products each kernel executes (dq: S, dP, dQ; dkdv: S, dP,
+    dV, dK). Unavoidable bytes: every tensor the kernel must read or write, once."""
     sys.path.insert(0, ROOT)
     import workloads
 
     w = workloads.BY_NAME[workload]
-    trace = [r for r in _rows(_find(out, "kt", "kernel_trace.csv")) if "fa_fwd_kernel" in r["Kernel_Name"]]
-    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in trace]
-    timed = durs[-steps:]
-    ms = statistics.mean(timed)
-    fetch_copy = _counter(out, "fetch", "FETCH_SIZE", "copyBuffer")
-    write_copy = _counter(out, "write", "WRITE_SIZE", "copyBuffer")
-    fetch_k = _counter(out, "fetch", "FETCH_SIZE", "fa_fwd_kernel")
-    write_k = _counter(out, "write", "WRITE_SIZE", "fa_fwd_kernel")
-    f_fac = COPY_MIB * 1024.0 / statistics.mean(fetch_copy)
-    w_fac = COPY_MIB * 1024.0 / statistics.mean(write_copy)
-    fetch_b = statistics.mean(fetch_k) * f_fac * 1024
-    write_b = statistics.mean(write_k) * w_fac * 1024
-    gui = statistics.mean(_counter(out, "mfma", "GRBM_GUI_ACTIVE", "fa_fwd_kernel"))
-    busy = statistics.mean(_counter(out, "mfma", "SQ_VALU_MFMA_BUSY_CYCLES", "fa_fwd_kernel"))
-    mops = sum(statistics.mean(v) for v in (_counter(out, "mfma", "SQ_INSTS_VALU_MFMA_MOPS_F16", "fa_fwd_kernel"),
-                                            _counter(out, "mfma", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "fa_fwd_kernel")) if v)
-    util = busy / N_SIMD / (gui / N_XCD)
-    unavoidable = w.B * w.H * (4 * w.N * w.d * 2 + 4 * w.N)
-    rec = {
-        "kernel_sha256": kernel_sha(),
-        "workload": workload,
-        "kernel_ms_mean_timed": ms,
-        "dispatch_ms": durs,
-        "bytes_per_launch": fetch_b + write_b,
-        "fetch_bytes": fetch_b,
-        "write_bytes": write_b,
-        "fetch_scale": f_fac,
-        "write_scale": w_fac,
-        "achieved_gb_per_s": (fetch_b + write_b) / (ms * 1e-3) / 1e9,
-        "unavoidable_bytes": unavoidable,
-        "traffic_over_unavoidable": (fetch_b + write_b) / unavoidable,
-        "mfma_flop_per_launch": mops * 512,
-        "mfma_busy_fraction": util,
-        "tflops_from_trace": w.flops() / (ms * 1e-3) / 1e12,
-        "commands": cmds or [],
-    }
-    return rec
+    BH, N, d = w.B * w.H, w.N, w.d
+    per_product = 2.0 * BH * N * N * d / (2 if w.causal else 1)
+    t = N * d * 2  # one [N, d] tensor of one head
+    if which == "fwd":
+        return [("fa_fwd_kernel", 2 * per_product, BH * (4 * t + 4 * N))]
+    return [("fa_bwd_dq_kernel", 3 * per_product, BH * (6 * t + 8 * N)),   # q k v o dO lse -> dq delta
+            ("fa_bwd_dkdv_kernel", 4 * per_product, BH * (6 * t + 8 * N))]  # q k v dO lse delta -> dk dv
+
+
+def summarize(workload: str, out: str, steps: int, cmds=None, which: str = "fwd") -> list:
+    """One record per kernel of the pass (see ``kernels``)."""
+    recs = []
+    for kname, flops, unavoidable in kernels(workload, which):
+        trace = [r for r in _rows(_find(out, "kt", "kernel_trace.csv")) if kname in r["Kernel_Name"]]
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in trace]
+        timed = durs[-steps:]
+        ms = statistics.mean(timed)
+        fetch_copy = _counter(out, "fetch", "FETCH_SIZE", "copyBuffer")
+        write_copy = _counter(out, "write", "WRITE_SIZE", "copyBuffer")
+        fetch_k = _counter(out, "fetch", "FETCH_SIZE", kname)
+        write_k = _counter(out, "write", "WRITE_SIZE", kname)
+        f_fac = COPY_MIB * 1024.0 / statistics.mean(fetch_copy)
+        w_fac = COPY_MIB * 1024.0 / statistics.mean(write_copy)
+        fetch_b = statistics.mean(fetch_k) * f_fac * 1024
+        write_b = statistics.mean(write_k) * w_fac * 1024
+        gui = statistics.mean(_counter(out, "mfma", "GRBM_GUI_ACTIVE", kname))
+        busy = statistics.mean(_counter(out, "mfma", "SQ_VALU_MFMA_BUSY_CYCLES", kname))
+        mops = sum(statistics.mean(v) for v in (_counter(out, "mfma", "SQ_INSTS_VALU_MFMA_MOPS_F16", kname),
+                                                _counter(out, "mfma", "SQ_INSTS_VALU_MFMA_MOPS_BF16", kname)) if v)
+        util = busy / N_SIMD / (gui / N_XCD)
+        recs.append({
+            "kernel": kname,
+            "kernel_sha256": kernel_sha(which),
+            "workload": workload,
+            "kernel_ms_mean_timed": ms,
+            "dispatch_ms": durs,
+            "bytes_per_launch": fetch_b + write_b,
+            "fetch_bytes": fetch_b,
+            "write_bytes": write_b,
+            "fetch_scale": f_fac,
+            "write_scale": w_fac,
+            "achieved_gb_per_s": (fetch_b + write_b) / (ms * 1e-3) / 1e9,
+            "unavoidable_bytes": unavoidable,
+            "traffic_over_unavoidable": (fetch_b + write_b) / unavoidable,
+            "mfma_flop_per_launch": mops * 512,
+            "mfma_busy_fraction": util,
+            "tflops_from_trace": flops / (ms * 1e-3) / 1e12,
+            "commands": cmds or [],
+            "pass": which,
+        })
+    return recs
 
 
 def write_summary(rec: dict, summary_dir: str):
     os.makedirs(summary_dir, exist_ok=True)
-    name = f"fa_fwd_kernel_{rec['workload']}"
-    lines = [f"# fa_fwd_kernel — {rec['workload']}", ""]
+    name = f"{rec['kernel']}_{rec['workload']}"
+    lines = [f"# {rec['kernel']} — {rec['workload']}", ""]
     if rec["commands"]:
         lines += ["Made by `python -m exact_tiled_softmax_fa_amd.rocprof_harness --workload "
-                  f"{rec['workload']}` (repository root, GPU box), which ran:", "", "```",
+                  f"{rec['workload']} --pass {rec['pass']}` (repository root, GPU box), which ran:", "", "```",
                   *rec["commands"], "```", ""]
     d = rec["dispatch_ms"]
     lines += [
         "## Kernel time (rocprofv3 --kernel-trace --stats)", "",
         f"- dispatches (ms): {', '.join(f'{x:.3f}' for x in d)}",
         f"- mean of the timed dispatches: **{rec['kernel_ms_mean_timed']:.4f} ms** "
-        f"= {rec['tflops_from_trace']:.1f} TFLOP/s (conventional flop count)", "",
+        f"= {rec['tflops_from_trace']:.1f} TFLOP/s (the matrix products this kernel executes)", "",
         "## Device-memory traffic (FETCH_SIZE, WRITE_SIZE; one counter per pass)", "",
         f"- scale factors from a {COPY_MIB} MiB device copy: fetch x{rec['fetch_scale']:.3f}, "
         f"write x{rec['write_scale']:.3f}",
         f"- per launch: {rec['fetch_bytes'] / 2**20:.1f} MiB read + {rec['write_bytes'] / 2**20:.1f} MiB written "
-        f"= {rec['bytes_per_launch'] / 2**20:.1f} MiB; unavoidable (Q, K, V once; O, lse once) "
+        f"= {rec['bytes_per_launch'] / 2**20:.1f} MiB; unavoidable (each tensor read or written once) "
         f"{rec['unavoidable_bytes'] / 2**20:.1f} MiB; ratio {rec['traffic_over_unavoidable']:.3f}",
         f"- achieved device-memory bandwidth: {rec['achieved_gb_per_s']:.1f} GB/s (of about 8000)", "",
         "## Matrix cores (SQ_INSTS_VALU_MFMA_MOPS_*, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE)", "",
@@ -173,6 +202,7 @@ def write_summary(rec: dict, summary_dir: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="B1-H32-N8192-d128-f16")
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"])
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "rocprof"))
     ap.add_argument("--summary-dir", default=os.path.join(ROOT, "gpurun_out", "rocprof"))
     ap.add_argument("--steps", type=int, default=20)
@@ -180,12 +210,12 @@ def main():
     ap.add_argument("--timeout", type=int, default=240, help="seconds per rocprofv3 pass")
     ap.add_argument("--parse-only", action="store_true", help="summarise existing outputs under --out")
     args = ap.parse_args()
-    out = os.path.join(args.out, args.workload)
+    out = os.path.join(args.out, f"{args.which}_{args.workload}")
     cmds = None
     if not args.parse_only:
-        cmds = run(args.workload, out, args.steps, args.warmup, args.timeout)
-    rec = summarize(args.workload, out, args.steps, cmds)
-    write_summary(rec, args.summary_dir)
+        cmds = run(args.workload, out, args.steps, args.warmup, args.timeout, args.which)
+    for rec in summarize(args.workload, out, args.steps, cmds, args.which):
+        write_summary(rec, args.summary_dir)
 
 
 if __name__ == "__main__":

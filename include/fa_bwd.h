@@ -1,0 +1,73 @@
+/*
+ * fa_bwd.h -- backward pass of exact attention on MI355X (gfx950).
+ *
+ * Given the forward inputs q, k, v, its output o and per-row log-sum-exp lse
+ * (from fa_fwd), and the gradient dout = dL/do of some loss L, fa_bwd returns
+ * dq, dk, dv = dL/dq, dL/dk, dL/dv. With p_ij = exp(s_ij - lse_i) the softmax
+ * weights of the forward pass (s_ij = scale * q_i . k_j over the allowed keys):
+ *     dP_ij = dout_i . v_j
+ *     D_i   = dout_i . o_i                   (= sum_j p_ij dP_ij)
+ *     dS_ij = p_ij (dP_ij - D_i)
+ *     dv_j  = sum_i p_ij dout_i
+ *     dk_j  = scale * sum_i dS_ij q_i
+ *     dq_i  = scale * sum_j dS_ij k_j
+ * (the chain rule through the definition of fa_fwd.h). As the pages describe
+ * for the backward pass, only the compact per-row statistic is kept from the
+ * forward pass and the score tiles are recomputed from q, k and lse, so no
+ * N x N matrix reaches device memory ("Decoding flash attention",
+ * bibekananda.in, section "The backward pass"; "FlashAttention tiles exact
+ * softmax without materializing the score matrix", nalar.dev, section
+ * "Backward computation can trade recomputation for stored intermediates").
+ * Allowed keys and the causal convention are those of fa_fwd.h.
+ */
+#ifndef FA_BWD_H
+#define FA_BWD_H
+
+#include "fa_fwd.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * fa_bwd -- enqueue the attention backward pass on `stream`.
+ *
+ * q, k, v, o, dout : device pointers, contiguous row-major [B, H, N, d] of
+ *                    `dtype`, 16-byte aligned; o is fa_fwd's output for the
+ *                    same q, k, v, scale and causal.
+ * lse              : device pointer, contiguous [B, H, N] fp32, fa_fwd's
+ *                    per-row log-sum-exp (natural log); 4-byte aligned.
+ * dq, dk, dv       : device pointers, contiguous [B, H, N, d] of `dtype`,
+ *                    16-byte aligned; receive the gradients, rounded to
+ *                    nearest-even from fp32.
+ * delta            : device pointer, contiguous [B, H, N] fp32, 4-byte
+ *                    aligned; receives D_i = dout_i . o_i (the backward pass
+ *                    computes it first and reads it back; the caller may
+ *                    reuse the buffer after the call completes).
+ * B, H, N, d, scale, causal, stream, dtype : as for fa_fwd, with the same
+ *                    limits (d = 64 or 128; B*H*ceil(N/256) <= 2^31 - 1;
+ *                    N*d*2 < 2^31).
+ *
+ * Ownership: the caller allocates and frees every buffer; the library
+ * allocates nothing and keeps no state between calls. dq, dk, dv and delta
+ * must not overlap each other or any input. Every output element is written
+ * by exactly one thread with a fixed order of summation, so repeated calls
+ * give bit-identical results.
+ * Numerics: products accumulate in fp32 on the matrix cores; p and dS are
+ * rounded to `dtype` as operands of the products that consume them.
+ * Errors: the fa_status codes of fa_fwd.h (FA_ERR_NULL for any NULL pointer,
+ * FA_ERR_ALIGN, FA_ERR_ALIAS for an overlapping output, ...), all returned
+ * before any device work except FA_ERR_LAUNCH. Device faults surface at the
+ * caller's next synchronisation.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const void* dout, const float* lse,
+           void* dq, void* dk, void* dv, float* delta,
+           int64_t B, int64_t H, int64_t N, int64_t d,
+           float scale, int causal, hipStream_t stream, int dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_BWD_H */

@@ -67,7 +67,11 @@ typedef enum fa_status {
  *   unnormalised probabilities stay <= 2^t and most tiles skip the rescale
  *   ("fewer rescaling operations", "Decoding flash attention",
  *   bibekananda.in, "Later versions"). Range [0, 15]; fa_fwd uses 8.
- * variant: kernel variant; 0 (the default kernel) is the only one.
+ * variant: which kernel evaluates it. 0 = the default (variant 1);
+ *   1 = 32 query rows per wave, two waves per SIMD (the fast one);
+ *   2 = 64 query rows per wave, one wave per SIMD (fewer shared-memory reads
+ *   per product, slower; kept as an independently blocked check).
+ *   Both give the same result to rounding; range [0, 2].
  */
 typedef struct fa_fwd_options {
     float rescale_threshold_log2;

@@ -17,9 +17,9 @@ _MIN_EXP = {"f16": -14, "bf16": -126}
 
 
 def ulp(x, dtype):
-    """Spacing of the dtype's grid at |x| (subnormal spacing below the normal range)."""
+    """Spacing of the dtype's grid at |x| (subnormal spacing below the normal range, and at 0)."""
     a = np.abs(np.asarray(x, dtype=np.float64))
-    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.floor(np.log2(np.where(a > 0, a, 2.0 ** _MIN_EXP[dtype])))
     e = np.maximum(e, _MIN_EXP[dtype])
     return np.exp2(e - _MANT[dtype])
 

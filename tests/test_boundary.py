@@ -1,4 +1,4 @@
-"""The C-ABI library without a GPU: it loads, exports what include/fa_fwd.h declares,
+"""The C-ABI library without a GPU: it loads, exports what include/*.h declare,
 and rejects bad arguments synchronously, before any device work.
 
 Pointers passed here are never dereferenced: each call fails validation first.
@@ -10,14 +10,17 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "fa_fwd.h")
+INCLUDE = os.path.join(ROOT, "include")
 PKG = os.path.join(ROOT, "exact_tiled_softmax_fa_amd")
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(fa_\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for f in sorted(os.listdir(INCLUDE)):
+        if f.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, f)).read(), flags=re.S)
+            names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(fa_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -27,7 +30,7 @@ def L():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_fwd", "fa_fwd_ex", "fa_status_string", "fa_version"]
+    assert _declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_ex", "fa_status_string", "fa_version"]
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -118,3 +121,40 @@ def test_argument_errors_precede_option_errors(L):
     st = fa.fa_fwd(None, a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"], a["scale"],
                    a["causal"], a["stream"], a["dtype"], fa.FaOptions(-1.0, 0))
     assert st == 1
+
+
+# fa_bwd: fake, well-aligned, non-overlapping addresses (validation fails before any is used)
+BWD = dict(q=0x100000, k=0x200000, v=0x300000, o=0x400000, dout=0x500000, lse=0x600000, dq=0x700000,
+           dk=0x800000, dv=0x900000, delta=0xA00000, B=1, H=2, N=64, d=64, scale=0.125, causal=0, stream=None,
+           dtype=0)
+
+
+def _bwd(**kw):
+    import exact_tiled_softmax_fa_amd as fa
+    a = dict(BWD)
+    a.update(kw)
+    return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"], a["delta"],
+                     a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"], a["stream"], a["dtype"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    *[(dict(**{p: None}), 1) for p in ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "delta")],
+    (dict(B=0), 2), (dict(N=0), 2), (dict(N=(1 << 24), d=128), 2), (dict(B=1 << 20, H=1 << 20, N=1 << 20), 2),
+    (dict(d=96), 3), (dict(dtype=2), 4),
+    (dict(q=0x100008), 5), (dict(dout=0x500004), 5), (dict(dq=0x700002), 5), (dict(lse=0x600002), 5),
+    (dict(delta=0xA00001), 5),
+    (dict(scale=0.0), 6), (dict(scale=float("nan")), 6),
+    (dict(dq=0x100000), 7), (dict(dk=0x500000 + 64), 7), (dict(dv=0x700000), 7), (dict(delta=0x600000), 7),
+    (dict(delta=0x900000), 7), (dict(dk=0x700000 + 16), 7),
+])
+def test_backward_argument_errors(L, kw, code):
+    assert _bwd(**kw) == code
+
+
+def test_backward_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    import exact_tiled_softmax_fa_amd as fa
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    lse = torch.zeros(1, 1, 8)
+    with pytest.raises(ValueError):
+        fa.backward(q, q, q, q, lse, q)

@@ -47,7 +47,7 @@ def fake_run(tmp_path):
 
 
 def test_summarize_arithmetic(fake_run, tmp_path):
-    rec = rh.summarize("B1-H32-N8192-d128-f16", fake_run, steps=20, cmds=["rocprofv3 ..."])
+    (rec,) = rh.summarize("B1-H32-N8192-d128-f16", fake_run, steps=20, cmds=["rocprofv3 ..."])
     assert rec["kernel_ms_mean_timed"] == pytest.approx(1.0)
     assert rec["fetch_scale"] == pytest.approx(2.0)
     assert rec["write_scale"] == pytest.approx(1.0)
@@ -57,7 +57,7 @@ def test_summarize_arithmetic(fake_run, tmp_path):
     assert rec["mfma_flop_per_launch"] == pytest.approx(2 ** 40)
     assert rec["mfma_busy_fraction"] == pytest.approx(0.5)
     assert rec["unavoidable_bytes"] == 32 * (4 * 8192 * 128 * 2 + 4 * 8192)
-    assert rec["tflops_from_trace"] == pytest.approx(2 ** 40 / 1e-3 / 1e12)
+    assert rec["tflops_from_trace"] == pytest.approx(4 * 32 * 8192 ** 2 * 128 / 1e-3 / 1e12)
     assert rec["kernel_sha256"] == rh.kernel_sha()
     rh.write_summary(rec, str(tmp_path / "summ"))
     j = json.load(open(tmp_path / "summ" / "traffic_fa_fwd_kernel_B1-H32-N8192-d128-f16.json"))
@@ -75,3 +75,14 @@ def test_passes_keep_counters_within_one_pass_limits():
             assert sum(c.startswith("GRBM_") for c in counters) <= 2
             assert len([c for c in counters if c in ("FETCH_SIZE", "WRITE_SIZE")]) <= 1
         assert "--no-cpu-baseline" in prog
+
+
+def test_backward_kernels_work_and_bytes():
+    ks = rh.kernels("B2-H16-N8192-d128-bf16-causal", "bwd")
+    assert [k[0] for k in ks] == ["fa_bwd_dq_kernel", "fa_bwd_dkdv_kernel"]
+    per_product = 2.0 * 32 * 8192 ** 2 * 128 / 2
+    assert ks[0][1] == pytest.approx(3 * per_product) and ks[1][1] == pytest.approx(4 * per_product)
+    assert ks[0][2] == 32 * (6 * 8192 * 128 * 2 + 8 * 8192)
+    assert rh.kernel_sha("bwd") != rh.kernel_sha("fwd")
+    for name, prof_args, prog in rh.passes("B2-H16-N8192-d128-bf16-causal", "/tmp/x", 5, 2, "bwd"):
+        assert prog[prog.index("--pass") + 1] == "bwd"

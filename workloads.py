@@ -16,6 +16,13 @@ Each workload is a forward-attention problem [B, H, N, d]:
   per (b, h), in order, a generator seeded with ``seed + 1000`` draws
   randperm(N)[:rows_per_head]; rows 0 and N-1 are forced in (replacing the last
   draws if absent) and the set is sorted.
+
+The backward pass of a workload also needs the upstream gradient dout = dL/do:
+iid N(0, 1) in fp32 from a generator seeded with ``seed + 2000``, rounded to the
+workload's dtype. Its parity checks on the large problems cover a seeded subset
+of heads (``sample_heads``, generator ``seed + 3000``) and, within them, the
+sampled query rows (for dq) and the same number of sampled keys (for dk, dv;
+``sample_rows`` with generator ``seed + 4000``).
 """
 from dataclasses import dataclass
 from typing import Optional
@@ -100,3 +107,27 @@ def sample_rows(w: Workload):
             rows[r - 2 if rows[r - 1] == 0 else r - 1] = w.N - 1
         out[bh] = np.sort(rows)
     return out
+
+
+def make_dout(w: Workload):
+    """The upstream gradient dout [B, H, N, d] (CPU tensor of the workload's dtype)."""
+    g = torch.Generator(device="cpu").manual_seed(w.seed + 2000)
+    return torch.randn((w.B, w.H, w.N, w.d), generator=g, dtype=torch.float32).to(w.torch_dtype)
+
+
+def sample_heads(w: Workload, count: int):
+    """Sorted flat (b * H + h) indices of `count` heads drawn without replacement."""
+    n = w.B * w.H
+    if count >= n:
+        return np.arange(n, dtype=np.int64)
+    g = torch.Generator(device="cpu").manual_seed(w.seed + 3000)
+    return np.sort(torch.randperm(n, generator=g)[:count].numpy().astype(np.int64))
+
+
+def sample_keys(w: Workload):
+    """int64 array [B*H, R] of keys to check (same recipe as sample_rows, its own generator)."""
+    if w.rows_per_head is None or w.rows_per_head >= w.N:
+        return None
+    shifted = Workload(w.name, w.B, w.H, w.N, w.d, w.dtype, w.causal, w.sigma_qk, w.seed + 3000,
+                       w.rows_per_head)
+    return sample_rows(shifted)
