@@ -1,8 +1,9 @@
 // Exact tiled-softmax attention forward for gfx950 (CDNA4), behind the C ABI of fa_fwd.h.
 //
-// One workgroup = 8 waves = 256 query rows of one (batch, head); each wave owns 32 rows.
-// The workgroup walks the keys in tiles of 64 (ascending), staging each K and V tile in LDS
-// with coalesced 16-byte global loads that are issued one tile ahead. Per tile and wave:
+// One workgroup = 8 waves = 256 query rows of one (batch, head); each wave owns 32 rows, held
+// in registers (one row per lane) for the whole kernel. The workgroup walks the keys in tiles
+// of 64 (ascending), staging each K and V tile in LDS with coalesced 16-byte global loads that
+// are issued one tile ahead. Per tile and wave:
 //
 //   S^T = K_tile . Q^T          v_mfma_f32_32x32x16_{f16,bf16}, fp32 accumulate.
 //                               Computing the transpose puts one query row in each lane
@@ -56,17 +57,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     constexpr int TILE = kBlockN * D;          // elements per tile
     static_assert(IPW >= 1 && IPW * RPI * kWaves == kBlockN, "tile must split evenly over the waves");
 
-    // Two buffers each for K and V, and the Q rows of the workgroup (each wave's 32 rows), all
-    // filled straight from global memory (global_load_lds) in the same swizzled layout. The
-    // K and V buffers come first so that every K/V operand address is a per-lane register plus
-    // an immediate below 64 KiB (the ds_read offset field).
-    // (Separate arrays let the compiler see that the loads into one buffer never alias the
-    // reads of another; the larger alignment of the K/V buffers places them first.)
+    // Two buffers each for K and V, filled straight from global memory (global_load_lds) in the
+    // swizzled layout; 64 KiB in all at D = 128, so every operand address is a per-lane register
+    // plus an immediate below 64 KiB (the ds_read offset field). (Separate arrays let the
+    // compiler see that the loads into one buffer never alias the reads of another.)
     __shared__ __attribute__((aligned(4096))) uint16_t k_lds0[TILE];
     __shared__ __attribute__((aligned(4096))) uint16_t k_lds1[TILE];
     __shared__ __attribute__((aligned(4096))) uint16_t v_lds0[TILE];
     __shared__ __attribute__((aligned(4096))) uint16_t v_lds1[TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t q_lds[kBlockM * D];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -87,7 +85,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int kv_end = CAUSAL ? min(N, q0 + kBlockM) : N;
     const int T = (kv_end + kBlockN - 1) / kBlockN;  // key tiles this workgroup visits
     // tiles this wave computes: causal waves stop at the tile holding their last row
-    const int T_w = CAUSAL ? min(T, (min(wq0 + 32, N) + kBlockN - 1) / kBlockN) : T;
+    // (Non-causal: T_w = T, hidden from the compiler. Folded away, the tests on it disappear and
+    // the compiler keeps the output accumulators of the loop's two exit paths in two register
+    // sets, which spills; a per-lane opaque value keeps the control flow of the causal kernel.)
+    int T_w = CAUSAL ? min(T, (min(wq0 + 32, N) + kBlockN - 1) / kBlockN) : T;
+    if constexpr (!CAUSAL) asm volatile("" : "+v"(T_w));
 
     // Load g of a tile covers rows RPI*g .. RPI*g+RPI-1; lane l writes LDS bytes [1024 g + 16 l,
     // +16), i.e. row RPI*g + l/CPR at chunk position l % CPR, which holds global chunk
@@ -107,20 +109,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
     };
 
-    // This wave's 32 query rows go to q_lds rows 32*wave.. (the B operand of the first product
-    // is read from there each tile, which keeps 32 VGPRs free). Rows past N repeat row N-1;
-    // they are never stored.
+    // This lane's query row as the B operand of the first product (columns 16t + 8h .. +7),
+    // held in registers for the whole kernel. Rows past N repeat row N-1 (never stored).
+    u32x4 qreg[D / 16];
     {
-        constexpr int QPW = 32 / RPI;  // 1 KiB loads per wave for 32 rows
+        const uint16_t* qrp = Qh + (int64_t)min(qrow, N - 1) * D + 8 * h;
 #pragma unroll
-        for (int i = 0; i < QPW; ++i) {
-            const int r = RPI * i + lane / CPR;  // row within the wave's 32
-            const int ch = (lane % CPR) ^ swz<D>(r);
-            const unsigned src = (unsigned)min(wq0 + r, N - 1) * D + 8 * ch;
-            __builtin_amdgcn_global_load_lds((const void*)(Qh + src), (lds_void*)(q_lds + (32 * wave + RPI * i) * D), 16, 0, 0);
-        }
+        for (int t = 0; t < D / 16; ++t) qreg[t] = *reinterpret_cast<const u32x4*>(qrp + 16 * t);
     }
-    const uint16_t* q_wave = q_lds + 32 * wave * D;
 
     f32x16 oacc[DB];
 #pragma unroll
@@ -165,7 +161,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     };
     // Q^T (B operand of the first product): lane holds row qrow, columns 16t + 8h .. +7.
     auto q_operand = [&](int t) __attribute__((always_inline)) {
-        return *reinterpret_cast<const u32x4*>(q_wave + koff[t]);
+        return qreg[t];
     };
     auto p_operand = [&](int kk) __attribute__((always_inline)) {
         const int kb = kk >> 1, hf = kk & 1;
@@ -274,8 +270,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             // issues, and one pair of exponentials follows each MFMA; sched_barrier(0) pins that
             // order so the LDS latency stays behind two MFMAs instead of stalling every one.
             constexpr int NQ = 2 * DK;  // 16 MFMAs for D = 128, 8 for D = 64
-            u32x4 ka[NQ], qa[DK];
-            qa[0] = q_operand(0);
+            u32x4 ka[NQ];
             ka[0] = k_operand(k_nxt, 0, 0);
             ka[1] = k_operand(k_nxt, 0, 1);
 #pragma unroll
@@ -283,11 +278,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 const int t = i >> 1, kb = i & 1;
                 if (i + 2 < NQ) {
                     const int t2 = (i + 2) >> 1, kb2 = (i + 2) & 1;
-                    if (kb2 == 0) qa[t2] = q_operand(t2);
                     ka[i + 2] = k_operand(k_nxt, t2, kb2);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                s_nxt[kb] = mfma32<BF16>(ka[i], qa[t], t == 0 ? (f32x16){} : s_nxt[kb]);
+                s_nxt[kb] = mfma32<BF16>(ka[i], qreg[t], t == 0 ? (f32x16){} : s_nxt[kb]);
                 __builtin_amdgcn_sched_barrier(0);
                 // exponentials: pair i of the 16 pairs of S^T(j) held by this lane (NQ == 16),
                 // or pairs 2i, 2i+1 when D = 64 (NQ == 8)
@@ -421,7 +415,8 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(1, 1)
 
     const int kv_end = CAUSAL ? min(N, q0 + kBlockMB) : N;
     const int T = (kv_end + kBlockN - 1) / kBlockN;
-    const int T_w = CAUSAL ? min(T, (min(wq0 + 64, N) + kBlockN - 1) / kBlockN) : T;
+    int T_w = CAUSAL ? min(T, (min(wq0 + 64, N) + kBlockN - 1) / kBlockN) : T;
+    if constexpr (!CAUSAL) asm volatile("" : "+v"(T_w));  // as in the first kernel
 
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     auto issue = [&](const uint16_t* src_head, int j, uint16_t* dst) __attribute__((always_inline)) {
