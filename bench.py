@@ -1,11 +1,14 @@
 """Throughput of the attention forward (or backward) pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd]
-                    [--no-cpu-baseline]
+                    [--splits S] [--no-cpu-baseline]
 
 A step is one fa_fwd call over the whole workload (every query row of every
 head), with q, k, v already resident in device memory. The default workload is
 B=1, H=32, N=8192, d=128, non-causal, fp16. Prints one JSON line.
+
+--splits S times fa_fwd_splitkv with S key splits (0: the library's heuristic) instead of
+fa_fwd; the roofline then covers both of its kernels (split reduction and merge).
 
 --pass bwd times one fa_bwd call instead (dq, dk, dv from q, k, v, o, lse and a
 seeded dout, all resident), priced by the conventional backward count of 2.5x
@@ -126,6 +129,8 @@ def main():
     ap.add_argument("--workload", default=workloads.HEADLINE.name, choices=sorted(workloads.BY_NAME))
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
                     help="time the forward pass (default) or the backward pass")
+    ap.add_argument("--splits", type=int, default=None,
+                    help="run the forward pass as split-KV with this many splits (0: heuristic)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="before timing, run 3 plain device copies of this many MiB (a known-size "
@@ -159,6 +164,15 @@ def main():
     def step():
         fa.forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
 
+    splits = None
+    if args.splits is not None and args.which == "fwd":
+        splits = args.splits or fa.splitkv_heuristic(w.B, w.H, w.N, w.d, w.causal)
+        ws = torch.empty(max(1, fa.splitkv_workspace_size(w.B, w.H, w.N, w.d, splits)), dtype=torch.uint8,
+                         device="cuda")
+
+        def step():  # noqa: F811
+            fa.forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, num_splits=splits, workspace=ws)
+
     if args.which == "bwd":
         step()
         dout = workloads.make_dout(w).cuda()
@@ -187,8 +201,9 @@ def main():
     value = flops / (wall / args.steps) / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     out = {
-        "metric": (HEADLINE_METRIC if w.name == workloads.HEADLINE.name and args.which == "fwd"
-                   else f"{args.which} attention TFLOP/s ({w.name})"),
+        "metric": (HEADLINE_METRIC if w.name == workloads.HEADLINE.name and args.which == "fwd" and splits is None
+                   else f"{args.which} attention TFLOP/s ({w.name}"
+                        + (f", split-KV {splits}" if splits is not None else "") + ")"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -202,6 +217,7 @@ def main():
         "data": "synthetic",
         "pct_mfma_peak": round(100.0 * value / PEAK_MFMA_F16_TFLOPS, 2),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "num_splits": splits,
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "none"},
         "roofline": {
             "bound": "mfma",
@@ -209,8 +225,9 @@ def main():
             "peak": PEAK_MFMA_F16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_MFMA_F16_TFLOPS, 4),
-            "traffic": measured_traffic(w.name) if args.which == "fwd" else None,
-            "kernel": KERNEL_NAME if args.which == "fwd" else "fa_bwd_dq_kernel + fa_bwd_dkdv_kernel",
+            "traffic": measured_traffic(w.name) if args.which == "fwd" and splits is None else None,
+            "kernel": ("fa_bwd_dq_kernel + fa_bwd_dkdv_kernel" if args.which == "bwd" else
+                       "fa_fwd_kernel (split) + fa_merge_kernel" if splits is not None else KERNEL_NAME),
             "kernel_ms": round(kernel_ms, 4),
         },
     }

@@ -66,6 +66,12 @@ def lib():
         ]
         L.fa_fwd_ex.restype = ctypes.c_int
         L.fa_fwd_ex.argtypes = L.fa_fwd.argtypes + [ctypes.POINTER(FaOptions)]
+        L.fa_fwd_splitkv.restype = ctypes.c_int
+        L.fa_fwd_splitkv.argtypes = L.fa_fwd.argtypes + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t]
+        L.fa_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
+        L.fa_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
+        L.fa_fwd_splitkv_heuristic.restype = ctypes.c_int
+        L.fa_fwd_splitkv_heuristic.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
         L.fa_bwd.restype = ctypes.c_int
         L.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
@@ -97,13 +103,31 @@ def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype, options=No
                                ctypes.byref(options)))
 
 
+def fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype, num_splits, workspace,
+                   workspace_bytes) -> int:
+    """Raw call of the C entry point fa_fwd_splitkv; returns the status code."""
+    return int(lib().fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, float(scale), int(causal), stream, int(dtype),
+                                    int(num_splits), workspace, int(workspace_bytes)))
+
+
+def splitkv_workspace_size(B, H, N, d, num_splits) -> int:
+    return int(lib().fa_fwd_splitkv_workspace_size(B, H, N, d, int(num_splits)))
+
+
+def splitkv_heuristic(B, H, N, d, causal) -> int:
+    return int(lib().fa_fwd_splitkv_heuristic(B, H, N, d, int(bool(causal))))
+
+
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale=None,
             out: torch.Tensor = None, lse: torch.Tensor = None, return_lse: bool = True,
-            rescale_threshold_log2=None, variant: int = 0):
+            rescale_threshold_log2=None, variant: int = 0, num_splits=None, workspace: torch.Tensor = None):
     """Attention forward on the current stream of q's device. See the module docstring.
 
     rescale_threshold_log2 / variant: the fa_fwd_options of include/fa_fwd.h (None and 0 keep the
-    library defaults, i.e. plain fa_fwd)."""
+    library defaults, i.e. plain fa_fwd).
+    num_splits: None for fa_fwd / fa_fwd_ex; an int runs fa_fwd_splitkv with that many key splits
+    (0: the library's heuristic). workspace: a device tensor of at least
+    splitkv_workspace_size(...) bytes; allocated here when not given."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
@@ -129,6 +153,25 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
     if lse is not None and (lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous()
                             or lse.device != q.device):
         raise ValueError("lse must be a contiguous float32 tensor [B, H, N] on q's device")
+    if num_splits is not None:
+        if rescale_threshold_log2 is not None or variant != 0:
+            raise ValueError("num_splits cannot be combined with rescale_threshold_log2 or variant")
+        if num_splits == 0:
+            num_splits = splitkv_heuristic(B, H, N, d, causal)
+        need = splitkv_workspace_size(B, H, N, d, num_splits)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        elif not workspace.is_cuda or workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on q's device")
+        with torch.cuda.device(q.device):
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+            st = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                lse.data_ptr() if lse is not None else None, B, H, N, d, scale, causal, stream,
+                                _DTYPES[q.dtype], num_splits, workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size())
+        if st != 0:
+            raise FaError(st, status_string(st))
+        return (out, lse) if return_lse else out
     options = None
     if rescale_threshold_log2 is not None or variant != 0:
         options = FaOptions(8.0 if rescale_threshold_log2 is None else float(rescale_threshold_log2), int(variant))

@@ -31,6 +31,8 @@
 #include <stdint.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include "fa_fwd.h"
 #include "fa_device.h"
 
@@ -45,10 +47,14 @@ constexpr int kBlockN = 64;           // keys per tile
 constexpr float kDefaultRescaleLog2 = 8.f;  // default reference-max threshold (log2 units)
 constexpr int kDefaultVariant = 1;          // kernel fa_fwd runs: 1 = 32 rows per wave, 2 = 64
 
-template <int D, bool BF16, bool CAUSAL>
+// SPLIT: the key range of every query tile is cut into n_split equal runs of tiles, one per
+// workgroup; each writes its partial result (O normalised over its own keys, in fp32, and the
+// log-sum-exp of its keys) to PO / PL, and fa_merge_kernel combines them (split-KV).
+template <int D, bool BF16, bool CAUSAL, bool SPLIT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qt, int G, float c, float tau_raw) {
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qt, int G, float c, float tau_raw,
+    int n_split = 1, float* __restrict__ PO = nullptr, float* __restrict__ PL = nullptr) {
     constexpr int DK = D / 16;                 // k-steps of the first product
     constexpr int DB = D / 32;                 // 32-column blocks of the output
     constexpr int CPR = D / 8;                 // 16-byte chunks per row
@@ -72,8 +78,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int h = lane >> 5;   // which half of the keys of a 32-key block this lane holds
     const int lq = lane & 31;  // query row within the wave
 
-    int bh, qt;
-    map_block(blockIdx.x, G, n_qt, CAUSAL, bh, qt);
+    // With SPLIT, a "virtual head" vh = bh * n_split + split takes the place of bh in the map, so
+    // the workgroups that share one split's keys of one head sit together on an XCD.
+    int vh, qt;
+    map_block(blockIdx.x, G, n_qt, CAUSAL, vh, qt);
+    const int bh = SPLIT ? vh / n_split : vh;
     const int q0 = qt * kBlockM;
     const int64_t head = (int64_t)bh * N * D;
     const uint16_t* Qh = Q + head;
@@ -83,12 +92,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int qrow = wq0 + lq;       // this lane's query row
 
     const int kv_end = CAUSAL ? min(N, q0 + kBlockM) : N;
-    const int T = (kv_end + kBlockN - 1) / kBlockN;  // key tiles this workgroup visits
+    const int T_all = (kv_end + kBlockN - 1) / kBlockN;  // key tiles of this query tile
+    // tiles tb .. tb + T - 1 are this workgroup's (all of them without SPLIT); tile indices below
+    // are relative to tb
+    int tb = 0, T = T_all;
+    if constexpr (SPLIT) {
+        const int per = (T_all + n_split - 1) / n_split;
+        tb = (vh % n_split) * per;
+        T = max(0, min(T_all, tb + per) - tb);
+    }
     // tiles this wave computes: causal waves stop at the tile holding their last row
     // (Non-causal: T_w = T, hidden from the compiler. Folded away, the tests on it disappear and
     // the compiler keeps the output accumulators of the loop's two exit paths in two register
     // sets, which spills; a per-lane opaque value keeps the control flow of the causal kernel.)
-    int T_w = CAUSAL ? min(T, (min(wq0 + 32, N) + kBlockN - 1) / kBlockN) : T;
+    int T_w = CAUSAL ? max(0, min(T, (min(wq0 + 32, N) + kBlockN - 1) / kBlockN - tb)) : T;
     if constexpr (!CAUSAL) asm volatile("" : "+v"(T_w));
 
     // Load g of a tile covers rows RPI*g .. RPI*g+RPI-1; lane l writes LDS bytes [1024 g + 16 l,
@@ -98,7 +115,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // Offsets inside one head fit in 32 bits (the host limits N * d * 2 bytes to < 2^31).
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // scalar copy for LDS destinations
     auto issue = [&](const uint16_t* src_head, int j, uint16_t* dst) __attribute__((always_inline)) {
-        const int k0 = j * kBlockN;
+        const int k0 = (tb + j) * kBlockN;
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
             const int g = wave_s * IPW + i;
@@ -190,7 +207,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     };
     // keys past the end, and (causal) keys after the query, become -inf before the max
     auto mask = [&](int t, f32x16 (&sd)[2]) __attribute__((always_inline)) {
-        const int k0 = t * kBlockN;
+        const int k0 = (tb + t) * kBlockN;
         if ((k0 + kBlockN > N) || (CAUSAL && k0 + kBlockN - 1 > wq0)) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -344,6 +361,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // ---- epilogue: O = o~ / l, lse = m*scale + ln l ----
     const float l_tot = sum_with_partner(l_run);
     const float l_lse = BF16 ? sum_with_partner(l_f32) : l_tot;  // both halves active here
+    if constexpr (SPLIT) {
+        // partial result over this split's keys; a row none of whose keys fall in the split
+        // (l = 0) gets O = 0 and lse = -inf, i.e. zero weight in the merge
+        if (qrow < N) {
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            float* prow = PO + ((int64_t)vh * N + qrow) * D;
+#pragma unroll
+            for (int b = 0; b < DB; ++b)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float4 st = {oacc[b][4 * g + 0] * inv, oacc[b][4 * g + 1] * inv,
+                                       oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv};
+                    *reinterpret_cast<float4*>(prow + b * 32 + 8 * g + 4 * h) = st;
+                }
+            if (h == 0) {
+                // [0]: log-sum-exp of the denominator O was normalised by (the merge weights);
+                // [1]: of the unrounded sum (the final lse; the same value in f16)
+                const float mcf = (m_run == -INFINITY) ? 0.f : m_run * c;
+                const float2 ls = {l_tot > 0.f ? (mcf + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY,
+                                   l_lse > 0.f ? (mcf + __log2f(l_lse)) * 0.69314718055994531f : -INFINITY};
+                *reinterpret_cast<float2*>(PL + 2 * ((int64_t)vh * N + qrow)) = ls;
+            }
+        }
+        return;
+    }
     if (qrow < N) {
         const float inv = 1.f / l_tot;
         uint16_t* orow = O + head + (int64_t)qrow * D;
@@ -682,6 +724,68 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(1, 1)
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Merge of split-KV partial results. Each split s of a row holds O_s, its output normalised over
+// the split's own keys, and L_s, the log-sum-exp of the split's logits. Rescaling every split to a
+// common reference (the rescaling identity of "transformer math: flash attention math",
+// aicassindra.com, "The rescaling identity, derived") gives exact attention over all keys, since
+// grouping and order of the key blocks never enter the result (same page, "Proof of exactness"):
+//     lse = ln sum_s exp(L_s),      o = sum_s exp(L_s - lse) O_s.
+// One thread per (row, 8 output columns); memory-bound. PL holds two L per row (see the kernel).
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__ PO, const float* __restrict__ PL,
+                                                       uint16_t* __restrict__ O, float* __restrict__ LSE, int N,
+                                                       int n_split, int64_t total) {
+    constexpr int CPR = D / 8;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= total) return;  // total = B * H * N * CPR
+    const int64_t row = t / CPR;  // bh * N + i
+    const int ch = (int)(t % CPR);
+    const int64_t bh = row / N, i = row % N;
+    const int64_t first = bh * n_split * (int64_t)N + i;  // partial (bh, split 0, i); split s is + s * N
+    float mw = -INFINITY, ml = -INFINITY;
+    for (int sp = 0; sp < n_split; ++sp) {
+        const float2 L = *reinterpret_cast<const float2*>(PL + 2 * (first + (int64_t)sp * N));
+        mw = fmaxf(mw, L.x);
+        ml = fmaxf(ml, L.y);
+    }
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f, lsum = 0.f;
+    for (int sp = 0; sp < n_split; ++sp) {
+        const int64_t pr = first + (int64_t)sp * N;
+        const float2 L = *reinterpret_cast<const float2*>(PL + 2 * pr);
+        // exp2 of a non-positive argument; a split with no keys for this row has L = -inf: weight 0
+        const float w = __builtin_amdgcn_exp2f((L.x - mw) * 1.4426950408889634f);
+        lsum += __builtin_amdgcn_exp2f((L.y - ml) * 1.4426950408889634f);
+        wsum += w;
+        const float4* src = reinterpret_cast<const float4*>(PO + pr * D + 8 * ch);
+        const float4 a = src[0], b = src[1];
+        acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
+        acc[4] += w * b.x; acc[5] += w * b.y; acc[6] += w * b.z; acc[7] += w * b.w;
+    }
+    const float inv = 1.f / wsum;  // split 0 holds key 0 of every row, so wsum >= 1
+    const u32x4 st = {pack2<BF16>(acc[0] * inv, acc[1] * inv), pack2<BF16>(acc[2] * inv, acc[3] * inv),
+                      pack2<BF16>(acc[4] * inv, acc[5] * inv), pack2<BF16>(acc[6] * inv, acc[7] * inv)};
+    *reinterpret_cast<u32x4*>(O + row * D + 8 * ch) = st;
+    if (LSE != nullptr && ch == 0) LSE[row] = ml + __log2f(lsum) * 0.69314718055994531f;
+}
+
+template <int D, bool BF16, bool CAUSAL>
+hipError_t launch_split(const void* q, const void* k, const void* v, void* o, float* lse, int N, int n_qt, int BH,
+                        float c, float tau_raw, int n_split, float* po, float* pl, hipStream_t stream) {
+    const int G = BH * n_split * n_qt;
+    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, true>), dim3(G), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qt, G, c, tau_raw,
+                       n_split, po, pl);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t total = (int64_t)BH * N * (D / 8);
+    hipLaunchKernelGGL((fa_merge_kernel<D, BF16>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, po, pl,
+                       static_cast<uint16_t*>(o), lse, N, n_split, total);
+    return hipGetLastError();
+}
+
 template <int D, bool BF16, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int N, int n_qt, int G,
                   float c, float tau_raw, hipStream_t stream) {
@@ -700,38 +804,17 @@ hipError_t launch_w64(const void* q, const void* k, const void* v, void* o, floa
     return hipGetLastError();
 }
 
-}  // namespace
-
-extern "C" {
-
-int fa_version(void) { return 100; }
-
-const char* fa_status_string(int status) {
-    switch (status) {
-        case FA_OK: return "ok";
-        case FA_ERR_NULL: return "q, k, v or o is NULL";
-        case FA_ERR_SHAPE: return "B, H and N must be >= 1 and within the size limits";
-        case FA_ERR_HEAD_DIM: return "head dimension d must be 64 or 128";
-        case FA_ERR_DTYPE: return "dtype must be FA_F16 or FA_BF16";
-        case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
-        case FA_ERR_SCALE: return "scale must be finite and > 0";
-        case FA_ERR_ALIAS: return "o and lse must not overlap the inputs or each other";
-        case FA_ERR_LAUNCH: return "kernel launch failed";
-        case FA_ERR_OPTION: return "fa_fwd_options out of range (rescale threshold 0..15, variant 0..2)";
-        default: return "unknown status";
-    }
-}
-
-int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
-              int64_t d, float scale, int causal, hipStream_t stream, int dtype, const fa_fwd_options* opts) {
+// Checks shared by the forward entry points (everything but options and workspace). n_split
+// multiplies the grid.
+int validate(const void* q, const void* k, const void* v, const void* o, const float* lse, int64_t B, int64_t H,
+             int64_t N, int64_t d, float scale, int dtype, int64_t n_split) {
     if (!q || !k || !v || !o) return FA_ERR_NULL;
     if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
     if (N * d * 2 > INT32_MAX) return FA_ERR_SHAPE;  // one head of q, k or v stays under 2 GiB
     if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
     const int64_t n_qt = (N + kBlockM - 1) / kBlockM;
-    if (B > INT32_MAX || H > INT32_MAX || B * H > INT32_MAX / n_qt) return FA_ERR_SHAPE;
-    const int64_t G = B * H * n_qt;
+    if (B > INT32_MAX || H > INT32_MAX || B * H > INT32_MAX / (n_qt * n_split)) return FA_ERR_SHAPE;
     if (B * H * N > INT64_MAX / (d * 2)) return FA_ERR_SHAPE;
     auto misaligned = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; };
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
@@ -745,6 +828,40 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
     if (lse && (overlaps(lse, lbytes, q, nbytes) || overlaps(lse, lbytes, k, nbytes) ||
                 overlaps(lse, lbytes, v, nbytes) || overlaps(lse, lbytes, o, nbytes)))
         return FA_ERR_ALIAS;
+    return FA_OK;
+}
+
+constexpr int kMaxSplits = 64;
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return 200; }
+
+const char* fa_status_string(int status) {
+    switch (status) {
+        case FA_OK: return "ok";
+        case FA_ERR_NULL: return "q, k, v or o is NULL";
+        case FA_ERR_SHAPE: return "B, H and N must be >= 1 and within the size limits";
+        case FA_ERR_HEAD_DIM: return "head dimension d must be 64 or 128";
+        case FA_ERR_DTYPE: return "dtype must be FA_F16 or FA_BF16";
+        case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+        case FA_ERR_SCALE: return "scale must be finite and > 0";
+        case FA_ERR_ALIAS: return "o and lse must not overlap the inputs or each other";
+        case FA_ERR_LAUNCH: return "kernel launch failed";
+        case FA_ERR_OPTION: return "option out of range (rescale threshold 0..15, variant 0..2, splits 1..64)";
+        case FA_ERR_WORKSPACE: return "workspace is NULL, misaligned, too small or overlaps an argument";
+        default: return "unknown status";
+    }
+}
+
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
+              int64_t d, float scale, int causal, hipStream_t stream, int dtype, const fa_fwd_options* opts) {
+    const int st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype, 1);
+    if (st != FA_OK) return st;
+    const int64_t n_qt = (N + kBlockM - 1) / kBlockM;
+    const int64_t G = B * H * n_qt;
     // The reference max moves only when a score exceeds it by more than tau (log2 units), so the
     // unnormalised p stay <= 2^tau and most tiles skip the rescale; tau = 0 moves it on every
     // increase, the loop exactly as the pages write it.
@@ -787,6 +904,83 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
            int64_t d, float scale, int causal, hipStream_t stream, int dtype) {
     return fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype, nullptr);
+}
+
+size_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int num_splits) {
+    if (num_splits <= 1 || num_splits > kMaxSplits || B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+    if (B * H > INT64_MAX / N / (d + 2) / 4 / num_splits) return 0;
+    return static_cast<size_t>(num_splits * B * H * N * (d + 2) * 4);  // fp32 O_s [.., d] and two L_s per row
+}
+
+int fa_fwd_splitkv_heuristic(int64_t B, int64_t H, int64_t N, int64_t d, int causal) {
+    if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 1;
+    // Model, in microseconds. One workgroup runs per CU at a time (its registers fill the CU), so
+    // G query tiles cut in S splits take ceil(G S / 256) rounds. A round costs the split's share of
+    // the key tiles plus about two tiles of fill and drain, at about 2.2 us per 256 x 64 tile at
+    // d = 128 (1000 TFLOP/s over 256 CUs); the merge moves (d + 2) * 4 bytes per row and split at
+    // about 5 TB/s. Causal query tiles hold half the keys on average. (Measured on the thin grid
+    // B1 H2 N16384 d128: 2 splits best, 4 and 8 slower by 3% and 10%; the model says 4% and 12%.)
+    constexpr int64_t kCUs = 256;
+    const int64_t n_qt = (N + kBlockM - 1) / kBlockM;
+    const int64_t G = B * H * n_qt;
+    const double tiles = (double)((N + kBlockN - 1) / kBlockN) / (causal ? 2.0 : 1.0);
+    const double tile_us = 2.2 * (double)d / 128.0;
+    const double merge_us = (double)(B * H * N) * (double)(d + 2) * 4.0 / 5e12 * 1e6;
+    auto cost = [&](int64_t sp) {
+        const double rounds = (double)((G * sp + kCUs - 1) / kCUs);
+        return rounds * (tiles / (double)sp + 2.0) * tile_us + (sp > 1 ? (double)sp * merge_us : 0.0);
+    };
+    const int64_t s_max = std::max<int64_t>(1, std::min<int64_t>(kMaxSplits, (int64_t)(tiles / 4)));
+    int64_t best = 1;
+    double best_t = cost(1);
+    for (int64_t sp = 2; sp <= s_max; ++sp) {
+        const double t = cost(sp);
+        if (t < best_t) {
+            best_t = t;
+            best = sp;
+        }
+    }
+    return static_cast<int>(best);
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                   int64_t N, int64_t d, float scale, int causal, hipStream_t stream, int dtype, int num_splits,
+                   void* workspace, size_t workspace_bytes) {
+    if (num_splits < 1 || num_splits > kMaxSplits) {
+        const int st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype, 1);
+        return st != FA_OK ? st : FA_ERR_OPTION;
+    }
+    const int st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype, num_splits);
+    if (st != FA_OK) return st;
+    if (num_splits == 1) return fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype);
+    const size_t need = fa_fwd_splitkv_workspace_size(B, H, N, d, num_splits);
+    const size_t nbytes = static_cast<size_t>(B * H * N * d * 2);
+    const size_t lbytes = static_cast<size_t>(B * H * N * 4);
+    if (!workspace || need == 0 || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15) ||
+        overlaps(workspace, need, q, nbytes) || overlaps(workspace, need, k, nbytes) ||
+        overlaps(workspace, need, v, nbytes) || overlaps(workspace, need, o, nbytes) ||
+        (lse && overlaps(workspace, need, lse, lbytes)))
+        return FA_ERR_WORKSPACE;
+    float* po = static_cast<float*>(workspace);
+    float* pl = po + num_splits * B * H * N * d;
+    const float c = scale * 1.4426950408889634f;
+    const float tau_raw = kDefaultRescaleLog2 / c;
+    const int n = static_cast<int>(N), nq = static_cast<int>((N + kBlockM - 1) / kBlockM);
+    const int bh = static_cast<int>(B * H);
+    const bool bf = dtype == FA_BF16;
+    hipError_t e;
+    if (d == 64) {
+        if (bf) e = causal ? launch_split<64, true, true>(q, k, v, o, lse, n, nq, bh, c, tau_raw, num_splits, po, pl, stream)
+                           : launch_split<64, true, false>(q, k, v, o, lse, n, nq, bh, c, tau_raw, num_splits, po, pl, stream);
+        else e = causal ? launch_split<64, false, true>(q, k, v, o, lse, n, nq, bh, c, tau_raw, num_splits, po, pl, stream)
+                        : launch_split<64, false, false>(q, k, v, o, lse, n, nq, bh, c, tau_raw, num_splits, po, pl, stream);
+    } else {
+        if (bf) e = causal ? launch_split<128, true, true>(q, k, v, o, lse, n, nq, bh, c, tau_raw, num_splits, po, pl, stream)
+                           : launch_split<128, true, false>(q, k, v, o, lse, n, nq, bh, c, tau_raw, num_splits, po, pl, stream);
+        else e = causal ? launch_split<128, false, true>(q, k, v, o, lse, n, nq, bh, c, tau_raw, num_splits, po, pl, stream)
+                        : launch_split<128, false, false>(q, k, v, o, lse, n, nq, bh, c, tau_raw, num_splits, po, pl, stream);
+    }
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 }  // extern "C"

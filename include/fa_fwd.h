@@ -24,6 +24,7 @@
 #ifndef FA_FWD_H
 #define FA_FWD_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -49,7 +50,9 @@ typedef enum fa_status {
     FA_ERR_SCALE = 6,     /* scale is not finite and > 0 */
     FA_ERR_ALIAS = 7,     /* o or lse overlaps an input, or o overlaps lse */
     FA_ERR_LAUNCH = 8,    /* the kernel launch failed (hipGetLastError) */
-    FA_ERR_OPTION = 9     /* an fa_fwd_options field is out of range */
+    FA_ERR_OPTION = 9,    /* an fa_fwd_options field or num_splits is out of range */
+    FA_ERR_WORKSPACE = 10 /* fa_fwd_splitkv: workspace NULL, not 16-byte aligned, smaller than
+                             fa_fwd_splitkv_workspace_size, or overlapping an argument */
 } fa_status;
 
 /*
@@ -118,6 +121,42 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               int64_t B, int64_t H, int64_t N, int64_t d,
               float scale, int causal, hipStream_t stream, int dtype,
               const fa_fwd_options* opts);
+
+/*
+ * fa_fwd_splitkv -- fa_fwd with the keys of every query tile cut into num_splits runs that run
+ * as separate workgroups (split-KV), for shapes whose B*H*ceil(N/256) query tiles leave compute
+ * units idle. Each split writes a partial result -- its output normalised over its own keys, in
+ * fp32, and the log-sum-exp of its logits -- to `workspace`; a second kernel merges them with the
+ * rescaling identity ("transformer math: flash attention math", aicassindra.com, "The rescaling
+ * identity, derived"): lse = ln sum_s exp(L_s), o = sum_s exp(L_s - lse) o_s. By that page's
+ * "Proof of exactness" the grouping of the keys does not change the result, which is that of
+ * fa_fwd up to rounding.
+ *
+ * Arguments as for fa_fwd, plus:
+ * num_splits      : 1 .. 64 (1 is exactly fa_fwd and needs no workspace);
+ *                   fa_fwd_splitkv_heuristic suggests a value.
+ * workspace       : device memory of at least fa_fwd_splitkv_workspace_size(B, H, N, d,
+ *                   num_splits) bytes, 16-byte aligned, not overlapping q, k, v, o or lse. The
+ *                   caller owns it; its contents before and after the call are unspecified, and
+ *                   two calls in flight at once need two workspaces.
+ * Errors: those of fa_fwd, FA_ERR_OPTION for num_splits out of range, FA_ERR_WORKSPACE.
+ * Uses the default kernel and rescale threshold of fa_fwd.
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int64_t B, int64_t H, int64_t N, int64_t d,
+                   float scale, int causal, hipStream_t stream, int dtype,
+                   int num_splits, void* workspace, size_t workspace_bytes);
+
+/* Bytes of workspace fa_fwd_splitkv needs: num_splits * B*H*N * (d + 2) * 4, or 0 when
+ * num_splits <= 1 or an argument is out of range. */
+size_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int num_splits);
+
+/* A split count for fa_fwd_splitkv from a cost model: one workgroup of 256 query rows runs per
+ * compute unit at a time, so G = B*H*ceil(N/256) tiles cut in S splits take ceil(G*S/256) rounds
+ * of 1/S of the key tiles (plus a fixed start-up cost per workgroup), and the merge reads S
+ * partial results per row. At least four key tiles of 64 per split (half as many keys counted
+ * when causal), at most 64; 1 when splitting cannot help. */
+int fa_fwd_splitkv_heuristic(int64_t B, int64_t H, int64_t N, int64_t d, int causal);
 
 /* Static, NUL-terminated description of a return code (never NULL). */
 const char* fa_status_string(int status);

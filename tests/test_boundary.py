@@ -30,7 +30,8 @@ def L():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_ex", "fa_status_string", "fa_version"]
+    assert _declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_ex", "fa_fwd_splitkv", "fa_fwd_splitkv_heuristic",
+                                     "fa_fwd_splitkv_workspace_size", "fa_status_string", "fa_version"]
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -48,7 +49,7 @@ def test_exported_symbols_match_with_nm():
 
 
 def test_status_strings(L):
-    for st in range(0, 10):
+    for st in range(0, 11):
         s = L.fa_status_string(st)
         assert s and s != b"unknown status"
     assert L.fa_status_string(99) == b"unknown status"
@@ -158,3 +159,42 @@ def test_backward_binding_fails_loudly_without_gpu_tensors():
     lse = torch.zeros(1, 1, 8)
     with pytest.raises(ValueError):
         fa.backward(q, q, q, q, lse, q)
+
+
+def _split(num_splits, ws, ws_bytes, **kw):
+    import exact_tiled_softmax_fa_amd as fa
+    a = dict(GOOD)
+    a.update(kw)
+    return fa.fa_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                             a["causal"], a["stream"], a["dtype"], num_splits, ws, ws_bytes)
+
+
+def test_splitkv_workspace_size_and_heuristic(L):
+    import exact_tiled_softmax_fa_amd as fa
+    assert fa.splitkv_workspace_size(1, 2, 64, 64, 4) == 4 * 2 * 64 * 66 * 4
+    assert fa.splitkv_workspace_size(1, 2, 64, 64, 1) == 0
+    assert fa.splitkv_workspace_size(1, 2, 64, 64, 65) == 0
+    assert fa.splitkv_workspace_size(1, 2, 64, 96, 4) == 0
+    # cost model: rounds of ceil(G S / 256) workgroups of 1/S of the key tiles plus a start-up cost,
+    # and a merge that grows with S
+    assert fa.splitkv_heuristic(1, 32, 8192, 128, 0) == 1      # G = 1024: 4 full rounds already
+    assert fa.splitkv_heuristic(1, 2, 16384, 128, 0) == 2      # G = 128: 2 splits fill one round
+    assert fa.splitkv_heuristic(1, 1, 25600, 128, 0) == 5      # G = 100: 5 splits, 500 in 2 rounds
+    assert fa.splitkv_heuristic(1, 1, 2048, 128, 0) == 8       # G = 8: capped at 32 key tiles / 4
+    assert fa.splitkv_heuristic(1, 100, 512, 64, 0) == 1       # G = 200: splitting cannot shorten it
+    assert fa.splitkv_heuristic(1, 1, 256, 64, 1) == 1         # too few key tiles to split
+    assert 1 <= fa.splitkv_heuristic(1, 1, 1 << 22, 128, 0) <= 64
+
+
+WS = 0xB00000
+
+
+@pytest.mark.parametrize("num_splits,ws,ws_bytes,kw,code", [
+    (0, WS, 1 << 20, {}, 9), (65, WS, 1 << 30, {}, 9), (-1, WS, 1 << 20, {}, 9),
+    (4, None, 1 << 20, {}, 10), (4, WS, 100, {}, 10), (4, WS + 8, 1 << 20, {}, 10),
+    (4, QA, 1 << 20, {}, 10), (4, OA - 64, 1 << 20, {}, 10), (4, LA, 1 << 20, {}, 10),
+    (4, WS, 1 << 20, dict(q=None), 1), (4, WS, 1 << 20, dict(d=96), 3), (4, WS, 1 << 20, dict(o=QA), 7),
+    (0, WS, 1 << 20, dict(q=None), 1),
+])
+def test_splitkv_argument_errors(L, num_splits, ws, ws_bytes, kw, code):
+    assert _split(num_splits, ws, ws_bytes, **kw) == code

@@ -67,7 +67,11 @@ WORKLOADS = [
     Workload("B1-H8-N32768-d128-bf16-causal-qk4", 1, 8, 32768, 128, "bf16", True, 4.0, 5, 1024),
 ]
 
-BY_NAME = {w.name: w for w in WORKLOADS}
+# A thin grid for split-KV: 2 heads x 64 query tiles of 256 rows leave half of the 256 compute
+# units idle under the plain grid (same recipe; not one of the five parity configurations).
+THIN = Workload("B1-H2-N16384-d128-f16", 1, 2, 16384, 128, "f16", False, 1.0, 6, 1024)
+
+BY_NAME = {w.name: w for w in WORKLOADS + [THIN]}
 
 # The configuration the headline throughput is quoted on.
 HEADLINE = BY_NAME["B1-H32-N8192-d128-f16"]
