@@ -4,7 +4,8 @@
                                                          [--out DIR] [--summary-dir DIR] [--parse-only]
 
 --pass fwd (default) profiles fa_fwd's kernel; --pass bwd profiles the two kernels of fa_bwd
-(fa_bwd_dq_kernel, fa_bwd_dkdv_kernel), each summarised on its own.
+(fa_bwd_dq_kernel, fa_bwd_dkdv_kernel), each summarised on its own; --splits S (with --pass fwd)
+profiles fa_fwd_splitkv's split kernel and its merge kernel.
 
 Runs four rocprofv3 passes over ``bench.py`` as child processes (this process
 never touches the GPU, so the profiler's preload stays in its own process):
@@ -56,9 +57,11 @@ def kernel_sha(which: str = "fwd") -> str:
     return h.hexdigest()
 
 
-def passes(workload: str, out: str, steps: int, warmup: int, which: str = "fwd"):
+def passes(workload: str, out: str, steps: int, warmup: int, which: str = "fwd", splits=None):
     bench = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload, "--pass", which,
              "--no-cpu-baseline"]
+    if splits is not None:
+        bench += ["--splits", str(splits)]
     timed = bench + ["--steps", str(steps), "--warmup", str(warmup)]
     short = bench + ["--steps", "2", "--warmup", "1"]
     copy = ["--copy-ref-mib", str(COPY_MIB)]
@@ -71,9 +74,9 @@ def passes(workload: str, out: str, steps: int, warmup: int, which: str = "fwd")
     ]
 
 
-def run(workload: str, out: str, steps: int, warmup: int, timeout: int, which: str = "fwd") -> list:
+def run(workload: str, out: str, steps: int, warmup: int, timeout: int, which: str = "fwd", splits=None) -> list:
     cmds = []
-    for name, prof_args, prog in passes(workload, out, steps, warmup, which):
+    for name, prof_args, prog in passes(workload, out, steps, warmup, which, splits):
         cmd = ["rocprofv3", *prof_args, "--output-format", "csv", "-d", os.path.join(out, name), "-o", name,
                "--", *prog]
         cmds.append(" ".join(shlex.quote(c) for c in cmd))
@@ -104,7 +107,7 @@ def _counter(out, name, counter, kernel):
             if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]]
 
 
-def kernels(workload: str, which: str = "fwd"):
+def kernels(workload: str, which: str = "fwd", splits=None):
     """(kernel name, matrix-product flops per launch, unavoidable bytes per launch) of a pass.
     Flops: 2 N^2 d per product per head (halved when causal); forward: the two products of the
     conventional count; backward: the products each kernel executes (dq: S, dP, dQ; dkdv: S, dP,
@@ -116,16 +119,22 @@ def kernels(workload: str, which: str = "fwd"):
     BH, N, d = w.B * w.H, w.N, w.d
     per_product = 2.0 * BH * N * N * d / (2 if w.causal else 1)
     t = N * d * 2  # one [N, d] tensor of one head
+    if which == "fwd" and splits:
+        # split reduction: reads q, k, v, writes the partials (fp32 o and two lse per row and split);
+        # merge: reads the partials, writes o and lse
+        part = splits * BH * N * (d + 2) * 4
+        return [("fa_fwd_kernel", 2 * per_product, BH * 3 * t + part),
+                ("fa_merge_kernel", 0.0, part + BH * (t + 4 * N))]
     if which == "fwd":
         return [("fa_fwd_kernel", 2 * per_product, BH * (4 * t + 4 * N))]
     return [("fa_bwd_dq_kernel", 3 * per_product, BH * (6 * t + 8 * N)),   # q k v o dO lse -> dq delta
             ("fa_bwd_dkdv_kernel", 4 * per_product, BH * (6 * t + 8 * N))]  # q k v dO lse delta -> dk dv
 
 
-def summarize(workload: str, out: str, steps: int, cmds=None, which: str = "fwd") -> list:
+def summarize(workload: str, out: str, steps: int, cmds=None, which: str = "fwd", splits=None) -> list:
     """One record per kernel of the pass (see ``kernels``)."""
     recs = []
-    for kname, flops, unavoidable in kernels(workload, which):
+    for kname, flops, unavoidable in kernels(workload, which, splits):
         trace = [r for r in _rows(_find(out, "kt", "kernel_trace.csv")) if kname in r["Kernel_Name"]]
         durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in trace]
         timed = durs[-steps:]
@@ -162,17 +171,20 @@ def summarize(workload: str, out: str, steps: int, cmds=None, which: str = "fwd"
             "tflops_from_trace": flops / (ms * 1e-3) / 1e12,
             "commands": cmds or [],
             "pass": which,
+            "splits": splits,
         })
     return recs
 
 
 def write_summary(rec: dict, summary_dir: str):
     os.makedirs(summary_dir, exist_ok=True)
-    name = f"{rec['kernel']}_{rec['workload']}"
+    name = f"{rec['kernel']}_{rec['workload']}" + (f"_split{rec['splits']}" if rec.get("splits") else "")
     lines = [f"# {rec['kernel']} — {rec['workload']}", ""]
     if rec["commands"]:
         lines += ["Made by `python -m exact_tiled_softmax_fa_amd.rocprof_harness --workload "
-                  f"{rec['workload']} --pass {rec['pass']}` (repository root, GPU box), which ran:", "", "```",
+                  f"{rec['workload']} --pass {rec['pass']}"
+                  + (f" --splits {rec['splits']}" if rec.get("splits") else "")
+                  + "` (repository root, GPU box), which ran:", "", "```",
                   *rec["commands"], "```", ""]
     d = rec["dispatch_ms"]
     lines += [
@@ -203,6 +215,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="B1-H32-N8192-d128-f16")
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"])
+    ap.add_argument("--splits", type=int, default=None, help="profile fa_fwd_splitkv with this many splits")
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "rocprof"))
     ap.add_argument("--summary-dir", default=os.path.join(ROOT, "gpurun_out", "rocprof"))
     ap.add_argument("--steps", type=int, default=20)
@@ -210,11 +223,12 @@ def main():
     ap.add_argument("--timeout", type=int, default=240, help="seconds per rocprofv3 pass")
     ap.add_argument("--parse-only", action="store_true", help="summarise existing outputs under --out")
     args = ap.parse_args()
-    out = os.path.join(args.out, f"{args.which}_{args.workload}")
+    tag = f"{args.which}_{args.workload}" + (f"_split{args.splits}" if args.splits else "")
+    out = os.path.join(args.out, tag)
     cmds = None
     if not args.parse_only:
-        cmds = run(args.workload, out, args.steps, args.warmup, args.timeout, args.which)
-    for rec in summarize(args.workload, out, args.steps, cmds, args.which):
+        cmds = run(args.workload, out, args.steps, args.warmup, args.timeout, args.which, args.splits)
+    for rec in summarize(args.workload, out, args.steps, cmds, args.which, args.splits):
         write_summary(rec, args.summary_dir)
 
 
