@@ -7,7 +7,9 @@ binding never do, and this package imports nothing from them.
 Contents
   core        ctypes front end of ``fa_oracle.c``: fp64 three-pass safe-softmax
               attention (the definition written out), and its gradients with
-              respect to q, k, v by the chain rule (``attention_backward``).
+              respect to q, k, v by the chain rule (``attention_backward``), and the
+              definition under a sliding-window / key-padding mask
+              (``attention_masked``).
   recurrence  the online-softmax recurrence for one query in fp64, block by
               block, in any block partition and order, with switches that plant
               the four classic implementation mistakes (used only to show that
@@ -21,7 +23,10 @@ Pins (tests/test_oracle_*.py): the two worked examples printed on the pages
 softmax rows summing to 1, shift invariance, block order/size invariance and
 the brute force. The gradients (tests/test_oracle_bwd_pins.py): decimal
 finite differences, fp64 autograd, sum rules, translation invariance,
-linearity and closed forms. Every function here is pinned; none is "parity unpinned"
+linearity and closed forms. The masked definition
+(tests/test_oracle_mask_pins.py): brute force with the same predicate,
+reductions to unmasked attention over each row's key slice and over truncated
+keys, and the causal / unmasked special cases. Every function here is pinned; none is "parity unpinned"
 except the second worked example's output vector, whose value vectors the
 page does not print.
 """

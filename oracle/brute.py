@@ -11,8 +11,9 @@ no code with the C oracle it checks.
 from decimal import Decimal, localcontext
 
 
-def attention(q, k, v, scale, causal=False):
-    """q, k, v: nested sequences [N][d] of floats for one head.
+def attention(q, k, v, scale, causal=False, allowed=None):
+    """q, k, v: nested sequences [N][d] of floats for one head. allowed(i, j) -> bool, if given,
+    replaces the causal rule; a row with no allowed key gets o = 0 and lse = -inf.
 
     Returns (o, lse) as lists of Python floats: o [N][d], lse [N].
     """
@@ -26,7 +27,14 @@ def attention(q, k, v, scale, causal=False):
         vd = [[Decimal(float(x)) for x in row] for row in v]
         for i in range(n):
             qi = [Decimal(float(x)) for x in q[i]]
-            keys = range(i + 1) if causal else range(n)
+            if allowed is not None:
+                keys = [j for j in range(n) if allowed(i, j)]
+            else:
+                keys = range(i + 1) if causal else range(n)
+            if not keys:
+                out.append([0.0] * d)
+                lses.append(float("-inf"))
+                continue
             e = {}
             for j in keys:
                 dot = sum((qi[c] * kd[j][c] for c in range(d)), Decimal(0))

@@ -28,6 +28,12 @@ def _load():
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
         ]
+        lib.fa_oracle_fwd_masked.restype = ctypes.c_int
+        lib.fa_oracle_fwd_masked.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+        ]
         lib.fa_oracle_bwd.restype = ctypes.c_int
         lib.fa_oracle_bwd.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -123,3 +129,39 @@ def attention_backward(q, k, v, dout, scale, causal=False, rows=None, keys=None)
     if rc != 0:
         raise RuntimeError(f"fa_oracle_bwd failed with code {rc}")
     return dq, dk, dv, lse, delta
+
+
+def attention_masked(q, k, v, scale, window_left=-1, window_right=-1, seqlens_k=None, rows=None):
+    """Exact attention in fp64 under a general mask (``fa_oracle_fwd_masked``): key j is allowed
+    for query i when j >= i - window_left (window_left >= 0), j <= i + window_right
+    (window_right >= 0) and j < seqlens_k[b] (seqlens_k given). A row with no allowed key gets
+    o = 0 and lse = -inf. Shapes and ``rows`` as for ``attention``."""
+    q = np.ascontiguousarray(np.asarray(q, dtype=np.float64))
+    k = np.ascontiguousarray(np.asarray(k, dtype=np.float64))
+    v = np.ascontiguousarray(np.asarray(v, dtype=np.float64))
+    if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError(f"q, k, v must share one [B,H,N,d] shape, got {q.shape} {k.shape} {v.shape}")
+    B, H, N, d = q.shape
+    sl = None
+    if seqlens_k is not None:
+        sl = np.ascontiguousarray(np.asarray(seqlens_k, dtype=np.int64))
+        if sl.shape != (B,):
+            raise ValueError(f"seqlens_k must be [B], got {sl.shape}")
+    if rows is None:
+        o = np.empty((B, H, N, d))
+        lse = np.empty((B, H, N))
+        rows_p, n_rows = None, 0
+    else:
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        if rows.ndim != 2 or rows.shape[0] != B * H:
+            raise ValueError(f"rows must be [B*H, R], got {rows.shape}")
+        n_rows = rows.shape[1]
+        o = np.empty((B * H, n_rows, d))
+        lse = np.empty((B * H, n_rows))
+        rows_p = rows.ctypes.data
+    rc = _load().fa_oracle_fwd_masked(q.ctypes.data, k.ctypes.data, v.ctypes.data, o.ctypes.data, lse.ctypes.data,
+                                      B, H, N, d, float(scale), int(window_left), int(window_right),
+                                      sl.ctypes.data if sl is not None else None, rows_p, n_rows)
+    if rc != 0:
+        raise RuntimeError(f"fa_oracle_fwd_masked failed with code {rc}")
+    return o, lse

@@ -274,3 +274,92 @@ int fa_oracle_bwd(const double* q, const double* k, const double* v, const doubl
     free(m_all); free(l_all); free(D_all); free(s_all); free(dp_all);
     return 0;
 }
+
+/*
+ * The definition above with a general mask: key j is allowed for query i when
+ *   (window_left  < 0 or j >= i - window_left)  and
+ *   (window_right < 0 or j <= i + window_right) and
+ *   j < kv_len_b,   kv_len_b = seqlens_k ? seqlens_k[b] : N.
+ * Masked keys carry no probability mass, which is how the pages admit masks other
+ * than the causal one ("Causal masking fits inside the tiled computation", nalar.dev,
+ * last paragraph; aicassindra.com, "Pitfalls in implementing the recurrence": masked
+ * scores are -inf before the max, "for causal or padded attention"). window_right = 0
+ * with window_left = -1 is the causal mask; seqlens_k is key padding.
+ * A row with no allowed key has no softmax; its output is 0 and its lse is -inf.
+ *
+ * Arguments as fa_oracle_fwd, with causal replaced by window_left, window_right and
+ * seqlens_k (host pointer, [B], or NULL). Same return codes.
+ */
+int fa_oracle_fwd_masked(const double* q, const double* k, const double* v, double* o, double* lse,
+                         int64_t B, int64_t H, int64_t N, int64_t d, double scale,
+                         int64_t window_left, int64_t window_right, const int64_t* seqlens_k,
+                         const int64_t* rows, int64_t n_rows) {
+    if (!q || !k || !v || !o || !lse || B < 1 || H < 1 || N < 1 || d < 1) return 1;
+    if (window_left < -1 || window_right < -1) return 1;
+    int64_t per_head = rows ? n_rows : N;
+    if (per_head < 1) return 1;
+    for (int64_t t = 0; rows && t < B * H * n_rows; ++t)
+        if (rows[t] < 0 || rows[t] >= N) return 1;
+    for (int64_t b = 0; seqlens_k && b < B; ++b)
+        if (seqlens_k[b] < 0 || seqlens_k[b] > N) return 1;
+    int64_t total = B * H * per_head;
+    int nthreads = fa_oracle_threads();
+    double* s_all = (double*)malloc((size_t)nthreads * (size_t)N * sizeof(double));
+    double* acc_all = (double*)malloc((size_t)nthreads * (size_t)d * sizeof(double));
+    if (!s_all || !acc_all) {
+        free(s_all);
+        free(acc_all);
+        return 2;
+    }
+
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nthreads)
+    for (int64_t t = 0; t < total; ++t) {
+#ifdef _OPENMP
+        int tid = omp_get_thread_num();
+#else
+        int tid = 0;
+#endif
+        double* s = s_all + (size_t)tid * (size_t)N;
+        double* acc = acc_all + (size_t)tid * (size_t)d;
+        int64_t bh = t / per_head;
+        int64_t r = t % per_head;
+        int64_t i = rows ? rows[bh * n_rows + r] : r;
+        int64_t kv_len = seqlens_k ? seqlens_k[bh / H] : N;
+        /* the allowed keys form one interval [lo, hi) */
+        int64_t lo = window_left >= 0 ? i - window_left : 0;
+        int64_t hi = window_right >= 0 ? i + window_right + 1 : N;
+        if (lo < 0) lo = 0;
+        if (hi > kv_len) hi = kv_len;
+        const double* qi = q + (bh * N + i) * d;
+        const double* kh = k + bh * N * d;
+        const double* vh = v + bh * N * d;
+        double* oi = o + (bh * per_head + r) * d;
+        if (hi <= lo) {
+            for (int64_t c = 0; c < d; ++c) oi[c] = 0.0;
+            lse[bh * per_head + r] = -INFINITY;
+            continue;
+        }
+        for (int64_t j = lo; j < hi; ++j) {
+            double dot = 0.0;
+            for (int64_t c = 0; c < d; ++c) dot += qi[c] * kh[j * d + c];
+            s[j] = scale * dot;
+        }
+        /* the three passes of the safe softmax, over the allowed keys */
+        double m = -INFINITY;
+        for (int64_t j = lo; j < hi; ++j)
+            if (s[j] > m) m = s[j];
+        double l = 0.0;
+        for (int64_t j = lo; j < hi; ++j) {
+            s[j] = exp(s[j] - m);
+            l += s[j];
+        }
+        for (int64_t c = 0; c < d; ++c) acc[c] = 0.0;
+        for (int64_t j = lo; j < hi; ++j)
+            for (int64_t c = 0; c < d; ++c) acc[c] += s[j] * vh[j * d + c];
+        for (int64_t c = 0; c < d; ++c) oi[c] = acc[c] / l;
+        lse[bh * per_head + r] = m + log(l);
+    }
+    free(s_all);
+    free(acc_all);
+    return 0;
+}
