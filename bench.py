@@ -1,7 +1,7 @@
 """Throughput of the attention forward (or backward) pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd]
-                    [--splits S] [--no-cpu-baseline]
+                    [--splits S] [--window-left L --window-right R] [--no-cpu-baseline]
 
 A step is one fa_fwd call over the whole workload (every query row of every
 head), with q, k, v already resident in device memory. The default workload is
@@ -9,6 +9,10 @@ B=1, H=32, N=8192, d=128, non-causal, fp16. Prints one JSON line.
 
 --splits S times fa_fwd_splitkv with S key splits (0: the library's heuristic) instead of
 fa_fwd; the roofline then covers both of its kernels (split reduction and merge).
+
+--window-left L / --window-right R time fa_fwd_masked with that sliding window (-1 = no limit;
+the workload's causal flag is then ignored) and price it by the allowed (row, key) pairs:
+4 d flops each.
 
 --pass bwd times one fa_bwd call instead (dq, dk, dv from q, k, v, o, lse and a
 seeded dout, all resident), priced by the conventional backward count of 2.5x
@@ -131,6 +135,8 @@ def main():
                     help="time the forward pass (default) or the backward pass")
     ap.add_argument("--splits", type=int, default=None,
                     help="run the forward pass as split-KV with this many splits (0: heuristic)")
+    ap.add_argument("--window-left", type=int, default=None, help="sliding window: keys back (-1 = all)")
+    ap.add_argument("--window-right", type=int, default=None, help="sliding window: keys ahead (-1 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="before timing, run 3 plain device copies of this many MiB (a known-size "
@@ -173,6 +179,14 @@ def main():
         def step():  # noqa: F811
             fa.forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, num_splits=splits, workspace=ws)
 
+    window = None
+    if (args.window_left is not None or args.window_right is not None) and args.which == "fwd":
+        window = (-1 if args.window_left is None else args.window_left,
+                  -1 if args.window_right is None else args.window_right)
+
+        def step():  # noqa: F811
+            fa.forward_masked(q, k, v, window[0], window[1], None, scale=w.scale, out=o, lse=lse)
+
     if args.which == "bwd":
         step()
         dout = workloads.make_dout(w).cuda()
@@ -198,12 +212,19 @@ def main():
     kernel_ms = e0.elapsed_time(e1) / args.steps  # average launch duration on the kernel's stream
 
     flops = w.flops() * (2.5 if args.which == "bwd" else 1.0)
+    if window is not None:
+        import numpy as np
+        i = np.arange(w.N)
+        lo = np.maximum(0, i - window[0]) if window[0] >= 0 else np.zeros_like(i)
+        hi = np.minimum(w.N, i + window[1] + 1) if window[1] >= 0 else np.full_like(i, w.N)
+        flops = 4.0 * w.d * w.B * w.H * float(np.maximum(hi - lo, 0).sum())
     value = flops / (wall / args.steps) / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     out = {
         "metric": (HEADLINE_METRIC if w.name == workloads.HEADLINE.name and args.which == "fwd" and splits is None
                    else f"{args.which} attention TFLOP/s ({w.name}"
-                        + (f", split-KV {splits}" if splits is not None else "") + ")"),
+                        + (f", split-KV {splits}" if splits is not None else "")
+                        + (f", window {window[0]}/{window[1]}" if window is not None else "") + ")"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -217,7 +238,7 @@ def main():
         "data": "synthetic",
         "pct_mfma_peak": round(100.0 * value / PEAK_MFMA_F16_TFLOPS, 2),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "num_splits": splits,
+                   "num_splits": splits, "window": window,
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "none"},
         "roofline": {
             "bound": "mfma",
@@ -225,8 +246,9 @@ def main():
             "peak": PEAK_MFMA_F16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_MFMA_F16_TFLOPS, 4),
-            "traffic": measured_traffic(w.name) if args.which == "fwd" and splits is None else None,
+            "traffic": measured_traffic(w.name) if args.which == "fwd" and splits is None and window is None else None,
             "kernel": ("fa_bwd_dq_kernel + fa_bwd_dkdv_kernel" if args.which == "bwd" else
+                       "fa_fwd_kernel (masked)" if window is not None else
                        "fa_fwd_kernel (split) + fa_merge_kernel" if splits is not None else KERNEL_NAME),
             "kernel_ms": round(kernel_ms, 4),
         },

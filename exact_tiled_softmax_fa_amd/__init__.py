@@ -36,6 +36,11 @@ class FaOptions(ctypes.Structure):
     _fields_ = [("rescale_threshold_log2", ctypes.c_float), ("variant", ctypes.c_int)]
 
 
+class FaMask(ctypes.Structure):
+    """Mirror of fa_mask in include/fa_fwd.h."""
+    _fields_ = [("window_left", ctypes.c_int64), ("window_right", ctypes.c_int64), ("seqlens_k", ctypes.c_void_p)]
+
+
 class FaError(RuntimeError):
     """A non-zero status returned by the C library."""
 
@@ -66,6 +71,9 @@ def lib():
         ]
         L.fa_fwd_ex.restype = ctypes.c_int
         L.fa_fwd_ex.argtypes = L.fa_fwd.argtypes + [ctypes.POINTER(FaOptions)]
+        L.fa_fwd_masked.restype = ctypes.c_int
+        L.fa_fwd_masked.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [
+            ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(FaMask)]
         L.fa_fwd_splitkv.restype = ctypes.c_int
         L.fa_fwd_splitkv.argtypes = L.fa_fwd.argtypes + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t]
         L.fa_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
@@ -238,3 +246,40 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     if st != 0:
         raise FaError(st, status_string(st))
     return (dq, dk, dv, delta) if return_delta else (dq, dk, dv)
+
+
+def fa_fwd_masked(q, k, v, o, lse, B, H, N, d, scale, stream, dtype, mask) -> int:
+    """Raw call of the C entry point fa_fwd_masked (mask: an FaMask or None); returns the status."""
+    return int(lib().fa_fwd_masked(q, k, v, o, lse, B, H, N, d, float(scale), stream, int(dtype),
+                                   ctypes.byref(mask) if mask is not None else None))
+
+
+def forward_masked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, window_left: int = -1, window_right: int = -1,
+                   seqlens_k: torch.Tensor = None, scale=None, out: torch.Tensor = None, lse: torch.Tensor = None):
+    """Attention under a general mask (include/fa_fwd.h, fa_mask): key j is allowed for query i when
+    j >= i - window_left (window_left >= 0), j <= i + window_right (window_right >= 0) and
+    j < seqlens_k[b] (seqlens_k: int32 GPU tensor [B], or None). Returns (o, lse); rows with no
+    allowed key get o = 0 and lse = -inf."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor [B, H, N, d]")
+    if q.shape != k.shape or q.shape != v.shape or q.dtype != k.dtype or q.dtype != v.dtype or q.dtype not in _DTYPES:
+        raise ValueError("q, k, v must share one shape and one of float16 / bfloat16")
+    B, H, N, d = q.shape
+    if seqlens_k is not None and (not seqlens_k.is_cuda or seqlens_k.dtype != torch.int32 or seqlens_k.shape != (B,)
+                                  or not seqlens_k.is_contiguous() or seqlens_k.device != q.device):
+        raise ValueError("seqlens_k must be a contiguous int32 GPU tensor [B] on q's device")
+    if scale is None:
+        scale = default_scale(d)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_like("out", out, q)
+    _check_like("lse", lse, q, torch.float32, (B, H, N))
+    mask = FaMask(int(window_left), int(window_right), seqlens_k.data_ptr() if seqlens_k is not None else None)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = fa_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                           scale, stream, _DTYPES[q.dtype], mask)
+    if st != 0:
+        raise FaError(st, status_string(st))
+    return out, lse

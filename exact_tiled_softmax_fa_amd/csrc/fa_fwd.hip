@@ -50,11 +50,17 @@ constexpr int kDefaultVariant = 1;          // kernel fa_fwd runs: 1 = 32 rows p
 // SPLIT: the key range of every query tile is cut into n_split equal runs of tiles, one per
 // workgroup; each writes its partial result (O normalised over its own keys, in fp32, and the
 // log-sum-exp of its keys) to PO / PL, and fa_merge_kernel combines them (split-KV).
-template <int D, bool BF16, bool CAUSAL, bool SPLIT = false>
+// MASKED: a general mask in place of CAUSAL: key j is allowed for query i when
+// i - wl <= j (wl >= 0), j <= i + wr (wr >= 0) and j < seqlens[b] (seqlens given). Key tiles
+// outside the workgroup's window are neither loaded nor computed; a row with no allowed key
+// gets o = 0 and lse = -inf.
+template <int D, bool BF16, bool CAUSAL, bool SPLIT = false, bool MASKED = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qt, int G, float c, float tau_raw,
-    int n_split = 1, float* __restrict__ PO = nullptr, float* __restrict__ PL = nullptr) {
+    int n_split = 1, float* __restrict__ PO = nullptr, float* __restrict__ PL = nullptr, int H = 1, int wl = -1,
+    int wr = -1, const int* __restrict__ seqlens = nullptr) {
+    static_assert(!(MASKED && (CAUSAL || SPLIT)), "the general mask replaces the causal one and does not split");
     constexpr int DK = D / 16;                 // k-steps of the first product
     constexpr int DB = D / 32;                 // 32-column blocks of the output
     constexpr int CPR = D / 8;                 // 16-byte chunks per row
@@ -101,12 +107,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         tb = (vh % n_split) * per;
         T = max(0, min(T_all, tb + per) - tb);
     }
+    // MASKED: kv_len keys exist for this batch; the workgroup's rows q0 .. q0 + 255 need keys
+    // [lo, hi), a range of whole tiles from tb
+    int kv_len = N;
+    if constexpr (MASKED) {
+        if (seqlens != nullptr) kv_len = min(max(seqlens[bh / H], 0), N);
+        const int lo = wl >= 0 ? max(0, q0 - wl) : 0;
+        const int hi = wr >= 0 ? min(kv_len, q0 + kBlockM + wr) : kv_len;
+        tb = lo / kBlockN;
+        T = max(0, (hi + kBlockN - 1) / kBlockN - tb);
+    }
     // tiles this wave computes: causal waves stop at the tile holding their last row
     // (Non-causal: T_w = T, hidden from the compiler. Folded away, the tests on it disappear and
     // the compiler keeps the output accumulators of the loop's two exit paths in two register
     // sets, which spills; a per-lane opaque value keeps the control flow of the causal kernel.)
     int T_w = CAUSAL ? max(0, min(T, (min(wq0 + 32, N) + kBlockN - 1) / kBlockN - tb)) : T;
-    if constexpr (!CAUSAL) asm volatile("" : "+v"(T_w));
+    // MASKED: this wave's key tiles are T_w0 .. T_w - 1 (a window leaves the first ones to the
+    // workgroup's earlier rows); the wave joins every barrier and load but computes only those
+    int T_w0 = 0;
+    if constexpr (MASKED) {
+        const int hi_w = wr >= 0 ? min(kv_len, wq0 + 32 + wr) : kv_len;  // this wave's last key + 1
+        T_w = max(0, min(T, (hi_w + kBlockN - 1) / kBlockN - tb));
+        if (wl >= 0) T_w0 = min(T_w, max(0, wq0 - wl) / kBlockN - tb);
+    }
+    if constexpr (!CAUSAL && !MASKED) asm volatile("" : "+v"(T_w));
 
     // Load g of a tile covers rows RPI*g .. RPI*g+RPI-1; lane l writes LDS bytes [1024 g + 16 l,
     // +16), i.e. row RPI*g + l/CPR at chunk position l % CPR, which holds global chunk
@@ -208,6 +232,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // keys past the end, and (causal) keys after the query, become -inf before the max
     auto mask = [&](int t, f32x16 (&sd)[2]) __attribute__((always_inline)) {
         const int k0 = (tb + t) * kBlockN;
+        if constexpr (MASKED) {
+            if ((k0 + kBlockN > kv_len) || (wr >= 0 && k0 + kBlockN - 1 > wq0 + wr) ||
+                (wl >= 0 && k0 < wq0 + 31 - wl)) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                        if (key >= kv_len || (wr >= 0 && key > qrow + wr) || (wl >= 0 && key < qrow - wl))
+                            sd[kb][r] = -INFINITY;
+                    }
+            }
+            return;
+        }
         if ((k0 + kBlockN > N) || (CAUSAL && k0 + kBlockN - 1 > wq0)) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -270,7 +308,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (T > 1) issue(Kh, 1, k_lds1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (0 < T_w) {
+    if (T_w0 < T_w && T_w0 == 0) {
         qk(k_lds0, s0);
         mask(0, s0);
         rebase(row_max(s0));
@@ -281,7 +319,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         __syncthreads();
         if (j + 2 < T) issue(Kh, j + 2, k_load);
         if (j + 1 < T) issue(Vh, j + 1, v_load);
-        if (j + 1 < T_w) {
+        if (MASKED && j < T_w0) {
+            // before this wave's first tile: at most start the pipeline with S^T(j+1)
+            if (j + 1 == T_w0 && j + 1 < T_w) {
+                qk(k_nxt, s_nxt);
+                mask(j + 1, s_nxt);
+                rebase(row_max(s_nxt));
+            }
+        } else if (j + 1 < T_w) {
             // region 1: S^T(j+1) = K(j+1) . Q^T with the exponentials of tile j in between.
             // Explicit software pipeline: the LDS operands of MFMA i + 2 are read before MFMA i
             // issues, and one pair of exponentials follows each MFMA; sched_barrier(0) pins that
@@ -387,7 +432,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         return;
     }
     if (qrow < N) {
-        const float inv = 1.f / l_tot;
+        // (MASKED: a row with no allowed key has l = 0: o = 0, lse = -inf)
+        const float inv = (!MASKED || l_tot > 0.f) ? 1.f / l_tot : 0.f;
         uint16_t* orow = O + head + (int64_t)qrow * D;
 #pragma unroll
         for (int b = 0; b < DB; ++b)
@@ -399,7 +445,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
         if (LSE != nullptr && h == 0) {
             const float mcf = (m_run == -INFINITY) ? 0.f : m_run * c;
-            LSE[(int64_t)bh * N + qrow] = (mcf + __log2f(l_lse)) * 0.69314718055994531f;
+            LSE[(int64_t)bh * N + qrow] = (!MASKED || l_lse > 0.f) ? (mcf + __log2f(l_lse)) * 0.69314718055994531f
+                                                                    : -INFINITY;
         }
     }
 }
@@ -770,6 +817,16 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__
     if (LSE != nullptr && ch == 0) LSE[row] = ml + __log2f(lsum) * 0.69314718055994531f;
 }
 
+template <int D, bool BF16>
+hipError_t launch_masked(const void* q, const void* k, const void* v, void* o, float* lse, int N, int n_qt, int G,
+                         float c, float tau_raw, int H, int wl, int wr, const int* seqlens, hipStream_t stream) {
+    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, false, false, true>), dim3(G), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qt, G, c, tau_raw, 1,
+                       nullptr, nullptr, H, wl, wr, seqlens);
+    return hipGetLastError();
+}
+
 template <int D, bool BF16, bool CAUSAL>
 hipError_t launch_split(const void* q, const void* k, const void* v, void* o, float* lse, int N, int n_qt, int BH,
                         float c, float tau_raw, int n_split, float* po, float* pl, hipStream_t stream) {
@@ -904,6 +961,37 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
            int64_t d, float scale, int causal, hipStream_t stream, int dtype) {
     return fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype, nullptr);
+}
+
+int fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                  int64_t N, int64_t d, float scale, hipStream_t stream, int dtype, const fa_mask* mask) {
+    const int st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype, 1);
+    if (st != FA_OK) return st;
+    if (!mask) return FA_ERR_NULL;
+    if (mask->window_left < -1 || mask->window_right < -1 || mask->window_left > INT32_MAX ||
+        mask->window_right > INT32_MAX)
+        return FA_ERR_OPTION;
+    if (reinterpret_cast<uintptr_t>(mask->seqlens_k) & 3) return FA_ERR_ALIGN;
+    // A window of N or more keys is no limit; as -1 it keeps the kernel's index sums below 2^31.
+    const int64_t wl64 = mask->window_left >= N ? -1 : mask->window_left;
+    const int64_t wr64 = mask->window_right >= N ? -1 : mask->window_right;
+    // the two masks with kernels of their own
+    if (!mask->seqlens_k && wl64 == -1 && (wr64 == -1 || wr64 == 0))
+        return fa_fwd(q, k, v, o, lse, B, H, N, d, scale, wr64 == 0 ? 1 : 0, stream, dtype);
+    const int64_t n_qt = (N + kBlockM - 1) / kBlockM;
+    const float c = scale * 1.4426950408889634f;
+    const float tau_raw = kDefaultRescaleLog2 / c;
+    const int n = static_cast<int>(N), nq = static_cast<int>(n_qt), g = static_cast<int>(B * H * n_qt);
+    const int h = static_cast<int>(H), wl = static_cast<int>(wl64), wr = static_cast<int>(wr64);
+    const bool bf = dtype == FA_BF16;
+    hipError_t e;
+    if (d == 64)
+        e = bf ? launch_masked<64, true>(q, k, v, o, lse, n, nq, g, c, tau_raw, h, wl, wr, mask->seqlens_k, stream)
+               : launch_masked<64, false>(q, k, v, o, lse, n, nq, g, c, tau_raw, h, wl, wr, mask->seqlens_k, stream);
+    else
+        e = bf ? launch_masked<128, true>(q, k, v, o, lse, n, nq, g, c, tau_raw, h, wl, wr, mask->seqlens_k, stream)
+               : launch_masked<128, false>(q, k, v, o, lse, n, nq, g, c, tau_raw, h, wl, wr, mask->seqlens_k, stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 size_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int num_splits) {

@@ -123,6 +123,37 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               const fa_fwd_options* opts);
 
 /*
+ * A general mask for fa_fwd_masked. Key j is allowed for query i (of batch b) when
+ *   window_left  < 0  or  j >= i - window_left,
+ *   window_right < 0  or  j <= i + window_right,     and
+ *   seqlens_k == NULL or  j <  seqlens_k[b].
+ * window_left = -1, window_right = 0 is the causal mask; a window of w keys back and none ahead
+ * is sliding-window (local) attention; seqlens_k is key padding (per-batch key lengths). The pages
+ * admit any mask applied to every score tile before the max ("FlashAttention tiles exact
+ * softmax without materializing the score matrix", nalar.dev, "Causal masking fits inside the
+ * tiled computation", last paragraph; "transformer math: flash attention math",
+ * aicassindra.com, "Pitfalls in implementing the recurrence": masked scores are -inf before the
+ * block max). A row with no allowed key has no softmax: its output is 0 and its lse -inf.
+ */
+typedef struct fa_mask {
+    int64_t window_left;       /* -1 (no limit) or 0 .. 2^31 - 1 */
+    int64_t window_right;      /* -1 (no limit) or 0 .. 2^31 - 1 */
+    const int32_t* seqlens_k;  /* NULL, or device pointer to B int32 key lengths (4-byte aligned);
+                                  values are clamped to [0, N] on the device */
+} fa_mask;
+
+/*
+ * fa_fwd_masked -- fa_fwd under a general mask (see fa_mask). Key tiles outside a query tile's
+ * window are neither loaded nor computed, so a window of w keys costs O(N w), not O(N^2).
+ * Arguments as for fa_fwd, with `causal` replaced by `mask` (not NULL). The masks -1/-1 and -1/0
+ * without seqlens_k run fa_fwd's own kernels. Errors: those of fa_fwd; FA_ERR_NULL for a NULL
+ * mask, FA_ERR_OPTION for a window out of range, FA_ERR_ALIGN for a misaligned seqlens_k.
+ */
+int fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int64_t B, int64_t H, int64_t N, int64_t d,
+                  float scale, hipStream_t stream, int dtype, const fa_mask* mask);
+
+/*
  * fa_fwd_splitkv -- fa_fwd with the keys of every query tile cut into num_splits runs that run
  * as separate workgroups (split-KV), for shapes whose B*H*ceil(N/256) query tiles leave compute
  * units idle. Each split writes a partial result -- its output normalised over its own keys, in

@@ -30,8 +30,9 @@ def L():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_ex", "fa_fwd_splitkv", "fa_fwd_splitkv_heuristic",
-                                     "fa_fwd_splitkv_workspace_size", "fa_status_string", "fa_version"]
+    assert _declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_ex", "fa_fwd_masked", "fa_fwd_splitkv",
+                                     "fa_fwd_splitkv_heuristic", "fa_fwd_splitkv_workspace_size", "fa_status_string",
+                                     "fa_version"]
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -198,3 +199,17 @@ WS = 0xB00000
 ])
 def test_splitkv_argument_errors(L, num_splits, ws, ws_bytes, kw, code):
     assert _split(num_splits, ws, ws_bytes, **kw) == code
+
+
+@pytest.mark.parametrize("mask,kw,code", [
+    (None, {}, 1), ((-2, 0, None), {}, 9), ((0, -2, None), {}, 9), ((1 << 31, 0, None), {}, 9),
+    ((4, 0, 0x600002), {}, 5), ((4, 0, None), dict(q=None), 1), ((4, 0, None), dict(d=96), 3),
+    ((4, 0, None), dict(o=QA), 7),
+])
+def test_masked_argument_errors(L, mask, kw, code):
+    import exact_tiled_softmax_fa_amd as fa
+    a = dict(GOOD)
+    a.update(kw)
+    m = None if mask is None else fa.FaMask(*mask)
+    assert fa.fa_fwd_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                            a["stream"], a["dtype"], m) == code
