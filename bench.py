@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd]
                     [--splits S] [--window-left L --window-right R] [--no-cpu-baseline]
+    python bench.py --cpu-variant [--workload NAME] [--heads K] [--threads T]
 
 A step is one fa_fwd call over the whole workload (every query row of every
 head), with q, k, v already resident in device memory. The default workload is
@@ -13,6 +14,9 @@ fa_fwd; the roofline then covers both of its kernels (split reduction and merge)
 --window-left L / --window-right R time fa_fwd_masked with that sliding window (-1 = no limit;
 the workload's causal flag is then ignored) and price it by the allowed (row, key) pairs:
 4 d flops each.
+
+--cpu-variant times the host-CPU entry point fa_fwd_cpu instead (no GPU needed) on the first K
+heads of the workload (default 4), in TFLOP/s of the same flop convention.
 
 --pass bwd times one fa_bwd call instead (dq, dk, dv from q, k, v, o, lse and a
 seeded dout, all resident), priced by the conventional backward count of 2.5x
@@ -125,6 +129,30 @@ def cpu_baseline_bwd(w):
     }
 
 
+def cpu_variant(w, heads, threads, steps):
+    """fa_fwd_cpu on the first `heads` (b, h) heads of the workload; one JSON line."""
+    import os
+    import exact_tiled_softmax_fa_amd as fa
+
+    q, k, v = workloads.make_inputs(w)
+    nh = min(heads, w.B * w.H)
+    q, k, v = (t.reshape(w.B * w.H, w.N, w.d)[:nh].reshape(1, nh, w.N, w.d).contiguous() for t in (q, k, v))
+    fa.forward_cpu(q[:, :1, :256].contiguous(), k[:, :1, :256].contiguous(), v[:, :1, :256].contiguous(),
+                   causal=w.causal, scale=w.scale, num_threads=threads)  # warm-up
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fa.forward_cpu(q, k, v, causal=w.causal, scale=w.scale, num_threads=threads)
+    dt = (time.perf_counter() - t0) / steps
+    flops = 4.0 * nh * w.N * w.N * w.d / (2 if w.causal else 1)
+    cores = threads if threads > 0 else len(os.sched_getaffinity(0))
+    print(json.dumps({
+        "metric": f"fwd attention TFLOP/s on the host CPU, tiled online softmax ({w.name}, {nh} heads)",
+        "value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "n_gpus": 0, "steps": steps,
+        "ms_per_step": round(dt * 1e3, 2), "higher_is_better": True, "dtype": w.dtype, "data": "synthetic",
+        "cores": cores, "config": {"workload": w.name, "heads": nh, "N": w.N, "d": w.d, "causal": w.causal},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +166,9 @@ def main():
     ap.add_argument("--window-left", type=int, default=None, help="sliding window: keys back (-1 = all)")
     ap.add_argument("--window-right", type=int, default=None, help="sliding window: keys ahead (-1 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--cpu-variant", action="store_true", help="time fa_fwd_cpu on host cores instead")
+    ap.add_argument("--heads", type=int, default=4, help="--cpu-variant: heads of the workload to run")
+    ap.add_argument("--threads", type=int, default=0, help="--cpu-variant: worker threads (0: all)")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="before timing, run 3 plain device copies of this many MiB (a known-size "
                          "reference for hardware byte counters)")
@@ -147,6 +178,10 @@ def main():
               "(the forward pass shards over heads with no communication; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.cpu_variant:
+        cpu_variant(workloads.BY_NAME[args.workload], args.heads, args.threads, max(1, min(args.steps, 3)))
+        return
 
     import torch
     import exact_tiled_softmax_fa_amd as fa

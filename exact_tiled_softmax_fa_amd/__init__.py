@@ -8,6 +8,7 @@ the HIP kernels. PyTorch supplies device memory and streams.
 
     o, lse = forward(q, k, v, causal=False, scale=None)
     dq, dk, dv = backward(q, k, v, o, lse, dout, causal=False, scale=None)
+    o, lse = forward_cpu(q_cpu, k_cpu, v_cpu, causal=False)   # the host-CPU variant (fa_cpu.h)
 
 q, k, v: contiguous CUDA (HIP) tensors [B, H, N, d], float16 or bfloat16,
 d in {64, 128}. forward returns o (same shape and dtype) and lse ([B, H, N]
@@ -80,6 +81,9 @@ def lib():
         L.fa_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
         L.fa_fwd_splitkv_heuristic.restype = ctypes.c_int
         L.fa_fwd_splitkv_heuristic.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
+        L.fa_fwd_cpu.restype = ctypes.c_int
+        L.fa_fwd_cpu.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         L.fa_bwd.restype = ctypes.c_int
         L.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
@@ -280,6 +284,38 @@ def forward_masked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, window_lef
         stream = torch.cuda.current_stream(q.device).cuda_stream
         st = fa_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
                            scale, stream, _DTYPES[q.dtype], mask)
+    if st != 0:
+        raise FaError(st, status_string(st))
+    return out, lse
+
+
+def fa_fwd_cpu(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, num_threads) -> int:
+    """Raw call of the C entry point fa_fwd_cpu (host pointers); returns the status code."""
+    return int(lib().fa_fwd_cpu(q, k, v, o, lse, B, H, N, d, float(scale), int(causal), int(dtype),
+                                int(num_threads)))
+
+
+def forward_cpu(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale=None,
+                num_threads: int = 0, out: torch.Tensor = None, lse: torch.Tensor = None):
+    """The same attention on the host CPU (include/fa_cpu.h): contiguous CPU tensors [B, H, N, d] of
+    float16 or bfloat16. Returns (o, lse). Explicitly a host entry point: the GPU functions above
+    never call it."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.is_cuda or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous CPU tensor [B, H, N, d]")
+    if q.shape != k.shape or q.shape != v.shape or q.dtype != k.dtype or q.dtype != v.dtype or q.dtype not in _DTYPES:
+        raise ValueError("q, k, v must share one shape and one of float16 / bfloat16")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = default_scale(d)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32) if lse is None else lse
+    if out.shape != q.shape or out.dtype != q.dtype or out.is_cuda or not out.is_contiguous():
+        raise ValueError("out must be a contiguous CPU tensor like q")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or lse.is_cuda or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 CPU tensor [B, H, N]")
+    st = fa_fwd_cpu(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d, scale,
+                    causal, _DTYPES[q.dtype], num_threads)
     if st != 0:
         raise FaError(st, status_string(st))
     return out, lse

@@ -28,32 +28,11 @@
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
+#include "fa_types.h"
+
 #ifdef __cplusplus
 extern "C" {
 #endif
-
-/* Element type of q, k, v and o. */
-typedef enum fa_dtype {
-    FA_F16 = 0,  /* IEEE binary16 */
-    FA_BF16 = 1  /* bfloat16 */
-} fa_dtype;
-
-/* Return codes. Every code except FA_ERR_LAUNCH is returned before any device
- * work is enqueued, and nothing is written. */
-typedef enum fa_status {
-    FA_OK = 0,
-    FA_ERR_NULL = 1,      /* q, k, v or o is NULL */
-    FA_ERR_SHAPE = 2,     /* B, H or N < 1, or a size beyond the limits below */
-    FA_ERR_HEAD_DIM = 3,  /* d is not 64 or 128 */
-    FA_ERR_DTYPE = 4,     /* dtype is not FA_F16 or FA_BF16 */
-    FA_ERR_ALIGN = 5,     /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
-    FA_ERR_SCALE = 6,     /* scale is not finite and > 0 */
-    FA_ERR_ALIAS = 7,     /* o or lse overlaps an input, or o overlaps lse */
-    FA_ERR_LAUNCH = 8,    /* the kernel launch failed (hipGetLastError) */
-    FA_ERR_OPTION = 9,    /* an fa_fwd_options field or num_splits is out of range */
-    FA_ERR_WORKSPACE = 10 /* fa_fwd_splitkv: workspace NULL, not 16-byte aligned, smaller than
-                             fa_fwd_splitkv_workspace_size, or overlapping an argument */
-} fa_status;
 
 /*
  * Tuning options for fa_fwd_ex. They change how the result is reached, never

@@ -30,7 +30,7 @@ def L():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_ex", "fa_fwd_masked", "fa_fwd_splitkv",
+    assert _declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_cpu", "fa_fwd_ex", "fa_fwd_masked", "fa_fwd_splitkv",
                                      "fa_fwd_splitkv_heuristic", "fa_fwd_splitkv_workspace_size", "fa_status_string",
                                      "fa_version"]
 
