@@ -108,7 +108,7 @@ __device__ __forceinline__ void store_rows(uint16_t* row, const f32x16 (&acc)[D 
         }
 }
 
-// Stage `rows` rows starting at r0 of one head into a swizzled LDS tile with global_load_lds
+// Stage `rows` rows starting at r0 of one head into a swizzled LDS tile by LDS DMA (lds_load16)
 // (rows past the end repeat row N-1); each of the kWaves waves issues its share of 1 KiB loads.
 template <int D>
 __device__ __forceinline__ void stage_rows(const uint16_t* src_head, int r0, int rows, int N, uint16_t* dst,
@@ -121,7 +121,7 @@ __device__ __forceinline__ void stage_rows(const uint16_t* src_head, int r0, int
         const int r = RPI * g + lane / CPR;
         const int ch = (lane % CPR) ^ swz<D>(r);
         const unsigned src = (unsigned)min(r0 + r, N - 1) * D + 8 * ch;
-        __builtin_amdgcn_global_load_lds((const void*)(src_head + src), (lds_void*)(dst + g * 512), 16, 0, 0);
+        lds_load16(src_head, N * D * 2, 2 * src, (lds_void*)(dst + g * 512));
     }
 }
 

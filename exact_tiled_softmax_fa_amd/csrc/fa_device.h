@@ -114,4 +114,16 @@ inline bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
+// 16 bytes at byte offset `off` of one head's n_bytes into LDS, lane l's at dst + 16 l
+// (buffer_load_dwordx4 ... lds). Offsets past n_bytes read zero; the callers clamp their rows so
+// none are. This is the MUBUF form of the LDS DMA on purpose: the compiler's wait-count pass
+// takes the FLAT-encoded global_load_lds for an access that may touch LDS and finish out of
+// order, and while one is in flight it waits for every LDS read (lgkmcnt(0)), also for those a
+// register ring issued ahead; the MUBUF form counts only against vmcnt and leaves those waits
+// exact. (The fourth descriptor word is gfx9's plain byte-addressed setting.)
+__device__ __forceinline__ void lds_load16(const uint16_t* head, int n_bytes, unsigned off, lds_void* dst) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)head, (short)0, n_bytes, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off, 0, 0, 0);
+}
+
 }  // namespace fa_detail

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     constexpr int TILE = kBlockN * D;          // elements per tile
     static_assert(IPW >= 1 && IPW * RPI * kWaves == kBlockN, "tile must split evenly over the waves");
 
-    // Two buffers each for K and V, filled straight from global memory (global_load_lds) in the
+    // Two buffers each for K and V, filled straight from global memory (LDS DMA, lds_load16) in the
     // swizzled layout; 64 KiB in all at D = 128, so every operand address is a per-lane register
     // plus an immediate below 64 KiB (the ds_read offset field). (Separate arrays let the
     // compiler see that the loads into one buffer never alias the reads of another.)
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             const int r = RPI * g + lane / CPR;
             const int ch = (lane % CPR) ^ swz<D>(r);
             const unsigned src = (unsigned)min(k0 + r, N - 1) * D + 8 * ch;
-            __builtin_amdgcn_global_load_lds((const void*)(src_head + src), (lds_void*)(dst + g * 512), 16, 0, 0);
+            lds_load16(src_head, N * D * 2, 2 * src, (lds_void*)(dst + g * 512));
         }
     };
 
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(1, 1)
             const int r = RPI * g + lane / CPR;
             const int ch = (lane % CPR) ^ swz<D>(r);
             const unsigned src = (unsigned)min(k0 + r, N - 1) * D + 8 * ch;
-            __builtin_amdgcn_global_load_lds((const void*)(src_head + src), (lds_void*)(dst + g * 512), 16, 0, 0);
+            lds_load16(src_head, N * D * 2, 2 * src, (lds_void*)(dst + g * 512));
         }
     };
 
