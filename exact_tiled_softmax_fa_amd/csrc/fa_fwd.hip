@@ -77,6 +77,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __shared__ __attribute__((aligned(4096))) uint16_t k_lds1[TILE];
     __shared__ __attribute__((aligned(4096))) uint16_t v_lds0[TILE];
     __shared__ __attribute__((aligned(4096))) uint16_t v_lds1[TILE];
+    __shared__ __attribute__((aligned(4096))) uint16_t v_lds2[TILE];
+    __shared__ __attribute__((aligned(4096))) uint16_t v_lds3[TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -295,14 +297,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     };
 
     // ---- schedule ----
-    // Tile t's K sits in buffer t % 2 and so does its V. Iteration j runs, in each wave:
+    // Tile t's K sits in buffer t % 2. Iteration j runs, in each wave:
     //   region 1: S^T(j+1) = K(j+1) . Q^T on the matrix cores, with the exponentials of tile j
     //             (S^T(j) -> P^T(j)) interleaved between the MFMAs on the vector ALU;
     //   region 2: O^T += V(j)^T . P^T(j), with the row max of S^T(j+1) interleaved;
     //   then the (rare) move of the reference max for tile j+1, after P(j) has been used.
-    // So each wave overlaps its own softmax with its own products, one tile apart. At the top of
-    // iteration j a barrier makes K(j+1) and V(j) visible (loaded during iteration j - 1) and
-    // frees the buffers of K(j) and V(j-1), which then take K(j+2) and V(j+1).
+    // So each wave overlaps its own softmax with its own products, one tile apart. Barrier j
+    // makes K(j+1) and V(j) visible (loaded after barrier j - 1) and frees the buffer of K(j) for
+    // K(j+2) and one V buffer for V(j+1): V(j-1)'s when V alternates between two buffers (the
+    // masked kernel), V(j-3)'s when it rotates through four (the ping-pong below).
     issue(Kh, 0, k_lds0);
     issue(Vh, 0, v_lds0);
     if (T > 1) issue(Kh, 1, k_lds1);
@@ -313,94 +316,150 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         mask(0, s0);
         rebase(row_max(s0));
     }
-    auto iteration = [&](int j, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], const uint16_t* k_nxt,
-                         const uint16_t* v_cur, uint16_t* k_load, uint16_t* v_load) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (j + 2 < T) issue(Kh, j + 2, k_load);
-        if (j + 1 < T) issue(Vh, j + 1, v_load);
-        if (MASKED && j < T_w0) {
-            // before this wave's first tile: at most start the pipeline with S^T(j+1)
-            if (j + 1 == T_w0 && j + 1 < T_w) {
-                qk(k_nxt, s_nxt);
-                mask(j + 1, s_nxt);
-                rebase(row_max(s_nxt));
+    // region 1 of tile j: S^T(j+1) = K(j+1) . Q^T with the exponentials of tile j in between.
+    auto region1 = [&](f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], const uint16_t* k_nxt) __attribute__((always_inline)) {
+        // Explicit software pipeline: the LDS operands of MFMA i + 2 are read before MFMA i
+        // issues, and one pair of exponentials follows each MFMA; sched_barrier(0) pins that
+        // order so the LDS latency stays behind two MFMAs instead of stalling every one.
+        constexpr int NQ = 2 * DK;  // 16 MFMAs for D = 128, 8 for D = 64
+        u32x4 ka[NQ];
+        ka[0] = k_operand(k_nxt, 0, 0);
+        ka[1] = k_operand(k_nxt, 0, 1);
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int t = i >> 1, kb = i & 1;
+            if (i + 2 < NQ) {
+                const int t2 = (i + 2) >> 1, kb2 = (i + 2) & 1;
+                ka[i + 2] = k_operand(k_nxt, t2, kb2);
             }
-        } else if (j + 1 < T_w) {
-            // region 1: S^T(j+1) = K(j+1) . Q^T with the exponentials of tile j in between.
-            // Explicit software pipeline: the LDS operands of MFMA i + 2 are read before MFMA i
-            // issues, and one pair of exponentials follows each MFMA; sched_barrier(0) pins that
-            // order so the LDS latency stays behind two MFMAs instead of stalling every one.
-            constexpr int NQ = 2 * DK;  // 16 MFMAs for D = 128, 8 for D = 64
-            u32x4 ka[NQ];
-            ka[0] = k_operand(k_nxt, 0, 0);
-            ka[1] = k_operand(k_nxt, 0, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            s_nxt[kb] = mfma32<BF16>(ka[i], qreg[t], t == 0 ? (f32x16){} : s_nxt[kb]);
+            __builtin_amdgcn_sched_barrier(0);
+            // exponentials: pair i of the 16 pairs of S^T(j) held by this lane (NQ == 16),
+            // or pairs 2i, 2i+1 when D = 64 (NQ == 8)
 #pragma unroll
-            for (int i = 0; i < NQ; ++i) {
-                const int t = i >> 1, kb = i & 1;
-                if (i + 2 < NQ) {
-                    const int t2 = (i + 2) >> 1, kb2 = (i + 2) & 1;
-                    ka[i + 2] = k_operand(k_nxt, t2, kb2);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                s_nxt[kb] = mfma32<BF16>(ka[i], qreg[t], t == 0 ? (f32x16){} : s_nxt[kb]);
-                __builtin_amdgcn_sched_barrier(0);
-                // exponentials: pair i of the 16 pairs of S^T(j) held by this lane (NQ == 16),
-                // or pairs 2i, 2i+1 when D = 64 (NQ == 8)
-#pragma unroll
-                for (int u = 0; u < 16 / NQ; ++u) {
-                    const int pr = i * (16 / NQ) + u;  // pair index 0..15
-                    const int kbp = pr >> 3, r = 2 * (pr & 7);
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[kbp][r], c, -mc));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[kbp][r + 1], c, -mc));
-                    pk[kbp][r >> 1] = pack2<BF16>(p0, p1);
-                    l_run = add_pair<BF16>(pk[kbp][r >> 1], l_run);
-                    if constexpr (BF16) l_f32 += p0 + p1;
-                }
-                __builtin_amdgcn_sched_barrier(0);
+            for (int u = 0; u < 16 / NQ; ++u) {
+                const int pr = i * (16 / NQ) + u;  // pair index 0..15
+                const int kbp = pr >> 3, r = 2 * (pr & 7);
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[kbp][r], c, -mc));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[kbp][r + 1], c, -mc));
+                pk[kbp][r >> 1] = pack2<BF16>(p0, p1);
+                l_run = add_pair<BF16>(pk[kbp][r >> 1], l_run);
+                if constexpr (BF16) l_f32 += p0 + p1;
             }
-            // Keep the exponentials in region 1: without this the compiler sinks them past the
-            // mask branch into region 2, next to their only consumer.
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 8; ++r) asm volatile("" : "+v"(pk[kb][r]));
-            asm volatile("" : "+v"(l_run));
-            if constexpr (BF16) asm volatile("" : "+v"(l_f32));
-            mask(j + 1, s_nxt);
-            // region 2: O^T += V(j)^T . P^T(j) with the row max of S^T(j+1) in between, V^T
-            // operands read two MFMAs ahead.
-            constexpr int NP = 4 * DB;  // 16 MFMAs for D = 128, 8 for D = 64
-            u32x4 va[NP];
-            va[0] = v_operand(v_cur, 0, 0);
-            va[1] = v_operand(v_cur, 1 / DB, 1 % DB);
-            float mx = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < NP; ++i) {
-                const int kk = i / DB, b = i % DB;
-                if (i + 2 < NP) va[i + 2] = v_operand(v_cur, (i + 2) / DB, (i + 2) % DB);
-                __builtin_amdgcn_sched_barrier(0);
-                oacc[b] = mfma32<BF16>(va[i], p_operand(kk), oacc[b]);
-                __builtin_amdgcn_sched_barrier(0);
-                // row max: the 32 scores of this lane, 32 / NP per MFMA
-#pragma unroll
-                for (int u = 0; u < 32 / NP; ++u) {
-                    const int e = i * (32 / NP) + u;
-                    mx = fmaxf(mx, s_nxt[e >> 4][e & 15]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            rebase(max_with_partner(mx));
-        } else if (j < T_w) {
-            expo(s_cur);
-            pv(v_cur);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        // Keep the exponentials in region 1: without this the compiler sinks them past the
+        // mask branch into region 2, next to their only consumer.
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 8; ++r) asm volatile("" : "+v"(pk[kb][r]));
+        asm volatile("" : "+v"(l_run));
+        if constexpr (BF16) asm volatile("" : "+v"(l_f32));
     };
-    for (int j = 0; j < T; j += 2) {
-        // even j: K(j+1) in buffer 1, V(j) in buffer 0; K(j+2) -> buffer 0, V(j+1) -> buffer 1
-        iteration(j, s0, s1, k_lds1, v_lds0, k_lds0, v_lds1);
-        if (j + 1 >= T) break;
-        iteration(j + 1, s1, s0, k_lds0, v_lds1, k_lds1, v_lds0);
+    // region 2 of tile j: O^T += V(j)^T . P^T(j) with the row max of S^T(j+1) in between, then
+    // the move of the reference max for tile j+1.
+    auto region2 = [&](f32x16 (&s_nxt)[2], const uint16_t* v_cur) __attribute__((always_inline)) {
+        // V^T operands read two MFMAs ahead.
+        constexpr int NP = 4 * DB;  // 16 MFMAs for D = 128, 8 for D = 64
+        u32x4 va[NP];
+        va[0] = v_operand(v_cur, 0, 0);
+        va[1] = v_operand(v_cur, 1 / DB, 1 % DB);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int kk = i / DB, b = i % DB;
+            if (i + 2 < NP) va[i + 2] = v_operand(v_cur, (i + 2) / DB, (i + 2) % DB);
+            __builtin_amdgcn_sched_barrier(0);
+            oacc[b] = mfma32<BF16>(va[i], p_operand(kk), oacc[b]);
+            __builtin_amdgcn_sched_barrier(0);
+            // row max: the 32 scores of this lane, 32 / NP per MFMA
+#pragma unroll
+            for (int u = 0; u < 32 / NP; ++u) {
+                const int e = i * (32 / NP) + u;
+                mx = fmaxf(mx, s_nxt[e >> 4][e & 15]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        rebase(max_with_partner(mx));
+    };
+    if constexpr (MASKED) {
+        // every wave: barrier, loads, region 1, region 2 (V in two buffers)
+        auto iteration = [&](int j, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], const uint16_t* k_nxt,
+                             const uint16_t* v_cur, uint16_t* k_load, uint16_t* v_load) __attribute__((always_inline)) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (j + 2 < T) issue(Kh, j + 2, k_load);
+            if (j + 1 < T) issue(Vh, j + 1, v_load);
+            if (j < T_w0) {
+                // before this wave's first tile: at most start the pipeline with S^T(j+1)
+                if (j + 1 == T_w0 && j + 1 < T_w) {
+                    qk(k_nxt, s_nxt);
+                    mask(j + 1, s_nxt);
+                    rebase(row_max(s_nxt));
+                }
+            } else if (j + 1 < T_w) {
+                region1(s_cur, s_nxt, k_nxt);
+                mask(j + 1, s_nxt);
+                region2(s_nxt, v_cur);
+            } else if (j < T_w) {
+                expo(s_cur);
+                pv(v_cur);
+            }
+        };
+        for (int j = 0; j < T; j += 2) {
+            // even j: K(j+1) in buffer 1, V(j) in buffer 0; K(j+2) -> buffer 0, V(j+1) -> buffer 1
+            iteration(j, s0, s1, k_lds1, v_lds0, k_lds0, v_lds1);
+            if (j + 1 >= T) break;
+            iteration(j + 1, s1, s0, k_lds0, v_lds1, k_lds1, v_lds0);
+        }
+    } else {
+        // Ping-pong. The two waves on a SIMD run the same sequence of regions half an iteration
+        // apart: waves 0-3 pass barrier j before region 1 of tile j, waves 4-7 ("lag") before
+        // region 2 of tile j-1. While one wave of the pair runs the exponentials of region 1 on
+        // the vector ALU, the other runs the MFMA-only region 2, instead of both contending for
+        // the vector ALU and then both for the matrix core. A lagging wave still reads V(j-1)
+        // after barrier j, so V rotates through four buffers (V(t) in buffer t % 4). Every wave
+        // issues its share of the loads of step j (K(j+2) into K(j)'s buffer, V(j+1) into
+        // V(j-3)'s) at the top of the step, after barrier j in waves 0-3 and after region 2 of
+        // tile j-1 in waves 4-7, and waits for them at the top of the next step: one
+        // unconditional wait, so the compiler sees no path on which a read could overtake them.
+        const bool lag = wave_s >= kWaves / 2;
+        auto step = [&](int j, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], uint16_t* k_cur, const uint16_t* k_nxt,
+                        const uint16_t* v_cur, uint16_t* v_p1) __attribute__((always_inline)) {
+            __builtin_amdgcn_s_waitcnt(0);
+            if (!lag) __syncthreads();  // barrier j
+            if (j + 2 < T) issue(Kh, j + 2, k_cur);
+            if (j + 1 < T) issue(Vh, j + 1, v_p1);
+            if (j + 1 < T_w) {
+                region1(s_cur, s_nxt, k_nxt);
+                mask(j + 1, s_nxt);
+            } else if (j < T_w) {
+                expo(s_cur);
+            }
+            if (lag && j + 1 < T) {
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();  // barrier j + 1
+            }
+            if (j + 1 < T_w) {
+                region2(s_nxt, v_cur);
+            } else if (j < T_w) {
+                pv(v_cur);
+            }
+        };
+        if (lag && T > 0) __syncthreads();  // barrier 0
+        // T barriers in every wave: waves 0-3 one per step; waves 4-7 barrier 0 above and one
+        // per step but the last
+        for (int j = 0; j < T; j += 4) {
+            step(j, s0, s1, k_lds0, k_lds1, v_lds0, v_lds1);
+            if (j + 1 >= T) break;
+            step(j + 1, s1, s0, k_lds1, k_lds0, v_lds1, v_lds2);
+            if (j + 2 >= T) break;
+            step(j + 2, s0, s1, k_lds0, k_lds1, v_lds2, v_lds3);
+            if (j + 3 >= T) break;
+            step(j + 3, s1, s0, k_lds1, k_lds0, v_lds3, v_lds0);
+        }
     }
 
     // ---- epilogue: O = o~ / l, lse = m*scale + ln l ----
