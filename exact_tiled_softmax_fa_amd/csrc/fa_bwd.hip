@@ -310,10 +310,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     // Per-lane element offsets with this wave's row block folded in (the swizzle depends on
     // row % 16 only, so moving whole 32-row blocks is a plain offset): qoff into a Q or dO tile
-    // (this wave's 32-row half), tlo/thi for the transpose reads of the same rows, and kvp = the
-    // LDS address of this lane's K chunk per k-step (its V chunk is kKeys * D elements further).
-    int qoff[DK], tlo[DB], thi[DB];
-    const lds_u16* kvp[DK];
+    // (this wave's 32-row half), tlo/thi for the transpose reads of the same rows, and kvo into
+    // kv_lds for this lane's K chunk per k-step (its V chunk is kKeys * D elements further).
+    int qoff[DK], tlo[DB], thi[DB], kvo[DK];
     transpose_offsets<D>(lane, tlo, thi);
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
@@ -323,7 +322,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int t = 0; t < DK; ++t) {
         qoff[t] = tile_off<D>(lq, 2 * t + h) + 32 * half * D;
-        kvp[t] = (const lds_u16*)kv_lds + tile_off<D>(lq, 2 * t + h) + 32 * kg * D;
+        kvo[t] = tile_off<D>(lq, 2 * t + h) + 32 * kg * D;
     }
 
     f32x16 dv[DB], dk[DB];
@@ -335,13 +334,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     // lse (log2 units) and D of the rows of query tile j, staged by wave 0 through registers
     float st_l = 0.f, st_d = 0.f;
+    // (The loaded values are first used at the store, at the end of the step: no wait for the
+    // loads before the step's products.)
     auto stats_load = [&](int j) __attribute__((always_inline)) {
         const int r = min(j * kQueryTile + lane, N - 1);
-        st_l = lse_h[r] * kLog2e;
+        st_l = lse_h[r];
         st_d = del_h[r];
     };
     auto stats_store = [&](int buf) __attribute__((always_inline)) {
-        st_lds[buf][0][lane] = st_l;
+        st_lds[buf][0][lane] = st_l * kLog2e;
         st_lds[buf][1][lane] = st_d;
     };
 
@@ -355,17 +356,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int qs = j * kQueryTile + 32 * half;  // first query row of this wave's half
         if (qs + 31 < skip_below) return;           // every key of this wave is after these rows
         // Redefining the per-lane offsets each step keeps the compiler from hoisting every
-        // (offset + constant) LDS address of the unrolled loop into a register of its own.
+        // (offset + constant) LDS address of the unrolled loop into a register of its own. They
+        // stay offsets into known arrays: a pointer passed through the asm would be an unknown
+        // object to the compiler, which then waits for the tile loads in flight (vmcnt(0))
+        // before reading through it.
 #pragma unroll
-        for (int t = 0; t < DK; ++t) asm volatile("" : "+v"(qoff[t]), "+v"(kvp[t]));
+        for (int t = 0; t < DK; ++t) asm volatile("" : "+v"(qoff[t]), "+v"(kvo[t]));
 #pragma unroll
         for (int b = 0; b < DB; ++b) asm volatile("" : "+v"(tlo[b]), "+v"(thi[b]));
         f32x16 s = {}, dp = {};
 #pragma unroll
         for (int t = 0; t < DK; ++t) {
-            s = mfma32<BF16>(*reinterpret_cast<const u32x4*>(qt_ + qoff[t]), *(const lds_u32x4*)kvp[t], s);
+            s = mfma32<BF16>(*reinterpret_cast<const u32x4*>(qt_ + qoff[t]),
+                             *reinterpret_cast<const u32x4*>(kv_lds + kvo[t]), s);
             dp = mfma32<BF16>(*reinterpret_cast<const u32x4*>(dot_ + qoff[t]),
-                              *(const lds_u32x4*)(kvp[t] + kKeys * D), dp);
+                              *reinterpret_cast<const u32x4*>(kv_lds + kKeys * D + kvo[t]), dp);
         }
         __builtin_amdgcn_sched_barrier(0);
         // C layout: register r holds query row qs + 8(r/4) + 4h + r%4 of key `key`
