@@ -9,7 +9,8 @@ Contents
               attention (the definition written out), and its gradients with
               respect to q, k, v by the chain rule (``attention_backward``), and the
               definition under a sliding-window / key-padding mask
-              (``attention_masked``).
+              (``attention_masked``) and under a mask over blocks of the score
+              matrix (``attention_blocksparse``).
   recurrence  the online-softmax recurrence for one query in fp64, block by
               block, in any block partition and order, with switches that plant
               the four classic implementation mistakes (used only to show that
@@ -26,7 +27,10 @@ finite differences, fp64 autograd, sum rules, translation invariance,
 linearity and closed forms. The masked definition
 (tests/test_oracle_mask_pins.py): brute force with the same predicate,
 reductions to unmasked attention over each row's key slice and over truncated
-keys, and the causal / unmasked special cases. Every function here is pinned; none is "parity unpinned"
+keys, and the causal / unmasked special cases. The block-sparse definition
+(tests/test_oracle_blocksparse_pins.py): brute force, all-ones and
+block-diagonal and block-triangular reductions, a per-row gather, mask forms
+and empty rows. Every function here is pinned; none is "parity unpinned"
 except the second worked example's output vector, whose value vectors the
 page does not print.
 """

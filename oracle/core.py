@@ -34,6 +34,14 @@ def _load():
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
             ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
         ]
+        lib.fa_oracle_fwd_blocksparse.restype = ctypes.c_int
+        lib.fa_oracle_fwd_blocksparse.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_int64,
+        ]
         lib.fa_oracle_bwd.restype = ctypes.c_int
         lib.fa_oracle_bwd.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -164,4 +172,63 @@ def attention_masked(q, k, v, scale, window_left=-1, window_right=-1, seqlens_k=
                                       sl.ctypes.data if sl is not None else None, rows_p, n_rows)
     if rc != 0:
         raise RuntimeError(f"fa_oracle_fwd_masked failed with code {rc}")
+    return o, lse
+
+
+def block_mask_strides(mask, B, H, N, block_q, block_k):
+    """(contiguous uint8 mask, stride_b, stride_h) for a block mask of shape [n_qb, n_kb] (one
+    for every head), [H, n_qb, n_kb] (one per head, shared over the batch) or
+    [B, H, n_qb, n_kb], with n_qb = ceil(N / block_q) and n_kb = ceil(N / block_k)."""
+    mask = np.ascontiguousarray(np.asarray(mask) != 0, dtype=np.uint8)
+    n_qb, n_kb = -(-N // block_q), -(-N // block_k)
+    per = n_qb * n_kb
+    if mask.shape == (n_qb, n_kb):
+        return mask, 0, 0
+    if mask.shape == (H, n_qb, n_kb):
+        return mask, 0, per
+    if mask.shape == (B, H, n_qb, n_kb):
+        return mask, H * per, per
+    raise ValueError(f"block mask must be [{n_qb},{n_kb}], [H,{n_qb},{n_kb}] or [B,H,{n_qb},{n_kb}], "
+                     f"got {mask.shape}")
+
+
+def attention_blocksparse(q, k, v, scale, block_mask, block_q, block_k, window_left=-1, window_right=-1,
+                          seqlens_k=None, rows=None):
+    """Exact attention in fp64 under a mask over blocks of the score matrix
+    (``fa_oracle_fwd_blocksparse``): the pair (i, j) is allowed when the mask byte of query block
+    i // block_q and key block j // block_k is non-zero and the general mask of
+    ``attention_masked`` allows it. ``block_mask`` as in ``block_mask_strides``. A row with no
+    allowed key gets o = 0 and lse = -inf. Shapes and ``rows`` as for ``attention``."""
+    q = np.ascontiguousarray(np.asarray(q, dtype=np.float64))
+    k = np.ascontiguousarray(np.asarray(k, dtype=np.float64))
+    v = np.ascontiguousarray(np.asarray(v, dtype=np.float64))
+    if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError(f"q, k, v must share one [B,H,N,d] shape, got {q.shape} {k.shape} {v.shape}")
+    B, H, N, d = q.shape
+    if block_q < 1 or block_k < 1:
+        raise ValueError("block sizes must be >= 1")
+    bm, sb, sh = block_mask_strides(block_mask, B, H, N, block_q, block_k)
+    sl = None
+    if seqlens_k is not None:
+        sl = np.ascontiguousarray(np.asarray(seqlens_k, dtype=np.int64))
+        if sl.shape != (B,):
+            raise ValueError(f"seqlens_k must be [B], got {sl.shape}")
+    if rows is None:
+        o = np.empty((B, H, N, d))
+        lse = np.empty((B, H, N))
+        rows_p, n_rows = None, 0
+    else:
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        if rows.ndim != 2 or rows.shape[0] != B * H:
+            raise ValueError(f"rows must be [B*H, R], got {rows.shape}")
+        n_rows = rows.shape[1]
+        o = np.empty((B * H, n_rows, d))
+        lse = np.empty((B * H, n_rows))
+        rows_p = rows.ctypes.data
+    rc = _load().fa_oracle_fwd_blocksparse(q.ctypes.data, k.ctypes.data, v.ctypes.data, o.ctypes.data,
+                                           lse.ctypes.data, B, H, N, d, float(scale), int(window_left),
+                                           int(window_right), sl.ctypes.data if sl is not None else None,
+                                           bm.ctypes.data, int(block_q), int(block_k), sb, sh, rows_p, n_rows)
+    if rc != 0:
+        raise RuntimeError(f"fa_oracle_fwd_blocksparse failed with code {rc}")
     return o, lse

@@ -28,6 +28,8 @@
  * tiled computation"). There is no tiling, blocking or reordering here: one
  * N-length fp64 score buffer per row, summed in ascending key order.
  *
+ * fa_oracle_fwd_masked and fa_oracle_fwd_blocksparse restrict the allowed keys
+ * further (windows, key padding, a mask over blocks of the score matrix).
  * fa_oracle_bwd, at the end of the file, gives the gradients of the same
  * definition with respect to q, k and v by the chain rule.
  */
@@ -356,6 +358,103 @@ int fa_oracle_fwd_masked(const double* q, const double* k, const double* v, doub
         for (int64_t c = 0; c < d; ++c) acc[c] = 0.0;
         for (int64_t j = lo; j < hi; ++j)
             for (int64_t c = 0; c < d; ++c) acc[c] += s[j] * vh[j * d + c];
+        for (int64_t c = 0; c < d; ++c) oi[c] = acc[c] / l;
+        lse[bh * per_head + r] = m + log(l);
+    }
+    free(s_all);
+    free(acc_all);
+    return 0;
+}
+
+/*
+ * Block-sparse attention: the general mask of fa_oracle_fwd_masked and, on top of it, a
+ * mask over blocks of the score matrix. Query i lies in query block i / block_q, key j in
+ * key block j / block_k; the pair is allowed only when the byte
+ *   block_mask[b * stride_b + h * stride_h + (i / block_q) * n_kb + j / block_k]
+ * is non-zero, with n_kb = ceil(N / block_k) bytes per mask row (a stride of 0 shares one
+ * mask across batches or heads). Any mask applied to the scores before the max is
+ * admitted by the pages ("Causal masking fits inside the tiled computation", nalar.dev,
+ * last paragraph; aicassindra.com, "Pitfalls in implementing the recurrence"); a mask given
+ * per block is the plainest such mask that decides whole tiles at once.
+ * A row with no allowed key has no softmax; its output is 0 and its lse is -inf.
+ *
+ * Arguments as fa_oracle_fwd_masked, plus block_mask (host pointer), block_q, block_k >= 1,
+ * stride_b, stride_h >= 0. Same return codes.
+ */
+int fa_oracle_fwd_blocksparse(const double* q, const double* k, const double* v, double* o, double* lse,
+                              int64_t B, int64_t H, int64_t N, int64_t d, double scale,
+                              int64_t window_left, int64_t window_right, const int64_t* seqlens_k,
+                              const uint8_t* block_mask, int64_t block_q, int64_t block_k,
+                              int64_t stride_b, int64_t stride_h, const int64_t* rows, int64_t n_rows) {
+    if (!q || !k || !v || !o || !lse || !block_mask || B < 1 || H < 1 || N < 1 || d < 1) return 1;
+    if (window_left < -1 || window_right < -1 || block_q < 1 || block_k < 1 || stride_b < 0 || stride_h < 0)
+        return 1;
+    int64_t per_head = rows ? n_rows : N;
+    if (per_head < 1) return 1;
+    for (int64_t t = 0; rows && t < B * H * n_rows; ++t)
+        if (rows[t] < 0 || rows[t] >= N) return 1;
+    for (int64_t b = 0; seqlens_k && b < B; ++b)
+        if (seqlens_k[b] < 0 || seqlens_k[b] > N) return 1;
+    const int64_t n_kb = (N + block_k - 1) / block_k;
+    int64_t total = B * H * per_head;
+    int nthreads = fa_oracle_threads();
+    double* s_all = (double*)malloc((size_t)nthreads * (size_t)N * sizeof(double));
+    double* acc_all = (double*)malloc((size_t)nthreads * (size_t)d * sizeof(double));
+    if (!s_all || !acc_all) {
+        free(s_all);
+        free(acc_all);
+        return 2;
+    }
+
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nthreads)
+    for (int64_t t = 0; t < total; ++t) {
+#ifdef _OPENMP
+        int tid = omp_get_thread_num();
+#else
+        int tid = 0;
+#endif
+        double* s = s_all + (size_t)tid * (size_t)N;
+        double* acc = acc_all + (size_t)tid * (size_t)d;
+        int64_t bh = t / per_head;
+        int64_t r = t % per_head;
+        int64_t i = rows ? rows[bh * n_rows + r] : r;
+        int64_t kv_len = seqlens_k ? seqlens_k[bh / H] : N;
+        int64_t lo = window_left >= 0 ? i - window_left : 0;
+        int64_t hi = window_right >= 0 ? i + window_right + 1 : N;
+        if (lo < 0) lo = 0;
+        if (hi > kv_len) hi = kv_len;
+        const uint8_t* mrow = block_mask + (bh / H) * stride_b + (bh % H) * stride_h + (i / block_q) * n_kb;
+        const double* qi = q + (bh * N + i) * d;
+        const double* kh = k + bh * N * d;
+        const double* vh = v + bh * N * d;
+        double* oi = o + (bh * per_head + r) * d;
+        /* scores of the allowed keys; the others stay out of every pass */
+        double m = -INFINITY;
+        int64_t allowed = 0;
+        for (int64_t j = lo; j < hi; ++j) {
+            if (!mrow[j / block_k]) continue;
+            double dot = 0.0;
+            for (int64_t c = 0; c < d; ++c) dot += qi[c] * kh[j * d + c];
+            s[j] = scale * dot;
+            if (s[j] > m) m = s[j];
+            ++allowed;
+        }
+        if (allowed == 0) {
+            for (int64_t c = 0; c < d; ++c) oi[c] = 0.0;
+            lse[bh * per_head + r] = -INFINITY;
+            continue;
+        }
+        double l = 0.0;
+        for (int64_t j = lo; j < hi; ++j) {
+            if (!mrow[j / block_k]) continue;
+            s[j] = exp(s[j] - m);
+            l += s[j];
+        }
+        for (int64_t c = 0; c < d; ++c) acc[c] = 0.0;
+        for (int64_t j = lo; j < hi; ++j) {
+            if (!mrow[j / block_k]) continue;
+            for (int64_t c = 0; c < d; ++c) acc[c] += s[j] * vh[j * d + c];
+        }
         for (int64_t c = 0; c < d; ++c) oi[c] = acc[c] / l;
         lse[bh * per_head + r] = m + log(l);
     }
