@@ -1,7 +1,8 @@
 """Throughput of the attention forward (or backward) pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd]
-                    [--splits S] [--window-left L --window-right R] [--no-cpu-baseline]
+                    [--splits S] [--window-left L --window-right R]
+                    [--block-density P [--block-size S]] [--no-cpu-baseline]
     python bench.py --cpu-variant [--workload NAME] [--heads K] [--threads T]
 
 A step is one fa_fwd call over the whole workload (every query row of every
@@ -14,6 +15,11 @@ fa_fwd; the roofline then covers both of its kernels (split reduction and merge)
 --window-left L / --window-right R time fa_fwd_masked with that sliding window (-1 = no limit;
 the workload's causal flag is then ignored) and price it by the allowed (row, key) pairs:
 4 d flops each.
+
+--block-density P times fa_fwd_blocksparse with a seeded random block mask (blocks of
+--block-size S rows and keys, default 128; each block kept with probability P, the diagonal
+always), shared by all heads, the workload's causal flag ignored, and prices it by the allowed
+(row, key) pairs: 4 d flops each.
 
 --cpu-variant times the host-CPU entry point fa_fwd_cpu instead (no GPU needed) on the first K
 heads of the workload (default 4), in TFLOP/s of the same flop convention.
@@ -165,6 +171,8 @@ def main():
                     help="run the forward pass as split-KV with this many splits (0: heuristic)")
     ap.add_argument("--window-left", type=int, default=None, help="sliding window: keys back (-1 = all)")
     ap.add_argument("--window-right", type=int, default=None, help="sliding window: keys ahead (-1 = all)")
+    ap.add_argument("--block-density", type=float, default=None, help="block-sparse: fraction of blocks kept")
+    ap.add_argument("--block-size", type=int, default=128, help="block-sparse: rows and keys per block")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--cpu-variant", action="store_true", help="time fa_fwd_cpu on host cores instead")
     ap.add_argument("--heads", type=int, default=4, help="--cpu-variant: heads of the workload to run")
@@ -222,6 +230,17 @@ def main():
         def step():  # noqa: F811
             fa.forward_masked(q, k, v, window[0], window[1], None, scale=w.scale, out=o, lse=lse)
 
+    blocks = None
+    if args.block_density is not None and args.which == "fwd":
+        bmask = workloads.make_block_mask(w, args.block_size, args.block_density)
+        blocks = (args.block_size, args.block_density, workloads.block_mask_pairs(bmask, w.N, args.block_size,
+                                                                                   args.block_size))
+        bmask_dev = torch.from_numpy(bmask).cuda()
+
+        def step():  # noqa: F811
+            fa.forward_blocksparse(q, k, v, bmask_dev, args.block_size, args.block_size, scale=w.scale, out=o,
+                                   lse=lse)
+
     if args.which == "bwd":
         step()
         dout = workloads.make_dout(w).cuda()
@@ -253,13 +272,17 @@ def main():
         lo = np.maximum(0, i - window[0]) if window[0] >= 0 else np.zeros_like(i)
         hi = np.minimum(w.N, i + window[1] + 1) if window[1] >= 0 else np.full_like(i, w.N)
         flops = 4.0 * w.d * w.B * w.H * float(np.maximum(hi - lo, 0).sum())
+    if blocks is not None:
+        flops = 4.0 * w.d * w.B * w.H * float(blocks[2])
     value = flops / (wall / args.steps) / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     out = {
         "metric": (HEADLINE_METRIC if w.name == workloads.HEADLINE.name and args.which == "fwd" and splits is None
                    else f"{args.which} attention TFLOP/s ({w.name}"
                         + (f", split-KV {splits}" if splits is not None else "")
-                        + (f", window {window[0]}/{window[1]}" if window is not None else "") + ")"),
+                        + (f", window {window[0]}/{window[1]}" if window is not None else "")
+                        + (f", block-sparse {blocks[0]}x{blocks[0]} blocks, density {blocks[1]}" if blocks else "")
+                        + ")"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -274,6 +297,8 @@ def main():
         "pct_mfma_peak": round(100.0 * value / PEAK_MFMA_F16_TFLOPS, 2),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "num_splits": splits, "window": window,
+                   "block_sparse": ({"block": blocks[0], "density": blocks[1], "allowed_pairs_per_head": blocks[2]}
+                                    if blocks else None),
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "none"},
         "roofline": {
             "bound": "mfma",
@@ -281,9 +306,11 @@ def main():
             "peak": PEAK_MFMA_F16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_MFMA_F16_TFLOPS, 4),
-            "traffic": measured_traffic(w.name) if args.which == "fwd" and splits is None and window is None else None,
+            "traffic": (measured_traffic(w.name) if args.which == "fwd" and splits is None and window is None
+                        and blocks is None else None),
             "kernel": ("fa_bwd_dq_kernel + fa_bwd_dkdv_kernel" if args.which == "bwd" else
                        "fa_fwd_kernel (masked)" if window is not None else
+                       "fa_fwd_kernel (block-sparse)" if blocks is not None else
                        "fa_fwd_kernel (split) + fa_merge_kernel" if splits is not None else KERNEL_NAME),
             "kernel_ms": round(kernel_ms, 4),
         },

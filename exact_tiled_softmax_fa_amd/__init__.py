@@ -42,6 +42,12 @@ class FaMask(ctypes.Structure):
     _fields_ = [("window_left", ctypes.c_int64), ("window_right", ctypes.c_int64), ("seqlens_k", ctypes.c_void_p)]
 
 
+class FaBlockMask(ctypes.Structure):
+    """Mirror of fa_block_mask in include/fa_fwd.h."""
+    _fields_ = [("mask", ctypes.c_void_p), ("block_q", ctypes.c_int64), ("block_k", ctypes.c_int64),
+                ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
+
+
 class FaError(RuntimeError):
     """A non-zero status returned by the C library."""
 
@@ -75,6 +81,9 @@ def lib():
         L.fa_fwd_masked.restype = ctypes.c_int
         L.fa_fwd_masked.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [
             ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(FaMask)]
+        L.fa_fwd_blocksparse.restype = ctypes.c_int
+        L.fa_fwd_blocksparse.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [
+            ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(FaMask), ctypes.POINTER(FaBlockMask)]
         L.fa_fwd_splitkv.restype = ctypes.c_int
         L.fa_fwd_splitkv.argtypes = L.fa_fwd.argtypes + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t]
         L.fa_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
@@ -284,6 +293,62 @@ def forward_masked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, window_lef
         stream = torch.cuda.current_stream(q.device).cuda_stream
         st = fa_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
                            scale, stream, _DTYPES[q.dtype], mask)
+    if st != 0:
+        raise FaError(st, status_string(st))
+    return out, lse
+
+
+def fa_fwd_blocksparse(q, k, v, o, lse, B, H, N, d, scale, stream, dtype, mask, blocks) -> int:
+    """Raw call of the C entry point fa_fwd_blocksparse (mask: an FaMask or None; blocks: an
+    FaBlockMask or None); returns the status code."""
+    return int(lib().fa_fwd_blocksparse(q, k, v, o, lse, B, H, N, d, float(scale), stream, int(dtype),
+                                        ctypes.byref(mask) if mask is not None else None,
+                                        ctypes.byref(blocks) if blocks is not None else None))
+
+
+def forward_blocksparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: torch.Tensor,
+                        block_q: int, block_k: int, window_left: int = -1, window_right: int = -1,
+                        seqlens_k: torch.Tensor = None, scale=None, out: torch.Tensor = None,
+                        lse: torch.Tensor = None):
+    """Block-sparse attention (include/fa_fwd.h, fa_block_mask): the pair (i, j) is allowed when
+    block_mask[.., i // block_q, j // block_k] != 0 and the window / key-length mask of
+    forward_masked allows it. block_mask: a contiguous uint8 (or bool) GPU tensor of shape
+    [n_qb, n_kb] (all heads), [H, n_qb, n_kb] (per head) or [B, H, n_qb, n_kb], with
+    n_qb = ceil(N / block_q), n_kb = ceil(N / block_k); block sizes are multiples of 64.
+    Returns (o, lse); rows with no allowed key get o = 0 and lse = -inf."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor [B, H, N, d]")
+    if q.shape != k.shape or q.shape != v.shape or q.dtype != k.dtype or q.dtype != v.dtype or q.dtype not in _DTYPES:
+        raise ValueError("q, k, v must share one shape and one of float16 / bfloat16")
+    B, H, N, d = q.shape
+    if block_q < 1 or block_k < 1:
+        raise ValueError("block sizes must be positive")
+    n_qb, n_kb = -(-N // block_q), -(-N // block_k)
+    if (not isinstance(block_mask, torch.Tensor) or not block_mask.is_cuda or block_mask.device != q.device
+            or block_mask.dtype not in (torch.uint8, torch.bool) or not block_mask.is_contiguous()):
+        raise ValueError("block_mask must be a contiguous uint8 or bool GPU tensor on q's device")
+    per = n_qb * n_kb
+    shapes = {(n_qb, n_kb): (0, 0), (H, n_qb, n_kb): (0, per), (B, H, n_qb, n_kb): (H * per, per)}
+    if tuple(block_mask.shape) not in shapes:
+        raise ValueError(f"block_mask must be [{n_qb},{n_kb}], [H,{n_qb},{n_kb}] or [B,H,{n_qb},{n_kb}], "
+                         f"got {tuple(block_mask.shape)}")
+    stride_b, stride_h = shapes[tuple(block_mask.shape)]
+    if seqlens_k is not None and (not seqlens_k.is_cuda or seqlens_k.dtype != torch.int32 or seqlens_k.shape != (B,)
+                                  or not seqlens_k.is_contiguous() or seqlens_k.device != q.device):
+        raise ValueError("seqlens_k must be a contiguous int32 GPU tensor [B] on q's device")
+    if scale is None:
+        scale = default_scale(d)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_like("out", out, q)
+    _check_like("lse", lse, q, torch.float32, (B, H, N))
+    mask = FaMask(int(window_left), int(window_right), seqlens_k.data_ptr() if seqlens_k is not None else None)
+    blocks = FaBlockMask(block_mask.data_ptr(), int(block_q), int(block_k), stride_b, stride_h)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = fa_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                                scale, stream, _DTYPES[q.dtype], mask, blocks)
     if st != 0:
         raise FaError(st, status_string(st))
     return out, lse

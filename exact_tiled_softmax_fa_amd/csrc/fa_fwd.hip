@@ -46,6 +46,7 @@ constexpr int kBlockM = 32 * kWaves;  // query rows per workgroup (32 per wave)
 constexpr int kBlockN = 64;           // keys per tile
 constexpr float kDefaultRescaleLog2 = 8.f;  // default reference-max threshold (log2 units)
 constexpr int kDefaultVariant = 1;          // kernel fa_fwd runs: 1 = 32 rows per wave, 2 = 64
+constexpr int kMaxListTiles = 1024;         // block-sparse: key tiles per query tile, N <= 65536
 
 // SPLIT: the key range of every query tile is cut into n_split equal runs of tiles, one per
 // workgroup; each writes its partial result (O normalised over its own keys, in fp32, and the
@@ -54,13 +55,15 @@ constexpr int kDefaultVariant = 1;          // kernel fa_fwd runs: 1 = 32 rows p
 // i - wl <= j (wl >= 0), j <= i + wr (wr >= 0) and j < seqlens[b] (seqlens given). Key tiles
 // outside the workgroup's window are neither loaded nor computed; a row with no allowed key
 // gets o = 0 and lse = -inf.
-template <int D, bool BF16, bool CAUSAL, bool SPLIT = false, bool MASKED = false>
+template <int D, bool BF16, bool CAUSAL, bool SPLIT = false, bool MASKED = false, bool BLOCKS = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qt, int G, float c, float tau_raw,
     int n_split = 1, float* __restrict__ PO = nullptr, float* __restrict__ PL = nullptr, int H = 1, int wl = -1,
-    int wr = -1, const int* __restrict__ seqlens = nullptr) {
+    int wr = -1, const int* __restrict__ seqlens = nullptr, const uint8_t* __restrict__ bmask = nullptr,
+    int bq = 0, int bk = 0, int64_t bstride_b = 0, int64_t bstride_h = 0) {
     static_assert(!(MASKED && (CAUSAL || SPLIT)), "the general mask replaces the causal one and does not split");
+    static_assert(!BLOCKS || MASKED, "the block mask rides on the general mask");
     constexpr int DK = D / 16;                 // k-steps of the first product
     constexpr int DB = D / 32;                 // 32-column blocks of the output
     constexpr int CPR = D / 8;                 // 16-byte chunks per row
@@ -119,6 +122,53 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         tb = lo / kBlockN;
         T = max(0, (hi + kBlockN - 1) / kBlockN - tb);
     }
+    // BLOCKS: of the tiles tb .. tb + T - 1, those that some wave of the workgroup needs (its
+    // rows' query block has a non-zero byte for the tile's key block), compacted into t_list
+    // (absolute tile index) with one bit per wave in t_wm; from here on a tile index j is a
+    // position in that list. (Block sizes are multiples of 64: one byte decides a wave's whole
+    // 32 x 64 part of a tile.)
+    __shared__ int t_list[BLOCKS ? kMaxListTiles : 1];
+    __shared__ uint8_t t_wm[BLOCKS ? kMaxListTiles : 1];
+    __shared__ int t_cnt[BLOCKS ? kWaves : 1];
+    if constexpr (BLOCKS) {
+        const uint8_t* mb = bmask + (int64_t)(bh / H) * bstride_b + (int64_t)(bh % H) * bstride_h;
+        const int n_kb = (N + bk - 1) / bk;
+        int count = 0;
+        for (int base = 0; base < T; base += kThreads) {
+            const int t = base + tid;
+            unsigned wm = 0;
+            if (t < T) {
+                const int kb = (tb + t) * kBlockN / bk;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) {
+                    const int r0 = q0 + 32 * w;
+                    if (r0 < N && mb[(int64_t)(r0 / bq) * n_kb + kb] != 0) wm |= 1u << w;
+                }
+            }
+            const uint64_t need = __builtin_amdgcn_ballot_w64(wm != 0);
+            if (lane == 0) t_cnt[wave] = __builtin_popcountll(need);
+            __syncthreads();
+            int before = count, total = count;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const int cw = t_cnt[w];
+                before += w < wave ? cw : 0;
+                total += cw;
+            }
+            if (wm != 0) {
+                const int pos = before + __builtin_popcountll(need & ((1ull << lane) - 1ull));
+                t_list[pos] = tb + t;
+                t_wm[pos] = (uint8_t)wm;
+            }
+            count = total;
+            __syncthreads();
+        }
+        T = count;
+        if (T == 0) {  // no tile at all: a valid entry for the loads the prologue still issues
+            if (tid == 0) t_list[0] = 0;
+            __syncthreads();
+        }
+    }
     // tiles this wave computes: causal waves stop at the tile holding their last row
     // (Non-causal: T_w = T, hidden from the compiler. Folded away, the tests on it disappear and
     // the compiler keeps the output accumulators of the loop's two exit paths in two register
@@ -127,7 +177,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // MASKED: this wave's key tiles are T_w0 .. T_w - 1 (a window leaves the first ones to the
     // workgroup's earlier rows); the wave joins every barrier and load but computes only those
     int T_w0 = 0;
-    if constexpr (MASKED) {
+    if constexpr (MASKED && !BLOCKS) {  // (the block-sparse schedule tests each tile's bits instead)
         const int hi_w = wr >= 0 ? min(kv_len, wq0 + 32 + wr) : kv_len;  // this wave's last key + 1
         T_w = max(0, min(T, (hi_w + kBlockN - 1) / kBlockN - tb));
         if (wl >= 0) T_w0 = min(T_w, max(0, wq0 - wl) / kBlockN - tb);
@@ -141,7 +191,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // Offsets inside one head fit in 32 bits (the host limits N * d * 2 bytes to < 2^31).
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // scalar copy for LDS destinations
     auto issue = [&](const uint16_t* src_head, int j, uint16_t* dst) __attribute__((always_inline)) {
-        const int k0 = (tb + j) * kBlockN;
+        const int k0 = (BLOCKS ? t_list[j] : tb + j) * kBlockN;
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
             const int g = wave_s * IPW + i;
@@ -233,7 +283,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     };
     // keys past the end, and (causal) keys after the query, become -inf before the max
     auto mask = [&](int t, f32x16 (&sd)[2]) __attribute__((always_inline)) {
-        const int k0 = (tb + t) * kBlockN;
+        const int k0 = (BLOCKS ? t_list[t] : tb + t) * kBlockN;
         if constexpr (MASKED) {
             if ((k0 + kBlockN > kv_len) || (wr >= 0 && k0 + kBlockN - 1 > wq0 + wr) ||
                 (wl >= 0 && k0 < wq0 + 31 - wl)) {
@@ -306,159 +356,191 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // makes K(j+1) and V(j) visible (loaded after barrier j - 1) and frees the buffer of K(j) for
     // K(j+2) and one V buffer for V(j+1): V(j-1)'s when V alternates between two buffers (the
     // masked kernel), V(j-3)'s when it rotates through four (the ping-pong below).
-    issue(Kh, 0, k_lds0);
-    issue(Vh, 0, v_lds0);
-    if (T > 1) issue(Kh, 1, k_lds1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (T_w0 < T_w && T_w0 == 0) {
-        qk(k_lds0, s0);
-        mask(0, s0);
-        rebase(row_max(s0));
-    }
-    // region 1 of tile j: S^T(j+1) = K(j+1) . Q^T with the exponentials of tile j in between.
-    auto region1 = [&](f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], const uint16_t* k_nxt) __attribute__((always_inline)) {
-        // Explicit software pipeline: the LDS operands of MFMA i + 2 are read before MFMA i
-        // issues, and one pair of exponentials follows each MFMA; sched_barrier(0) pins that
-        // order so the LDS latency stays behind two MFMAs instead of stalling every one.
-        constexpr int NQ = 2 * DK;  // 16 MFMAs for D = 128, 8 for D = 64
-        u32x4 ka[NQ];
-        ka[0] = k_operand(k_nxt, 0, 0);
-        ka[1] = k_operand(k_nxt, 0, 1);
-#pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-            const int t = i >> 1, kb = i & 1;
-            if (i + 2 < NQ) {
-                const int t2 = (i + 2) >> 1, kb2 = (i + 2) & 1;
-                ka[i + 2] = k_operand(k_nxt, t2, kb2);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            s_nxt[kb] = mfma32<BF16>(ka[i], qreg[t], t == 0 ? (f32x16){} : s_nxt[kb]);
-            __builtin_amdgcn_sched_barrier(0);
-            // exponentials: pair i of the 16 pairs of S^T(j) held by this lane (NQ == 16),
-            // or pairs 2i, 2i+1 when D = 64 (NQ == 8)
-#pragma unroll
-            for (int u = 0; u < 16 / NQ; ++u) {
-                const int pr = i * (16 / NQ) + u;  // pair index 0..15
-                const int kbp = pr >> 3, r = 2 * (pr & 7);
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[kbp][r], c, -mc));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[kbp][r + 1], c, -mc));
-                pk[kbp][r >> 1] = pack2<BF16>(p0, p1);
-                l_run = add_pair<BF16>(pk[kbp][r >> 1], l_run);
-                if constexpr (BF16) l_f32 += p0 + p1;
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // Keep the exponentials in region 1: without this the compiler sinks them past the
-        // mask branch into region 2, next to their only consumer.
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 8; ++r) asm volatile("" : "+v"(pk[kb][r]));
-        asm volatile("" : "+v"(l_run));
-        if constexpr (BF16) asm volatile("" : "+v"(l_f32));
-    };
-    // region 2 of tile j: O^T += V(j)^T . P^T(j) with the row max of S^T(j+1) in between, then
-    // the move of the reference max for tile j+1.
-    auto region2 = [&](f32x16 (&s_nxt)[2], const uint16_t* v_cur) __attribute__((always_inline)) {
-        // V^T operands read two MFMAs ahead.
-        constexpr int NP = 4 * DB;  // 16 MFMAs for D = 128, 8 for D = 64
-        u32x4 va[NP];
-        va[0] = v_operand(v_cur, 0, 0);
-        va[1] = v_operand(v_cur, 1 / DB, 1 % DB);
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            const int kk = i / DB, b = i % DB;
-            if (i + 2 < NP) va[i + 2] = v_operand(v_cur, (i + 2) / DB, (i + 2) % DB);
-            __builtin_amdgcn_sched_barrier(0);
-            oacc[b] = mfma32<BF16>(va[i], p_operand(kk), oacc[b]);
-            __builtin_amdgcn_sched_barrier(0);
-            // row max: the 32 scores of this lane, 32 / NP per MFMA
-#pragma unroll
-            for (int u = 0; u < 32 / NP; ++u) {
-                const int e = i * (32 / NP) + u;
-                mx = fmaxf(mx, s_nxt[e >> 4][e & 15]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        rebase(max_with_partner(mx));
-    };
-    if constexpr (MASKED) {
-        // every wave: barrier, loads, region 1, region 2 (V in two buffers)
-        auto iteration = [&](int j, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], const uint16_t* k_nxt,
-                             const uint16_t* v_cur, uint16_t* k_load, uint16_t* v_load) __attribute__((always_inline)) {
+    if constexpr (BLOCKS) {
+        // Block-sparse schedule. Barrier j makes K(j) and V(j) visible (buffer j % 2) and frees
+        // the other pair, which takes K(j+1) and V(j+1). A wave computes tile j start to finish
+        // (scores, mask, max, exponentials, product with V) only when its own bit is set, so the
+        // waves of a workgroup whose query blocks differ skip each other's tiles; the two waves
+        // of a SIMD still overlap each other's matrix and vector work.
+        issue(Kh, 0, k_lds0);
+        issue(Vh, 0, v_lds0);
+        const int wbit = 1 << wave_s;
+        auto tile = [&](int j, const uint16_t* kt, const uint16_t* vt, uint16_t* kn, uint16_t* vn)
+                        __attribute__((always_inline)) {
             __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            if (j + 2 < T) issue(Kh, j + 2, k_load);
-            if (j + 1 < T) issue(Vh, j + 1, v_load);
-            if (j < T_w0) {
-                // before this wave's first tile: at most start the pipeline with S^T(j+1)
-                if (j + 1 == T_w0 && j + 1 < T_w) {
-                    qk(k_nxt, s_nxt);
-                    mask(j + 1, s_nxt);
-                    rebase(row_max(s_nxt));
-                }
-            } else if (j + 1 < T_w) {
-                region1(s_cur, s_nxt, k_nxt);
-                mask(j + 1, s_nxt);
-                region2(s_nxt, v_cur);
-            } else if (j < T_w) {
-                expo(s_cur);
-                pv(v_cur);
+            __syncthreads();  // barrier j
+            if (j + 1 < T) {
+                issue(Kh, j + 1, kn);
+                issue(Vh, j + 1, vn);
+            }
+            if (__builtin_amdgcn_readfirstlane(t_wm[j]) & wbit) {
+                qk(kt, s0);
+                mask(j, s0);
+                rebase(row_max(s0));
+                expo(s0);
+                pv(vt);
             }
         };
         for (int j = 0; j < T; j += 2) {
-            // even j: K(j+1) in buffer 1, V(j) in buffer 0; K(j+2) -> buffer 0, V(j+1) -> buffer 1
-            iteration(j, s0, s1, k_lds1, v_lds0, k_lds0, v_lds1);
+            tile(j, k_lds0, v_lds0, k_lds1, v_lds1);
             if (j + 1 >= T) break;
-            iteration(j + 1, s1, s0, k_lds0, v_lds1, k_lds1, v_lds0);
+            tile(j + 1, k_lds1, v_lds1, k_lds0, v_lds0);
         }
     } else {
-        // Ping-pong. The two waves on a SIMD run the same sequence of regions half an iteration
-        // apart: waves 0-3 pass barrier j before region 1 of tile j, waves 4-7 ("lag") before
-        // region 2 of tile j-1. While one wave of the pair runs the exponentials of region 1 on
-        // the vector ALU, the other runs the MFMA-only region 2, instead of both contending for
-        // the vector ALU and then both for the matrix core. A lagging wave still reads V(j-1)
-        // after barrier j, so V rotates through four buffers (V(t) in buffer t % 4). Every wave
-        // issues its share of the loads of step j (K(j+2) into K(j)'s buffer, V(j+1) into
-        // V(j-3)'s) at the top of the step, after barrier j in waves 0-3 and after region 2 of
-        // tile j-1 in waves 4-7, and waits for them at the top of the next step: one
-        // unconditional wait, so the compiler sees no path on which a read could overtake them.
-        const bool lag = wave_s >= kWaves / 2;
-        auto step = [&](int j, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], uint16_t* k_cur, const uint16_t* k_nxt,
-                        const uint16_t* v_cur, uint16_t* v_p1) __attribute__((always_inline)) {
-            __builtin_amdgcn_s_waitcnt(0);
-            if (!lag) __syncthreads();  // barrier j
-            if (j + 2 < T) issue(Kh, j + 2, k_cur);
-            if (j + 1 < T) issue(Vh, j + 1, v_p1);
-            if (j + 1 < T_w) {
-                region1(s_cur, s_nxt, k_nxt);
-                mask(j + 1, s_nxt);
-            } else if (j < T_w) {
-                expo(s_cur);
+        issue(Kh, 0, k_lds0);
+        issue(Vh, 0, v_lds0);
+        if (T > 1) issue(Kh, 1, k_lds1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (T_w0 < T_w && T_w0 == 0) {
+            qk(k_lds0, s0);
+            mask(0, s0);
+            rebase(row_max(s0));
+        }
+        // region 1 of tile j: S^T(j+1) = K(j+1) . Q^T with the exponentials of tile j in between.
+        auto region1 = [&](f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], const uint16_t* k_nxt) __attribute__((always_inline)) {
+            // Explicit software pipeline: the LDS operands of MFMA i + 2 are read before MFMA i
+            // issues, and one pair of exponentials follows each MFMA; sched_barrier(0) pins that
+            // order so the LDS latency stays behind two MFMAs instead of stalling every one.
+            constexpr int NQ = 2 * DK;  // 16 MFMAs for D = 128, 8 for D = 64
+            u32x4 ka[NQ];
+            ka[0] = k_operand(k_nxt, 0, 0);
+            ka[1] = k_operand(k_nxt, 0, 1);
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const int t = i >> 1, kb = i & 1;
+                if (i + 2 < NQ) {
+                    const int t2 = (i + 2) >> 1, kb2 = (i + 2) & 1;
+                    ka[i + 2] = k_operand(k_nxt, t2, kb2);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                s_nxt[kb] = mfma32<BF16>(ka[i], qreg[t], t == 0 ? (f32x16){} : s_nxt[kb]);
+                __builtin_amdgcn_sched_barrier(0);
+                // exponentials: pair i of the 16 pairs of S^T(j) held by this lane (NQ == 16),
+                // or pairs 2i, 2i+1 when D = 64 (NQ == 8)
+#pragma unroll
+                for (int u = 0; u < 16 / NQ; ++u) {
+                    const int pr = i * (16 / NQ) + u;  // pair index 0..15
+                    const int kbp = pr >> 3, r = 2 * (pr & 7);
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[kbp][r], c, -mc));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[kbp][r + 1], c, -mc));
+                    pk[kbp][r >> 1] = pack2<BF16>(p0, p1);
+                    l_run = add_pair<BF16>(pk[kbp][r >> 1], l_run);
+                    if constexpr (BF16) l_f32 += p0 + p1;
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            if (lag && j + 1 < T) {
-                __builtin_amdgcn_s_waitcnt(0);
-                __syncthreads();  // barrier j + 1
-            }
-            if (j + 1 < T_w) {
-                region2(s_nxt, v_cur);
-            } else if (j < T_w) {
-                pv(v_cur);
-            }
+            // Keep the exponentials in region 1: without this the compiler sinks them past the
+            // mask branch into region 2, next to their only consumer.
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 8; ++r) asm volatile("" : "+v"(pk[kb][r]));
+            asm volatile("" : "+v"(l_run));
+            if constexpr (BF16) asm volatile("" : "+v"(l_f32));
         };
-        if (lag && T > 0) __syncthreads();  // barrier 0
-        // T barriers in every wave: waves 0-3 one per step; waves 4-7 barrier 0 above and one
-        // per step but the last
-        for (int j = 0; j < T; j += 4) {
-            step(j, s0, s1, k_lds0, k_lds1, v_lds0, v_lds1);
-            if (j + 1 >= T) break;
-            step(j + 1, s1, s0, k_lds1, k_lds0, v_lds1, v_lds2);
-            if (j + 2 >= T) break;
-            step(j + 2, s0, s1, k_lds0, k_lds1, v_lds2, v_lds3);
-            if (j + 3 >= T) break;
-            step(j + 3, s1, s0, k_lds1, k_lds0, v_lds3, v_lds0);
+        // region 2 of tile j: O^T += V(j)^T . P^T(j) with the row max of S^T(j+1) in between, then
+        // the move of the reference max for tile j+1.
+        auto region2 = [&](f32x16 (&s_nxt)[2], const uint16_t* v_cur) __attribute__((always_inline)) {
+            // V^T operands read two MFMAs ahead.
+            constexpr int NP = 4 * DB;  // 16 MFMAs for D = 128, 8 for D = 64
+            u32x4 va[NP];
+            va[0] = v_operand(v_cur, 0, 0);
+            va[1] = v_operand(v_cur, 1 / DB, 1 % DB);
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const int kk = i / DB, b = i % DB;
+                if (i + 2 < NP) va[i + 2] = v_operand(v_cur, (i + 2) / DB, (i + 2) % DB);
+                __builtin_amdgcn_sched_barrier(0);
+                oacc[b] = mfma32<BF16>(va[i], p_operand(kk), oacc[b]);
+                __builtin_amdgcn_sched_barrier(0);
+                // row max: the 32 scores of this lane, 32 / NP per MFMA
+#pragma unroll
+                for (int u = 0; u < 32 / NP; ++u) {
+                    const int e = i * (32 / NP) + u;
+                    mx = fmaxf(mx, s_nxt[e >> 4][e & 15]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            rebase(max_with_partner(mx));
+        };
+        if constexpr (MASKED) {
+            // every wave: barrier, loads, region 1, region 2 (V in two buffers)
+            auto iteration = [&](int j, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], const uint16_t* k_nxt,
+                                 const uint16_t* v_cur, uint16_t* k_load, uint16_t* v_load) __attribute__((always_inline)) {
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+                if (j + 2 < T) issue(Kh, j + 2, k_load);
+                if (j + 1 < T) issue(Vh, j + 1, v_load);
+                if (j < T_w0) {
+                    // before this wave's first tile: at most start the pipeline with S^T(j+1)
+                    if (j + 1 == T_w0 && j + 1 < T_w) {
+                        qk(k_nxt, s_nxt);
+                        mask(j + 1, s_nxt);
+                        rebase(row_max(s_nxt));
+                    }
+                } else if (j + 1 < T_w) {
+                    region1(s_cur, s_nxt, k_nxt);
+                    mask(j + 1, s_nxt);
+                    region2(s_nxt, v_cur);
+                } else if (j < T_w) {
+                    expo(s_cur);
+                    pv(v_cur);
+                }
+            };
+            for (int j = 0; j < T; j += 2) {
+                // even j: K(j+1) in buffer 1, V(j) in buffer 0; K(j+2) -> buffer 0, V(j+1) -> buffer 1
+                iteration(j, s0, s1, k_lds1, v_lds0, k_lds0, v_lds1);
+                if (j + 1 >= T) break;
+                iteration(j + 1, s1, s0, k_lds0, v_lds1, k_lds1, v_lds0);
+            }
+        } else {
+            // Ping-pong. The two waves on a SIMD run the same sequence of regions half an iteration
+            // apart: waves 0-3 pass barrier j before region 1 of tile j, waves 4-7 ("lag") before
+            // region 2 of tile j-1. While one wave of the pair runs the exponentials of region 1 on
+            // the vector ALU, the other runs the MFMA-only region 2, instead of both contending for
+            // the vector ALU and then both for the matrix core. A lagging wave still reads V(j-1)
+            // after barrier j, so V rotates through four buffers (V(t) in buffer t % 4). Every wave
+            // issues its share of the loads of step j (K(j+2) into K(j)'s buffer, V(j+1) into
+            // V(j-3)'s) at the top of the step, after barrier j in waves 0-3 and after region 2 of
+            // tile j-1 in waves 4-7, and waits for them at the top of the next step: one
+            // unconditional wait, so the compiler sees no path on which a read could overtake them.
+            const bool lag = wave_s >= kWaves / 2;
+            auto step = [&](int j, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], uint16_t* k_cur, const uint16_t* k_nxt,
+                            const uint16_t* v_cur, uint16_t* v_p1) __attribute__((always_inline)) {
+                __builtin_amdgcn_s_waitcnt(0);
+                if (!lag) __syncthreads();  // barrier j
+                if (j + 2 < T) issue(Kh, j + 2, k_cur);
+                if (j + 1 < T) issue(Vh, j + 1, v_p1);
+                if (j + 1 < T_w) {
+                    region1(s_cur, s_nxt, k_nxt);
+                    mask(j + 1, s_nxt);
+                } else if (j < T_w) {
+                    expo(s_cur);
+                }
+                if (lag && j + 1 < T) {
+                    __builtin_amdgcn_s_waitcnt(0);
+                    __syncthreads();  // barrier j + 1
+                }
+                if (j + 1 < T_w) {
+                    region2(s_nxt, v_cur);
+                } else if (j < T_w) {
+                    pv(v_cur);
+                }
+            };
+            if (lag && T > 0) __syncthreads();  // barrier 0
+            // T barriers in every wave: waves 0-3 one per step; waves 4-7 barrier 0 above and one
+            // per step but the last
+            for (int j = 0; j < T; j += 4) {
+                step(j, s0, s1, k_lds0, k_lds1, v_lds0, v_lds1);
+                if (j + 1 >= T) break;
+                step(j + 1, s1, s0, k_lds1, k_lds0, v_lds1, v_lds2);
+                if (j + 2 >= T) break;
+                step(j + 2, s0, s1, k_lds0, k_lds1, v_lds2, v_lds3);
+                if (j + 3 >= T) break;
+                step(j + 3, s1, s0, k_lds1, k_lds0, v_lds3, v_lds0);
+            }
         }
     }
 
@@ -886,6 +968,17 @@ hipError_t launch_masked(const void* q, const void* k, const void* v, void* o, f
     return hipGetLastError();
 }
 
+template <int D, bool BF16>
+hipError_t launch_blocks(const void* q, const void* k, const void* v, void* o, float* lse, int N, int n_qt, int G,
+                         float c, float tau_raw, int H, int wl, int wr, const int* seqlens, const uint8_t* bm, int bq,
+                         int bk, int64_t sb, int64_t sh, hipStream_t stream) {
+    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, false, false, true, true>), dim3(G), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qt, G, c, tau_raw, 1,
+                       nullptr, nullptr, H, wl, wr, seqlens, bm, bq, bk, sb, sh);
+    return hipGetLastError();
+}
+
 template <int D, bool BF16, bool CAUSAL>
 hipError_t launch_split(const void* q, const void* k, const void* v, void* o, float* lse, int N, int n_qt, int BH,
                         float c, float tau_raw, int n_split, float* po, float* pl, hipStream_t stream) {
@@ -1050,6 +1143,46 @@ int fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* l
     else
         e = bf ? launch_masked<128, true>(q, k, v, o, lse, n, nq, g, c, tau_raw, h, wl, wr, mask->seqlens_k, stream)
                : launch_masked<128, false>(q, k, v, o, lse, n, nq, g, c, tau_raw, h, wl, wr, mask->seqlens_k, stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                       int64_t N, int64_t d, float scale, hipStream_t stream, int dtype, const fa_mask* mask,
+                       const fa_block_mask* blocks) {
+    const int st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype, 1);
+    if (st != FA_OK) return st;
+    if (!blocks || !blocks->mask) return FA_ERR_NULL;
+    if (blocks->block_q < 64 || blocks->block_k < 64 || blocks->block_q % 64 != 0 || blocks->block_k % 64 != 0 ||
+        blocks->block_q > INT32_MAX || blocks->block_k > INT32_MAX || blocks->stride_b < 0 || blocks->stride_h < 0)
+        return FA_ERR_OPTION;
+    if (N > static_cast<int64_t>(kBlockN) * kMaxListTiles) return FA_ERR_SHAPE;
+    int64_t wl64 = -1, wr64 = -1;
+    const int32_t* seqlens = nullptr;
+    if (mask) {
+        if (mask->window_left < -1 || mask->window_right < -1 || mask->window_left > INT32_MAX ||
+            mask->window_right > INT32_MAX)
+            return FA_ERR_OPTION;
+        if (reinterpret_cast<uintptr_t>(mask->seqlens_k) & 3) return FA_ERR_ALIGN;
+        wl64 = mask->window_left >= N ? -1 : mask->window_left;
+        wr64 = mask->window_right >= N ? -1 : mask->window_right;
+        seqlens = mask->seqlens_k;
+    }
+    const int64_t n_qt = (N + kBlockM - 1) / kBlockM;
+    const float c = scale * 1.4426950408889634f;
+    const float tau_raw = kDefaultRescaleLog2 / c;
+    const int n = static_cast<int>(N), nq = static_cast<int>(n_qt), g = static_cast<int>(B * H * n_qt);
+    const int h = static_cast<int>(H), wl = static_cast<int>(wl64), wr = static_cast<int>(wr64);
+    const int bq = static_cast<int>(blocks->block_q), bk = static_cast<int>(blocks->block_k);
+    const bool bf = dtype == FA_BF16;
+    hipError_t e;
+#define FA_BLOCKS(DD, BB)                                                                                    \
+    launch_blocks<DD, BB>(q, k, v, o, lse, n, nq, g, c, tau_raw, h, wl, wr, seqlens, blocks->mask, bq, bk, \
+                          blocks->stride_b, blocks->stride_h, stream)
+    if (d == 64)
+        e = bf ? FA_BLOCKS(64, true) : FA_BLOCKS(64, false);
+    else
+        e = bf ? FA_BLOCKS(128, true) : FA_BLOCKS(128, false);
+#undef FA_BLOCKS
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -133,6 +133,37 @@ int fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* l
                   float scale, hipStream_t stream, int dtype, const fa_mask* mask);
 
 /*
+ * A mask over blocks of the score matrix (block-sparse attention) for fa_fwd_blocksparse. Query i
+ * lies in query block i / block_q, key j in key block j / block_k; the pair is allowed only when
+ *   mask[b * stride_b + h * stride_h + (i / block_q) * n_kb + j / block_k] != 0,
+ * n_kb = ceil(N / block_k), n_qb = ceil(N / block_q). Any mask applied to the scores before the
+ * max keeps the method exact ("Causal masking fits inside the tiled computation", nalar.dev, last
+ * paragraph); one given per block lets whole tiles be skipped.
+ */
+typedef struct fa_block_mask {
+    const uint8_t* mask;  /* device pointer; the caller's buffer holds every byte addressed:
+                             (B-1)*stride_b + (H-1)*stride_h + n_qb*n_kb bytes at least */
+    int64_t block_q;      /* query rows per block: a positive multiple of 64 */
+    int64_t block_k;      /* keys per block: a positive multiple of 64 */
+    int64_t stride_b;     /* bytes between the masks of consecutive batches (0: shared) */
+    int64_t stride_h;     /* bytes between the masks of consecutive heads (0: shared) */
+} fa_block_mask;
+
+/*
+ * fa_fwd_blocksparse -- fa_fwd under a block mask (see fa_block_mask), optionally combined with
+ * the window and key lengths of fa_mask (`mask` may be NULL: no further restriction; causal is
+ * window_left = -1, window_right = 0). Each 256-row query tile loads and computes only the 64-key
+ * tiles that one of its 32-row groups needs; a row with no allowed key gets o = 0, lse = -inf.
+ * Arguments as for fa_fwd_masked, plus `blocks` (not NULL). Errors: those of fa_fwd_masked;
+ * FA_ERR_NULL for a NULL `blocks` or blocks->mask, FA_ERR_OPTION for a block size that is not a
+ * positive multiple of 64 or a negative stride, FA_ERR_SHAPE for N > 65536.
+ */
+int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int64_t B, int64_t H, int64_t N, int64_t d,
+                       float scale, hipStream_t stream, int dtype, const fa_mask* mask,
+                       const fa_block_mask* blocks);
+
+/*
  * fa_fwd_splitkv -- fa_fwd with the keys of every query tile cut into num_splits runs that run
  * as separate workgroups (split-KV), for shapes whose B*H*ceil(N/256) query tiles leave compute
  * units idle. Each split writes a partial result -- its output normalised over its own keys, in

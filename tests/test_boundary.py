@@ -30,7 +30,8 @@ def L():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_cpu", "fa_fwd_ex", "fa_fwd_masked", "fa_fwd_splitkv",
+    assert _declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_blocksparse", "fa_fwd_cpu", "fa_fwd_ex",
+                                     "fa_fwd_masked", "fa_fwd_splitkv",
                                      "fa_fwd_splitkv_heuristic", "fa_fwd_splitkv_workspace_size", "fa_status_string",
                                      "fa_version"]
 
@@ -213,3 +214,25 @@ def test_masked_argument_errors(L, mask, kw, code):
     m = None if mask is None else fa.FaMask(*mask)
     assert fa.fa_fwd_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"], a["scale"],
                             a["stream"], a["dtype"], m) == code
+
+
+FAR = dict(q=0x10000000, k=0x20000000, v=0x30000000, o=0x40000000, lse=0x50000000)  # far apart: large N
+
+
+@pytest.mark.parametrize("blocks,mask,kw,code", [
+    (None, None, {}, 1), ((None, 64, 64, 0, 0), None, {}, 1),
+    ((0xC00000, 32, 64, 0, 0), None, {}, 9), ((0xC00000, 64, 96, 0, 0), None, {}, 9),
+    ((0xC00000, 0, 64, 0, 0), None, {}, 9), ((0xC00000, 64, 64, -1, 0), None, {}, 9),
+    ((0xC00000, 64, 64, 0, -8), None, {}, 9), ((0xC00000, 1 << 31, 64, 0, 0), None, {}, 9),
+    ((0xC00000, 64, 64, 0, 0), (-2, 0, None), {}, 9), ((0xC00000, 64, 64, 0, 0), (4, 0, 0x600002), {}, 5),
+    ((0xC00000, 64, 64, 0, 0), None, dict(q=None), 1), ((0xC00000, 64, 64, 0, 0), None, dict(d=96), 3),
+    ((0xC00000, 64, 64, 0, 0), None, dict(o=QA), 7), ((0xC00000, 64, 64, 0, 0), None, dict(N=65537, **FAR), 2),
+])
+def test_blocksparse_argument_errors(L, blocks, mask, kw, code):
+    import exact_tiled_softmax_fa_amd as fa
+    a = dict(GOOD)
+    a.update(kw)
+    b = None if blocks is None else fa.FaBlockMask(*blocks)
+    m = None if mask is None else fa.FaMask(*mask)
+    assert fa.fa_fwd_blocksparse(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                                 a["scale"], a["stream"], a["dtype"], m, b) == code

@@ -135,3 +135,22 @@ def sample_keys(w: Workload):
     shifted = Workload(w.name, w.B, w.H, w.N, w.d, w.dtype, w.causal, w.sigma_qk, w.seed + 3000,
                        w.rows_per_head)
     return sample_rows(shifted)
+
+
+def make_block_mask(w: Workload, block: int, density: float):
+    """A seeded random block mask [ceil(N/block), ceil(N/block)] (uint8 numpy array) for
+    block-sparse attention over the workload: each (query block, key block) byte is 1 with
+    probability ``density`` (generator seeded with ``seed + 5000``), and the diagonal blocks are
+    always 1 so that every row keeps its own key."""
+    n = -(-w.N // block)
+    g = torch.Generator(device="cpu").manual_seed(w.seed + 5000)
+    m = (torch.rand((n, n), generator=g, dtype=torch.float64) < density).numpy().astype(np.uint8)
+    np.fill_diagonal(m, 1)
+    return m
+
+
+def block_mask_pairs(mask, N: int, block_q: int, block_k: int) -> int:
+    """Number of (query row, key) pairs a [n_qb, n_kb] block mask allows over N rows and keys."""
+    rows = np.minimum(N, (np.arange(mask.shape[0]) + 1) * block_q) - np.arange(mask.shape[0]) * block_q
+    keys = np.minimum(N, (np.arange(mask.shape[1]) + 1) * block_k) - np.arange(mask.shape[1]) * block_k
+    return int((rows[:, None] * keys[None, :] * (np.asarray(mask) != 0)).sum())
