@@ -5,7 +5,9 @@
 
 --pass fwd (default) profiles fa_fwd's kernel; --pass bwd profiles the two kernels of fa_bwd
 (fa_bwd_dq_kernel, fa_bwd_dkdv_kernel), each summarised on its own; --splits S (with --pass fwd)
-profiles fa_fwd_splitkv's split kernel and its merge kernel.
+profiles fa_fwd_splitkv's split kernel and its merge kernel; --block-density P [--block-size S]
+(with --pass fwd) profiles fa_fwd_blocksparse on bench.py's seeded block mask, priced by the
+allowed (row, key) pairs.
 
 Runs four rocprofv3 passes over ``bench.py`` as child processes (this process
 never touches the GPU, so the profiler's preload stays in its own process):
@@ -25,7 +27,9 @@ the traffic only while that hash matches. Reported figures:
 - the mean kernel time over the timed dispatches;
 - MFMA busy fraction = busy cycles / SIMDs / (GUI-active cycles / XCDs);
 - device-memory bytes per launch and the achieved GB/s (bytes / mean kernel time);
-- the ratio of measured to unavoidable bytes (Q, K, V read once; O, lse written once).
+- the ratio of measured to unavoidable bytes (Q, K, V read once; O, lse written once);
+- the sustained clock, GUI-active cycles per XCD over the mean kernel time, and the dense MFMA
+  peak scaled to it (the counters and the trace come from separate runs of the same command).
 """
 import argparse
 import csv
@@ -47,6 +51,8 @@ KERNEL_SRCS = {
 N_SIMD = 1024   # MI355X: 256 CUs x 4 SIMDs
 N_XCD = 8
 COPY_MIB = 256
+PEAK_TFLOPS = 2516.6  # MI355X dense fp16/bf16 matrix-core peak
+PEAK_CLOCK_GHZ = 2.4  # the clock that peak is quoted at
 
 
 def kernel_sha(which: str = "fwd") -> str:
@@ -57,11 +63,13 @@ def kernel_sha(which: str = "fwd") -> str:
     return h.hexdigest()
 
 
-def passes(workload: str, out: str, steps: int, warmup: int, which: str = "fwd", splits=None):
+def passes(workload: str, out: str, steps: int, warmup: int, which: str = "fwd", splits=None, blocks=None):
     bench = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload, "--pass", which,
              "--no-cpu-baseline"]
     if splits is not None:
         bench += ["--splits", str(splits)]
+    if blocks is not None:
+        bench += ["--block-size", str(blocks[0]), "--block-density", str(blocks[1])]
     timed = bench + ["--steps", str(steps), "--warmup", str(warmup)]
     short = bench + ["--steps", "2", "--warmup", "1"]
     copy = ["--copy-ref-mib", str(COPY_MIB)]
@@ -74,9 +82,10 @@ def passes(workload: str, out: str, steps: int, warmup: int, which: str = "fwd",
     ]
 
 
-def run(workload: str, out: str, steps: int, warmup: int, timeout: int, which: str = "fwd", splits=None) -> list:
+def run(workload: str, out: str, steps: int, warmup: int, timeout: int, which: str = "fwd", splits=None,
+        blocks=None) -> list:
     cmds = []
-    for name, prof_args, prog in passes(workload, out, steps, warmup, which, splits):
+    for name, prof_args, prog in passes(workload, out, steps, warmup, which, splits, blocks):
         cmd = ["rocprofv3", *prof_args, "--output-format", "csv", "-d", os.path.join(out, name), "-o", name,
                "--", *prog]
         cmds.append(" ".join(shlex.quote(c) for c in cmd))
@@ -107,7 +116,7 @@ def _counter(out, name, counter, kernel):
             if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]]
 
 
-def kernels(workload: str, which: str = "fwd", splits=None):
+def kernels(workload: str, which: str = "fwd", splits=None, blocks=None):
     """(kernel name, matrix-product flops per launch, unavoidable bytes per launch) of a pass.
     Flops: 2 N^2 d per product per head (halved when causal); forward: the two products of the
     conventional count; backward: the products each kernel executes (dq: S, dP, dQ; dkdv: S, dP,
@@ -125,16 +134,21 @@ def kernels(workload: str, which: str = "fwd", splits=None):
         part = splits * BH * N * (d + 2) * 4
         return [("fa_fwd_kernel", 2 * per_product, BH * 3 * t + part),
                 ("fa_merge_kernel", 0.0, part + BH * (t + 4 * N))]
+    if which == "fwd" and blocks:
+        # the block-sparse kernel: 4 d flops per allowed (row, key) pair of bench.py's seeded mask
+        m = workloads.make_block_mask(w, blocks[0], blocks[1])
+        pairs = workloads.block_mask_pairs(m, N, blocks[0], blocks[0])
+        return [("fa_fwd_kernel", 4.0 * d * BH * pairs, BH * (4 * t + 4 * N))]
     if which == "fwd":
         return [("fa_fwd_kernel", 2 * per_product, BH * (4 * t + 4 * N))]
     return [("fa_bwd_dq_kernel", 3 * per_product, BH * (6 * t + 8 * N)),   # q k v o dO lse -> dq delta
             ("fa_bwd_dkdv_kernel", 4 * per_product, BH * (6 * t + 8 * N))]  # q k v dO lse delta -> dk dv
 
 
-def summarize(workload: str, out: str, steps: int, cmds=None, which: str = "fwd", splits=None) -> list:
+def summarize(workload: str, out: str, steps: int, cmds=None, which: str = "fwd", splits=None, blocks=None) -> list:
     """One record per kernel of the pass (see ``kernels``)."""
     recs = []
-    for kname, flops, unavoidable in kernels(workload, which, splits):
+    for kname, flops, unavoidable in kernels(workload, which, splits, blocks):
         trace = [r for r in _rows(_find(out, "kt", "kernel_trace.csv")) if kname in r["Kernel_Name"]]
         durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in trace]
         timed = durs[-steps:]
@@ -169,21 +183,30 @@ def summarize(workload: str, out: str, steps: int, cmds=None, which: str = "fwd"
             "mfma_flop_per_launch": mops * 512,
             "mfma_busy_fraction": util,
             "tflops_from_trace": flops / (ms * 1e-3) / 1e12,
+            "clock_ghz": gui / N_XCD / (ms * 1e-3) / 1e9,
             "commands": cmds or [],
             "pass": which,
             "splits": splits,
+            "blocks": list(blocks) if blocks else None,
         })
     return recs
 
 
+def variant_tag(splits=None, blocks=None) -> str:
+    """File-name suffix of a profiled variant."""
+    return (f"_split{splits}" if splits else "") + (f"_blocks{blocks[0]}_p{blocks[1]}" if blocks else "")
+
+
 def write_summary(rec: dict, summary_dir: str):
     os.makedirs(summary_dir, exist_ok=True)
-    name = f"{rec['kernel']}_{rec['workload']}" + (f"_split{rec['splits']}" if rec.get("splits") else "")
+    name = f"{rec['kernel']}_{rec['workload']}" + variant_tag(rec.get("splits"), rec.get("blocks"))
     lines = [f"# {rec['kernel']} — {rec['workload']}", ""]
     if rec["commands"]:
         lines += ["Made by `python -m exact_tiled_softmax_fa_amd.rocprof_harness --workload "
                   f"{rec['workload']} --pass {rec['pass']}"
                   + (f" --splits {rec['splits']}" if rec.get("splits") else "")
+                  + (f" --block-size {rec['blocks'][0]} --block-density {rec['blocks'][1]}" if rec.get("blocks")
+                     else "")
                   + "` (repository root, GPU box), which ran:", "", "```",
                   *rec["commands"], "```", ""]
     d = rec["dispatch_ms"]
@@ -201,7 +224,12 @@ def write_summary(rec: dict, summary_dir: str):
         f"- achieved device-memory bandwidth: {rec['achieved_gb_per_s']:.1f} GB/s (of about 8000)", "",
         "## Matrix cores (SQ_INSTS_VALU_MFMA_MOPS_*, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE)", "",
         f"- MFMA work per launch: {rec['mfma_flop_per_launch']:.4e} flop",
-        f"- MFMA busy: **{100 * rec['mfma_busy_fraction']:.1f} %** of elapsed cycles", "",
+        f"- MFMA busy: **{100 * rec['mfma_busy_fraction']:.1f} %** of elapsed cycles",
+        (f"- sustained clock: {rec['clock_ghz']:.2f} GHz; dense MFMA peak at that clock: "
+         f"{PEAK_TFLOPS * rec['clock_ghz'] / PEAK_CLOCK_GHZ:.0f} TFLOP/s (of {PEAK_TFLOPS} at {PEAK_CLOCK_GHZ} GHz)"
+         if rec["mfma_flop_per_launch"] > 0 else
+         "- sustained clock: not given (no matrix work; for a kernel this short the cycle count of a separate "
+         "run does not pair with the trace)"), "",
     ]
     with open(os.path.join(summary_dir, name + ".md"), "w") as f:
         f.write("\n".join(lines))
@@ -216,6 +244,8 @@ def main():
     ap.add_argument("--workload", default="B1-H32-N8192-d128-f16")
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"])
     ap.add_argument("--splits", type=int, default=None, help="profile fa_fwd_splitkv with this many splits")
+    ap.add_argument("--block-density", type=float, default=None, help="profile fa_fwd_blocksparse at this density")
+    ap.add_argument("--block-size", type=int, default=128, help="block-sparse: rows and keys per block")
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "rocprof"))
     ap.add_argument("--summary-dir", default=os.path.join(ROOT, "gpurun_out", "rocprof"))
     ap.add_argument("--steps", type=int, default=20)
@@ -223,12 +253,19 @@ def main():
     ap.add_argument("--timeout", type=int, default=240, help="seconds per rocprofv3 pass")
     ap.add_argument("--parse-only", action="store_true", help="summarise existing outputs under --out")
     args = ap.parse_args()
-    tag = f"{args.which}_{args.workload}" + (f"_split{args.splits}" if args.splits else "")
+    blocks = (args.block_size, args.block_density) if args.block_density is not None else None
+    tag = f"{args.which}_{args.workload}" + variant_tag(args.splits, blocks)
     out = os.path.join(args.out, tag)
     cmds = None
     if not args.parse_only:
-        cmds = run(args.workload, out, args.steps, args.warmup, args.timeout, args.which, args.splits)
-    for rec in summarize(args.workload, out, args.steps, cmds, args.which, args.splits):
+        cmds = run(args.workload, out, args.steps, args.warmup, args.timeout, args.which, args.splits, blocks)
+    for rec in summarize(args.workload, out, args.steps, cmds, args.which, args.splits, blocks):
+        if args.parse_only:  # keep the commands an earlier summary of the same run recorded
+            name = f"{rec['kernel']}_{rec['workload']}" + variant_tag(rec.get("splits"), rec.get("blocks"))
+            prev = os.path.join(args.summary_dir, "traffic_" + name + ".json")
+            if os.path.exists(prev):
+                with open(prev) as f:
+                    rec["commands"] = json.load(f).get("commands", [])
         write_summary(rec, args.summary_dir)
 
 

@@ -65,6 +65,8 @@ def test_summarize_arithmetic(fake_run, tmp_path):
     assert "dispatch_ms" not in j
     md = open(tmp_path / "summ" / "fa_fwd_kernel_B1-H32-N8192-d128-f16.md").read()
     assert "MFMA busy: **50.0 %**" in md
+    assert rec["clock_ghz"] == pytest.approx(2.0)  # 2e6 GUI-active cycles per XCD in 1 ms
+    assert "sustained clock: 2.00 GHz; dense MFMA peak at that clock: 2097 TFLOP/s" in md
 
 
 def test_passes_keep_counters_within_one_pass_limits():
@@ -86,3 +88,16 @@ def test_backward_kernels_work_and_bytes():
     assert rh.kernel_sha("bwd") != rh.kernel_sha("fwd")
     for name, prof_args, prog in rh.passes("B2-H16-N8192-d128-bf16-causal", "/tmp/x", 5, 2, "bwd"):
         assert prog[prog.index("--pass") + 1] == "bwd"
+
+
+def test_block_sparse_variant():
+    import workloads
+    w = workloads.HEADLINE
+    (k,) = rh.kernels(w.name, "fwd", blocks=(128, 0.25))
+    m = workloads.make_block_mask(w, 128, 0.25)
+    pairs = workloads.block_mask_pairs(m, w.N, 128, 128)
+    assert 0.25 * w.N ** 2 < pairs < 0.3 * w.N ** 2  # about the density, plus the forced diagonal
+    assert k[1] == pytest.approx(4.0 * w.d * w.B * w.H * pairs)
+    assert rh.variant_tag(blocks=(128, 0.25)) == "_blocks128_p0.25" and rh.variant_tag(splits=2) == "_split2"
+    for name, prof_args, prog in rh.passes(w.name, "/tmp/x", 5, 2, "fwd", blocks=(128, 0.25)):
+        assert prog[prog.index("--block-density") + 1] == "0.25" and prog[prog.index("--block-size") + 1] == "128"
