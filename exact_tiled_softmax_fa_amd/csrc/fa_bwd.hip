@@ -365,12 +365,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int b = 0; b < DB; ++b) asm volatile("" : "+v"(tlo[b]), "+v"(thi[b]));
         f32x16 s = {}, dp = {};
+        // The four LDS operands of k-step t + 1 are read before the two MFMAs of step t issue
+        // (sched_barrier pins the order), so their latency hides behind those MFMAs.
+        u32x4 oq[2], ok[2], od[2], ov[2];
+        auto fetch = [&](int t) __attribute__((always_inline)) {
+            const int r = t & 1;
+            oq[r] = *reinterpret_cast<const u32x4*>(qt_ + qoff[t]);
+            ok[r] = *reinterpret_cast<const u32x4*>(kv_lds + kvo[t]);
+            od[r] = *reinterpret_cast<const u32x4*>(dot_ + qoff[t]);
+            ov[r] = *reinterpret_cast<const u32x4*>(kv_lds + kKeys * D + kvo[t]);
+        };
+        fetch(0);
 #pragma unroll
         for (int t = 0; t < DK; ++t) {
-            s = mfma32<BF16>(*reinterpret_cast<const u32x4*>(qt_ + qoff[t]),
-                             *reinterpret_cast<const u32x4*>(kv_lds + kvo[t]), s);
-            dp = mfma32<BF16>(*reinterpret_cast<const u32x4*>(dot_ + qoff[t]),
-                              *reinterpret_cast<const u32x4*>(kv_lds + kKeys * D + kvo[t]), dp);
+            if (t + 1 < DK) fetch(t + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            s = mfma32<BF16>(oq[t & 1], ok[t & 1], s);
+            dp = mfma32<BF16>(od[t & 1], ov[t & 1], dp);
+            __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_sched_barrier(0);
         // C layout: register r holds query row qs + 8(r/4) + 4h + r%4 of key `key`
@@ -398,15 +410,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
         __builtin_amdgcn_sched_barrier(0);
         // dV^T += dO^T . P and dK^T += Q^T . dS over these 32 rows (2 steps of 16)
+        // the transposed operands of MFMA pair i + 1 are read before pair i issues
+        u32x4 ta[2], tb[2];
+        ta[0] = transposed_operand<D>(dot_, tlo, thi, 0, 0);
+        tb[0] = transposed_operand<D>(qt_, tlo, thi, 0, 0);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int i = 0; i < 2 * DB; ++i) {
+            const int kk = i / DB, b = i % DB;
+            if (i + 1 < 2 * DB) {
+                ta[(i + 1) & 1] = transposed_operand<D>(dot_, tlo, thi, (i + 1) / DB, (i + 1) % DB);
+                tb[(i + 1) & 1] = transposed_operand<D>(qt_, tlo, thi, (i + 1) / DB, (i + 1) % DB);
+            }
             const u32x4 pop = {pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]};
             const u32x4 dop = {dsk[4 * kk], dsk[4 * kk + 1], dsk[4 * kk + 2], dsk[4 * kk + 3]};
-#pragma unroll
-            for (int b = 0; b < DB; ++b) {
-                dv[b] = mfma32<BF16>(transposed_operand<D>(dot_, tlo, thi, kk, b), pop, dv[b]);
-                dk[b] = mfma32<BF16>(transposed_operand<D>(qt_, tlo, thi, kk, b), dop, dk[b]);
-            }
+            __builtin_amdgcn_sched_barrier(0);
+            dv[b] = mfma32<BF16>(ta[i & 1], pop, dv[b]);
+            dk[b] = mfma32<BF16>(tb[i & 1], dop, dk[b]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
