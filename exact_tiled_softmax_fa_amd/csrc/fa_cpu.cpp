@@ -9,10 +9,12 @@
 // For each block: S = Q K^T, mask, then per row m_new = max(m, max_j s), alpha = 2^(m - m_new),
 // p = 2^(s - m_new), l = alpha l + sum p, o~ = alpha o~ + p V, m = m_new (the loop of the page,
 // in base 2). At the end o = o~ / l and lse = (m + log2 l) ln 2. Every loop over d or over the
-// block runs in SIMD lanes; an AVX2/FMA/F16C build of the tile loop is chosen at run time.
+// block runs in SIMD lanes; an AVX-512 or AVX2/FMA/F16C build of the tile loop is chosen at run
+// time.
 
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -227,6 +229,158 @@ __attribute__((always_inline)) inline void tile(const uint16_t* Q, const uint16_
     }
 }
 
+// ---- AVX-512 build of the tile -----------------------------------------------------------------
+// The scores come out transposed, S^T[j][i] = sum_c K[j][c] q_i[c], vectorised over the 32 query
+// rows of the tile (two 16-lane registers): K is used in its natural row layout (no transpose per
+// block) and the softmax updates (max, exponentials, sums) run across rows in lanes, with no
+// horizontal reduction. The product with V is blocked over 2 rows (4 when d = 64) times the whole
+// head dimension, held in registers for the 64 keys of the block.
+#define FA_AVX512 __attribute__((target("avx512f,avx512bw,avx512dq,avx512vl,fma,f16c")))
+
+template <bool BF16>
+FA_AVX512 inline __m512 widen16(const uint16_t* p) {
+    const __m256i h = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(p));
+    if constexpr (BF16) return _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(h), 16));
+    else return _mm512_cvtph_ps(h);  // exact, subnormals included
+}
+
+// exp2_nonpos in 16 lanes: the same reduction and series; 2^n applied by vscalefps
+FA_AVX512 inline __m512 exp2_nonpos16(__m512 x) {
+    const __m512 lo = _mm512_set1_ps(-126.0f);
+    const __mmask16 keep = _mm512_cmp_ps_mask(x, lo, _CMP_GE_OQ);  // x >= -126 (not -inf, not nan)
+    const __m512 xc = _mm512_max_ps(x, lo);
+    const __m512 n = _mm512_roundscale_ps(xc, _MM_FROUND_TO_NEAREST_INT | _MM_FROUND_NO_EXC);
+    const __m512 t = _mm512_mul_ps(_mm512_sub_ps(xc, n), _mm512_set1_ps(0.693147180559945309f));
+    const __m512 one = _mm512_set1_ps(1.0f);
+    __m512 p = _mm512_fmadd_ps(t, _mm512_set1_ps(1.0f / 7.0f), one);
+    p = _mm512_fmadd_ps(_mm512_mul_ps(t, _mm512_set1_ps(1.0f / 6.0f)), p, one);
+    p = _mm512_fmadd_ps(_mm512_mul_ps(t, _mm512_set1_ps(1.0f / 5.0f)), p, one);
+    p = _mm512_fmadd_ps(_mm512_mul_ps(t, _mm512_set1_ps(1.0f / 4.0f)), p, one);
+    p = _mm512_fmadd_ps(_mm512_mul_ps(t, _mm512_set1_ps(1.0f / 3.0f)), p, one);
+    p = _mm512_fmadd_ps(_mm512_mul_ps(t, _mm512_set1_ps(1.0f / 2.0f)), p, one);
+    p = _mm512_fmadd_ps(t, p, one);
+    return _mm512_maskz_mov_ps(keep, _mm512_scalef_ps(p, n));
+}
+
+template <int D, bool BF16, bool CAUSAL>
+FA_AVX512 void tile_avx512(const uint16_t* Q, const uint16_t* K, const uint16_t* V, uint16_t* O, float* LSE,
+                           int64_t bh, int q0, int N, float c, Scratch& w) {
+    static_assert(kBQ == 32 && kBK % 8 == 0 && D % 16 == 0, "tile shape");
+    constexpr int RB = D == 64 ? 4 : 2;  // rows per register block of the product with V
+    const int64_t head = bh * (int64_t)N * D;
+    const int nq = std::min(kBQ, N - q0);
+    float* qt = w.q.data();   // Q^T [D][32], times scale * log2(e); missing rows are zero
+    float* kr = w.kt.data();  // the key block, fp32 rows [kBK][D]
+    float* vr = w.vf.data();  // the value block, fp32 rows [kBK][D]
+    float* st = w.s.data();   // S^T, then P^T, [kBK][32]
+    float* acc = w.acc.data();
+    // Q rows -> fp32 (through acc as staging) -> transposed into qt
+    for (int r = 0; r < kBQ; ++r)
+        for (int cc = 0; cc < D; cc += 16)
+            _mm512_storeu_ps(acc + r * D + cc, r < nq ? _mm512_mul_ps(widen16<BF16>(Q + head + (int64_t)(q0 + r) * D + cc),
+                                                                       _mm512_set1_ps(c))
+                                                       : _mm512_setzero_ps());
+    for (int cc = 0; cc < D; ++cc)
+        for (int r = 0; r < kBQ; ++r) qt[cc * kBQ + r] = acc[r * D + cc];
+    for (int i = 0; i < kBQ * D; i += 16) _mm512_storeu_ps(acc + i, _mm512_setzero_ps());
+    for (int i = 0; i < kBQ; ++i) {
+        w.m[i] = -INFINITY;
+        w.l[i] = 0.0f;
+    }
+    alignas(64) float alpha[kBQ];
+    const int kv_end = CAUSAL ? std::min(N, q0 + nq) : N;
+    for (int k0 = 0; k0 < kv_end; k0 += kBK) {
+        const int nk = std::min(kBK, kv_end - k0);
+        for (int r = 0; r < kBK; ++r)
+            for (int cc = 0; cc < D; cc += 16) {
+                const bool in = r < nk;
+                _mm512_storeu_ps(kr + r * D + cc, in ? widen16<BF16>(K + head + (int64_t)(k0 + r) * D + cc)
+                                                     : _mm512_setzero_ps());
+                _mm512_storeu_ps(vr + r * D + cc, in ? widen16<BF16>(V + head + (int64_t)(k0 + r) * D + cc)
+                                                     : _mm512_setzero_ps());
+            }
+        // S^T = K Q^T: 8 keys x 32 rows in 16 accumulators per pass over the head dimension
+        const int nkb = (nk + 7) & ~7;
+        for (int jb = 0; jb < nkb; jb += 8) {
+            __m512 a[8][2];
+            for (int u = 0; u < 8; ++u) a[u][0] = a[u][1] = _mm512_setzero_ps();
+            const float* k8 = kr + jb * D;
+            for (int cc = 0; cc < D; ++cc) {
+                const __m512 x0 = _mm512_loadu_ps(qt + cc * kBQ), x1 = _mm512_loadu_ps(qt + cc * kBQ + 16);
+                for (int u = 0; u < 8; ++u) {
+                    const __m512 kb = _mm512_set1_ps(k8[u * D + cc]);
+                    a[u][0] = _mm512_fmadd_ps(kb, x0, a[u][0]);
+                    a[u][1] = _mm512_fmadd_ps(kb, x1, a[u][1]);
+                }
+            }
+            for (int u = 0; u < 8; ++u) {
+                _mm512_storeu_ps(st + (jb + u) * kBQ, a[u][0]);
+                _mm512_storeu_ps(st + (jb + u) * kBQ + 16, a[u][1]);
+            }
+        }
+        // mask (keys after the row, or past the block) to -inf, then per row: max, alpha, p, l
+        for (int hh = 0; hh < 2; ++hh) {
+            const __m512i rows = _mm512_add_epi32(_mm512_set1_epi32(q0 + 16 * hh),
+                                                  _mm512_setr_epi32(0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15));
+            const __m512 ninf = _mm512_set1_ps(-INFINITY);
+            __m512 mx = ninf;
+            for (int j = 0; j < nk; ++j) {
+                __m512 sv = _mm512_loadu_ps(st + j * kBQ + 16 * hh);
+                if constexpr (CAUSAL) {
+                    const __mmask16 after = _mm512_cmpgt_epi32_mask(_mm512_set1_epi32(k0 + j), rows);
+                    sv = _mm512_mask_mov_ps(sv, after, ninf);
+                    _mm512_storeu_ps(st + j * kBQ + 16 * hh, sv);
+                }
+                mx = _mm512_max_ps(mx, sv);
+            }
+            const __m512 m_old = _mm512_loadu_ps(w.m + 16 * hh);
+            const __m512 m_new = _mm512_max_ps(m_old, mx);
+            // rows with nothing allowed yet keep m = -inf; subtracting 0 then gives p = alpha = 0
+            const __m512 m_sub = _mm512_mask_mov_ps(m_new, _mm512_cmp_ps_mask(m_new, ninf, _CMP_EQ_OQ),
+                                                    _mm512_setzero_ps());
+            const __m512 al = exp2_nonpos16(_mm512_sub_ps(m_old, m_sub));
+            __m512 sum = _mm512_setzero_ps();
+            for (int j = 0; j < nk; ++j) {
+                const __m512 pv = exp2_nonpos16(_mm512_sub_ps(_mm512_loadu_ps(st + j * kBQ + 16 * hh), m_sub));
+                _mm512_storeu_ps(st + j * kBQ + 16 * hh, pv);
+                sum = _mm512_add_ps(sum, pv);
+            }
+            _mm512_storeu_ps(w.l + 16 * hh, _mm512_fmadd_ps(al, _mm512_loadu_ps(w.l + 16 * hh), sum));
+            _mm512_storeu_ps(w.m + 16 * hh, m_new);
+            _mm512_store_ps(alpha + 16 * hh, al);
+        }
+        // o~ = alpha o~ + P V, RB rows at a time with the whole head dimension in registers
+        for (int i = 0; i < nq; i += RB) {
+            __m512 o[RB][D / 16];
+            for (int r = 0; r < RB; ++r) {
+                const int ri = std::min(i + r, kBQ - 1);
+                const __m512 a = _mm512_set1_ps(alpha[ri]);
+                for (int u = 0; u < D / 16; ++u) o[r][u] = _mm512_mul_ps(a, _mm512_loadu_ps(acc + ri * D + 16 * u));
+            }
+            for (int j = 0; j < nk; ++j) {
+                const float* pj = st + j * kBQ;
+                const float* vj = vr + j * D;
+                __m512 pr[RB];
+                for (int r = 0; r < RB; ++r) pr[r] = _mm512_set1_ps(pj[std::min(i + r, kBQ - 1)]);
+                for (int u = 0; u < D / 16; ++u) {
+                    const __m512 vv = _mm512_loadu_ps(vj + 16 * u);
+                    for (int r = 0; r < RB; ++r) o[r][u] = _mm512_fmadd_ps(pr[r], vv, o[r][u]);
+                }
+            }
+            for (int r = 0; r < RB; ++r)
+                if (i + r < nq)
+                    for (int u = 0; u < D / 16; ++u) _mm512_storeu_ps(acc + (i + r) * D + 16 * u, o[r][u]);
+        }
+    }
+    for (int i = 0; i < nq; ++i) {
+        const float inv = 1.0f / w.l[i];  // every row keeps key 0
+        const float* ai = acc + (size_t)i * D;
+        uint16_t* oi = O + head + (int64_t)(q0 + i) * D;
+        for (int cc = 0; cc < D; ++cc) oi[cc] = BF16 ? f32_to_bf16(ai[cc] * inv) : f32_to_f16(ai[cc] * inv);
+        if (LSE) LSE[bh * N + q0 + i] = (w.m[i] + log2f(w.l[i])) * 0.693147180559945309f;
+    }
+}
+
 template <int D, bool BF16, bool CAUSAL>
 __attribute__((target("avx2,fma,f16c"))) void tile_avx2(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                                                          uint16_t* O, float* LSE, int64_t bh, int q0, int N, float c,
@@ -242,10 +396,27 @@ void tile_generic(const uint16_t* Q, const uint16_t* K, const uint16_t* V, uint1
 using TileFn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, float*, int64_t, int, int, float,
                         Scratch&);
 
+// instruction sets of the tile loop: 2 = AVX-512, 1 = AVX2/FMA/F16C, 0 = plain C++
 template <int D, bool BF16>
-TileFn pick(bool causal, bool avx2) {
-    if (avx2) return causal ? tile_avx2<D, BF16, true> : tile_avx2<D, BF16, false>;
+TileFn pick(bool causal, int isa) {
+    if (isa == 2) return causal ? tile_avx512<D, BF16, true> : tile_avx512<D, BF16, false>;
+    if (isa == 1) return causal ? tile_avx2<D, BF16, true> : tile_avx2<D, BF16, false>;
     return causal ? tile_generic<D, BF16, true> : tile_generic<D, BF16, false>;
+}
+
+// The best build this CPU runs; FA_CPU_ISA=avx2 or =generic selects a lower one (used by the
+// tests to cover every build on one machine).
+int pick_isa() {
+    static const bool avx2 = __builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma") &&
+                             __builtin_cpu_supports("f16c");
+    static const bool avx512 = avx2 && __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
+                               __builtin_cpu_supports("avx512dq") && __builtin_cpu_supports("avx512vl");
+    int isa = avx512 ? 2 : avx2 ? 1 : 0;
+    if (const char* e = getenv("FA_CPU_ISA")) {
+        if (strcmp(e, "generic") == 0) isa = 0;
+        else if (strcmp(e, "avx2") == 0 && isa > 1) isa = 1;
+    }
+    return isa;
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -269,11 +440,10 @@ extern "C" int fa_fwd_cpu(const void* q, const void* k, const void* v, void* o, 
                  overlaps(lse, lb, o, nb))))
         return FA_ERR_ALIAS;
 
-    static const bool avx2 = __builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma") &&
-                             __builtin_cpu_supports("f16c");
+    const int isa = pick_isa();
     const bool bf = dtype == FA_BF16;
-    const TileFn fn = d == 64 ? (bf ? pick<64, true>(causal, avx2) : pick<64, false>(causal, avx2))
-                              : (bf ? pick<128, true>(causal, avx2) : pick<128, false>(causal, avx2));
+    const TileFn fn = d == 64 ? (bf ? pick<64, true>(causal, isa) : pick<64, false>(causal, isa))
+                              : (bf ? pick<128, true>(causal, isa) : pick<128, false>(causal, isa));
     const int n = (int)N;
     const int64_t n_qt = (N + kBQ - 1) / kBQ;
     const int64_t items = B * H * n_qt;
