@@ -10,7 +10,8 @@ Contents
               respect to q, k, v by the chain rule (``attention_backward``), and the
               definition under a sliding-window / key-padding mask
               (``attention_masked``) and under a mask over blocks of the score
-              matrix (``attention_blocksparse``).
+              matrix (``attention_blocksparse``); the gradients under the
+              window / key-padding mask (``attention_backward_masked``).
   recurrence  the online-softmax recurrence for one query in fp64, block by
               block, in any block partition and order, with switches that plant
               the four classic implementation mistakes (used only to show that
@@ -30,7 +31,10 @@ reductions to unmasked attention over each row's key slice and over truncated
 keys, and the causal / unmasked special cases. The block-sparse definition
 (tests/test_oracle_blocksparse_pins.py): brute force, all-ones and
 block-diagonal and block-triangular reductions, a per-row gather, mask forms
-and empty rows. Every function here is pinned; none is "parity unpinned"
+and empty rows. The masked gradients (tests/test_oracle_bwd_mask_pins.py):
+decimal finite differences with the same predicate, fp64 autograd through a
+masked softmax, reductions to the unmasked and causal gradients, sum rules and
+zero cases. Every function here is pinned; none is "parity unpinned"
 except the second worked example's output vector, whose value vectors the
 page does not print.
 """

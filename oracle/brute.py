@@ -45,12 +45,16 @@ def attention(q, k, v, scale, causal=False, allowed=None):
     return out, lses
 
 
-def _outputs(qd, kd, vd, sc, causal):
-    """The definition in Decimal: o [N][d] for Decimal inputs (no conversion, no rounding to float)."""
+def _outputs(qd, kd, vd, sc, causal, allowed=None):
+    """The definition in Decimal: o [N][d] for Decimal inputs (no conversion, no rounding to float).
+    allowed(i, j), if given, replaces the causal rule; a row with no allowed key gives o = 0."""
     n, d = len(qd), len(qd[0])
     out = []
     for i in range(n):
-        keys = range(i + 1) if causal else range(n)
+        keys = [j for j in range(n) if allowed(i, j)] if allowed is not None else (range(i + 1) if causal else range(n))
+        if not keys:
+            out.append([Decimal(0)] * d)
+            continue
         e = {}
         for j in keys:
             e[j] = (sc * sum((qd[i][c] * kd[j][c] for c in range(d)), Decimal(0))).exp()
@@ -59,14 +63,15 @@ def _outputs(qd, kd, vd, sc, causal):
     return out
 
 
-def loss_gradients(q, k, v, dout, scale, causal=False, h="1e-20"):
+def loss_gradients(q, k, v, dout, scale, causal=False, h="1e-20", allowed=None):
     """Gradients of L = sum_ic dout[i][c] * o[i][c] with respect to q, k and v, by central
     differences of the definition in 50-digit arithmetic: dL/dx = (L(x+h) - L(x-h)) / 2h.
 
     No chain rule is used, so this checks the analytic gradients independently. With h = 1e-20
     the truncation error is of order h^2 and the cancellation error of order 1e-50 / h, both far
     below fp64 resolution. Inputs are nested sequences [N][d] of floats for one head; returns
-    (dq, dk, dv) as nested lists of Python floats.
+    (dq, dk, dv) as nested lists of Python floats. allowed(i, j), if given, replaces the causal
+    rule (the loss then runs over the allowed pairs only).
     """
     with localcontext() as ctx:
         ctx.prec = 50
@@ -76,7 +81,7 @@ def loss_gradients(q, k, v, dout, scale, causal=False, h="1e-20"):
         go = [[Decimal(float(x)) for x in row] for row in dout]
 
         def loss(tensors):
-            o = _outputs(tensors[0], tensors[1], tensors[2], sc, causal)
+            o = _outputs(tensors[0], tensors[1], tensors[2], sc, causal, allowed)
             return sum((go[i][c] * o[i][c] for i in range(len(o)) for c in range(len(o[0]))), Decimal(0))
 
         grads = []

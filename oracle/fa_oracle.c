@@ -31,7 +31,8 @@
  * fa_oracle_fwd_masked and fa_oracle_fwd_blocksparse restrict the allowed keys
  * further (windows, key padding, a mask over blocks of the score matrix).
  * fa_oracle_bwd, at the end of the file, gives the gradients of the same
- * definition with respect to q, k and v by the chain rule.
+ * definition with respect to q, k and v by the chain rule; fa_oracle_bwd_masked the
+ * same under the window / key-length mask.
  */
 #include <math.h>
 #include <stdint.h>
@@ -460,5 +461,144 @@ int fa_oracle_fwd_blocksparse(const double* q, const double* k, const double* v,
     }
     free(s_all);
     free(acc_all);
+    return 0;
+}
+
+/*
+ * The gradients of fa_oracle_bwd under the general mask of fa_oracle_fwd_masked: key j is
+ * allowed for query i of batch b when j >= i - window_left (window_left >= 0), j <= i +
+ * window_right (window_right >= 0) and j < seqlens_k[b] (seqlens_k given). The chain rule is
+ * unchanged; every sum runs over the allowed pairs only (masked scores carry no probability,
+ * so they contribute nothing to any gradient). A row with no allowed key has lse = -inf,
+ * D = 0 and dq = 0, and adds nothing to dk or dv; a key no row allows gets dk = dv = 0.
+ *
+ * Arguments as fa_oracle_bwd, with G replaced by B, H (rows and keys are [B*H, ...]) and
+ * causal by window_left, window_right and seqlens_k (host pointer, [B], or NULL). Same
+ * return codes.
+ */
+int fa_oracle_bwd_masked(const double* q, const double* k, const double* v, const double* dout,
+                         double* dq, double* dk, double* dv, double* lse, double* delta,
+                         int64_t B, int64_t H, int64_t N, int64_t d, double scale,
+                         int64_t window_left, int64_t window_right, const int64_t* seqlens_k,
+                         const int64_t* rows, int64_t n_rows, const int64_t* keys, int64_t n_keys) {
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || B < 1 || H < 1 || N < 1 || d < 1) return 1;
+    if (window_left < -1 || window_right < -1) return 1;
+    const int64_t G = B * H;
+    int64_t R = rows ? n_rows : N;
+    int64_t C = keys ? n_keys : N;
+    if (R < 1 || C < 1) return 1;
+    for (int64_t t = 0; rows && t < G * n_rows; ++t)
+        if (rows[t] < 0 || rows[t] >= N) return 1;
+    for (int64_t t = 0; keys && t < G * n_keys; ++t)
+        if (keys[t] < 0 || keys[t] >= N) return 1;
+    for (int64_t b = 0; seqlens_k && b < B; ++b)
+        if (seqlens_k[b] < 0 || seqlens_k[b] > N) return 1;
+    int nthreads = fa_oracle_threads();
+    double* m_all = (double*)malloc((size_t)(G * N) * sizeof(double));
+    double* l_all = (double*)malloc((size_t)(G * N) * sizeof(double));
+    double* D_all = (double*)malloc((size_t)(G * N) * sizeof(double));
+    double* s_all = (double*)malloc((size_t)nthreads * (size_t)N * sizeof(double));
+    double* dp_all = (double*)malloc((size_t)nthreads * (size_t)N * sizeof(double));
+    if (!m_all || !l_all || !D_all || !s_all || !dp_all) {
+        free(m_all); free(l_all); free(D_all); free(s_all); free(dp_all);
+        return 2;
+    }
+#define FA_ORACLE_RANGE(g, i, lo, hi)                                              \
+    int64_t lo = window_left >= 0 ? (i) - window_left : 0;                         \
+    int64_t hi = window_right >= 0 ? (i) + window_right + 1 : N;                    \
+    {                                                                              \
+        const int64_t kv_len = seqlens_k ? seqlens_k[(g) / H] : N;                 \
+        if (lo < 0) lo = 0;                                                        \
+        if (hi > kv_len) hi = kv_len;                                              \
+    }
+
+    /* pass 1, every row: m_i, l_i (three-pass route over the allowed keys) and D_i */
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nthreads)
+    for (int64_t t = 0; t < G * N; ++t) {
+#ifdef _OPENMP
+        int tid = omp_get_thread_num();
+#else
+        int tid = 0;
+#endif
+        double* s = s_all + (size_t)tid * (size_t)N;
+        int64_t g = t / N, i = t % N;
+        FA_ORACLE_RANGE(g, i, lo, hi)
+        const double* qi = q + t * d;
+        const double* doi = dout + t * d;
+        const double* kh = k + g * N * d;
+        const double* vh = v + g * N * d;
+        double m = -INFINITY, l = 0.0, D = 0.0;
+        for (int64_t j = lo; j < hi; ++j) {
+            double dot = 0.0;
+            for (int64_t c = 0; c < d; ++c) dot += qi[c] * kh[j * d + c];
+            s[j] = scale * dot;
+            if (s[j] > m) m = s[j];
+        }
+        for (int64_t j = lo; j < hi; ++j) l += exp(s[j] - m);
+        for (int64_t j = lo; j < hi; ++j) {
+            double dp = 0.0;
+            for (int64_t c = 0; c < d; ++c) dp += doi[c] * vh[j * d + c];
+            D += (exp(s[j] - m) / l) * dp;
+        }
+        m_all[t] = m;
+        l_all[t] = l;
+        D_all[t] = D;
+        if (lse) lse[t] = hi > lo ? m + log(l) : -INFINITY;
+        if (delta) delta[t] = D;
+    }
+
+    /* pass 2, requested rows: dQ_i = scale * sum_j a_ij (dP_ij - D_i) k_j over the allowed j */
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nthreads)
+    for (int64_t t = 0; t < G * R; ++t) {
+        int64_t g = t / R, r = t % R;
+        int64_t i = rows ? rows[g * n_rows + r] : r;
+        FA_ORACLE_RANGE(g, i, lo, hi)
+        const double* qi = q + (g * N + i) * d;
+        const double* doi = dout + (g * N + i) * d;
+        const double* kh = k + g * N * d;
+        const double* vh = v + g * N * d;
+        double m = m_all[g * N + i], l = l_all[g * N + i], D = D_all[g * N + i];
+        double* out = dq + t * d;
+        for (int64_t c = 0; c < d; ++c) out[c] = 0.0;
+        for (int64_t j = lo; j < hi; ++j) {
+            double dot = 0.0, dpv = 0.0;
+            for (int64_t c = 0; c < d; ++c) dot += qi[c] * kh[j * d + c];
+            for (int64_t c = 0; c < d; ++c) dpv += doi[c] * vh[j * d + c];
+            double ds = exp(scale * dot - m) / l * (dpv - D);
+            for (int64_t c = 0; c < d; ++c) out[c] += ds * kh[j * d + c];
+        }
+        for (int64_t c = 0; c < d; ++c) out[c] *= scale;
+    }
+
+    /* pass 3, requested keys: dV_j = sum_i a_ij dO_i, dK_j = scale * sum_i a_ij (dP_ij - D_i) q_i
+       over the rows i that allow key j */
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads)
+    for (int64_t t = 0; t < G * C; ++t) {
+        int64_t g = t / C, r = t % C;
+        int64_t j = keys ? keys[g * n_keys + r] : r;
+        const double* kj = k + (g * N + j) * d;
+        const double* vj = v + (g * N + j) * d;
+        double* ok = dk + t * d;
+        double* ov = dv + t * d;
+        for (int64_t c = 0; c < d; ++c) ok[c] = ov[c] = 0.0;
+        for (int64_t i = 0; i < N; ++i) {
+            FA_ORACLE_RANGE(g, i, lo, hi)
+            if (j < lo || j >= hi) continue;
+            const double* qi = q + (g * N + i) * d;
+            const double* doi = dout + (g * N + i) * d;
+            double dot = 0.0, dpv = 0.0;
+            for (int64_t c = 0; c < d; ++c) dot += qi[c] * kj[c];
+            for (int64_t c = 0; c < d; ++c) dpv += doi[c] * vj[c];
+            double a = exp(scale * dot - m_all[g * N + i]) / l_all[g * N + i];
+            double ds = a * (dpv - D_all[g * N + i]);
+            for (int64_t c = 0; c < d; ++c) {
+                ov[c] += a * doi[c];
+                ok[c] += ds * qi[c];
+            }
+        }
+        for (int64_t c = 0; c < d; ++c) ok[c] *= scale;
+    }
+#undef FA_ORACLE_RANGE
+    free(m_all); free(l_all); free(D_all); free(s_all); free(dp_all);
     return 0;
 }
