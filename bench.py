@@ -12,9 +12,9 @@ B=1, H=32, N=8192, d=128, non-causal, fp16. Prints one JSON line.
 --splits S times fa_fwd_splitkv with S key splits (0: the library's heuristic) instead of
 fa_fwd; the roofline then covers both of its kernels (split reduction and merge).
 
---window-left L / --window-right R time fa_fwd_masked with that sliding window (-1 = no limit;
-the workload's causal flag is then ignored) and price it by the allowed (row, key) pairs:
-4 d flops each.
+--window-left L / --window-right R time fa_fwd_masked (with --pass bwd: fa_bwd_masked) with that
+sliding window (-1 = no limit; the workload's causal flag is then ignored) and price it by the
+allowed (row, key) pairs: 4 d flops each (10 d for the backward).
 
 --block-density P times fa_fwd_blocksparse with a seeded random block mask (blocks of
 --block-size S rows and keys, default 128; each block kept with probability P, the diagonal
@@ -223,7 +223,7 @@ def main():
             fa.forward(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, num_splits=splits, workspace=ws)
 
     window = None
-    if (args.window_left is not None or args.window_right is not None) and args.which == "fwd":
+    if args.window_left is not None or args.window_right is not None:
         window = (-1 if args.window_left is None else args.window_left,
                   -1 if args.window_right is None else args.window_right)
 
@@ -250,6 +250,11 @@ def main():
         def step():  # noqa: F811
             fa.backward(q, k, v, o, lse, dout, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, delta=delta)
 
+        if window is not None:
+            def step():  # noqa: F811
+                fa.backward_masked(q, k, v, o, lse, dout, window[0], window[1], None, scale=w.scale, dq=dq, dk=dk,
+                                   dv=dv, delta=delta)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -271,7 +276,7 @@ def main():
         i = np.arange(w.N)
         lo = np.maximum(0, i - window[0]) if window[0] >= 0 else np.zeros_like(i)
         hi = np.minimum(w.N, i + window[1] + 1) if window[1] >= 0 else np.full_like(i, w.N)
-        flops = 4.0 * w.d * w.B * w.H * float(np.maximum(hi - lo, 0).sum())
+        flops = 4.0 * w.d * w.B * w.H * float(np.maximum(hi - lo, 0).sum()) * (2.5 if args.which == "bwd" else 1.0)
     if blocks is not None:
         flops = 4.0 * w.d * w.B * w.H * float(blocks[2])
     value = flops / (wall / args.steps) / 1e12
@@ -308,7 +313,8 @@ def main():
             "frac": round(achieved / PEAK_MFMA_F16_TFLOPS, 4),
             "traffic": (measured_traffic(w.name) if args.which == "fwd" and splits is None and window is None
                         and blocks is None else None),
-            "kernel": ("fa_bwd_dq_kernel + fa_bwd_dkdv_kernel" if args.which == "bwd" else
+            "kernel": ("fa_bwd_dq_kernel + fa_bwd_dkdv_kernel" + (" (masked)" if window is not None else "")
+                       if args.which == "bwd" else
                        "fa_fwd_kernel (masked)" if window is not None else
                        "fa_fwd_kernel (block-sparse)" if blocks is not None else
                        "fa_fwd_kernel (split) + fa_merge_kernel" if splits is not None else KERNEL_NAME),

@@ -93,6 +93,9 @@ def lib():
         L.fa_fwd_cpu.restype = ctypes.c_int
         L.fa_fwd_cpu.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        L.fa_bwd_masked.restype = ctypes.c_int
+        L.fa_bwd_masked.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 4 + [
+            ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(FaMask)]
         L.fa_bwd.restype = ctypes.c_int
         L.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
@@ -223,13 +226,8 @@ def _check_like(name, t, ref, dtype=None, shape=None):
         raise ValueError(f"{name} must be contiguous and on {ref.device}")
 
 
-def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
-             dout: torch.Tensor, causal: bool = False, scale=None, dq=None, dk=None, dv=None, delta=None,
-             return_delta: bool = False):
-    """Gradients (dq, dk, dv) of a loss L with respect to q, k, v, given dout = dL/do and the
-    forward's o and lse (same q, k, v, causal and scale). Runs on the current stream of q's device.
-    delta ([B, H, N] float32, receives dout_i . o_i) is allocated if not given; with
-    return_delta=True it is returned as a fourth value."""
+def _backward_args(q, k, v, o, lse, dout, dq, dk, dv, delta):
+    """Checks shared by backward and backward_masked; allocates the outputs not given."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
@@ -249,6 +247,17 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         _check_like(name, t, q)
     _check_like("delta", delta, q, torch.float32, (B, H, N))
+    return B, H, N, d, dq, dk, dv, delta
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+             dout: torch.Tensor, causal: bool = False, scale=None, dq=None, dk=None, dv=None, delta=None,
+             return_delta: bool = False):
+    """Gradients (dq, dk, dv) of a loss L with respect to q, k, v, given dout = dL/do and the
+    forward's o and lse (same q, k, v, causal and scale). Runs on the current stream of q's device.
+    delta ([B, H, N] float32, receives dout_i . o_i) is allocated if not given; with
+    return_delta=True it is returned as a fourth value."""
+    B, H, N, d, dq, dk, dv, delta = _backward_args(q, k, v, o, lse, dout, dq, dk, dv, delta)
     if scale is None:
         scale = default_scale(d)
     with torch.cuda.device(q.device):
@@ -256,6 +265,36 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, scale, causal,
                     stream, _DTYPES[q.dtype])
+    if st != 0:
+        raise FaError(st, status_string(st))
+    return (dq, dk, dv, delta) if return_delta else (dq, dk, dv)
+
+
+def fa_bwd_masked(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, stream, dtype, mask) -> int:
+    """Raw call of the C entry point fa_bwd_masked (mask: an FaMask or None); returns the status."""
+    return int(lib().fa_bwd_masked(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, float(scale), stream,
+                                   int(dtype), ctypes.byref(mask) if mask is not None else None))
+
+
+def backward_masked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                    dout: torch.Tensor, window_left: int = -1, window_right: int = -1,
+                    seqlens_k: torch.Tensor = None, scale=None, dq=None, dk=None, dv=None, delta=None,
+                    return_delta: bool = False):
+    """Gradients under the mask of forward_masked (window_left / window_right / seqlens_k as there),
+    given the o and lse forward_masked returned with that mask. Rows with no allowed key get
+    dq = 0; keys no row allows get dk = dv = 0. Otherwise as backward."""
+    B, H, N, d, dq, dk, dv, delta = _backward_args(q, k, v, o, lse, dout, dq, dk, dv, delta)
+    if seqlens_k is not None and (not seqlens_k.is_cuda or seqlens_k.dtype != torch.int32 or seqlens_k.shape != (B,)
+                                  or not seqlens_k.is_contiguous() or seqlens_k.device != q.device):
+        raise ValueError("seqlens_k must be a contiguous int32 GPU tensor [B] on q's device")
+    if scale is None:
+        scale = default_scale(d)
+    mask = FaMask(int(window_left), int(window_right), seqlens_k.data_ptr() if seqlens_k is not None else None)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = fa_bwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, scale, stream,
+                           _DTYPES[q.dtype], mask)
     if st != 0:
         raise FaError(st, status_string(st))
     return (dq, dk, dv, delta) if return_delta else (dq, dk, dv)

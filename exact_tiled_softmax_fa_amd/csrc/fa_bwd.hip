@@ -125,11 +125,17 @@ __device__ __forceinline__ void stage_rows(const uint16_t* src_head, int r0, int
     }
 }
 
-template <int D, bool BF16, bool CAUSAL>
+// MASKED (both kernels): the general mask of fa_fwd_masked in place of CAUSAL -- key j allowed for
+// query i when i - wl <= j (wl >= 0), j <= i + wr (wr >= 0) and j < seqlens[b] (seqlens given).
+// Only the tiles a workgroup's window reaches are loaded; a row with no allowed key (lse = -inf)
+// takes the statistic 0, so its masked scores give p = 0 rather than NaN.
+template <int D, bool BF16, bool CAUSAL, bool MASKED = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
-    float* __restrict__ DELTA, uint16_t* __restrict__ dQ, int N, int n_qt, int G, float c, float scale) {
+    float* __restrict__ DELTA, uint16_t* __restrict__ dQ, int N, int n_qt, int G, float c, float scale, int H = 1,
+    int wl = -1, int wr = -1, const int* __restrict__ seqlens = nullptr) {
+    static_assert(!(MASKED && CAUSAL), "the general mask replaces the causal one");
     constexpr int DK = D / 16;
     constexpr int DB = D / 32;
     constexpr int TILE = kKeyTile * D;
@@ -174,11 +180,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     const float Dq = sum_with_partner(dsum);
     if (h == 0 && qrow < N) DELTA[(int64_t)bh * N + qrow] = Dq;
-    const float lse2 = LSE[(int64_t)bh * N + qr] * kLog2e;  // lse in log2 units
+    const float lse_raw = LSE[(int64_t)bh * N + qr];
+    const float lse2 = (MASKED && lse_raw == -INFINITY) ? 0.f : lse_raw * kLog2e;  // lse in log2 units
 
     const int kv_end = CAUSAL ? min(N, q0 + kRows) : N;
-    const int T = (kv_end + kKeyTile - 1) / kKeyTile;
-    const int T_w = CAUSAL ? min(T, (min(wq0 + 32, N) + kKeyTile - 1) / kKeyTile) : T;
+    // key tiles tb .. tb + T - 1 (tile indices below are relative to tb); this wave computes
+    // T_w0 .. T_w - 1 of them
+    int tb = 0, kv_len = N;
+    int T = (kv_end + kKeyTile - 1) / kKeyTile;
+    int T_w = CAUSAL ? min(T, (min(wq0 + 32, N) + kKeyTile - 1) / kKeyTile) : T;
+    int T_w0 = 0;
+    if constexpr (MASKED) {
+        if (seqlens != nullptr) kv_len = min(max(seqlens[bh / H], 0), N);
+        const int lo = wl >= 0 ? max(0, q0 - wl) : 0;
+        const int hi = wr >= 0 ? min(kv_len, q0 + kRows + wr) : kv_len;
+        tb = lo / kKeyTile;
+        T = max(0, (hi + kKeyTile - 1) / kKeyTile - tb);
+        const int hi_w = wr >= 0 ? min(kv_len, wq0 + 32 + wr) : kv_len;  // this wave's last key + 1
+        T_w = max(0, min(T, (hi_w + kKeyTile - 1) / kKeyTile - tb));
+        if (wl >= 0) T_w0 = min(T_w, max(0, wq0 - wl) / kKeyTile - tb);
+    }
 
     int koff[DK];
 #pragma unroll
@@ -191,8 +212,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int b = 0; b < DB; ++b) acc[b] = (f32x16){};
 
     auto tile = [&](int j, const uint16_t* kt, const uint16_t* vt) __attribute__((always_inline)) {
-        const int k0 = j * kKeyTile;
-        const bool masked = (k0 + kKeyTile > N) || (CAUSAL && k0 + kKeyTile - 1 > wq0);
+        const int k0 = (tb + j) * kKeyTile;
+        const bool masked = MASKED ? (k0 + kKeyTile > kv_len) || (wr >= 0 && k0 + kKeyTile - 1 > wq0 + wr) ||
+                                         (wl >= 0 && k0 < wq0 + 31 - wl)
+                                   : (k0 + kKeyTile > N) || (CAUSAL && k0 + kKeyTile - 1 > wq0);
         // keep the constant parts of the LDS addresses in the instructions (see the dkdv kernel)
 #pragma unroll
         for (int t = 0; t < DK; ++t) asm volatile("" : "+v"(koff[t]));
@@ -212,7 +235,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    if (key >= N || (CAUSAL && key > qrow)) s[r] = -INFINITY;
+                    const bool out = MASKED ? key >= kv_len || (wr >= 0 && key > qrow + wr) || (wl >= 0 && key < qrow - wl)
+                                            : key >= N || (CAUSAL && key > qrow);
+                    if (out) s[r] = -INFINITY;
                 }
             }
 #pragma unroll
@@ -239,34 +264,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // the accumulators of the two unrolled tiles in two register sets and spills.
     int T_ws = __builtin_amdgcn_readfirstlane(T_w);
     asm volatile("" : "+s"(T_ws));
-    stage_rows<D>(Kh, 0, kKeyTile, N, k_lds0, wave_s, lane);
-    stage_rows<D>(Vh, 0, kKeyTile, N, v_lds0, wave_s, lane);
+    const int T_w0s = __builtin_amdgcn_readfirstlane(T_w0);
+    stage_rows<D>(Kh, tb * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
+    stage_rows<D>(Vh, tb * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
     for (int j = 0; j < T; j += 2) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (j + 1 < T) {
-            stage_rows<D>(Kh, (j + 1) * kKeyTile, kKeyTile, N, k_lds1, wave_s, lane);
-            stage_rows<D>(Vh, (j + 1) * kKeyTile, kKeyTile, N, v_lds1, wave_s, lane);
+            stage_rows<D>(Kh, (tb + j + 1) * kKeyTile, kKeyTile, N, k_lds1, wave_s, lane);
+            stage_rows<D>(Vh, (tb + j + 1) * kKeyTile, kKeyTile, N, v_lds1, wave_s, lane);
         }
-        if (j < T_ws) tile(j, k_lds0, v_lds0);
+        if ((!MASKED || j >= T_w0s) && j < T_ws) tile(j, k_lds0, v_lds0);
         if (j + 1 >= T) break;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (j + 2 < T) {
-            stage_rows<D>(Kh, (j + 2) * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
-            stage_rows<D>(Vh, (j + 2) * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
+            stage_rows<D>(Kh, (tb + j + 2) * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
+            stage_rows<D>(Vh, (tb + j + 2) * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
         }
-        if (j + 1 < T_ws) tile(j + 1, k_lds1, v_lds1);
+        if ((!MASKED || j + 1 >= T_w0s) && j + 1 < T_ws) tile(j + 1, k_lds1, v_lds1);
     }
 
     if (qrow < N) store_rows<D, BF16>(dQ + head + (int64_t)qrow * D, acc, scale, h);
 }
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, bool CAUSAL, bool MASKED = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ DELTA,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_kt, int G, float c, float scale) {
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_kt, int G, float c, float scale, int H = 1,
+    int wl = -1, int wr = -1, const int* __restrict__ seqlens = nullptr) {
+    static_assert(!(MASKED && CAUSAL), "the general mask replaces the causal one");
     constexpr int DK = D / 16;
     constexpr int DB = D / 32;
     constexpr int TILE = kQueryTile * D;
@@ -329,8 +357,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int b = 0; b < DB; ++b) dv[b] = dk[b] = (f32x16){};
 
-    const int n_steps = (N + kQueryTile - 1) / kQueryTile;
-    const int j0 = CAUSAL ? k0 / kQueryTile : 0;
+    // query tiles j0 .. n_steps - 1 can see keys of this workgroup; rows [lo_w, hi_w) can see keys
+    // of this wave (MASKED: keys past the batch's length are seen by no row)
+    int n_steps = (N + kQueryTile - 1) / kQueryTile;
+    int j0 = CAUSAL ? k0 / kQueryTile : 0;
+    int kv_len = N, lo_w = CAUSAL ? kw0 : -1, hi_w = N;
+    if constexpr (MASKED) {
+        if (seqlens != nullptr) kv_len = min(max(seqlens[bh / H], 0), N);
+        const int i_lo = wr >= 0 ? max(0, k0 - wr) : 0;
+        const int k_end = min(k0 + kKeys, kv_len);  // this workgroup's last valid key + 1
+        const int i_hi = k_end <= k0 ? i_lo : (wl >= 0 ? min(N, k_end + wl) : N);
+        j0 = i_lo / kQueryTile;
+        n_steps = max(j0, (i_hi + kQueryTile - 1) / kQueryTile);
+        lo_w = wr >= 0 ? kw0 - wr : -1;
+        const int kw_end = min(kw0 + 32, kv_len);
+        hi_w = kw_end <= kw0 ? -1 : (wl >= 0 ? min(N, kw_end + wl) : N);
+    }
 
     // lse (log2 units) and D of the rows of query tile j, staged by wave 0 through registers
     float st_l = 0.f, st_d = 0.f;
@@ -342,19 +384,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         st_d = del_h[r];
     };
     auto stats_store = [&](int buf) __attribute__((always_inline)) {
-        st_lds[buf][0][lane] = st_l * kLog2e;
+        st_lds[buf][0][lane] = (MASKED && st_l == -INFINITY) ? 0.f : st_l * kLog2e;
         st_lds[buf][1][lane] = st_d;
     };
 
-    // Query rows below skip_below meet none of this wave's keys (causal). The bound is a scalar
+    // Query rows below skip_below meet none of this wave's keys (causal, or a window that reaches
+    // no further ahead; MASKED also skips rows from skip_from on). The bound is a scalar
     // the compiler cannot see through: with the test folded away (non-causal) it keeps the
     // accumulators of the two unrolled steps in two register sets and spills.
-    int skip_below = __builtin_amdgcn_readfirstlane(CAUSAL ? kw0 : -1);
+    int skip_below = __builtin_amdgcn_readfirstlane(lo_w);
     asm volatile("" : "+s"(skip_below));
+    const int skip_from = __builtin_amdgcn_readfirstlane(hi_w);  // (MASKED) rows from here see no key
     // One 32-row half of query tile j against this wave's 32 keys: 32 MFMAs at D = 128.
     auto step = [&](int j, const uint16_t* qt_, const uint16_t* dot_, int buf) __attribute__((always_inline)) {
         const int qs = j * kQueryTile + 32 * half;  // first query row of this wave's half
         if (qs + 31 < skip_below) return;           // every key of this wave is after these rows
+        if (MASKED && qs >= skip_from) return;       // or before them, beyond the window
         // Redefining the per-lane offsets each step keeps the compiler from hoisting every
         // (offset + constant) LDS address of the unrolled loop into a register of its own. They
         // stay offsets into known arrays: a pointer passed through the asm would be an unknown
@@ -386,11 +431,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
         __builtin_amdgcn_sched_barrier(0);
         // C layout: register r holds query row qs + 8(r/4) + 4h + r%4 of key `key`
-        if (qs + 32 > N || (CAUSAL && qs < kw0 + 31)) {
+        if (MASKED ? qs + 32 > N || kw0 + 31 >= kv_len || (wr >= 0 && kw0 + 31 > qs + wr) ||
+                         (wl >= 0 && kw0 < qs + 31 - wl)
+                   : qs + 32 > N || (CAUSAL && qs < kw0 + 31)) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int qrow = qs + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (qrow >= N || (CAUSAL && key > qrow)) s[r] = -INFINITY;
+                const bool out = MASKED ? key >= kv_len || (wr >= 0 && key > qrow + wr) || (wl >= 0 && key < qrow - wl)
+                                        : CAUSAL && key > qrow;
+                if (qrow >= N || out) s[r] = -INFINITY;
             }
         }
         unsigned pk[8], dsk[8];
@@ -490,33 +539,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 }
 
-template <int D, bool BF16, bool CAUSAL>
+template <int D, bool BF16, bool CAUSAL, bool MASKED = false>
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                       void* dq, void* dk, void* dv, float* delta, int N, int BH, float c, float scale,
-                      hipStream_t stream) {
+                      hipStream_t stream, int H = 1, int wl = -1, int wr = -1, const int* seqlens = nullptr) {
     const int n_qt = (N + kRows - 1) / kRows, n_kt = (N + kKeys - 1) / kKeys;
     const int Gq = BH * n_qt, Gk = BH * n_kt;
     const auto* Q = static_cast<const uint16_t*>(q);
     const auto* K = static_cast<const uint16_t*>(k);
     const auto* V = static_cast<const uint16_t*>(v);
     const auto* dO = static_cast<const uint16_t*>(dout);
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, CAUSAL>), dim3(Gq), dim3(kThreads), 0, stream, Q, K, V,
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, CAUSAL, MASKED>), dim3(Gq), dim3(kThreads), 0, stream, Q, K, V,
                        static_cast<const uint16_t*>(o), dO, lse, delta, static_cast<uint16_t*>(dq), N, n_qt, Gq, c,
-                       scale);
+                       scale, H, wl, wr, seqlens);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, CAUSAL>), dim3(Gk), dim3(kThreads), 0, stream, Q, K, V, dO, lse,
-                       delta, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), N, n_kt, Gk, c, scale);
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, CAUSAL, MASKED>), dim3(Gk), dim3(kThreads), 0, stream, Q, K, V,
+                       dO, lse, delta, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), N, n_kt, Gk, c, scale,
+                       H, wl, wr, seqlens);
     return hipGetLastError();
 }
 
-}  // namespace
-
-extern "C" {
-
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-           void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
-           int causal, hipStream_t stream, int dtype) {
+// Checks shared by the backward entry points (everything but the mask).
+int validate_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                 int dtype) {
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return FA_ERR_NULL;
     if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
@@ -542,7 +589,18 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
         for (int b = a + 1; b < 4; ++b)
             if (overlaps(outs[a], out_sz[a], outs[b], out_sz[b])) return FA_ERR_ALIAS;
     }
+    return FA_OK;
+}
 
+}  // namespace
+
+extern "C" {
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+           void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+           int causal, hipStream_t stream, int dtype) {
+    const int st = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, dtype);
+    if (st != FA_OK) return st;
     const float c = scale * kLog2e;
     const int n = static_cast<int>(N), BH = static_cast<int>(B * H);
     const bool bf = dtype == FA_BF16;
@@ -561,4 +619,36 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+int fa_bwd_masked(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                  void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                  hipStream_t stream, int dtype, const fa_mask* mask) {
+    const int st = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, dtype);
+    if (st != FA_OK) return st;
+    if (!mask) return FA_ERR_NULL;
+    if (mask->window_left < -1 || mask->window_right < -1 || mask->window_left > INT32_MAX ||
+        mask->window_right > INT32_MAX)
+        return FA_ERR_OPTION;
+    if (reinterpret_cast<uintptr_t>(mask->seqlens_k) & 3) return FA_ERR_ALIGN;
+    // a window of N or more keys is no limit (as in fa_fwd_masked)
+    const int64_t wl64 = mask->window_left >= N ? -1 : mask->window_left;
+    const int64_t wr64 = mask->window_right >= N ? -1 : mask->window_right;
+    if (!mask->seqlens_k && wl64 == -1 && (wr64 == -1 || wr64 == 0))
+        return fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, wr64 == 0 ? 1 : 0, stream, dtype);
+    const float c = scale * kLog2e;
+    const int n = static_cast<int>(N), BH = static_cast<int>(B * H), h = static_cast<int>(H);
+    const int wl = static_cast<int>(wl64), wr = static_cast<int>(wr64);
+    const bool bf = dtype == FA_BF16;
+    hipError_t e;
+#define FA_BWD_MASKED(DD, BB)                                                                                  \
+    launch_bwd<DD, BB, false, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, n, BH, c, scale, stream, h, wl, wr, \
+                                    mask->seqlens_k)
+    if (d == 64)
+        e = bf ? FA_BWD_MASKED(64, true) : FA_BWD_MASKED(64, false);
+    else
+        e = bf ? FA_BWD_MASKED(128, true) : FA_BWD_MASKED(128, false);
+#undef FA_BWD_MASKED
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 }  // extern "C"
+

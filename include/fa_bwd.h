@@ -66,6 +66,24 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            int64_t B, int64_t H, int64_t N, int64_t d,
            float scale, int causal, hipStream_t stream, int dtype);
 
+/*
+ * fa_bwd_masked -- fa_bwd under the general mask of fa_fwd_masked (fa_mask in fa_fwd.h: a
+ * sliding window and per-batch key lengths). The chain rule is unchanged; every sum runs over
+ * the allowed pairs only, since a masked score carries no probability ("Causal masking fits
+ * inside the tiled computation", nalar.dev: the mask applies before the max, so masked entries
+ * have p = 0 and add nothing). `o` and `lse` are those fa_fwd_masked returned under the same
+ * mask; a row with no allowed key (lse = -inf) gets dq = 0 and delta = 0, and a key no row
+ * allows gets dk = dv = 0. Only the tiles inside each workgroup's window are loaded.
+ * Arguments as for fa_bwd, with `causal` replaced by `mask` (not NULL); the masks -1/-1 and
+ * -1/0 without seqlens_k run fa_bwd's own kernels. Errors: those of fa_bwd; FA_ERR_NULL for a
+ * NULL mask, FA_ERR_OPTION for a window out of range, FA_ERR_ALIGN for a misaligned seqlens_k.
+ */
+int fa_bwd_masked(const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const float* lse,
+                  void* dq, void* dk, void* dv, float* delta,
+                  int64_t B, int64_t H, int64_t N, int64_t d,
+                  float scale, hipStream_t stream, int dtype, const fa_mask* mask);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,7 @@ def L():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_bwd", "fa_fwd", "fa_fwd_blocksparse", "fa_fwd_cpu", "fa_fwd_ex",
+    assert _declared_functions() == ["fa_bwd", "fa_bwd_masked", "fa_fwd", "fa_fwd_blocksparse", "fa_fwd_cpu", "fa_fwd_ex",
                                      "fa_fwd_masked", "fa_fwd_splitkv",
                                      "fa_fwd_splitkv_heuristic", "fa_fwd_splitkv_workspace_size", "fa_status_string",
                                      "fa_version"]
@@ -236,3 +236,21 @@ def test_blocksparse_argument_errors(L, blocks, mask, kw, code):
     m = None if mask is None else fa.FaMask(*mask)
     assert fa.fa_fwd_blocksparse(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
                                  a["scale"], a["stream"], a["dtype"], m, b) == code
+
+
+def _bwd_masked(mask, **kw):
+    import exact_tiled_softmax_fa_amd as fa
+    a = dict(BWD)
+    a.update(kw)
+    m = None if mask is None else fa.FaMask(*mask)
+    return fa.fa_bwd_masked(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"],
+                            a["delta"], a["B"], a["H"], a["N"], a["d"], a["scale"], a["stream"], a["dtype"], m)
+
+
+@pytest.mark.parametrize("mask,kw,code", [
+    (None, {}, 1), ((-2, 0, None), {}, 9), ((0, -2, None), {}, 9), ((1 << 31, 0, None), {}, 9),
+    ((4, 0, 0x600002), {}, 5), ((4, 0, None), dict(q=None), 1), ((4, 0, None), dict(delta=None), 1),
+    ((4, 0, None), dict(d=96), 3), ((4, 0, None), dict(dq=0x100000), 7), ((4, 0, None), dict(scale=0.0), 6),
+])
+def test_bwd_masked_argument_errors(L, mask, kw, code):
+    assert _bwd_masked(mask, **kw) == code
