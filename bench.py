@@ -78,7 +78,18 @@ def measured_traffic(workload_name: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w):
+def _window_keys(i, N, window):
+    """Allowed keys of each row i under a (back, ahead) window (-1 = no limit)."""
+    import numpy as np
+    lo = np.maximum(0, i - window[0]) if window[0] >= 0 else np.zeros_like(i)
+    hi = np.minimum(N, i + window[1] + 1) if window[1] >= 0 else np.full_like(i, N)
+    return np.maximum(hi - lo, 0)
+
+
+def cpu_baseline(w, window=None, blocks=None):
+    """The fp64 oracle on 1024 seeded rows per head (every row of the small workloads), in the GPU
+    line's unit: conventional TFLOP/s, or 4 d flops per allowed pair under a window (the masked
+    oracle) or a block mask (the block-sparse oracle; blocks = (block size, mask))."""
     import numpy as np
     from oracle import core
 
@@ -88,26 +99,43 @@ def cpu_baseline(w):
         rows = np.tile(np.arange(w.N, dtype=np.int64), (w.B * w.H, 1))
     qd, kd, vd = q.double().numpy(), k.double().numpy(), v.double().numpy()
     t0 = time.perf_counter()
-    core.attention(qd, kd, vd, w.scale, w.causal, rows)
+    if window is not None:
+        core.attention_masked(qd, kd, vd, w.scale, window[0], window[1], None, rows)
+        what = f"masked oracle, window {window[0]}/{window[1]}"
+    elif blocks is not None:
+        core.attention_blocksparse(qd, kd, vd, w.scale, blocks[1], blocks[0], blocks[0], rows=rows)
+        what = f"block-sparse oracle, {blocks[0]}x{blocks[0]} blocks"
+    else:
+        core.attention(qd, kd, vd, w.scale, w.causal, rows)
+        what = "fp64 three-pass"
     dt = time.perf_counter() - t0
-    keys = (rows + 1).sum() if w.causal else rows.size * w.N
-    flops = 4.0 * w.d * float(keys)
-    # the conventional count halves the causal pair count; scale the sample the same way
-    conv = flops * (w.flops() / (4.0 * w.d * (w.B * w.H * w.N * (w.N + 1) / 2 if w.causal else w.B * w.H * w.N * w.N)))
+    if window is not None:
+        conv = 4.0 * w.d * float(_window_keys(rows, w.N, window).sum())
+    elif blocks is not None:
+        bs, m = blocks
+        kb_keys = np.minimum(w.N, (np.arange(m.shape[1]) + 1) * bs) - np.arange(m.shape[1]) * bs
+        conv = 4.0 * w.d * float((np.asarray(m)[rows // bs] * kb_keys).sum())
+    else:
+        keys = (rows + 1).sum() if w.causal else rows.size * w.N
+        flops = 4.0 * w.d * float(keys)
+        # the conventional count halves the causal pair count; scale the sample the same way
+        conv = flops * (w.flops() / (4.0 * w.d * (w.B * w.H * w.N * (w.N + 1) / 2 if w.causal
+                                                   else w.B * w.H * w.N * w.N)))
     return {
         "value": conv / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": core.threads(),
         "kind": "oracle",
         "sample": f"{rows.shape[1]} seeded query rows per head x {rows.shape[0]} heads of {w.name} "
-                  f"({rows.size} rows, {dt:.2f} s, fp64 three-pass)",
+                  f"({rows.size} rows, {dt:.2f} s, {what})",
     }
 
 
-def cpu_baseline_bwd(w):
+def cpu_baseline_bwd(w, window=None):
     """The fp64 backward oracle on one head of the workload (1024 sampled rows of dq and 1024
     sampled keys of dk, dv when the workload samples rows, else everything), in conventional
-    backward TFLOP/s: 10 * d flops per (row, key) pair of the parts it computes."""
+    backward TFLOP/s: 10 * d flops per (row, key) pair of the parts it computes (allowed pairs
+    under a window, with the masked backward oracle)."""
     import numpy as np
     from oracle import core
 
@@ -118,9 +146,15 @@ def cpu_baseline_bwd(w):
     rows = None if rows is None else rows[:1]
     keys = None if keys is None else keys[:1]
     t0 = time.perf_counter()
-    core.attention_backward(head(q), head(k), head(v), head(dout), w.scale, w.causal, rows=rows, keys=keys)
+    if window is None:
+        core.attention_backward(head(q), head(k), head(v), head(dout), w.scale, w.causal, rows=rows, keys=keys)
+        pairs = w.N * (w.N + 1) / 2 if w.causal else float(w.N) * w.N
+    else:
+        one = lambda t: head(t).reshape(1, 1, w.N, w.d)  # noqa: E731
+        core.attention_backward_masked(one(q), one(k), one(v), one(dout), w.scale, window[0], window[1],
+                                       rows=rows, keys=keys)
+        pairs = float(_window_keys(np.arange(w.N), w.N, window).sum())
     dt = time.perf_counter() - t0
-    pairs = w.N * (w.N + 1) / 2 if w.causal else float(w.N) * w.N
     # every row's statistics cost a full pass; dq and dk/dv are computed for the sampled part only
     frac = 1.0 if rows is None else (rows.shape[1] + keys.shape[1]) / (2.0 * w.N)
     flops = 10.0 * w.d * pairs * (0.4 + 0.6 * frac)
@@ -131,7 +165,8 @@ def cpu_baseline_bwd(w):
         "kind": "oracle",
         "sample": f"one head of {w.name}: every row's softmax statistics and D, dq of "
                   f"{'all' if rows is None else rows.shape[1]} rows, dk and dv of "
-                  f"{'all' if keys is None else keys.shape[1]} keys ({dt:.2f} s, fp64 chain rule)",
+                  f"{'all' if keys is None else keys.shape[1]} keys ({dt:.2f} s, fp64 chain rule"
+                  + (f", window {window[0]}/{window[1]})" if window is not None else ")"),
     }
 
 
@@ -273,10 +308,8 @@ def main():
     flops = w.flops() * (2.5 if args.which == "bwd" else 1.0)
     if window is not None:
         import numpy as np
-        i = np.arange(w.N)
-        lo = np.maximum(0, i - window[0]) if window[0] >= 0 else np.zeros_like(i)
-        hi = np.minimum(w.N, i + window[1] + 1) if window[1] >= 0 else np.full_like(i, w.N)
-        flops = 4.0 * w.d * w.B * w.H * float(np.maximum(hi - lo, 0).sum()) * (2.5 if args.which == "bwd" else 1.0)
+        flops = (4.0 * w.d * w.B * w.H * float(_window_keys(np.arange(w.N), w.N, window).sum())
+                 * (2.5 if args.which == "bwd" else 1.0))
     if blocks is not None:
         flops = 4.0 * w.d * w.B * w.H * float(blocks[2])
     value = flops / (wall / args.steps) / 1e12
@@ -322,7 +355,10 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w) if args.which == "fwd" else cpu_baseline_bwd(w)
+        if args.which == "fwd":
+            out["cpu_baseline"] = cpu_baseline(w, window, (args.block_size, bmask) if blocks else None)
+        else:
+            out["cpu_baseline"] = cpu_baseline_bwd(w, window)
     print(json.dumps(out), flush=True)
 
 
