@@ -11,7 +11,8 @@ Contents
               definition under a sliding-window / key-padding mask
               (``attention_masked``) and under a mask over blocks of the score
               matrix (``attention_blocksparse``); the gradients under the
-              window / key-padding mask (``attention_backward_masked``).
+              window / key-padding mask (``attention_backward_masked``) and under
+              a block mask (``attention_backward_blocksparse``).
   recurrence  the online-softmax recurrence for one query in fp64, block by
               block, in any block partition and order, with switches that plant
               the four classic implementation mistakes (used only to show that
@@ -34,7 +35,8 @@ block-diagonal and block-triangular reductions, a per-row gather, mask forms
 and empty rows. The masked gradients (tests/test_oracle_bwd_mask_pins.py):
 decimal finite differences with the same predicate, fp64 autograd through a
 masked softmax, reductions to the unmasked and causal gradients, sum rules and
-zero cases. Every function here is pinned; none is "parity unpinned"
+zero cases; the block-masked gradients (tests/test_oracle_bwd_blocksparse_pins.py)
+likewise, with block-diagonal and all-ones reductions. Every function here is pinned; none is "parity unpinned"
 except the second worked example's output vector, whose value vectors the
 page does not print.
 """

@@ -57,6 +57,15 @@ def _load():
             ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
         ]
+        lib.fa_oracle_bwd_blocksparse.restype = ctypes.c_int
+        lib.fa_oracle_bwd_blocksparse.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+        ]
         lib.fa_oracle_threads.restype = ctypes.c_int
         lib.fa_oracle_threads.argtypes = []
         _lib = lib
@@ -179,6 +188,44 @@ def attention_backward_masked(q, k, v, dout, scale, window_left=-1, window_right
                                       rows_p, n_rows, keys_p, n_keys)
     if rc != 0:
         raise RuntimeError(f"fa_oracle_bwd_masked failed with code {rc}")
+    return dq, dk, dv, lse, delta
+
+
+def attention_backward_blocksparse(q, k, v, dout, scale, block_mask, block_q, block_k, window_left=-1,
+                                   window_right=-1, seqlens_k=None, rows=None, keys=None):
+    """Gradients of L = sum(dout * o) under the block mask of ``attention_blocksparse`` (on top of
+    the window / key-length mask), in fp64 (``fa_oracle_bwd_blocksparse``). Shapes and results as
+    ``attention_backward_masked``; ``block_mask`` as in ``block_mask_strides``."""
+    arrs = [np.ascontiguousarray(np.asarray(t, dtype=np.float64)) for t in (q, k, v, dout)]
+    shape = arrs[0].shape
+    if len(shape) != 4 or any(a.shape != shape for a in arrs):
+        raise ValueError(f"q, k, v, dout must share one [B,H,N,d] shape, got {[a.shape for a in arrs]}")
+    B, H, N, d = shape
+    if block_q < 1 or block_k < 1:
+        raise ValueError("block sizes must be >= 1")
+    bm, sb, sh = block_mask_strides(block_mask, B, H, N, block_q, block_k)
+    G = B * H
+    q, k, v, dout = (a.reshape(G, N, d) for a in arrs)
+    sl = None
+    if seqlens_k is not None:
+        sl = np.ascontiguousarray(np.asarray(seqlens_k, dtype=np.int64))
+        if sl.shape != (B,):
+            raise ValueError(f"seqlens_k must be [B], got {sl.shape}")
+    rows, n_rows, rows_p = _index_list(rows, G, "rows")
+    keys, n_keys, keys_p = _index_list(keys, G, "keys")
+    dq = np.empty((G, n_rows if rows is not None else N, d), dtype=np.float64)
+    dk = np.empty((G, n_keys if keys is not None else N, d), dtype=np.float64)
+    dv = np.empty_like(dk)
+    lse = np.empty((G, N), dtype=np.float64)
+    delta = np.empty((G, N), dtype=np.float64)
+    rc = _load().fa_oracle_bwd_blocksparse(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+                                           dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, lse.ctypes.data,
+                                           delta.ctypes.data, B, H, N, d, float(scale), int(window_left),
+                                           int(window_right), sl.ctypes.data if sl is not None else None,
+                                           bm.ctypes.data, int(block_q), int(block_k), sb, sh,
+                                           rows_p, n_rows, keys_p, n_keys)
+    if rc != 0:
+        raise RuntimeError(f"fa_oracle_bwd_blocksparse failed with code {rc}")
     return dq, dk, dv, lse, delta
 
 

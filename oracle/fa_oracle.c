@@ -31,8 +31,8 @@
  * fa_oracle_fwd_masked and fa_oracle_fwd_blocksparse restrict the allowed keys
  * further (windows, key padding, a mask over blocks of the score matrix).
  * fa_oracle_bwd, at the end of the file, gives the gradients of the same
- * definition with respect to q, k and v by the chain rule; fa_oracle_bwd_masked the
- * same under the window / key-length mask.
+ * definition with respect to q, k and v by the chain rule; fa_oracle_bwd_masked and
+ * fa_oracle_bwd_blocksparse the same under the window / key-length and block masks.
  */
 #include <math.h>
 #include <stdint.h>
@@ -465,24 +465,41 @@ int fa_oracle_fwd_blocksparse(const double* q, const double* k, const double* v,
 }
 
 /*
- * The gradients of fa_oracle_bwd under the general mask of fa_oracle_fwd_masked: key j is
- * allowed for query i of batch b when j >= i - window_left (window_left >= 0), j <= i +
- * window_right (window_right >= 0) and j < seqlens_k[b] (seqlens_k given). The chain rule is
- * unchanged; every sum runs over the allowed pairs only (masked scores carry no probability,
- * so they contribute nothing to any gradient). A row with no allowed key has lse = -inf,
- * D = 0 and dq = 0, and adds nothing to dk or dv; a key no row allows gets dk = dv = 0.
- *
- * Arguments as fa_oracle_bwd, with G replaced by B, H (rows and keys are [B*H, ...]) and
- * causal by window_left, window_right and seqlens_k (host pointer, [B], or NULL). Same
- * return codes.
+ * The gradients of fa_oracle_bwd under a general mask. Key j is allowed for query i of batch b
+ * when j >= i - window_left (window_left >= 0), j <= i + window_right (window_right >= 0),
+ * j < seqlens_k[b] (seqlens_k given) and, with a block mask, the byte of query block
+ * i / block_q and key block j / block_k is non-zero (the layout of fa_oracle_fwd_blocksparse).
+ * The chain rule is unchanged; every sum runs over the allowed pairs only (masked scores carry
+ * no probability, so they contribute nothing to any gradient). A row with no allowed key has
+ * lse = -inf, D = 0 and dq = 0, and adds nothing to dk or dv; a key no row allows gets
+ * dk = dv = 0.
  */
-int fa_oracle_bwd_masked(const double* q, const double* k, const double* v, const double* dout,
-                         double* dq, double* dk, double* dv, double* lse, double* delta,
-                         int64_t B, int64_t H, int64_t N, int64_t d, double scale,
-                         int64_t window_left, int64_t window_right, const int64_t* seqlens_k,
-                         const int64_t* rows, int64_t n_rows, const int64_t* keys, int64_t n_keys) {
+typedef struct {
+    int64_t H, N, window_left, window_right, block_q, block_k, n_kb, stride_b, stride_h;
+    const int64_t* seqlens_k;
+    const uint8_t* block_mask; /* NULL: no block mask */
+} mask_spec;
+
+/* the allowed keys of row i of head g lie in [lo, hi) (and pass allowed_block) */
+static void key_range(const mask_spec* ms, int64_t g, int64_t i, int64_t* lo, int64_t* hi) {
+    int64_t a = ms->window_left >= 0 ? i - ms->window_left : 0;
+    int64_t b = ms->window_right >= 0 ? i + ms->window_right + 1 : ms->N;
+    const int64_t kv_len = ms->seqlens_k ? ms->seqlens_k[g / ms->H] : ms->N;
+    *lo = a < 0 ? 0 : a;
+    *hi = b > kv_len ? kv_len : b;
+}
+static int allowed_block(const mask_spec* ms, int64_t g, int64_t i, int64_t j) {
+    if (!ms->block_mask) return 1;
+    return ms->block_mask[(g / ms->H) * ms->stride_b + (g % ms->H) * ms->stride_h +
+                          (i / ms->block_q) * ms->n_kb + j / ms->block_k] != 0;
+}
+
+static int bwd_general(const double* q, const double* k, const double* v, const double* dout,
+                       double* dq, double* dk, double* dv, double* lse, double* delta,
+                       int64_t B, int64_t H, int64_t N, int64_t d, double scale, const mask_spec* ms,
+                       const int64_t* rows, int64_t n_rows, const int64_t* keys, int64_t n_keys) {
     if (!q || !k || !v || !dout || !dq || !dk || !dv || B < 1 || H < 1 || N < 1 || d < 1) return 1;
-    if (window_left < -1 || window_right < -1) return 1;
+    if (ms->window_left < -1 || ms->window_right < -1) return 1;
     const int64_t G = B * H;
     int64_t R = rows ? n_rows : N;
     int64_t C = keys ? n_keys : N;
@@ -491,25 +508,16 @@ int fa_oracle_bwd_masked(const double* q, const double* k, const double* v, cons
         if (rows[t] < 0 || rows[t] >= N) return 1;
     for (int64_t t = 0; keys && t < G * n_keys; ++t)
         if (keys[t] < 0 || keys[t] >= N) return 1;
-    for (int64_t b = 0; seqlens_k && b < B; ++b)
-        if (seqlens_k[b] < 0 || seqlens_k[b] > N) return 1;
+    for (int64_t b = 0; ms->seqlens_k && b < B; ++b)
+        if (ms->seqlens_k[b] < 0 || ms->seqlens_k[b] > N) return 1;
     int nthreads = fa_oracle_threads();
     double* m_all = (double*)malloc((size_t)(G * N) * sizeof(double));
     double* l_all = (double*)malloc((size_t)(G * N) * sizeof(double));
     double* D_all = (double*)malloc((size_t)(G * N) * sizeof(double));
     double* s_all = (double*)malloc((size_t)nthreads * (size_t)N * sizeof(double));
-    double* dp_all = (double*)malloc((size_t)nthreads * (size_t)N * sizeof(double));
-    if (!m_all || !l_all || !D_all || !s_all || !dp_all) {
-        free(m_all); free(l_all); free(D_all); free(s_all); free(dp_all);
+    if (!m_all || !l_all || !D_all || !s_all) {
+        free(m_all); free(l_all); free(D_all); free(s_all);
         return 2;
-    }
-#define FA_ORACLE_RANGE(g, i, lo, hi)                                              \
-    int64_t lo = window_left >= 0 ? (i) - window_left : 0;                         \
-    int64_t hi = window_right >= 0 ? (i) + window_right + 1 : N;                    \
-    {                                                                              \
-        const int64_t kv_len = seqlens_k ? seqlens_k[(g) / H] : N;                 \
-        if (lo < 0) lo = 0;                                                        \
-        if (hi > kv_len) hi = kv_len;                                              \
     }
 
     /* pass 1, every row: m_i, l_i (three-pass route over the allowed keys) and D_i */
@@ -521,21 +529,26 @@ int fa_oracle_bwd_masked(const double* q, const double* k, const double* v, cons
         int tid = 0;
 #endif
         double* s = s_all + (size_t)tid * (size_t)N;
-        int64_t g = t / N, i = t % N;
-        FA_ORACLE_RANGE(g, i, lo, hi)
+        int64_t g = t / N, i = t % N, lo, hi;
+        key_range(ms, g, i, &lo, &hi);
         const double* qi = q + t * d;
         const double* doi = dout + t * d;
         const double* kh = k + g * N * d;
         const double* vh = v + g * N * d;
         double m = -INFINITY, l = 0.0, D = 0.0;
+        int64_t n_allowed = 0;
         for (int64_t j = lo; j < hi; ++j) {
+            if (!allowed_block(ms, g, i, j)) continue;
             double dot = 0.0;
             for (int64_t c = 0; c < d; ++c) dot += qi[c] * kh[j * d + c];
             s[j] = scale * dot;
             if (s[j] > m) m = s[j];
+            ++n_allowed;
         }
-        for (int64_t j = lo; j < hi; ++j) l += exp(s[j] - m);
+        for (int64_t j = lo; j < hi; ++j)
+            if (allowed_block(ms, g, i, j)) l += exp(s[j] - m);
         for (int64_t j = lo; j < hi; ++j) {
+            if (!allowed_block(ms, g, i, j)) continue;
             double dp = 0.0;
             for (int64_t c = 0; c < d; ++c) dp += doi[c] * vh[j * d + c];
             D += (exp(s[j] - m) / l) * dp;
@@ -543,7 +556,7 @@ int fa_oracle_bwd_masked(const double* q, const double* k, const double* v, cons
         m_all[t] = m;
         l_all[t] = l;
         D_all[t] = D;
-        if (lse) lse[t] = hi > lo ? m + log(l) : -INFINITY;
+        if (lse) lse[t] = n_allowed > 0 ? m + log(l) : -INFINITY;
         if (delta) delta[t] = D;
     }
 
@@ -551,8 +564,8 @@ int fa_oracle_bwd_masked(const double* q, const double* k, const double* v, cons
 #pragma omp parallel for schedule(dynamic, 16) num_threads(nthreads)
     for (int64_t t = 0; t < G * R; ++t) {
         int64_t g = t / R, r = t % R;
-        int64_t i = rows ? rows[g * n_rows + r] : r;
-        FA_ORACLE_RANGE(g, i, lo, hi)
+        int64_t i = rows ? rows[g * n_rows + r] : r, lo, hi;
+        key_range(ms, g, i, &lo, &hi);
         const double* qi = q + (g * N + i) * d;
         const double* doi = dout + (g * N + i) * d;
         const double* kh = k + g * N * d;
@@ -561,6 +574,7 @@ int fa_oracle_bwd_masked(const double* q, const double* k, const double* v, cons
         double* out = dq + t * d;
         for (int64_t c = 0; c < d; ++c) out[c] = 0.0;
         for (int64_t j = lo; j < hi; ++j) {
+            if (!allowed_block(ms, g, i, j)) continue;
             double dot = 0.0, dpv = 0.0;
             for (int64_t c = 0; c < d; ++c) dot += qi[c] * kh[j * d + c];
             for (int64_t c = 0; c < d; ++c) dpv += doi[c] * vh[j * d + c];
@@ -582,8 +596,9 @@ int fa_oracle_bwd_masked(const double* q, const double* k, const double* v, cons
         double* ov = dv + t * d;
         for (int64_t c = 0; c < d; ++c) ok[c] = ov[c] = 0.0;
         for (int64_t i = 0; i < N; ++i) {
-            FA_ORACLE_RANGE(g, i, lo, hi)
-            if (j < lo || j >= hi) continue;
+            int64_t lo, hi;
+            key_range(ms, g, i, &lo, &hi);
+            if (j < lo || j >= hi || !allowed_block(ms, g, i, j)) continue;
             const double* qi = q + (g * N + i) * d;
             const double* doi = dout + (g * N + i) * d;
             double dot = 0.0, dpv = 0.0;
@@ -598,7 +613,40 @@ int fa_oracle_bwd_masked(const double* q, const double* k, const double* v, cons
         }
         for (int64_t c = 0; c < d; ++c) ok[c] *= scale;
     }
-#undef FA_ORACLE_RANGE
-    free(m_all); free(l_all); free(D_all); free(s_all); free(dp_all);
+    free(m_all); free(l_all); free(D_all); free(s_all);
     return 0;
+}
+
+/*
+ * fa_oracle_bwd_masked: the gradients under the window / key-length mask. Arguments as
+ * fa_oracle_bwd, with G replaced by B, H (rows and keys are [B*H, ...]) and causal by
+ * window_left, window_right and seqlens_k (host pointer, [B], or NULL). Same return codes.
+ */
+int fa_oracle_bwd_masked(const double* q, const double* k, const double* v, const double* dout,
+                         double* dq, double* dk, double* dv, double* lse, double* delta,
+                         int64_t B, int64_t H, int64_t N, int64_t d, double scale,
+                         int64_t window_left, int64_t window_right, const int64_t* seqlens_k,
+                         const int64_t* rows, int64_t n_rows, const int64_t* keys, int64_t n_keys) {
+    mask_spec ms = {H, N, window_left, window_right, 1, 1, 0, 0, 0, seqlens_k, NULL};
+    return bwd_general(q, k, v, dout, dq, dk, dv, lse, delta, B, H, N, d, scale, &ms, rows, n_rows, keys,
+                       n_keys);
+}
+
+/*
+ * fa_oracle_bwd_blocksparse: the gradients under the block mask of fa_oracle_fwd_blocksparse
+ * on top of the window / key-length mask. Arguments as fa_oracle_bwd_masked, plus block_mask
+ * (host pointer), block_q, block_k >= 1 and stride_b, stride_h >= 0. Same return codes.
+ */
+int fa_oracle_bwd_blocksparse(const double* q, const double* k, const double* v, const double* dout,
+                              double* dq, double* dk, double* dv, double* lse, double* delta,
+                              int64_t B, int64_t H, int64_t N, int64_t d, double scale,
+                              int64_t window_left, int64_t window_right, const int64_t* seqlens_k,
+                              const uint8_t* block_mask, int64_t block_q, int64_t block_k,
+                              int64_t stride_b, int64_t stride_h,
+                              const int64_t* rows, int64_t n_rows, const int64_t* keys, int64_t n_keys) {
+    if (!block_mask || block_q < 1 || block_k < 1 || stride_b < 0 || stride_h < 0) return 1;
+    mask_spec ms = {H, N, window_left, window_right, block_q, block_k, (N + block_k - 1) / block_k,
+                    stride_b, stride_h, seqlens_k, block_mask};
+    return bwd_general(q, k, v, dout, dq, dk, dv, lse, delta, B, H, N, d, scale, &ms, rows, n_rows, keys,
+                       n_keys);
 }
