@@ -16,10 +16,10 @@ fa_fwd; the roofline then covers both of its kernels (split reduction and merge)
 sliding window (-1 = no limit; the workload's causal flag is then ignored) and price it by the
 allowed (row, key) pairs: 4 d flops each (10 d for the backward).
 
---block-density P times fa_fwd_blocksparse with a seeded random block mask (blocks of
---block-size S rows and keys, default 128; each block kept with probability P, the diagonal
-always), shared by all heads, the workload's causal flag ignored, and prices it by the allowed
-(row, key) pairs: 4 d flops each.
+--block-density P times fa_fwd_blocksparse (with --pass bwd: fa_bwd_blocksparse) with a seeded
+random block mask (blocks of --block-size S rows and keys, default 128; each block kept with
+probability P, the diagonal always), shared by all heads, the workload's causal flag ignored, and
+prices it by the allowed (row, key) pairs: 4 d flops each (10 d for the backward).
 
 --cpu-variant times the host-CPU entry point fa_fwd_cpu instead (no GPU needed) on the first K
 heads of the workload (default 4), in TFLOP/s of the same flop convention.
@@ -131,11 +131,12 @@ def cpu_baseline(w, window=None, blocks=None):
     }
 
 
-def cpu_baseline_bwd(w, window=None):
+def cpu_baseline_bwd(w, window=None, blocks=None):
     """The fp64 backward oracle on one head of the workload (1024 sampled rows of dq and 1024
     sampled keys of dk, dv when the workload samples rows, else everything), in conventional
     backward TFLOP/s: 10 * d flops per (row, key) pair of the parts it computes (allowed pairs
-    under a window, with the masked backward oracle)."""
+    under a window or a block mask, with the masked or block-sparse backward oracle; blocks =
+    (block size, mask))."""
     import numpy as np
     from oracle import core
 
@@ -146,14 +147,19 @@ def cpu_baseline_bwd(w, window=None):
     rows = None if rows is None else rows[:1]
     keys = None if keys is None else keys[:1]
     t0 = time.perf_counter()
-    if window is None:
-        core.attention_backward(head(q), head(k), head(v), head(dout), w.scale, w.causal, rows=rows, keys=keys)
-        pairs = w.N * (w.N + 1) / 2 if w.causal else float(w.N) * w.N
-    else:
-        one = lambda t: head(t).reshape(1, 1, w.N, w.d)  # noqa: E731
+    one = lambda t: head(t).reshape(1, 1, w.N, w.d)  # noqa: E731
+    if window is not None:
         core.attention_backward_masked(one(q), one(k), one(v), one(dout), w.scale, window[0], window[1],
                                        rows=rows, keys=keys)
         pairs = float(_window_keys(np.arange(w.N), w.N, window).sum())
+    elif blocks is not None:
+        bs, m = blocks
+        core.attention_backward_blocksparse(one(q), one(k), one(v), one(dout), w.scale, m, bs, bs, rows=rows,
+                                            keys=keys)
+        pairs = float(workloads.block_mask_pairs(m, w.N, bs, bs))
+    else:
+        core.attention_backward(head(q), head(k), head(v), head(dout), w.scale, w.causal, rows=rows, keys=keys)
+        pairs = w.N * (w.N + 1) / 2 if w.causal else float(w.N) * w.N
     dt = time.perf_counter() - t0
     # every row's statistics cost a full pass; dq and dk/dv are computed for the sampled part only
     frac = 1.0 if rows is None else (rows.shape[1] + keys.shape[1]) / (2.0 * w.N)
@@ -166,7 +172,8 @@ def cpu_baseline_bwd(w, window=None):
         "sample": f"one head of {w.name}: every row's softmax statistics and D, dq of "
                   f"{'all' if rows is None else rows.shape[1]} rows, dk and dv of "
                   f"{'all' if keys is None else keys.shape[1]} keys ({dt:.2f} s, fp64 chain rule"
-                  + (f", window {window[0]}/{window[1]})" if window is not None else ")"),
+                  + (f", window {window[0]}/{window[1]})" if window is not None else
+                     f", {blocks[0]}x{blocks[0]} block mask)" if blocks is not None else ")"),
     }
 
 
@@ -266,7 +273,7 @@ def main():
             fa.forward_masked(q, k, v, window[0], window[1], None, scale=w.scale, out=o, lse=lse)
 
     blocks = None
-    if args.block_density is not None and args.which == "fwd":
+    if args.block_density is not None:
         bmask = workloads.make_block_mask(w, args.block_size, args.block_density)
         blocks = (args.block_size, args.block_density, workloads.block_mask_pairs(bmask, w.N, args.block_size,
                                                                                    args.block_size))
@@ -289,6 +296,10 @@ def main():
             def step():  # noqa: F811
                 fa.backward_masked(q, k, v, o, lse, dout, window[0], window[1], None, scale=w.scale, dq=dq, dk=dk,
                                    dv=dv, delta=delta)
+        if blocks is not None:
+            def step():  # noqa: F811
+                fa.backward_blocksparse(q, k, v, o, lse, dout, bmask_dev, args.block_size, args.block_size,
+                                        scale=w.scale, dq=dq, dk=dk, dv=dv, delta=delta)
 
     for _ in range(args.warmup):
         step()
@@ -311,11 +322,12 @@ def main():
         flops = (4.0 * w.d * w.B * w.H * float(_window_keys(np.arange(w.N), w.N, window).sum())
                  * (2.5 if args.which == "bwd" else 1.0))
     if blocks is not None:
-        flops = 4.0 * w.d * w.B * w.H * float(blocks[2])
+        flops = 4.0 * w.d * w.B * w.H * float(blocks[2]) * (2.5 if args.which == "bwd" else 1.0)
     value = flops / (wall / args.steps) / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     out = {
-        "metric": (HEADLINE_METRIC if w.name == workloads.HEADLINE.name and args.which == "fwd" and splits is None
+        "metric": (HEADLINE_METRIC if (w.name == workloads.HEADLINE.name and args.which == "fwd" and splits is None
+                                       and window is None and blocks is None)
                    else f"{args.which} attention TFLOP/s ({w.name}"
                         + (f", split-KV {splits}" if splits is not None else "")
                         + (f", window {window[0]}/{window[1]}" if window is not None else "")
@@ -346,7 +358,8 @@ def main():
             "frac": round(achieved / PEAK_MFMA_F16_TFLOPS, 4),
             "traffic": (measured_traffic(w.name) if args.which == "fwd" and splits is None and window is None
                         and blocks is None else None),
-            "kernel": ("fa_bwd_dq_kernel + fa_bwd_dkdv_kernel" + (" (masked)" if window is not None else "")
+            "kernel": ("fa_bwd_dq_kernel + fa_bwd_dkdv_kernel" + (" (masked)" if window is not None else
+                                                                  " (block-sparse)" if blocks is not None else "")
                        if args.which == "bwd" else
                        "fa_fwd_kernel (masked)" if window is not None else
                        "fa_fwd_kernel (block-sparse)" if blocks is not None else
@@ -358,7 +371,7 @@ def main():
         if args.which == "fwd":
             out["cpu_baseline"] = cpu_baseline(w, window, (args.block_size, bmask) if blocks else None)
         else:
-            out["cpu_baseline"] = cpu_baseline_bwd(w, window)
+            out["cpu_baseline"] = cpu_baseline_bwd(w, window, (args.block_size, bmask) if blocks else None)
     print(json.dumps(out), flush=True)
 
 

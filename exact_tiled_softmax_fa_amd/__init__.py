@@ -96,6 +96,8 @@ def lib():
         L.fa_bwd_masked.restype = ctypes.c_int
         L.fa_bwd_masked.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 4 + [
             ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(FaMask)]
+        L.fa_bwd_blocksparse.restype = ctypes.c_int
+        L.fa_bwd_blocksparse.argtypes = L.fa_bwd_masked.argtypes + [ctypes.POINTER(FaBlockMask)]
         L.fa_bwd.restype = ctypes.c_int
         L.fa_bwd.argtypes = [ctypes.c_void_p] * 10 + [
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
@@ -284,9 +286,7 @@ def backward_masked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.
     given the o and lse forward_masked returned with that mask. Rows with no allowed key get
     dq = 0; keys no row allows get dk = dv = 0. Otherwise as backward."""
     B, H, N, d, dq, dk, dv, delta = _backward_args(q, k, v, o, lse, dout, dq, dk, dv, delta)
-    if seqlens_k is not None and (not seqlens_k.is_cuda or seqlens_k.dtype != torch.int32 or seqlens_k.shape != (B,)
-                                  or not seqlens_k.is_contiguous() or seqlens_k.device != q.device):
-        raise ValueError("seqlens_k must be a contiguous int32 GPU tensor [B] on q's device")
+    _check_seqlens(seqlens_k, q)
     if scale is None:
         scale = default_scale(d)
     mask = FaMask(int(window_left), int(window_right), seqlens_k.data_ptr() if seqlens_k is not None else None)
@@ -295,6 +295,64 @@ def backward_masked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.
         st = fa_bwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, scale, stream,
                            _DTYPES[q.dtype], mask)
+    if st != 0:
+        raise FaError(st, status_string(st))
+    return (dq, dk, dv, delta) if return_delta else (dq, dk, dv)
+
+
+def _check_seqlens(seqlens_k, q):
+    if seqlens_k is not None and (not seqlens_k.is_cuda or seqlens_k.dtype != torch.int32
+                                  or seqlens_k.shape != (q.shape[0],) or not seqlens_k.is_contiguous()
+                                  or seqlens_k.device != q.device):
+        raise ValueError("seqlens_k must be a contiguous int32 GPU tensor [B] on q's device")
+
+
+def _block_mask_arg(block_mask, block_q, block_k, q) -> "FaBlockMask":
+    """The FaBlockMask of a [n_qb, n_kb], [H, n_qb, n_kb] or [B, H, n_qb, n_kb] byte mask."""
+    B, H, N, _ = q.shape
+    if block_q < 1 or block_k < 1:
+        raise ValueError("block sizes must be positive")
+    n_qb, n_kb = -(-N // block_q), -(-N // block_k)
+    if (not isinstance(block_mask, torch.Tensor) or not block_mask.is_cuda or block_mask.device != q.device
+            or block_mask.dtype not in (torch.uint8, torch.bool) or not block_mask.is_contiguous()):
+        raise ValueError("block_mask must be a contiguous uint8 or bool GPU tensor on q's device")
+    per = n_qb * n_kb
+    shapes = {(n_qb, n_kb): (0, 0), (H, n_qb, n_kb): (0, per), (B, H, n_qb, n_kb): (H * per, per)}
+    if tuple(block_mask.shape) not in shapes:
+        raise ValueError(f"block_mask must be [{n_qb},{n_kb}], [H,{n_qb},{n_kb}] or [B,H,{n_qb},{n_kb}], "
+                         f"got {tuple(block_mask.shape)}")
+    stride_b, stride_h = shapes[tuple(block_mask.shape)]
+    return FaBlockMask(block_mask.data_ptr(), int(block_q), int(block_k), stride_b, stride_h)
+
+
+def fa_bwd_blocksparse(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, stream, dtype, mask,
+                       blocks) -> int:
+    """Raw call of the C entry point fa_bwd_blocksparse (mask: an FaMask or None; blocks: an
+    FaBlockMask or None); returns the status code."""
+    return int(lib().fa_bwd_blocksparse(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, float(scale), stream,
+                                        int(dtype), ctypes.byref(mask) if mask is not None else None,
+                                        ctypes.byref(blocks) if blocks is not None else None))
+
+
+def backward_blocksparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                         dout: torch.Tensor, block_mask: torch.Tensor, block_q: int, block_k: int,
+                         window_left: int = -1, window_right: int = -1, seqlens_k: torch.Tensor = None, scale=None,
+                         dq=None, dk=None, dv=None, delta=None, return_delta: bool = False):
+    """Gradients under the masks of forward_blocksparse (block_mask, block_q, block_k, window_left,
+    window_right, seqlens_k as there), given the o and lse forward_blocksparse returned with those
+    masks. Rows with no allowed key get dq = 0; keys no row allows get dk = dv = 0. Otherwise as
+    backward."""
+    B, H, N, d, dq, dk, dv, delta = _backward_args(q, k, v, o, lse, dout, dq, dk, dv, delta)
+    blocks = _block_mask_arg(block_mask, block_q, block_k, q)
+    _check_seqlens(seqlens_k, q)
+    if scale is None:
+        scale = default_scale(d)
+    mask = FaMask(int(window_left), int(window_right), seqlens_k.data_ptr() if seqlens_k is not None else None)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = fa_bwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N,
+                                d, scale, stream, _DTYPES[q.dtype], mask, blocks)
     if st != 0:
         raise FaError(st, status_string(st))
     return (dq, dk, dv, delta) if return_delta else (dq, dk, dv)
@@ -318,9 +376,7 @@ def forward_masked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, window_lef
     if q.shape != k.shape or q.shape != v.shape or q.dtype != k.dtype or q.dtype != v.dtype or q.dtype not in _DTYPES:
         raise ValueError("q, k, v must share one shape and one of float16 / bfloat16")
     B, H, N, d = q.shape
-    if seqlens_k is not None and (not seqlens_k.is_cuda or seqlens_k.dtype != torch.int32 or seqlens_k.shape != (B,)
-                                  or not seqlens_k.is_contiguous() or seqlens_k.device != q.device):
-        raise ValueError("seqlens_k must be a contiguous int32 GPU tensor [B] on q's device")
+    _check_seqlens(seqlens_k, q)
     if scale is None:
         scale = default_scale(d)
     out = torch.empty_like(q) if out is None else out
@@ -361,21 +417,8 @@ def forward_blocksparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block
     if q.shape != k.shape or q.shape != v.shape or q.dtype != k.dtype or q.dtype != v.dtype or q.dtype not in _DTYPES:
         raise ValueError("q, k, v must share one shape and one of float16 / bfloat16")
     B, H, N, d = q.shape
-    if block_q < 1 or block_k < 1:
-        raise ValueError("block sizes must be positive")
-    n_qb, n_kb = -(-N // block_q), -(-N // block_k)
-    if (not isinstance(block_mask, torch.Tensor) or not block_mask.is_cuda or block_mask.device != q.device
-            or block_mask.dtype not in (torch.uint8, torch.bool) or not block_mask.is_contiguous()):
-        raise ValueError("block_mask must be a contiguous uint8 or bool GPU tensor on q's device")
-    per = n_qb * n_kb
-    shapes = {(n_qb, n_kb): (0, 0), (H, n_qb, n_kb): (0, per), (B, H, n_qb, n_kb): (H * per, per)}
-    if tuple(block_mask.shape) not in shapes:
-        raise ValueError(f"block_mask must be [{n_qb},{n_kb}], [H,{n_qb},{n_kb}] or [B,H,{n_qb},{n_kb}], "
-                         f"got {tuple(block_mask.shape)}")
-    stride_b, stride_h = shapes[tuple(block_mask.shape)]
-    if seqlens_k is not None and (not seqlens_k.is_cuda or seqlens_k.dtype != torch.int32 or seqlens_k.shape != (B,)
-                                  or not seqlens_k.is_contiguous() or seqlens_k.device != q.device):
-        raise ValueError("seqlens_k must be a contiguous int32 GPU tensor [B] on q's device")
+    blocks = _block_mask_arg(block_mask, block_q, block_k, q)
+    _check_seqlens(seqlens_k, q)
     if scale is None:
         scale = default_scale(d)
     out = torch.empty_like(q) if out is None else out
@@ -383,7 +426,6 @@ def forward_blocksparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block
     _check_like("out", out, q)
     _check_like("lse", lse, q, torch.float32, (B, H, N))
     mask = FaMask(int(window_left), int(window_right), seqlens_k.data_ptr() if seqlens_k is not None else None)
-    blocks = FaBlockMask(block_mask.data_ptr(), int(block_q), int(block_k), stride_b, stride_h)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         st = fa_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,

@@ -129,13 +129,18 @@ __device__ __forceinline__ void stage_rows(const uint16_t* src_head, int r0, int
 // query i when i - wl <= j (wl >= 0), j <= i + wr (wr >= 0) and j < seqlens[b] (seqlens given).
 // Only the tiles a workgroup's window reaches are loaded; a row with no allowed key (lse = -inf)
 // takes the statistic 0, so its masked scores give p = 0 rather than NaN.
-template <int D, bool BF16, bool CAUSAL, bool MASKED = false>
+// BLOCKS (both kernels, on top of MASKED): the block mask of fa_fwd_blocksparse. Each workgroup
+// lists the tiles one of its waves needs (compact_tiles) and walks only those; a wave computes a
+// listed tile only when its own bit is set.
+template <int D, bool BF16, bool CAUSAL, bool MASKED = false, bool BLOCKS = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
     float* __restrict__ DELTA, uint16_t* __restrict__ dQ, int N, int n_qt, int G, float c, float scale, int H = 1,
-    int wl = -1, int wr = -1, const int* __restrict__ seqlens = nullptr) {
+    int wl = -1, int wr = -1, const int* __restrict__ seqlens = nullptr, const uint8_t* __restrict__ bmask = nullptr,
+    int bq = 0, int bk = 0, int64_t bstride_b = 0, int64_t bstride_h = 0) {
     static_assert(!(MASKED && CAUSAL), "the general mask replaces the causal one");
+    static_assert(!BLOCKS || MASKED, "the block mask rides on the general mask");
     constexpr int DK = D / 16;
     constexpr int DB = D / 32;
     constexpr int TILE = kKeyTile * D;
@@ -200,6 +205,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         T_w = max(0, min(T, (hi_w + kKeyTile - 1) / kKeyTile - tb));
         if (wl >= 0) T_w0 = min(T_w, max(0, wq0 - wl) / kKeyTile - tb);
     }
+    // BLOCKS: tile index j becomes a position in t_list; every wave walks the whole list
+    __shared__ int t_list[BLOCKS ? kMaxListTiles : 1];
+    __shared__ uint8_t t_wm[BLOCKS ? kMaxListTiles : 1];
+    __shared__ int t_cnt[BLOCKS ? kWaves : 1];
+    if constexpr (BLOCKS) {
+        const uint8_t* mb = bmask + (int64_t)(bh / H) * bstride_b + (int64_t)(bh % H) * bstride_h;
+        const int n_kb = (N + bk - 1) / bk;
+        // wave w needs key tile t when its rows and the tile's keys hold an allowed pair: the
+        // block byte is set and the offsets key - row, which run over one interval, meet the window
+        auto need = [&](int w, int t) {
+            const int r0 = q0 + 32 * w, r1 = min(r0 + 32, N) - 1;
+            const int c0 = t * kKeyTile, c1 = min(c0 + kKeyTile, kv_len) - 1;
+            return r0 < N && c0 < kv_len && (wr < 0 || c0 - r1 <= wr) && (wl < 0 || r0 - c1 <= wl) &&
+                   mb[(int64_t)(r0 / bq) * n_kb + c0 / bk] != 0;
+        };
+        T = compact_tiles<kWaves>(tb, T, need, t_list, t_wm, t_cnt, tid);
+        T_w0 = 0;
+        T_w = T;
+    }
+    auto key_tile = [&](int j) { return BLOCKS ? __builtin_amdgcn_readfirstlane(t_list[j]) : tb + j; };
 
     int koff[DK];
 #pragma unroll
@@ -212,7 +237,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int b = 0; b < DB; ++b) acc[b] = (f32x16){};
 
     auto tile = [&](int j, const uint16_t* kt, const uint16_t* vt) __attribute__((always_inline)) {
-        const int k0 = (tb + j) * kKeyTile;
+        const int k0 = key_tile(j) * kKeyTile;
         const bool masked = MASKED ? (k0 + kKeyTile > kv_len) || (wr >= 0 && k0 + kKeyTile - 1 > wq0 + wr) ||
                                          (wl >= 0 && k0 < wq0 + 31 - wl)
                                    : (k0 + kKeyTile > N) || (CAUSAL && k0 + kKeyTile - 1 > wq0);
@@ -265,36 +290,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     int T_ws = __builtin_amdgcn_readfirstlane(T_w);
     asm volatile("" : "+s"(T_ws));
     const int T_w0s = __builtin_amdgcn_readfirstlane(T_w0);
-    stage_rows<D>(Kh, tb * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
-    stage_rows<D>(Vh, tb * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
+    // BLOCKS: this wave's bit for list entry j
+    auto mine = [&](int j) { return !BLOCKS || ((__builtin_amdgcn_readfirstlane(t_wm[j]) >> wave_s) & 1); };
+    stage_rows<D>(Kh, key_tile(0) * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
+    stage_rows<D>(Vh, key_tile(0) * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
     for (int j = 0; j < T; j += 2) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (j + 1 < T) {
-            stage_rows<D>(Kh, (tb + j + 1) * kKeyTile, kKeyTile, N, k_lds1, wave_s, lane);
-            stage_rows<D>(Vh, (tb + j + 1) * kKeyTile, kKeyTile, N, v_lds1, wave_s, lane);
+            stage_rows<D>(Kh, key_tile(j + 1) * kKeyTile, kKeyTile, N, k_lds1, wave_s, lane);
+            stage_rows<D>(Vh, key_tile(j + 1) * kKeyTile, kKeyTile, N, v_lds1, wave_s, lane);
         }
-        if ((!MASKED || j >= T_w0s) && j < T_ws) tile(j, k_lds0, v_lds0);
+        if ((!MASKED || j >= T_w0s) && j < T_ws && mine(j)) tile(j, k_lds0, v_lds0);
         if (j + 1 >= T) break;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (j + 2 < T) {
-            stage_rows<D>(Kh, (tb + j + 2) * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
-            stage_rows<D>(Vh, (tb + j + 2) * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
+            stage_rows<D>(Kh, key_tile(j + 2) * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
+            stage_rows<D>(Vh, key_tile(j + 2) * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
         }
-        if ((!MASKED || j + 1 >= T_w0s) && j + 1 < T_ws) tile(j + 1, k_lds1, v_lds1);
+        if ((!MASKED || j + 1 >= T_w0s) && j + 1 < T_ws && mine(j + 1)) tile(j + 1, k_lds1, v_lds1);
     }
 
     if (qrow < N) store_rows<D, BF16>(dQ + head + (int64_t)qrow * D, acc, scale, h);
 }
 
-template <int D, bool BF16, bool CAUSAL, bool MASKED = false>
+template <int D, bool BF16, bool CAUSAL, bool MASKED = false, bool BLOCKS = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ DELTA,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_kt, int G, float c, float scale, int H = 1,
-    int wl = -1, int wr = -1, const int* __restrict__ seqlens = nullptr) {
+    int wl = -1, int wr = -1, const int* __restrict__ seqlens = nullptr, const uint8_t* __restrict__ bmask = nullptr,
+    int bq = 0, int bk = 0, int64_t bstride_b = 0, int64_t bstride_h = 0) {
     static_assert(!(MASKED && CAUSAL), "the general mask replaces the causal one");
+    static_assert(!BLOCKS || MASKED, "the block mask rides on the general mask");
     constexpr int DK = D / 16;
     constexpr int DB = D / 32;
     constexpr int TILE = kQueryTile * D;
@@ -373,6 +402,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int kw_end = min(kw0 + 32, kv_len);
         hi_w = kw_end <= kw0 ? -1 : (wl >= 0 ? min(N, kw_end + wl) : N);
     }
+
+    // The query tiles walked: j0 + p for p < n_list, or (BLOCKS) the listed tiles t_list[p] that one
+    // of the waves needs, a wave computing the ones whose bit it holds.
+    int n_list = n_steps - j0;
+    __shared__ int t_list[BLOCKS ? kMaxListTiles : 1];
+    __shared__ uint8_t t_wm[BLOCKS ? kMaxListTiles : 1];
+    __shared__ int t_cnt[BLOCKS ? kWaves : 1];
+    if constexpr (BLOCKS) {
+        const uint8_t* mb = bmask + (int64_t)(bh / H) * bstride_b + (int64_t)(bh % H) * bstride_h;
+        const int n_kb = (N + bk - 1) / bk;
+        // wave w: row half w >> 2 of query tile t against key group w & 3 (the window test is the
+        // dQ kernel's)
+        auto need = [&](int w, int t) {
+            const int r0 = t * kQueryTile + 32 * (w >> 2), r1 = min(r0 + 32, N) - 1;
+            const int c0 = k0 + 32 * (w & 3), c1 = min(c0 + 32, kv_len) - 1;
+            return r0 < N && c0 < kv_len && (wr < 0 || c0 - r1 <= wr) && (wl < 0 || r0 - c1 <= wl) &&
+                   mb[(int64_t)(r0 / bq) * n_kb + c0 / bk] != 0;
+        };
+        n_list = compact_tiles<kWaves>(j0, n_list, need, t_list, t_wm, t_cnt, tid);
+    }
+    auto q_tile = [&](int p) { return BLOCKS ? __builtin_amdgcn_readfirstlane(t_list[p]) : j0 + p; };
+    auto mine = [&](int p) { return !BLOCKS || ((__builtin_amdgcn_readfirstlane(t_wm[p]) >> wave_s) & 1); };
 
     // lse (log2 units) and D of the rows of query tile j, staged by wave 0 through registers
     float st_l = 0.f, st_d = 0.f;
@@ -479,34 +530,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
     };
 
-    // Q(j), dO(j) and the statistics of tile j sit in buffer (j - j0) % 2. The tensor tiles of
-    // j + 1 are requested right after the barrier that publishes tile j; wave 0 fetches the
-    // statistics of j + 1 into registers at the same time and writes them to LDS at the end of
-    // the step (the buffer they go to was last read in step j - 1, before that barrier).
-    if (wave == 0) stats_load(j0);
-    stage_rows<D>(Qh, j0 * kQueryTile, kQueryTile, N, q_lds0, wave_s, lane);
-    stage_rows<D>(dOh, j0 * kQueryTile, kQueryTile, N, do_lds0, wave_s, lane);
+    // Q, dO and the statistics of walk position p sit in buffer p % 2. The tensor tiles of p + 1
+    // are requested right after the barrier that publishes p; wave 0 fetches the statistics of
+    // p + 1 into registers at the same time and writes them to LDS at the end of the step (the
+    // buffer they go to was last read in step p - 1, before that barrier).
+    if (wave == 0) stats_load(q_tile(0));
+    stage_rows<D>(Qh, q_tile(0) * kQueryTile, kQueryTile, N, q_lds0, wave_s, lane);
+    stage_rows<D>(dOh, q_tile(0) * kQueryTile, kQueryTile, N, do_lds0, wave_s, lane);
     if (wave == 0) stats_store(0);
-    for (int j = j0; j < n_steps; j += 2) {
+    for (int p = 0; p < n_list; p += 2) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (j + 1 < n_steps) {
-            if (wave == 0) stats_load(j + 1);
-            stage_rows<D>(Qh, (j + 1) * kQueryTile, kQueryTile, N, q_lds1, wave_s, lane);
-            stage_rows<D>(dOh, (j + 1) * kQueryTile, kQueryTile, N, do_lds1, wave_s, lane);
+        if (p + 1 < n_list) {
+            if (wave == 0) stats_load(q_tile(p + 1));
+            stage_rows<D>(Qh, q_tile(p + 1) * kQueryTile, kQueryTile, N, q_lds1, wave_s, lane);
+            stage_rows<D>(dOh, q_tile(p + 1) * kQueryTile, kQueryTile, N, do_lds1, wave_s, lane);
         }
-        step(j, q_lds0, do_lds0, 0);
-        if (j + 1 >= n_steps) break;
+        if (mine(p)) step(q_tile(p), q_lds0, do_lds0, 0);
+        if (p + 1 >= n_list) break;
         if (wave == 0) stats_store(1);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (j + 2 < n_steps) {
-            if (wave == 0) stats_load(j + 2);
-            stage_rows<D>(Qh, (j + 2) * kQueryTile, kQueryTile, N, q_lds0, wave_s, lane);
-            stage_rows<D>(dOh, (j + 2) * kQueryTile, kQueryTile, N, do_lds0, wave_s, lane);
+        if (p + 2 < n_list) {
+            if (wave == 0) stats_load(q_tile(p + 2));
+            stage_rows<D>(Qh, q_tile(p + 2) * kQueryTile, kQueryTile, N, q_lds0, wave_s, lane);
+            stage_rows<D>(dOh, q_tile(p + 2) * kQueryTile, kQueryTile, N, do_lds0, wave_s, lane);
         }
-        step(j + 1, q_lds1, do_lds1, 1);
-        if (j + 2 < n_steps && wave == 0) stats_store(0);
+        if (mine(p + 1)) step(q_tile(p + 1), q_lds1, do_lds1, 1);
+        if (p + 2 < n_list && wave == 0) stats_store(0);
     }
 
     // The two waves of a key group summed over different query rows: the second half hands its
@@ -539,24 +590,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 }
 
-template <int D, bool BF16, bool CAUSAL, bool MASKED = false>
+template <int D, bool BF16, bool CAUSAL, bool MASKED = false, bool BLOCKS = false>
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                       void* dq, void* dk, void* dv, float* delta, int N, int BH, float c, float scale,
-                      hipStream_t stream, int H = 1, int wl = -1, int wr = -1, const int* seqlens = nullptr) {
+                      hipStream_t stream, int H = 1, int wl = -1, int wr = -1, const int* seqlens = nullptr,
+                      const uint8_t* bmask = nullptr, int bq = 0, int bk = 0, int64_t bstride_b = 0,
+                      int64_t bstride_h = 0) {
     const int n_qt = (N + kRows - 1) / kRows, n_kt = (N + kKeys - 1) / kKeys;
     const int Gq = BH * n_qt, Gk = BH * n_kt;
     const auto* Q = static_cast<const uint16_t*>(q);
     const auto* K = static_cast<const uint16_t*>(k);
     const auto* V = static_cast<const uint16_t*>(v);
     const auto* dO = static_cast<const uint16_t*>(dout);
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, CAUSAL, MASKED>), dim3(Gq), dim3(kThreads), 0, stream, Q, K, V,
-                       static_cast<const uint16_t*>(o), dO, lse, delta, static_cast<uint16_t*>(dq), N, n_qt, Gq, c,
-                       scale, H, wl, wr, seqlens);
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, CAUSAL, MASKED, BLOCKS>), dim3(Gq), dim3(kThreads), 0, stream, Q,
+                       K, V, static_cast<const uint16_t*>(o), dO, lse, delta, static_cast<uint16_t*>(dq), N, n_qt, Gq,
+                       c, scale, H, wl, wr, seqlens, bmask, bq, bk, bstride_b, bstride_h);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, CAUSAL, MASKED>), dim3(Gk), dim3(kThreads), 0, stream, Q, K, V,
-                       dO, lse, delta, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), N, n_kt, Gk, c, scale,
-                       H, wl, wr, seqlens);
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, CAUSAL, MASKED, BLOCKS>), dim3(Gk), dim3(kThreads), 0, stream,
+                       Q, K, V, dO, lse, delta, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), N, n_kt, Gk,
+                       c, scale, H, wl, wr, seqlens, bmask, bq, bk, bstride_b, bstride_h);
     return hipGetLastError();
 }
 
@@ -589,6 +642,22 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
         for (int b = a + 1; b < 4; ++b)
             if (overlaps(outs[a], out_sz[a], outs[b], out_sz[b])) return FA_ERR_ALIAS;
     }
+    return FA_OK;
+}
+
+// The window of a fa_mask (NULL: none) as the kernels take it; a window of N or more keys is no
+// limit (as in fa_fwd_masked).
+int read_mask(const fa_mask* mask, int64_t N, int& wl, int& wr, const int32_t*& seqlens) {
+    wl = wr = -1;
+    seqlens = nullptr;
+    if (!mask) return FA_OK;
+    if (mask->window_left < -1 || mask->window_right < -1 || mask->window_left > INT32_MAX ||
+        mask->window_right > INT32_MAX)
+        return FA_ERR_OPTION;
+    if (reinterpret_cast<uintptr_t>(mask->seqlens_k) & 3) return FA_ERR_ALIGN;
+    wl = mask->window_left >= N ? -1 : static_cast<int>(mask->window_left);
+    wr = mask->window_right >= N ? -1 : static_cast<int>(mask->window_right);
+    seqlens = mask->seqlens_k;
     return FA_OK;
 }
 
@@ -625,28 +694,57 @@ int fa_bwd_masked(const void* q, const void* k, const void* v, const void* o, co
     const int st = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, dtype);
     if (st != FA_OK) return st;
     if (!mask) return FA_ERR_NULL;
-    if (mask->window_left < -1 || mask->window_right < -1 || mask->window_left > INT32_MAX ||
-        mask->window_right > INT32_MAX)
-        return FA_ERR_OPTION;
-    if (reinterpret_cast<uintptr_t>(mask->seqlens_k) & 3) return FA_ERR_ALIGN;
-    // a window of N or more keys is no limit (as in fa_fwd_masked)
-    const int64_t wl64 = mask->window_left >= N ? -1 : mask->window_left;
-    const int64_t wr64 = mask->window_right >= N ? -1 : mask->window_right;
-    if (!mask->seqlens_k && wl64 == -1 && (wr64 == -1 || wr64 == 0))
-        return fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, wr64 == 0 ? 1 : 0, stream, dtype);
+    int wl, wr;
+    const int32_t* seqlens;
+    const int ms = read_mask(mask, N, wl, wr, seqlens);
+    if (ms != FA_OK) return ms;
+    if (!seqlens && wl == -1 && (wr == -1 || wr == 0))
+        return fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, wr == 0 ? 1 : 0, stream, dtype);
     const float c = scale * kLog2e;
     const int n = static_cast<int>(N), BH = static_cast<int>(B * H), h = static_cast<int>(H);
-    const int wl = static_cast<int>(wl64), wr = static_cast<int>(wr64);
     const bool bf = dtype == FA_BF16;
     hipError_t e;
 #define FA_BWD_MASKED(DD, BB)                                                                                  \
     launch_bwd<DD, BB, false, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, n, BH, c, scale, stream, h, wl, wr, \
-                                    mask->seqlens_k)
+                                    seqlens)
     if (d == 64)
         e = bf ? FA_BWD_MASKED(64, true) : FA_BWD_MASKED(64, false);
     else
         e = bf ? FA_BWD_MASKED(128, true) : FA_BWD_MASKED(128, false);
 #undef FA_BWD_MASKED
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                       const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t N,
+                       int64_t d, float scale, hipStream_t stream, int dtype, const fa_mask* mask,
+                       const fa_block_mask* blocks) {
+    const int st = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, dtype);
+    if (st != FA_OK) return st;
+    if (!blocks || !blocks->mask) return FA_ERR_NULL;
+    if (blocks->block_q < 64 || blocks->block_k < 64 || blocks->block_q % 64 != 0 || blocks->block_k % 64 != 0 ||
+        blocks->block_q > INT32_MAX || blocks->block_k > INT32_MAX || blocks->stride_b < 0 || blocks->stride_h < 0)
+        return FA_ERR_OPTION;
+    // the work lists hold one entry per 64-key tile (dQ) or 64-row tile (dK, dV)
+    if (N > static_cast<int64_t>(kKeyTile) * kMaxListTiles || N > static_cast<int64_t>(kQueryTile) * kMaxListTiles)
+        return FA_ERR_SHAPE;
+    int wl, wr;
+    const int32_t* seqlens;
+    const int ms = read_mask(mask, N, wl, wr, seqlens);
+    if (ms != FA_OK) return ms;
+    const float c = scale * kLog2e;
+    const int n = static_cast<int>(N), BH = static_cast<int>(B * H), h = static_cast<int>(H);
+    const int bq = static_cast<int>(blocks->block_q), bk = static_cast<int>(blocks->block_k);
+    const bool bf = dtype == FA_BF16;
+    hipError_t e;
+#define FA_BWD_BLOCKS(DD, BB)                                                                                     \
+    launch_bwd<DD, BB, false, true, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, n, BH, c, scale, stream, h, wl, \
+                                          wr, seqlens, blocks->mask, bq, bk, blocks->stride_b, blocks->stride_h)
+    if (d == 64)
+        e = bf ? FA_BWD_BLOCKS(64, true) : FA_BWD_BLOCKS(64, false);
+    else
+        e = bf ? FA_BWD_BLOCKS(128, true) : FA_BWD_BLOCKS(128, false);
+#undef FA_BWD_BLOCKS
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -19,6 +19,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin to 8 XCDs
+constexpr int kMaxListTiles = 1024;  // block-sparse work lists: 64-row or 64-key tiles, N <= 65536
 
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
@@ -124,6 +125,51 @@ inline bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 __device__ __forceinline__ void lds_load16(const uint16_t* head, int n_bytes, unsigned off, lds_void* dst) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)head, (short)0, n_bytes, 0x00020000);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off, 0, 0, 0);
+}
+
+// Block-sparse work lists. Of the tiles t0 .. t0 + T - 1, those that some wave of the workgroup
+// needs (need(w, t) for wave w and absolute tile t) are compacted in ascending order into list
+// (absolute tile index), with a byte per entry holding one bit per wave in wm. A ballot per wave
+// and a prefix over the waves (through cnt[waves]) give each needed tile its position. Every
+// thread of the workgroup calls it (it holds barriers); returns the number of entries, which is
+// workgroup-uniform. With no entry, list[0] = t0 so that loads issued for entry 0 stay in range.
+// The caller bounds T by the list's capacity.
+template <int kWaves, typename Need>
+__device__ __forceinline__ int compact_tiles(int t0, int T, Need need, int* list, uint8_t* wm, int* cnt, int tid) {
+    constexpr int kThreads = 64 * kWaves;
+    const int lane = tid & 63, wave = tid >> 6;
+    int count = 0;
+    for (int base = 0; base < T; base += kThreads) {
+        const int t = base + tid;
+        unsigned bits = 0;
+        if (t < T) {
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w)
+                if (need(w, t0 + t)) bits |= 1u << w;
+        }
+        const uint64_t any = __builtin_amdgcn_ballot_w64(bits != 0);
+        if (lane == 0) cnt[wave] = __builtin_popcountll(any);
+        __syncthreads();
+        int before = count, total = count;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const int cw = cnt[w];
+            before += w < wave ? cw : 0;
+            total += cw;
+        }
+        if (bits != 0) {
+            const int pos = before + __builtin_popcountll(any & ((1ull << lane) - 1ull));
+            list[pos] = t0 + t;
+            wm[pos] = (uint8_t)bits;
+        }
+        count = total;
+        __syncthreads();
+    }
+    if (count == 0) {
+        if (tid == 0) list[0] = t0;
+        __syncthreads();
+    }
+    return count;
 }
 
 }  // namespace fa_detail

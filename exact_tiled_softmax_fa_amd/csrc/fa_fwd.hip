@@ -46,7 +46,6 @@ constexpr int kBlockM = 32 * kWaves;  // query rows per workgroup (32 per wave)
 constexpr int kBlockN = 64;           // keys per tile
 constexpr float kDefaultRescaleLog2 = 8.f;  // default reference-max threshold (log2 units)
 constexpr int kDefaultVariant = 1;          // kernel fa_fwd runs: 1 = 32 rows per wave, 2 = 64
-constexpr int kMaxListTiles = 1024;         // block-sparse: key tiles per query tile, N <= 65536
 
 // SPLIT: the key range of every query tile is cut into n_split equal runs of tiles, one per
 // workgroup; each writes its partial result (O normalised over its own keys, in fp32, and the
@@ -133,41 +132,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if constexpr (BLOCKS) {
         const uint8_t* mb = bmask + (int64_t)(bh / H) * bstride_b + (int64_t)(bh % H) * bstride_h;
         const int n_kb = (N + bk - 1) / bk;
-        int count = 0;
-        for (int base = 0; base < T; base += kThreads) {
-            const int t = base + tid;
-            unsigned wm = 0;
-            if (t < T) {
-                const int kb = (tb + t) * kBlockN / bk;
-#pragma unroll
-                for (int w = 0; w < kWaves; ++w) {
-                    const int r0 = q0 + 32 * w;
-                    if (r0 < N && mb[(int64_t)(r0 / bq) * n_kb + kb] != 0) wm |= 1u << w;
-                }
-            }
-            const uint64_t need = __builtin_amdgcn_ballot_w64(wm != 0);
-            if (lane == 0) t_cnt[wave] = __builtin_popcountll(need);
-            __syncthreads();
-            int before = count, total = count;
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                const int cw = t_cnt[w];
-                before += w < wave ? cw : 0;
-                total += cw;
-            }
-            if (wm != 0) {
-                const int pos = before + __builtin_popcountll(need & ((1ull << lane) - 1ull));
-                t_list[pos] = tb + t;
-                t_wm[pos] = (uint8_t)wm;
-            }
-            count = total;
-            __syncthreads();
-        }
-        T = count;
-        if (T == 0) {  // no tile at all: a valid entry for the loads the prologue still issues
-            if (tid == 0) t_list[0] = 0;
-            __syncthreads();
-        }
+        auto need = [&](int w, int t) {
+            const int r0 = q0 + 32 * w;
+            return r0 < N && mb[(int64_t)(r0 / bq) * n_kb + t * kBlockN / bk] != 0;
+        };
+        T = compact_tiles<kWaves>(tb, T, need, t_list, t_wm, t_cnt, tid);
     }
     // tiles this wave computes: causal waves stop at the tile holding their last row
     // (Non-causal: T_w = T, hidden from the compiler. Folded away, the tests on it disappear and

@@ -84,6 +84,28 @@ int fa_bwd_masked(const void* q, const void* k, const void* v, const void* o,
                   int64_t B, int64_t H, int64_t N, int64_t d,
                   float scale, hipStream_t stream, int dtype, const fa_mask* mask);
 
+/*
+ * fa_bwd_blocksparse -- fa_bwd under the block mask of fa_fwd_blocksparse (fa_block_mask in
+ * fa_fwd.h), optionally combined with a window and key lengths (`mask` may be NULL). The sums of
+ * the chain rule run over the allowed pairs only: a block the mask drops holds no probability,
+ * so it adds nothing to any gradient (the same reading of "Causal masking fits inside the tiled
+ * computation", nalar.dev, as for fa_bwd_masked). `o` and `lse` are those fa_fwd_blocksparse
+ * returned under the same masks. Each dQ workgroup (256 rows) loads only the 64-key tiles one of
+ * its 32-row groups needs, and each dK/dV workgroup (128 keys) only the 64-row query tiles one of
+ * its 32 x 32 pairs of rows and keys needs. A row with no allowed key gets dq = 0 and delta = 0,
+ * a key no row allows dk = dv = 0.
+ * Arguments as for fa_bwd_masked, plus `blocks` (not NULL); `mask` may be NULL.
+ * Errors: those of fa_bwd_masked; FA_ERR_NULL for a NULL `blocks` or blocks->mask,
+ * FA_ERR_OPTION for a block size that is not a positive multiple of 64 or a negative stride,
+ * FA_ERR_SHAPE for N > 65536.
+ */
+int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse,
+                       void* dq, void* dk, void* dv, float* delta,
+                       int64_t B, int64_t H, int64_t N, int64_t d,
+                       float scale, hipStream_t stream, int dtype, const fa_mask* mask,
+                       const fa_block_mask* blocks);
+
 #ifdef __cplusplus
 }
 #endif

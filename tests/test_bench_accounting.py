@@ -29,4 +29,5 @@ def test_baselines_run_the_matching_oracle():
     m = workloads.make_block_mask(w, 64, 0.5)
     assert "block-sparse oracle" in bench.cpu_baseline(w, blocks=(64, m))["sample"]
     assert "window 31/0" in bench.cpu_baseline_bwd(w, window=(31, 0))["sample"]
+    assert "64x64 block mask" in bench.cpu_baseline_bwd(w, blocks=(64, m))["sample"]
     assert "three-pass" in bench.cpu_baseline(w)["sample"]

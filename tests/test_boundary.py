@@ -30,8 +30,8 @@ def L():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_bwd", "fa_bwd_masked", "fa_fwd", "fa_fwd_blocksparse", "fa_fwd_cpu", "fa_fwd_ex",
-                                     "fa_fwd_masked", "fa_fwd_splitkv",
+    assert _declared_functions() == ["fa_bwd", "fa_bwd_blocksparse", "fa_bwd_masked", "fa_fwd", "fa_fwd_blocksparse",
+                                     "fa_fwd_cpu", "fa_fwd_ex", "fa_fwd_masked", "fa_fwd_splitkv",
                                      "fa_fwd_splitkv_heuristic", "fa_fwd_splitkv_workspace_size", "fa_status_string",
                                      "fa_version"]
 
@@ -254,3 +254,29 @@ def _bwd_masked(mask, **kw):
 ])
 def test_bwd_masked_argument_errors(L, mask, kw, code):
     assert _bwd_masked(mask, **kw) == code
+
+
+BWD_FAR = {name: (i + 1) << 28 for i, name in enumerate(("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv",
+                                                           "delta"))}  # far apart: large N
+
+
+@pytest.mark.parametrize("blocks,mask,kw,code", [
+    (None, None, {}, 1), ((None, 64, 64, 0, 0), None, {}, 1),
+    ((0xC00000, 32, 64, 0, 0), None, {}, 9), ((0xC00000, 64, 96, 0, 0), None, {}, 9),
+    ((0xC00000, 64, 0, 0, 0), None, {}, 9), ((0xC00000, 64, 64, -1, 0), None, {}, 9),
+    ((0xC00000, 64, 64, 0, -8), None, {}, 9), ((0xC00000, 64, 1 << 31, 0, 0), None, {}, 9),
+    ((0xC00000, 64, 64, 0, 0), (-2, 0, None), {}, 9), ((0xC00000, 64, 64, 0, 0), (4, 0, 0x600002), {}, 5),
+    ((0xC00000, 64, 64, 0, 0), None, dict(q=None), 1), ((0xC00000, 64, 64, 0, 0), None, dict(delta=None), 1),
+    ((0xC00000, 64, 64, 0, 0), None, dict(d=96), 3), ((0xC00000, 64, 64, 0, 0), None, dict(dk=0x100000), 7),
+    ((0xC00000, 64, 64, 0, 0), None, dict(scale=-1.0), 6),
+    ((0xC00000, 64, 64, 0, 0), None, dict(N=65537, **BWD_FAR), 2),
+])
+def test_bwd_blocksparse_argument_errors(L, blocks, mask, kw, code):
+    import exact_tiled_softmax_fa_amd as fa
+    a = dict(BWD)
+    a.update(kw)
+    b = None if blocks is None else fa.FaBlockMask(*blocks)
+    m = None if mask is None else fa.FaMask(*mask)
+    assert fa.fa_bwd_blocksparse(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"],
+                                 a["delta"], a["B"], a["H"], a["N"], a["d"], a["scale"], a["stream"], a["dtype"], m,
+                                 b) == code
