@@ -134,11 +134,15 @@ def kernels(workload: str, which: str = "fwd", splits=None, blocks=None):
         part = splits * BH * N * (d + 2) * 4
         return [("fa_fwd_kernel", 2 * per_product, BH * 3 * t + part),
                 ("fa_merge_kernel", 0.0, part + BH * (t + 4 * N))]
-    if which == "fwd" and blocks:
-        # the block-sparse kernel: 4 d flops per allowed (row, key) pair of bench.py's seeded mask
+    if blocks:
+        # the block-sparse kernels: 2 d flops per product and allowed (row, key) pair of bench.py's
+        # seeded mask (forward 2 products, dq 3, dkdv 4)
         m = workloads.make_block_mask(w, blocks[0], blocks[1])
         pairs = workloads.block_mask_pairs(m, N, blocks[0], blocks[0])
-        return [("fa_fwd_kernel", 4.0 * d * BH * pairs, BH * (4 * t + 4 * N))]
+        if which == "fwd":
+            return [("fa_fwd_kernel", 4.0 * d * BH * pairs, BH * (4 * t + 4 * N))]
+        return [("fa_bwd_dq_kernel", 6.0 * d * BH * pairs, BH * (6 * t + 8 * N)),
+                ("fa_bwd_dkdv_kernel", 8.0 * d * BH * pairs, BH * (6 * t + 8 * N))]
     if which == "fwd":
         return [("fa_fwd_kernel", 2 * per_product, BH * (4 * t + 4 * N))]
     return [("fa_bwd_dq_kernel", 3 * per_product, BH * (6 * t + 8 * N)),   # q k v o dO lse -> dq delta
@@ -244,7 +248,8 @@ def main():
     ap.add_argument("--workload", default="B1-H32-N8192-d128-f16")
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"])
     ap.add_argument("--splits", type=int, default=None, help="profile fa_fwd_splitkv with this many splits")
-    ap.add_argument("--block-density", type=float, default=None, help="profile fa_fwd_blocksparse at this density")
+    ap.add_argument("--block-density", type=float, default=None,
+                    help="profile fa_fwd_blocksparse (fa_bwd_blocksparse with --pass bwd) at this density")
     ap.add_argument("--block-size", type=int, default=128, help="block-sparse: rows and keys per block")
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "rocprof"))
     ap.add_argument("--summary-dir", default=os.path.join(ROOT, "gpurun_out", "rocprof"))

@@ -101,3 +101,10 @@ def test_block_sparse_variant():
     assert rh.variant_tag(blocks=(128, 0.25)) == "_blocks128_p0.25" and rh.variant_tag(splits=2) == "_split2"
     for name, prof_args, prog in rh.passes(w.name, "/tmp/x", 5, 2, "fwd", blocks=(128, 0.25)):
         assert prog[prog.index("--block-density") + 1] == "0.25" and prog[prog.index("--block-size") + 1] == "128"
+    # the backward: dq executes 3 products per allowed pair, dkdv 4
+    dq, dkdv = rh.kernels(w.name, "bwd", blocks=(128, 0.25))
+    assert dq[0] == "fa_bwd_dq_kernel" and dkdv[0] == "fa_bwd_dkdv_kernel"
+    assert dq[1] == pytest.approx(6.0 * w.d * w.B * w.H * pairs)
+    assert dkdv[1] == pytest.approx(8.0 * w.d * w.B * w.H * pairs)
+    for name, prof_args, prog in rh.passes(w.name, "/tmp/x", 5, 2, "bwd", blocks=(128, 0.25)):
+        assert prog[prog.index("--pass") + 1] == "bwd" and prog[prog.index("--block-density") + 1] == "0.25"
