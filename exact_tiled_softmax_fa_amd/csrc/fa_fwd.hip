@@ -63,30 +63,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     int bq = 0, int bk = 0, int64_t bstride_b = 0, int64_t bstride_h = 0) {
     static_assert(!(MASKED && (CAUSAL || SPLIT)), "the general mask replaces the causal one and does not split");
     static_assert(!BLOCKS || MASKED, "the block mask rides on the general mask");
-    constexpr int DK = D / 16;                 // k-steps of the first product
-    constexpr int DB = D / 32;                 // 32-column blocks of the output
+    constexpr int DT = D / 32;                 // 32-column k-steps of the first product
+    constexpr int DB = D / 16;                 // 16-column blocks of the output
     constexpr int CPR = D / 8;                 // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;              // rows one wave-wide 1 KiB load covers
     constexpr int IPW = kBlockN / RPI / kWaves;  // such loads per wave per tile (each of K, V)
     constexpr int TILE = kBlockN * D;          // elements per tile
     static_assert(IPW >= 1 && IPW * RPI * kWaves == kBlockN, "tile must split evenly over the waves");
 
-    // Two buffers each for K and V, filled straight from global memory (LDS DMA, lds_load16) in the
-    // swizzled layout; 64 KiB in all at D = 128, so every operand address is a per-lane register
-    // plus an immediate below 64 KiB (the ds_read offset field). (Separate arrays let the
+    // Two buffers for K and up to four for V, filled straight from global memory (LDS DMA,
+    // lds_load16) in the swizzled layout. A ds_read address is a register plus an immediate below
+    // 64 KiB, so a buffer that starts above 64 KiB costs registers of its own for its operand
+    // addresses; the V buffers (each step reads V^T operands at 8 column blocks, K at 4 column
+    // steps) take the larger alignment, which places them first. (Separate arrays let the
     // compiler see that the loads into one buffer never alias the reads of another.)
+    __shared__ __attribute__((aligned(8192))) uint16_t v_lds0[TILE];
+    __shared__ __attribute__((aligned(8192))) uint16_t v_lds1[TILE];
+    __shared__ __attribute__((aligned(8192))) uint16_t v_lds2[TILE];
+    __shared__ __attribute__((aligned(8192))) uint16_t v_lds3[TILE];
     __shared__ __attribute__((aligned(4096))) uint16_t k_lds0[TILE];
     __shared__ __attribute__((aligned(4096))) uint16_t k_lds1[TILE];
-    __shared__ __attribute__((aligned(4096))) uint16_t v_lds0[TILE];
-    __shared__ __attribute__((aligned(4096))) uint16_t v_lds1[TILE];
-    __shared__ __attribute__((aligned(4096))) uint16_t v_lds2[TILE];
-    __shared__ __attribute__((aligned(4096))) uint16_t v_lds3[TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int h = lane >> 5;   // which half of the keys of a 32-key block this lane holds
-    const int lq = lane & 31;  // query row within the wave
+    // 16x16x32 products: lane l holds query column li = l % 16 of the S^T and O^T tiles, and row
+    // group g = l / 16 (tile rows 4g .. 4g + 3; operand k slots 8g .. 8g + 7)
+    const int g = lane >> 4;
+    const int li = lane & 15;
 
     // With SPLIT, a "virtual head" vh = bh * n_split + split takes the place of bh in the map, so
     // the workgroups that share one split's keys of one head sit together on an XCD.
@@ -98,8 +102,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint16_t* Qh = Q + head;
     const uint16_t* Kh = K + head;
     const uint16_t* Vh = V + head;
-    const int wq0 = q0 + 32 * wave;  // first query row of this wave
-    const int qrow = wq0 + lq;       // this lane's query row
+    const int wq0 = q0 + 32 * wave;  // first query row of this wave (two 16-row blocks)
 
     const int kv_end = CAUSAL ? min(N, q0 + kBlockM) : N;
     const int T_all = (kv_end + kBlockN - 1) / kBlockN;  // key tiles of this query tile
@@ -155,164 +158,184 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     // Load g of a tile covers rows RPI*g .. RPI*g+RPI-1; lane l writes LDS bytes [1024 g + 16 l,
     // +16), i.e. row RPI*g + l/CPR at chunk position l % CPR, which holds global chunk
-    // (l % CPR) ^ swz(row). Rows past the end of the sequence repeat row N-1 (finite data; those
-    // keys are masked before they can carry weight).
+    // (l % CPR) ^ swz_k(row) (K tiles) or ^ swz_v(row) (V tiles). Rows past the end of the sequence
+    // repeat row N-1 (finite data; those keys are masked before they can carry weight).
     // Offsets inside one head fit in 32 bits (the host limits N * d * 2 bytes to < 2^31).
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // scalar copy for LDS destinations
-    auto issue = [&](const uint16_t* src_head, int j, uint16_t* dst) __attribute__((always_inline)) {
+    auto issue = [&](const uint16_t* src_head, int j, uint16_t* dst, bool v_tile) __attribute__((always_inline)) {
         const int k0 = (BLOCKS ? t_list[j] : tb + j) * kBlockN;
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
-            const int g = wave_s * IPW + i;
-            const int r = RPI * g + lane / CPR;
-            const int ch = (lane % CPR) ^ swz<D>(r);
+            const int ld = wave_s * IPW + i;
+            const int r = RPI * ld + lane / CPR;
+            const int ch = (lane % CPR) ^ (v_tile ? swz_v<D>(r) : swz_k<D>(r));
             const unsigned src = (unsigned)min(k0 + r, N - 1) * D + 8 * ch;
-            lds_load16(src_head, N * D * 2, 2 * src, (lds_void*)(dst + g * 512));
+            lds_load16(src_head, N * D * 2, 2 * src, (lds_void*)(dst + ld * 512));
         }
     };
 
-    // This lane's query row as the B operand of the first product (columns 16t + 8h .. +7),
-    // held in registers for the whole kernel. Rows past N repeat row N-1 (never stored).
-    u32x4 qreg[D / 16];
-    {
-        const uint16_t* qrp = Qh + (int64_t)min(qrow, N - 1) * D + 8 * h;
+    // The k slots 8g .. 8g + 7 of k-step t of the first product are the columns of 16-byte chunk
+    // t + DT*g (any one-to-one map of (t, g) to chunks sums every column once; with this one the
+    // K operand reads, one chunk per lane group, are free of bank conflicts).
+    // This lane's two query rows (wq0 + li and wq0 + 16 + li, query blocks qb = 0, 1) as B
+    // operands of the first product, held in registers for the whole kernel. Rows past N repeat
+    // row N-1 (never stored).
+    u32x4 qf[2][DT];
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) qreg[t] = *reinterpret_cast<const u32x4*>(qrp + 16 * t);
+    for (int qb = 0; qb < 2; ++qb) {
+        const uint16_t* qrp = Qh + (int64_t)min(wq0 + 16 * qb + li, N - 1) * D + 8 * DT * g;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) qf[qb][t] = *reinterpret_cast<const u32x4*>(qrp + 8 * t);
     }
 
-    f32x16 oacc[DB];
+    // O^T of this wave: block (qb, b) holds columns d = 16b + 4g .. +3 of query row wq0 + 16qb + li
+    f32x4 oacc[2][DB];
 #pragma unroll
-    for (int b = 0; b < DB; ++b) oacc[b] = (f32x16){};
-    unsigned pk[2][8];        // P^T of the tile between its softmax and its product with V
-    float m_run = -INFINITY;  // reference max of raw dot products for l and oacc
-    float l_run = 0.f;        // this lane's half of the running denominator (rounded p)
-    float l_f32 = 0.f;        // the same sum of unrounded p: bf16 keeps 8 mantissa bits, too few
-                              // for lse to 1e-3 on rows with few keys, so lse uses this one
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int b = 0; b < DB; ++b) oacc[qb][b] = (f32x4){};
+    unsigned pk[2][2][4];  // P^T of the tile between its softmax and its product with V: [qb][kk][.]
+    // per query row (qb): reference max of raw dot products for l and oacc, this lane's quarter of
+    // the running denominator (rounded p), and the same sum of unrounded p (bf16 keeps 8 mantissa
+    // bits, too few for lse to 1e-3 on rows with few keys, so lse uses that one)
+    float m_run[2] = {-INFINITY, -INFINITY};
+    float l_run[2] = {0.f, 0.f};
+    float l_f32[2] = {0.f, 0.f};
 
-    // LDS operand addresses (elements). The swizzle depends on row & 15 only, so moving 16 rows
-    // down a tile is the constant offset 16*D: one address per k-step serves both 32-key halves
-    // of the K tile, and one per column block serves all four 16-key steps of the V tile.
-    int koff[DK];
+    // LDS operand addresses (elements). Both swizzles depend on row & 15 only, so moving 16 rows
+    // down a tile is the constant offset 16*D: one address per k-step serves the four 16-key
+    // blocks of the K tile, and one per column block serves both 32-key steps of the V tile.
+    int koff[DT];
 #pragma unroll
-    for (int t = 0; t < DK; ++t) koff[t] = tile_off<D>(lq, 2 * t + h);
-    // ds_read_b64_tr_b16 source pattern: within each 16-lane group, lane s reads 4 consecutive
-    // columns 4*(s%4).. of key row s/4; the instruction hands lane i element e of that 4x16
-    // block as (key row e, column i), i.e. one V^T row of 4 keys per lane. The upper 4 keys of
-    // each 8 come from rows + 8.
-    int voff_lo[DB], voff_hi[DB];
-    {
-        const int s16 = lane & 15;
-        const int tr_row = 4 * h + (s16 >> 2);
-        const int tr_chunk = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
-        const int tr_half = 4 * (s16 & 1);
+    for (int t = 0; t < DT; ++t) koff[t] = tile_off_k<D>(li, t + DT * g);
+    // ds_read_b64_tr_b16: within each 16-lane group, lane i receives element e from the 4 values
+    // lane 4e + i/4 points at, position i % 4. Lane s of group g points at key row 4g + s/4,
+    // columns 16b + 4(s % 4) .. +3, so lane i receives V[4g + e][16b + i] for e = 0..3: one V^T
+    // row (column d = 16b + i) over 4 keys. The second read takes keys 16 + 4g .. +3.
+    int voff[DB];
 #pragma unroll
-        for (int b = 0; b < DB; ++b) {
-            voff_lo[b] = tile_off<D>(tr_row, 4 * b + tr_chunk) + tr_half;
-            voff_hi[b] = tile_off<D>(tr_row + 8, 4 * b + tr_chunk) + tr_half;
-        }
-    }
+    for (int b = 0; b < DB; ++b) voff[b] = tile_off_v<D>(4 * g + (li >> 2), 2 * b + ((li & 3) >> 1)) + 4 * (li & 1);
+    // A operand of S^T: keys 16kb + li, chunk t + DT*g
     auto k_operand = [&](const uint16_t* kt, int t, int kb) __attribute__((always_inline)) {
-        return *reinterpret_cast<const u32x4*>(kt + koff[t] + kb * 32 * D);
+        return *reinterpret_cast<const u32x4*>(kt + koff[t] + kb * 16 * D);
     };
+    // A operand of O^T: V^T rows d = 16b + li; its k slots 8g + s are keys 32kk + 4g + s (s < 4)
+    // and 32kk + 16 + 4g + s - 4 (s >= 4), the order in which this lane holds P^T
     auto v_operand = [&](const uint16_t* vt, int kk, int b) __attribute__((always_inline)) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + voff_lo[b] + kk * 16 * D));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + voff_hi[b] + kk * 16 * D));
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + voff[b] + kk * 32 * D));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + voff[b] + kk * 32 * D + 16 * D));
         const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
         const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
         return (u32x4){lo2[0], lo2[1], hi2[0], hi2[1]};
     };
-    // Q^T (B operand of the first product): lane holds row qrow, columns 16t + 8h .. +7.
-    auto q_operand = [&](int t) __attribute__((always_inline)) {
-        return qreg[t];
-    };
-    auto p_operand = [&](int kk) __attribute__((always_inline)) {
-        const int kb = kk >> 1, hf = kk & 1;
-        return (u32x4){pk[kb][4 * hf + 0], pk[kb][4 * hf + 1], pk[kb][4 * hf + 2], pk[kb][4 * hf + 3]};
+    // B operand of O^T: P^T of query block qb over the 32 keys of step kk
+    auto p_operand = [&](int qb, int kk) __attribute__((always_inline)) {
+        return (u32x4){pk[qb][kk][0], pk[qb][kk][1], pk[qb][kk][2], pk[qb][kk][3]};
     };
 
     // ---- the pieces of one tile's work ----
-    f32x16 s0[2], s1[2];  // S^T of two consecutive tiles: one being produced, one being consumed
-    float mc = 0.f;       // m_run * c with m_run the current reference (0 while m_run = -inf)
+    // S^T of two consecutive tiles (one being produced, one being consumed): [qb][kb] holds keys
+    // 16kb + 4g .. +3 of query row wq0 + 16qb + li
+    f32x4 s0[2][4], s1[2][4];
+    float mc[2] = {0.f, 0.f};  // m_run * c with m_run the current reference (0 while m_run = -inf)
 
-    // S^T(t) = K(t) . Q^T into s (16 MFMAs for D = 128; K and Q operands from LDS)
-    auto qk = [&](const uint16_t* kt, f32x16 (&sd)[2]) __attribute__((always_inline)) {
+    // S^T(t) = K(t) . Q^T into s (32 MFMAs for D = 128; each K operand feeds both query blocks)
+    auto qk = [&](const uint16_t* kt, f32x4 (&sd)[2][4]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 2 * DK; ++i) {
-            const int t = i >> 1, kb = i & 1;
-            sd[kb] = mfma32<BF16>(k_operand(kt, t, kb), q_operand(t), t == 0 ? (f32x16){} : sd[kb]);
+        for (int i = 0; i < 4 * DT; ++i) {
+            const int t = i >> 2, kb = i & 3;
+            const u32x4 a = k_operand(kt, t, kb);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) sd[qb][kb] = mfma16<BF16>(a, qf[qb][t], t == 0 ? (f32x4){} : sd[qb][kb]);
         }
     };
-    // O^T += V(t)^T . P^T (16 MFMAs for D = 128; V^T operand from LDS transpose reads)
+    // O^T += V(t)^T . P^T (32 MFMAs for D = 128; each V^T operand feeds both query blocks)
     auto pv = [&](const uint16_t* vt) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4 * DB; ++i) {
+        for (int i = 0; i < 2 * DB; ++i) {
             const int kk = i / DB, b = i % DB;
-            oacc[b] = mfma32<BF16>(v_operand(vt, kk, b), p_operand(kk), oacc[b]);
+            const u32x4 a = v_operand(vt, kk, b);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) oacc[qb][b] = mfma16<BF16>(a, p_operand(qb, kk), oacc[qb][b]);
         }
     };
     // keys past the end, and (causal) keys after the query, become -inf before the max
-    auto mask = [&](int t, f32x16 (&sd)[2]) __attribute__((always_inline)) {
+    auto mask = [&](int t, f32x4 (&sd)[2][4]) __attribute__((always_inline)) {
         const int k0 = (BLOCKS ? t_list[t] : tb + t) * kBlockN;
         if constexpr (MASKED) {
             if ((k0 + kBlockN > kv_len) || (wr >= 0 && k0 + kBlockN - 1 > wq0 + wr) ||
                 (wl >= 0 && k0 < wq0 + 31 - wl)) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                        if (key >= kv_len || (wr >= 0 && key > qrow + wr) || (wl >= 0 && key < qrow - wl))
-                            sd[kb][r] = -INFINITY;
-                    }
+                    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int key = k0 + 16 * kb + 4 * g + r, qrow = wq0 + 16 * qb + li;
+                            if (key >= kv_len || (wr >= 0 && key > qrow + wr) || (wl >= 0 && key < qrow - wl))
+                                sd[qb][kb][r] = -INFINITY;
+                        }
             }
             return;
         }
         if ((k0 + kBlockN > N) || (CAUSAL && k0 + kBlockN - 1 > wq0)) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    if (key >= N || (CAUSAL && key > qrow)) sd[kb][r] = -INFINITY;
-                }
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int key = k0 + 16 * kb + 4 * g + r, qrow = wq0 + 16 * qb + li;
+                        if (key >= N || (CAUSAL && key > qrow)) sd[qb][kb][r] = -INFINITY;
+                    }
         }
     };
-    auto row_max = [&](const f32x16 (&sd)[2]) __attribute__((always_inline)) {
-        float mx = fmaxf(sd[0][0], sd[0][1]);
+    // Move the reference max of each row (and rescale l, o~ by alpha = exp(m_old - m_new)) only
+    // when some row of the wave has a score more than tau above its reference; otherwise p stays
+    // <= 2^tau_log2. mx0, mx1: the rows' maxima over the tile (reduced over the four lane rows).
+    auto rebase = [&](float mx0, float mx1) __attribute__((always_inline)) {
+        if (__builtin_amdgcn_ballot_w64(mx0 > m_run[0] + tau_raw || mx1 > m_run[1] + tau_raw)) {
+            const float mx[2] = {mx0, mx1};
 #pragma unroll
-        for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sd[0][r]);
+            for (int qb = 0; qb < 2; ++qb) {
+                const float m_new = fmaxf(m_run[qb], mx[qb]);
+                const float alpha = (m_new == m_run[qb]) ? 1.f : __builtin_amdgcn_exp2f((m_run[qb] - m_new) * c);
+                l_run[qb] *= alpha;
+                if constexpr (BF16) l_f32[qb] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sd[1][r]);
-        return max_with_partner(mx);
-    };
-    // Move the reference max (and rescale l, o~ by alpha = exp(m_old - m_new)) only when some row
-    // of the wave has a score more than tau above it; otherwise p stays <= 2^tau_log2.
-    auto rebase = [&](float mx) __attribute__((always_inline)) {
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + tau_raw)) {
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
-            l_run *= alpha;
-            if constexpr (BF16) l_f32 *= alpha;
+                for (int b = 0; b < DB; ++b)
 #pragma unroll
-            for (int b = 0; b < DB; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
-            m_run = m_new;
-            mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-        }
-    };
-    // p = exp2(s*c - m*c), rounded to the operand type; row sum of the rounded values
-    auto expo = [&](const f32x16 (&sd)[2]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(sd[kb][r], c, -mc));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(sd[kb][r + 1], c, -mc));
-                pk[kb][r >> 1] = pack2<BF16>(p0, p1);
-                l_run = add_pair<BF16>(pk[kb][r >> 1], l_run);
-                if constexpr (BF16) l_f32 += p0 + p1;
+                    for (int r = 0; r < 4; ++r) oacc[qb][b][r] *= alpha;
+                m_run[qb] = m_new;
+                mc[qb] = (m_new == -INFINITY) ? 0.f : m_new * c;
             }
+        }
+    };
+    auto rebase_from = [&](const f32x4 (&sd)[2][4]) __attribute__((always_inline)) {
+        float mx[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            float m = fmaxf(sd[qb][0][0], sd[qb][0][1]);
+#pragma unroll
+            for (int e = 2; e < 16; ++e) m = fmaxf(m, sd[qb][e >> 2][e & 3]);
+            mx[qb] = max_over_rows(m);
+        }
+        rebase(mx[0], mx[1]);
+    };
+    // exponential pair pr (0..15) of S^T: p = exp2(s*c - m*c), rounded to the operand type, and the
+    // row sum of the rounded values. Pair pr = 8qb + 2kb + r/2 lands in pk[qb][kb/2][2(kb%2) + r/2].
+    auto exp_pair = [&](const f32x4 (&sd)[2][4], int pr) __attribute__((always_inline)) {
+        const int qb = pr >> 3, kb = (pr >> 1) & 3, r = 2 * (pr & 1);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sd[qb][kb][r], c, -mc[qb]));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sd[qb][kb][r + 1], c, -mc[qb]));
+        unsigned& dst = pk[qb][kb >> 1][2 * (kb & 1) + (r >> 1)];
+        dst = pack2<BF16>(p0, p1);
+        l_run[qb] = add_pair<BF16>(dst, l_run[qb]);
+        if constexpr (BF16) l_f32[qb] += p0 + p1;
+    };
+    auto expo = [&](const f32x4 (&sd)[2][4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int pr = 0; pr < 16; ++pr) exp_pair(sd, pr);
     };
 
     // ---- schedule ----
@@ -331,21 +354,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         // (scores, mask, max, exponentials, product with V) only when its own bit is set, so the
         // waves of a workgroup whose query blocks differ skip each other's tiles; the two waves
         // of a SIMD still overlap each other's matrix and vector work.
-        issue(Kh, 0, k_lds0);
-        issue(Vh, 0, v_lds0);
+        issue(Kh, 0, k_lds0, false);
+        issue(Vh, 0, v_lds0, true);
         const int wbit = 1 << wave_s;
         auto tile = [&](int j, const uint16_t* kt, const uint16_t* vt, uint16_t* kn, uint16_t* vn)
                         __attribute__((always_inline)) {
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();  // barrier j
             if (j + 1 < T) {
-                issue(Kh, j + 1, kn);
-                issue(Vh, j + 1, vn);
+                issue(Kh, j + 1, kn, false);
+                issue(Vh, j + 1, vn, true);
             }
             if (__builtin_amdgcn_readfirstlane(t_wm[j]) & wbit) {
                 qk(kt, s0);
                 mask(j, s0);
-                rebase(row_max(s0));
+                rebase_from(s0);
                 expo(s0);
                 pv(vt);
             }
@@ -356,98 +379,96 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             tile(j + 1, k_lds1, v_lds1, k_lds0, v_lds0);
         }
     } else {
-        issue(Kh, 0, k_lds0);
-        issue(Vh, 0, v_lds0);
-        if (T > 1) issue(Kh, 1, k_lds1);
+        issue(Kh, 0, k_lds0, false);
+        issue(Vh, 0, v_lds0, true);
+        if (T > 1) issue(Kh, 1, k_lds1, false);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (T_w0 < T_w && T_w0 == 0) {
             qk(k_lds0, s0);
             mask(0, s0);
-            rebase(row_max(s0));
+            rebase_from(s0);
         }
         // region 1 of tile j: S^T(j+1) = K(j+1) . Q^T with the exponentials of tile j in between.
-        auto region1 = [&](f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], const uint16_t* k_nxt) __attribute__((always_inline)) {
-            // Explicit software pipeline: the LDS operands of MFMA i + 2 are read before MFMA i
-            // issues, and one pair of exponentials follows each MFMA; sched_barrier(0) pins that
-            // order so the LDS latency stays behind two MFMAs instead of stalling every one.
-            constexpr int NQ = 2 * DK;  // 16 MFMAs for D = 128, 8 for D = 64
-            u32x4 ka[NQ];
+        auto region1 = [&](f32x4 (&s_cur)[2][4], f32x4 (&s_nxt)[2][4], const uint16_t* k_nxt) __attribute__((always_inline)) {
+            // Explicit software pipeline: the LDS operand of K step i + 2 is read before the two
+            // MFMAs of step i issue, and the 16 pairs of exponentials are spread over the steps;
+            // sched_barrier(0) pins that order so the LDS latency stays behind the MFMAs.
+            constexpr int NK = 4 * DT;  // K operands: 16 for D = 128, 8 for D = 64
+            constexpr int PPS = 16 / NK;  // exponential pairs per step: 1 (after the first MFMA) or 2
+            static_assert(PPS == 1 || PPS == 2, "one or two pairs of exponentials per step");
+            u32x4 ka[NK];
             ka[0] = k_operand(k_nxt, 0, 0);
             ka[1] = k_operand(k_nxt, 0, 1);
 #pragma unroll
-            for (int i = 0; i < NQ; ++i) {
-                const int t = i >> 1, kb = i & 1;
-                if (i + 2 < NQ) {
-                    const int t2 = (i + 2) >> 1, kb2 = (i + 2) & 1;
-                    ka[i + 2] = k_operand(k_nxt, t2, kb2);
-                }
+            for (int i = 0; i < NK; ++i) {
+                const int t = i >> 2, kb = i & 3;
+                if (i + 2 < NK) ka[i + 2] = k_operand(k_nxt, (i + 2) >> 2, (i + 2) & 3);
                 __builtin_amdgcn_sched_barrier(0);
-                s_nxt[kb] = mfma32<BF16>(ka[i], qreg[t], t == 0 ? (f32x16){} : s_nxt[kb]);
-                __builtin_amdgcn_sched_barrier(0);
-                // exponentials: pair i of the 16 pairs of S^T(j) held by this lane (NQ == 16),
-                // or pairs 2i, 2i+1 when D = 64 (NQ == 8)
 #pragma unroll
-                for (int u = 0; u < 16 / NQ; ++u) {
-                    const int pr = i * (16 / NQ) + u;  // pair index 0..15
-                    const int kbp = pr >> 3, r = 2 * (pr & 7);
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[kbp][r], c, -mc));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[kbp][r + 1], c, -mc));
-                    pk[kbp][r >> 1] = pack2<BF16>(p0, p1);
-                    l_run = add_pair<BF16>(pk[kbp][r >> 1], l_run);
-                    if constexpr (BF16) l_f32 += p0 + p1;
+                for (int qb = 0; qb < 2; ++qb) {
+                    s_nxt[qb][kb] = mfma16<BF16>(ka[i], qf[qb][t], t == 0 ? (f32x4){} : s_nxt[qb][kb]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (PPS == 2 || qb == 0) exp_pair(s_cur, i * PPS + qb);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
             // Keep the exponentials in region 1: without this the compiler sinks them past the
             // mask branch into region 2, next to their only consumer.
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
-                for (int r = 0; r < 8; ++r) asm volatile("" : "+v"(pk[kb][r]));
-            asm volatile("" : "+v"(l_run));
-            if constexpr (BF16) asm volatile("" : "+v"(l_f32));
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(pk[qb][kk][r]));
+                asm volatile("" : "+v"(l_run[qb]));
+                if constexpr (BF16) asm volatile("" : "+v"(l_f32[qb]));
+            }
         };
         // region 2 of tile j: O^T += V(j)^T . P^T(j) with the row max of S^T(j+1) in between, then
         // the move of the reference max for tile j+1.
-        auto region2 = [&](f32x16 (&s_nxt)[2], const uint16_t* v_cur) __attribute__((always_inline)) {
-            // V^T operands read two MFMAs ahead.
-            constexpr int NP = 4 * DB;  // 16 MFMAs for D = 128, 8 for D = 64
-            u32x4 va[NP];
+        auto region2 = [&](f32x4 (&s_nxt)[2][4], const uint16_t* v_cur) __attribute__((always_inline)) {
+            // V^T operands read two steps ahead.
+            constexpr int NV = 2 * DB;  // V^T operands: 16 for D = 128, 8 for D = 64
+            constexpr int EPS = 32 / NV;  // scores scanned for the max per step
+            u32x4 va[NV];
             va[0] = v_operand(v_cur, 0, 0);
             va[1] = v_operand(v_cur, 1 / DB, 1 % DB);
-            float mx = -INFINITY;
+            float mx[2] = {-INFINITY, -INFINITY};
 #pragma unroll
-            for (int i = 0; i < NP; ++i) {
+            for (int i = 0; i < NV; ++i) {
                 const int kk = i / DB, b = i % DB;
-                if (i + 2 < NP) va[i + 2] = v_operand(v_cur, (i + 2) / DB, (i + 2) % DB);
+                if (i + 2 < NV) va[i + 2] = v_operand(v_cur, (i + 2) / DB, (i + 2) % DB);
                 __builtin_amdgcn_sched_barrier(0);
-                oacc[b] = mfma32<BF16>(va[i], p_operand(kk), oacc[b]);
-                __builtin_amdgcn_sched_barrier(0);
-                // row max: the 32 scores of this lane, 32 / NP per MFMA
 #pragma unroll
-                for (int u = 0; u < 32 / NP; ++u) {
-                    const int e = i * (32 / NP) + u;
-                    mx = fmaxf(mx, s_nxt[e >> 4][e & 15]);
+                for (int qb = 0; qb < 2; ++qb) {
+                    oacc[qb][b] = mfma16<BF16>(va[i], p_operand(qb, kk), oacc[qb][b]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                // row max: the 32 scores of this lane, EPS per step (score e = 16qb + 4kb + r)
+#pragma unroll
+                for (int u = 0; u < EPS; ++u) {
+                    const int e = i * EPS + u;
+                    mx[e >> 4] = fmaxf(mx[e >> 4], s_nxt[e >> 4][(e >> 2) & 3][e & 3]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            rebase(max_with_partner(mx));
+            rebase(max_over_rows(mx[0]), max_over_rows(mx[1]));
         };
         if constexpr (MASKED) {
             // every wave: barrier, loads, region 1, region 2 (V in two buffers)
-            auto iteration = [&](int j, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], const uint16_t* k_nxt,
+            auto iteration = [&](int j, f32x4 (&s_cur)[2][4], f32x4 (&s_nxt)[2][4], const uint16_t* k_nxt,
                                  const uint16_t* v_cur, uint16_t* k_load, uint16_t* v_load) __attribute__((always_inline)) {
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();
-                if (j + 2 < T) issue(Kh, j + 2, k_load);
-                if (j + 1 < T) issue(Vh, j + 1, v_load);
+                if (j + 2 < T) issue(Kh, j + 2, k_load, false);
+                if (j + 1 < T) issue(Vh, j + 1, v_load, true);
                 if (j < T_w0) {
                     // before this wave's first tile: at most start the pipeline with S^T(j+1)
                     if (j + 1 == T_w0 && j + 1 < T_w) {
                         qk(k_nxt, s_nxt);
                         mask(j + 1, s_nxt);
-                        rebase(row_max(s_nxt));
+                        rebase_from(s_nxt);
                     }
                 } else if (j + 1 < T_w) {
                     region1(s_cur, s_nxt, k_nxt);
@@ -476,12 +497,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             // tile j-1 in waves 4-7, and waits for them at the top of the next step: one
             // unconditional wait, so the compiler sees no path on which a read could overtake them.
             const bool lag = wave_s >= kWaves / 2;
-            auto step = [&](int j, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], uint16_t* k_cur, const uint16_t* k_nxt,
+            auto step = [&](int j, f32x4 (&s_cur)[2][4], f32x4 (&s_nxt)[2][4], uint16_t* k_cur, const uint16_t* k_nxt,
                             const uint16_t* v_cur, uint16_t* v_p1) __attribute__((always_inline)) {
                 __builtin_amdgcn_s_waitcnt(0);
                 if (!lag) __syncthreads();  // barrier j
-                if (j + 2 < T) issue(Kh, j + 2, k_cur);
-                if (j + 1 < T) issue(Vh, j + 1, v_p1);
+                if (j + 2 < T) issue(Kh, j + 2, k_cur, false);
+                if (j + 1 < T) issue(Vh, j + 1, v_p1, true);
                 if (j + 1 < T_w) {
                     region1(s_cur, s_nxt, k_nxt);
                     mask(j + 1, s_nxt);
@@ -513,50 +534,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
     }
 
-    // ---- epilogue: O = o~ / l, lse = m*scale + ln l ----
-    const float l_tot = sum_with_partner(l_run);
-    const float l_lse = BF16 ? sum_with_partner(l_f32) : l_tot;  // both halves active here
-    if constexpr (SPLIT) {
-        // partial result over this split's keys; a row none of whose keys fall in the split
-        // (l = 0) gets O = 0 and lse = -inf, i.e. zero weight in the merge
-        if (qrow < N) {
-            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-            float* prow = PO + ((int64_t)vh * N + qrow) * D;
+    // ---- epilogue: O = o~ / l, lse = m*scale + ln l, per query row (qb) ----
 #pragma unroll
-            for (int b = 0; b < DB; ++b)
+    for (int qb = 0; qb < 2; ++qb) {
+        const int qrow = wq0 + 16 * qb + li;
+        const float l_tot = sum_over_rows(l_run[qb]);
+        const float l_lse = BF16 ? sum_over_rows(l_f32[qb]) : l_tot;  // every lane active here
+        const float mcf = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb] * c;
+        if constexpr (SPLIT) {
+            // partial result over this split's keys; a row none of whose keys fall in the split
+            // (l = 0) gets O = 0 and lse = -inf, i.e. zero weight in the merge
+            if (qrow < N) {
+                const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+                float* prow = PO + ((int64_t)vh * N + qrow) * D;
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const float4 st = {oacc[b][4 * g + 0] * inv, oacc[b][4 * g + 1] * inv,
-                                       oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv};
-                    *reinterpret_cast<float4*>(prow + b * 32 + 8 * g + 4 * h) = st;
+                for (int b = 0; b < DB; ++b) {
+                    const float4 st = {oacc[qb][b][0] * inv, oacc[qb][b][1] * inv, oacc[qb][b][2] * inv,
+                                       oacc[qb][b][3] * inv};
+                    *reinterpret_cast<float4*>(prow + 16 * b + 4 * g) = st;
                 }
-            if (h == 0) {
-                // [0]: log-sum-exp of the denominator O was normalised by (the merge weights);
-                // [1]: of the unrounded sum (the final lse; the same value in f16)
-                const float mcf = (m_run == -INFINITY) ? 0.f : m_run * c;
-                const float2 ls = {l_tot > 0.f ? (mcf + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY,
-                                   l_lse > 0.f ? (mcf + __log2f(l_lse)) * 0.69314718055994531f : -INFINITY};
-                *reinterpret_cast<float2*>(PL + 2 * ((int64_t)vh * N + qrow)) = ls;
+                if (g == 0) {
+                    // [0]: log-sum-exp of the denominator O was normalised by (the merge weights);
+                    // [1]: of the unrounded sum (the final lse; the same value in f16)
+                    const float2 ls = {l_tot > 0.f ? (mcf + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY,
+                                       l_lse > 0.f ? (mcf + __log2f(l_lse)) * 0.69314718055994531f : -INFINITY};
+                    *reinterpret_cast<float2*>(PL + 2 * ((int64_t)vh * N + qrow)) = ls;
+                }
             }
-        }
-        return;
-    }
-    if (qrow < N) {
-        // (MASKED: a row with no allowed key has l = 0: o = 0, lse = -inf)
-        const float inv = (!MASKED || l_tot > 0.f) ? 1.f / l_tot : 0.f;
-        uint16_t* orow = O + head + (int64_t)qrow * D;
+        } else if (qrow < N) {
+            // (MASKED: a row with no allowed key has l = 0: o = 0, lse = -inf)
+            const float inv = (!MASKED || l_tot > 0.f) ? 1.f / l_tot : 0.f;
+            uint16_t* orow = O + head + (int64_t)qrow * D;
 #pragma unroll
-        for (int b = 0; b < DB; ++b)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const u32x2 st = {pack2<BF16>(oacc[b][4 * g + 0] * inv, oacc[b][4 * g + 1] * inv),
-                                  pack2<BF16>(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv)};
-                *reinterpret_cast<u32x2*>(orow + b * 32 + 8 * g + 4 * h) = st;
+            for (int b = 0; b < DB; ++b) {
+                const u32x2 st = {pack2<BF16>(oacc[qb][b][0] * inv, oacc[qb][b][1] * inv),
+                                  pack2<BF16>(oacc[qb][b][2] * inv, oacc[qb][b][3] * inv)};
+                *reinterpret_cast<u32x2*>(orow + 16 * b + 4 * g) = st;
             }
-        if (LSE != nullptr && h == 0) {
-            const float mcf = (m_run == -INFINITY) ? 0.f : m_run * c;
-            LSE[(int64_t)bh * N + qrow] = (!MASKED || l_lse > 0.f) ? (mcf + __log2f(l_lse)) * 0.69314718055994531f
-                                                                    : -INFINITY;
+            if (LSE != nullptr && g == 0)
+                LSE[(int64_t)bh * N + qrow] = (!MASKED || l_lse > 0.f) ? (mcf + __log2f(l_lse)) * 0.69314718055994531f
+                                                                       : -INFINITY;
         }
     }
 }
