@@ -201,6 +201,21 @@ def variant_tag(splits=None, blocks=None) -> str:
     return (f"_split{splits}" if splits else "") + (f"_blocks{blocks[0]}_p{blocks[1]}" if blocks else "")
 
 
+def clock_line(rec: dict) -> str:
+    """The sustained-clock line of a summary. The cycle count comes from the short counter run and
+    the time from the trace run; when they cannot belong together (no matrix work, or a clock
+    above the part's maximum) the line says so instead of giving a number."""
+    ghz = rec["clock_ghz"]
+    if rec["mfma_flop_per_launch"] <= 0:
+        return ("- sustained clock: not given (no matrix work; for a kernel this short the cycle count of a "
+                "separate run does not pair with the trace)")
+    if ghz > 1.02 * PEAK_CLOCK_GHZ:
+        return (f"- sustained clock: not given (the counter run's cycles over the trace's time give {ghz:.2f} GHz, "
+                f"above the {PEAK_CLOCK_GHZ} GHz maximum: the two runs do not pair for this kernel)")
+    return (f"- sustained clock: {ghz:.2f} GHz; dense MFMA peak at that clock: "
+            f"{PEAK_TFLOPS * ghz / PEAK_CLOCK_GHZ:.0f} TFLOP/s (of {PEAK_TFLOPS} at {PEAK_CLOCK_GHZ} GHz)")
+
+
 def write_summary(rec: dict, summary_dir: str):
     os.makedirs(summary_dir, exist_ok=True)
     name = f"{rec['kernel']}_{rec['workload']}" + variant_tag(rec.get("splits"), rec.get("blocks"))
@@ -229,11 +244,7 @@ def write_summary(rec: dict, summary_dir: str):
         "## Matrix cores (SQ_INSTS_VALU_MFMA_MOPS_*, SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE)", "",
         f"- MFMA work per launch: {rec['mfma_flop_per_launch']:.4e} flop",
         f"- MFMA busy: **{100 * rec['mfma_busy_fraction']:.1f} %** of elapsed cycles",
-        (f"- sustained clock: {rec['clock_ghz']:.2f} GHz; dense MFMA peak at that clock: "
-         f"{PEAK_TFLOPS * rec['clock_ghz'] / PEAK_CLOCK_GHZ:.0f} TFLOP/s (of {PEAK_TFLOPS} at {PEAK_CLOCK_GHZ} GHz)"
-         if rec["mfma_flop_per_launch"] > 0 else
-         "- sustained clock: not given (no matrix work; for a kernel this short the cycle count of a separate "
-         "run does not pair with the trace)"), "",
+        clock_line(rec), "",
     ]
     with open(os.path.join(summary_dir, name + ".md"), "w") as f:
         f.write("\n".join(lines))

@@ -108,3 +108,10 @@ def test_block_sparse_variant():
     assert dkdv[1] == pytest.approx(8.0 * w.d * w.B * w.H * pairs)
     for name, prof_args, prog in rh.passes(w.name, "/tmp/x", 5, 2, "bwd", blocks=(128, 0.25)):
         assert prog[prog.index("--pass") + 1] == "bwd" and prog[prog.index("--block-density") + 1] == "0.25"
+
+
+def test_clock_line_refuses_impossible_pairings():
+    base = {"mfma_flop_per_launch": 1e12}
+    assert "2.10 GHz" in rh.clock_line(dict(base, clock_ghz=2.1))
+    assert "not given" in rh.clock_line(dict(base, clock_ghz=2.57)) and "2.57" in rh.clock_line(dict(base, clock_ghz=2.57))
+    assert "no matrix work" in rh.clock_line({"mfma_flop_per_launch": 0.0, "clock_ghz": 4.0})
