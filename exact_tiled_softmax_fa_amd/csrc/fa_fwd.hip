@@ -25,7 +25,10 @@
 // mechanism of "FlashAttention tiles exact softmax without materializing the score matrix"
 // (nalar.dev), sections "A score tile is temporary state" and "IO behavior is the mechanism".
 // Fewer rescales (a wave skips the alpha multiply when no row's max moved) follow the
-// FlashAttention-2 remark on "Decoding flash attention" (bibekananda.in), "Later versions".
+// FlashAttention-2 remark on "Decoding flash attention" (bibekananda.in), "Later versions". The
+// rescaling identity holds for any reference value, so the reference need not be the running
+// max: the default kernel keeps every unnormalised p within 2^tau and tests that on the tile
+// sums it forms anyway, instead of taking a max over every tile.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -201,6 +204,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     float m_run[2] = {-INFINITY, -INFINITY};
     float l_run[2] = {0.f, 0.f};
     float l_f32[2] = {0.f, 0.f};
+    // the current tile's part of l_run and l_f32, added once the tile is accepted (settle)
+    float l_tile[2] = {0.f, 0.f};
+    float lf_tile[2] = {0.f, 0.f};
+    // bound on every unnormalised p: 2^tau_log2 (tau_raw is tau_log2 in raw score units)
+    const float p_cap = __builtin_amdgcn_exp2f(tau_raw * c);
+    // a moved reference sits this far above the maximum that moved it (0 for tau = 0, where it is
+    // the exact running maximum), so later scores must rise by more before it moves again
+    const float headroom = 0.5f * tau_raw;
 
     // LDS operand addresses (elements). Both swizzles depend on row & 15 only, so moving 16 rows
     // down a tile is the constant offset 16*D: one address per k-step serves the four 16-key
@@ -290,15 +301,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     }
         }
     };
-    // Move the reference max of each row (and rescale l, o~ by alpha = exp(m_old - m_new)) only
-    // when some row of the wave has a score more than tau above its reference; otherwise p stays
-    // <= 2^tau_log2. mx0, mx1: the rows' maxima over the tile (reduced over the four lane rows).
-    auto rebase = [&](float mx0, float mx1) __attribute__((always_inline)) {
-        if (__builtin_amdgcn_ballot_w64(mx0 > m_run[0] + tau_raw || mx1 > m_run[1] + tau_raw)) {
+    // Move the reference max of each row (and rescale l, o~ by alpha = exp(m_old - m_new)) when
+    // `force`, or when some row of the wave has a score more than tau above its reference;
+    // otherwise p stays <= 2^tau_log2. mx0, mx1: the rows' maxima over the tile (reduced over the
+    // four lane rows). The new reference is the larger of the old one and max + headroom.
+    auto rebase = [&](float mx0, float mx1, bool force) __attribute__((always_inline)) {
+        if (force || __builtin_amdgcn_ballot_w64(mx0 > m_run[0] + tau_raw || mx1 > m_run[1] + tau_raw)) {
             const float mx[2] = {mx0, mx1};
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
-                const float m_new = fmaxf(m_run[qb], mx[qb]);
+                const float m_new = fmaxf(m_run[qb], mx[qb] + headroom);
                 const float alpha = (m_new == m_run[qb]) ? 1.f : __builtin_amdgcn_exp2f((m_run[qb] - m_new) * c);
                 l_run[qb] *= alpha;
                 if constexpr (BF16) l_f32[qb] *= alpha;
@@ -311,7 +323,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
         }
     };
-    auto rebase_from = [&](const f32x4 (&sd)[2][4]) __attribute__((always_inline)) {
+    auto rebase_from = [&](const f32x4 (&sd)[2][4], bool force) __attribute__((always_inline)) {
         float mx[2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
@@ -320,7 +332,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             for (int e = 2; e < 16; ++e) m = fmaxf(m, sd[qb][e >> 2][e & 3]);
             mx[qb] = max_over_rows(m);
         }
-        rebase(mx[0], mx[1]);
+        rebase(mx[0], mx[1], force);
     };
     // exponential pair pr (0..15) of S^T: p = exp2(s*c - m*c), rounded to the operand type, and the
     // row sum of the rounded values. Pair pr = 8qb + 2kb + r/2 lands in pk[qb][kb/2][2(kb%2) + r/2].
@@ -330,12 +342,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const float p1 = __builtin_amdgcn_exp2f(fmaf(sd[qb][kb][r + 1], c, -mc[qb]));
         unsigned& dst = pk[qb][kb >> 1][2 * (kb & 1) + (r >> 1)];
         dst = pack2<BF16>(p0, p1);
-        l_run[qb] = add_pair<BF16>(dst, l_run[qb]);
-        if constexpr (BF16) l_f32[qb] += p0 + p1;
+        l_tile[qb] = add_pair<BF16>(dst, l_tile[qb]);
+        if constexpr (BF16) lf_tile[qb] += p0 + p1;
     };
     auto expo = [&](const f32x4 (&sd)[2][4]) __attribute__((always_inline)) {
 #pragma unroll
+        for (int qb = 0; qb < 2; ++qb) l_tile[qb] = lf_tile[qb] = 0.f;
+#pragma unroll
         for (int pr = 0; pr < 16; ++pr) exp_pair(sd, pr);
+    };
+    // Accept the exponentials of a tile (taken against the current reference) when no lane's sum
+    // of a row's values exceeds 2^tau_log2: then no single p does either, the bound the reference
+    // max exists to keep. Otherwise (rare: the scores rose past the reference, or a row has no
+    // reference yet) move the reference to the running max and take them again. This replaces a
+    // max over every tile by a test on sums the softmax forms anyway.
+    auto settle = [&](const f32x4 (&sd)[2][4]) __attribute__((always_inline)) {
+        if (__builtin_amdgcn_ballot_w64(l_tile[0] > p_cap || l_tile[1] > p_cap || m_run[0] == -INFINITY ||
+                                        m_run[1] == -INFINITY)) {
+            rebase_from(sd, true);
+            expo(sd);
+        }
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            l_run[qb] += l_tile[qb];
+            if constexpr (BF16) l_f32[qb] += lf_tile[qb];
+        }
     };
 
     // ---- schedule ----
@@ -368,8 +399,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             if (__builtin_amdgcn_readfirstlane(t_wm[j]) & wbit) {
                 qk(kt, s0);
                 mask(j, s0);
-                rebase_from(s0);
                 expo(s0);
+                settle(s0);
                 pv(vt);
             }
         };
@@ -384,10 +415,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         if (T > 1) issue(Kh, 1, k_lds1, false);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (T_w0 < T_w && T_w0 == 0) {
+        if (T_w0 < T_w && T_w0 == 0) {  // the first tile sets the reference (m_run = -inf until then)
             qk(k_lds0, s0);
             mask(0, s0);
-            rebase_from(s0);
+            rebase_from(s0, false);
         }
         // region 1 of tile j: S^T(j+1) = K(j+1) . Q^T with the exponentials of tile j in between.
         auto region1 = [&](f32x4 (&s_cur)[2][4], f32x4 (&s_nxt)[2][4], const uint16_t* k_nxt) __attribute__((always_inline)) {
@@ -400,6 +431,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             u32x4 ka[NK];
             ka[0] = k_operand(k_nxt, 0, 0);
             ka[1] = k_operand(k_nxt, 0, 1);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) l_tile[qb] = lf_tile[qb] = 0.f;
 #pragma unroll
             for (int i = 0; i < NK; ++i) {
                 const int t = i >> 2, kb = i & 3;
@@ -421,20 +454,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(pk[qb][kk][r]));
-                asm volatile("" : "+v"(l_run[qb]));
-                if constexpr (BF16) asm volatile("" : "+v"(l_f32[qb]));
+                asm volatile("" : "+v"(l_tile[qb]));
+                if constexpr (BF16) asm volatile("" : "+v"(lf_tile[qb]));
             }
         };
-        // region 2 of tile j: O^T += V(j)^T . P^T(j) with the row max of S^T(j+1) in between, then
-        // the move of the reference max for tile j+1.
-        auto region2 = [&](f32x4 (&s_nxt)[2][4], const uint16_t* v_cur) __attribute__((always_inline)) {
+        // region 2 of tile j: O^T += V(j)^T . P^T(j).
+        auto region2 = [&](const uint16_t* v_cur) __attribute__((always_inline)) {
             // V^T operands read two steps ahead.
             constexpr int NV = 2 * DB;  // V^T operands: 16 for D = 128, 8 for D = 64
-            constexpr int EPS = 32 / NV;  // scores scanned for the max per step
             u32x4 va[NV];
             va[0] = v_operand(v_cur, 0, 0);
             va[1] = v_operand(v_cur, 1 / DB, 1 % DB);
-            float mx[2] = {-INFINITY, -INFINITY};
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
                 const int kk = i / DB, b = i % DB;
@@ -445,15 +475,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     oacc[qb][b] = mfma16<BF16>(va[i], p_operand(qb, kk), oacc[qb][b]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                // row max: the 32 scores of this lane, EPS per step (score e = 16qb + 4kb + r)
-#pragma unroll
-                for (int u = 0; u < EPS; ++u) {
-                    const int e = i * EPS + u;
-                    mx[e >> 4] = fmaxf(mx[e >> 4], s_nxt[e >> 4][(e >> 2) & 3][e & 3]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
             }
-            rebase(max_over_rows(mx[0]), max_over_rows(mx[1]));
         };
         if constexpr (MASKED) {
             // every wave: barrier, loads, region 1, region 2 (V in two buffers)
@@ -468,14 +490,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     if (j + 1 == T_w0 && j + 1 < T_w) {
                         qk(k_nxt, s_nxt);
                         mask(j + 1, s_nxt);
-                        rebase_from(s_nxt);
+                        rebase_from(s_nxt, false);
                     }
                 } else if (j + 1 < T_w) {
                     region1(s_cur, s_nxt, k_nxt);
+                    settle(s_cur);
                     mask(j + 1, s_nxt);
-                    region2(s_nxt, v_cur);
+                    region2(v_cur);
                 } else if (j < T_w) {
                     expo(s_cur);
+                    settle(s_cur);
                     pv(v_cur);
                 }
             };
@@ -505,16 +529,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 if (j + 1 < T) issue(Vh, j + 1, v_p1, true);
                 if (j + 1 < T_w) {
                     region1(s_cur, s_nxt, k_nxt);
+                    settle(s_cur);
                     mask(j + 1, s_nxt);
                 } else if (j < T_w) {
                     expo(s_cur);
+                    settle(s_cur);
                 }
                 if (lag && j + 1 < T) {
                     __builtin_amdgcn_s_waitcnt(0);
                     __syncthreads();  // barrier j + 1
                 }
                 if (j + 1 < T_w) {
-                    region2(s_nxt, v_cur);
+                    region2(v_cur);
                 } else if (j < T_w) {
                     pv(v_cur);
                 }

@@ -42,13 +42,16 @@ extern "C" {
  *   relative to a reference maximum m and rescales them by
  *   alpha = exp(m_old - m_new) when m moves ("transformer math: flash
  *   attention math", aicassindra.com, "The rescaling identity, derived").
- *   With 0 the reference moves whenever a row's running maximum rises, the
- *   loop exactly as that page writes it ("The block-wise update, and the full
- *   algorithm"). With t > 0 a wave moves it (to the exact running maximum)
- *   only when some score exceeds it by more than t in log2 units, so the
- *   unnormalised probabilities stay <= 2^t and most tiles skip the rescale
- *   ("fewer rescaling operations", "Decoding flash attention",
- *   bibekananda.in, "Later versions"). Range [0, 15]; fa_fwd uses 8.
+ *   With 0 the reference is the running maximum at every step, the loop
+ *   exactly as that page writes it ("The block-wise update, and the full
+ *   algorithm"). With t > 0 it moves only when needed to keep every
+ *   unnormalised probability <= 2^t, and then to t/2 above the running
+ *   maximum, so most tiles skip the rescale ("fewer rescaling operations",
+ *   "Decoding flash attention", bibekananda.in, "Later versions"). The
+ *   default kernel tests this on the sums of each tile's probabilities that
+ *   the recurrence forms anyway: when a sum exceeds 2^t (which any score
+ *   more than t above the reference makes happen) the wave moves the
+ *   reference and recomputes that tile. Range [0, 15]; fa_fwd uses 8.
  * variant: which kernel evaluates it. 0 = the default (variant 1);
  *   1 = 32 query rows per wave, two waves per SIMD (the fast one);
  *   2 = 64 query rows per wave, one wave per SIMD (fewer shared-memory reads
