@@ -110,18 +110,71 @@ __device__ __forceinline__ void store_rows(uint16_t* row, const f32x16 (&acc)[D 
 
 // Stage `rows` rows starting at r0 of one head into a swizzled LDS tile by LDS DMA (lds_load16)
 // (rows past the end repeat row N-1); each of the kWaves waves issues its share of 1 KiB loads.
+// SW16: the swizzle of the tiles read by 16x16x32 products (swz16), else that of swz.
+template <int D, bool SW16 = false>
+__device__ __forceinline__ void stage_rows(const uint16_t* src_head, int r0, int rows, int N, uint16_t* dst,
+                                           int wave_s, int lane);
+
+// ---- 16x16x32 products (the dQ kernel) ----
+// A tile read by these products is read in two patterns: as a row operand (ds_read_b128, lane
+// (li, g) reads row r0 + li, chunk kchunk(t, g) of k-step t) and, for the K tile, transposed
+// (ds_read_b64_tr_b16 over chunks 2b, 2b + 1 of 16 rows). The swizzle swz16 and the chunk order
+// kchunk keep both free of bank conflicts (by measured LDS read rates: 187-197 and 130-135 B/clk
+// per CU); the row operands of the other product (Q, dO in registers) take the same order, so
+// every column is summed once.
 template <int D>
+__device__ __forceinline__ int swz16(int r) {
+    if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
+    else return r & 7;
+}
+template <int D>
+__device__ __forceinline__ int kchunk(int t, int g) {
+    return D == 128 ? t + 4 * g : 4 * t + g;
+}
+template <int D>
+__device__ __forceinline__ int off16(int r, int c) {
+    return r * D + ((c ^ swz16<D>(r)) << 3);
+}
+template <int D, bool SW16>
 __device__ __forceinline__ void stage_rows(const uint16_t* src_head, int r0, int rows, int N, uint16_t* dst,
                                            int wave_s, int lane) {
     constexpr int CPR = D / 8;
     constexpr int RPI = 64 / CPR;
     const int per_wave = rows / RPI / kWaves;
     for (int i = 0; i < per_wave; ++i) {
-        const int g = wave_s * per_wave + i;
-        const int r = RPI * g + lane / CPR;
-        const int ch = (lane % CPR) ^ swz<D>(r);
+        const int ld = wave_s * per_wave + i;
+        const int r = RPI * ld + lane / CPR;
+        const int ch = (lane % CPR) ^ (SW16 ? swz16<D>(r) : swz<D>(r));
         const unsigned src = (unsigned)min(r0 + r, N - 1) * D + 8 * ch;
-        lds_load16(src_head, N * D * 2, 2 * src, (lds_void*)(dst + g * 512));
+        lds_load16(src_head, N * D * 2, 2 * src, (lds_void*)(dst + ld * 512));
+    }
+}
+// Transposed A operand of a 16x16x32 product: rows d = 16b + li, k slots 8g + s = tile rows
+// 32kk + 4g + s (s < 4) and 32kk + 16 + 4g + s - 4 (s >= 4), the order in which a lane holds
+// a 16x16 C tile's rows 4g .. 4g + 3 of two consecutive tiles. off: per-lane offsets of
+// transpose16_offsets.
+template <int D>
+__device__ __forceinline__ void transpose16_offsets(int lane, int (&off)[D / 16]) {
+    const int g = lane >> 4, li = lane & 15;
+#pragma unroll
+    for (int b = 0; b < D / 16; ++b) off[b] = off16<D>(4 * g + (li >> 2), 2 * b + ((li & 3) >> 1)) + 4 * (li & 1);
+}
+template <int D>
+__device__ __forceinline__ u32x4 transposed16(const uint16_t* tile, const int (&off)[D / 16], int kk, int b) {
+    const i16x4 l4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off[b] + kk * 32 * D));
+    const i16x4 h4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off[b] + kk * 32 * D + 16 * D));
+    const u32x2 a = __builtin_bit_cast(u32x2, l4);
+    const u32x2 c = __builtin_bit_cast(u32x2, h4);
+    return (u32x4){a[0], a[1], c[0], c[1]};
+}
+// Store a row of a transposed 16x16 accumulator set (lane: row; registers of block b: columns
+// 16b + 4g .. +3) times f.
+template <int D, bool BF16>
+__device__ __forceinline__ void store_row16(uint16_t* row, const f32x4 (&acc)[D / 16], float f, int g) {
+#pragma unroll
+    for (int b = 0; b < D / 16; ++b) {
+        const u32x2 st = {pack2<BF16>(acc[b][0] * f, acc[b][1] * f), pack2<BF16>(acc[b][2] * f, acc[b][3] * f)};
+        *reinterpret_cast<u32x2*>(row + 16 * b + 4 * g) = st;
     }
 }
 
@@ -141,8 +194,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     int bq = 0, int bk = 0, int64_t bstride_b = 0, int64_t bstride_h = 0) {
     static_assert(!(MASKED && CAUSAL), "the general mask replaces the causal one");
     static_assert(!BLOCKS || MASKED, "the block mask rides on the general mask");
-    constexpr int DK = D / 16;
-    constexpr int DB = D / 32;
+    constexpr int DT = D / 32;  // 32-column k-steps of the first two products
+    constexpr int DB = D / 16;  // 16-column blocks of dQ
     constexpr int TILE = kKeyTile * D;
     static_assert(kKeyTile * D / (64 * 8) % kWaves == 0, "tile loads must split evenly over the waves");
 
@@ -154,8 +207,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int h = lane >> 5;
-    const int lq = lane & 31;
+    // 16x16x32 products: lane l holds query column li = l % 16 of the S^T, dP^T and dQ^T tiles of
+    // both 16-row blocks of the wave, and row group g = l / 16 (tile rows 4g .. 4g + 3; operand k
+    // slots 8g .. 8g + 7)
+    const int g = lane >> 4;
+    const int li = lane & 15;
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
 
     int bh, qt;
@@ -165,28 +221,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint16_t* Kh = K + head;
     const uint16_t* Vh = V + head;
     const int wq0 = q0 + 32 * wave;
-    const int qrow = wq0 + lq;
-    const int qr = min(qrow, N - 1);  // row the lane loads (rows past N repeat N-1, never stored)
 
-    // This lane's query row as the B operand of the first two products: columns 16t + 8h .. +7.
-    // The same columns of o give the lane's half of D = dO . o.
-    u32x4 qreg[DK], dreg[DK];
-    float dsum = 0.f;
-    {
-        const uint16_t* qrp = Q + head + (int64_t)qr * D + 8 * h;
-        const uint16_t* drp = dO + head + (int64_t)qr * D + 8 * h;
-        const uint16_t* orp = O + head + (int64_t)qr * D + 8 * h;
+    // The lane's two query rows (wq0 + li and wq0 + 16 + li, blocks qb = 0, 1) as B operands of
+    // the first two products (chunk kchunk(t, g) of k-step t). The same chunks of o give the
+    // lane's quarter of D = dO . o. Rows past N repeat row N-1 (never stored).
+    u32x4 qf[2][DT], df[2][DT];
+    float Dq[2], lse2[2];
 #pragma unroll
-        for (int t = 0; t < DK; ++t) {
-            qreg[t] = *reinterpret_cast<const u32x4*>(qrp + 16 * t);
-            dreg[t] = *reinterpret_cast<const u32x4*>(drp + 16 * t);
-            dsum = dot8<BF16>(dreg[t], *reinterpret_cast<const u32x4*>(orp + 16 * t), dsum);
+    for (int qb = 0; qb < 2; ++qb) {
+        const int qrow = wq0 + 16 * qb + li;
+        const int64_t qr = min(qrow, N - 1);
+        const uint16_t* qrp = Q + head + qr * D;
+        const uint16_t* drp = dO + head + qr * D;
+        const uint16_t* orp = O + head + qr * D;
+        float dsum = 0.f;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+            const int col = 8 * kchunk<D>(t, g);
+            qf[qb][t] = *reinterpret_cast<const u32x4*>(qrp + col);
+            df[qb][t] = *reinterpret_cast<const u32x4*>(drp + col);
+            dsum = dot8<BF16>(df[qb][t], *reinterpret_cast<const u32x4*>(orp + col), dsum);
         }
+        Dq[qb] = sum_over_rows(dsum);
+        if (g == 0 && qrow < N) DELTA[(int64_t)bh * N + qrow] = Dq[qb];
+        const float lse_raw = LSE[(int64_t)bh * N + qr];
+        lse2[qb] = (MASKED && lse_raw == -INFINITY) ? 0.f : lse_raw * kLog2e;  // lse in log2 units
     }
-    const float Dq = sum_with_partner(dsum);
-    if (h == 0 && qrow < N) DELTA[(int64_t)bh * N + qrow] = Dq;
-    const float lse_raw = LSE[(int64_t)bh * N + qr];
-    const float lse2 = (MASKED && lse_raw == -INFINITY) ? 0.f : lse_raw * kLog2e;  // lse in log2 units
 
     const int kv_end = CAUSAL ? min(N, q0 + kRows) : N;
     // key tiles tb .. tb + T - 1 (tile indices below are relative to tb); this wave computes
@@ -226,15 +286,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     auto key_tile = [&](int j) { return BLOCKS ? __builtin_amdgcn_readfirstlane(t_list[j]) : tb + j; };
 
-    int koff[DK];
+    // row operands of K and V (keys 16kb + li, chunk kchunk(t, g)) and the K^T operand
+    int aoff[DT];
 #pragma unroll
-    for (int t = 0; t < DK; ++t) koff[t] = tile_off<D>(lq, 2 * t + h);
-    int tlo[DB], thi[DB];
-    transpose_offsets<D>(lane, tlo, thi);
+    for (int t = 0; t < DT; ++t) aoff[t] = off16<D>(li, kchunk<D>(t, g));
+    int troff[DB];
+    transpose16_offsets<D>(lane, troff);
 
-    f32x16 acc[DB];
+    // dQ^T of this wave: block (qb, b) holds columns 16b + 4g .. +3 of query row wq0 + 16qb + li
+    f32x4 acc[2][DB];
 #pragma unroll
-    for (int b = 0; b < DB; ++b) acc[b] = (f32x16){};
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int b = 0; b < DB; ++b) acc[qb][b] = (f32x4){};
 
     auto tile = [&](int j, const uint16_t* kt, const uint16_t* vt) __attribute__((always_inline)) {
         const int k0 = key_tile(j) * kKeyTile;
@@ -243,43 +307,68 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                                    : (k0 + kKeyTile > N) || (CAUSAL && k0 + kKeyTile - 1 > wq0);
         // keep the constant parts of the LDS addresses in the instructions (see the dkdv kernel)
 #pragma unroll
-        for (int t = 0; t < DK; ++t) asm volatile("" : "+v"(koff[t]));
+        for (int t = 0; t < DT; ++t) asm volatile("" : "+v"(aoff[t]));
 #pragma unroll
-        for (int b = 0; b < DB; ++b) asm volatile("" : "+v"(tlo[b]), "+v"(thi[b]));
-        unsigned dsk[2][8];
+        for (int b = 0; b < DB; ++b) asm volatile("" : "+v"(troff[b]));
+        // dS^T of the tile as B operands of the last product: [qb][kk][.] covers keys 32kk ..
+        // 32kk + 31 in the k-slot order of transposed16 (pairs of 16-key blocks 2kk, 2kk + 1)
+        unsigned dsk[2][2][4];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            __builtin_amdgcn_sched_barrier(0);  // one 32-key block at a time
-            f32x16 s = {}, dp = {};
+        for (int kk = 0; kk < 2; ++kk) {
+            __builtin_amdgcn_sched_barrier(0);  // 32 keys at a time
+            f32x4 s[2][2], dp[2][2];            // [qb][16-key block 2kk + u]
 #pragma unroll
-            for (int t = 0; t < DK; ++t) {
-                s = mfma32<BF16>(*reinterpret_cast<const u32x4*>(kt + koff[t] + kb * 32 * D), qreg[t], s);
-                dp = mfma32<BF16>(*reinterpret_cast<const u32x4*>(vt + koff[t] + kb * 32 * D), dreg[t], dp);
-            }
+            for (int t = 0; t < DT; ++t)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int kb = 2 * kk + u;
+                    const u32x4 ka = *reinterpret_cast<const u32x4*>(kt + aoff[t] + kb * 16 * D);
+                    const u32x4 va = *reinterpret_cast<const u32x4*>(vt + aoff[t] + kb * 16 * D);
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb) {
+                        s[qb][u] = mfma16<BF16>(ka, qf[qb][t], t == 0 ? (f32x4){} : s[qb][u]);
+                        dp[qb][u] = mfma16<BF16>(va, df[qb][t], t == 0 ? (f32x4){} : dp[qb][u]);
+                    }
+                }
+            // C layout: register r of (qb, u) holds key k0 + 32kk + 16u + 4g + r of query row
+            // wq0 + 16qb + li
             if (masked) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const bool out = MASKED ? key >= kv_len || (wr >= 0 && key > qrow + wr) || (wl >= 0 && key < qrow - wl)
-                                            : key >= N || (CAUSAL && key > qrow);
-                    if (out) s[r] = -INFINITY;
-                }
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int key = k0 + 32 * kk + 16 * u + 4 * g + r, qrow = wq0 + 16 * qb + li;
+                            const bool out = MASKED ? key >= kv_len || (wr >= 0 && key > qrow + wr) ||
+                                                          (wl >= 0 && key < qrow - wl)
+                                                    : key >= N || (CAUSAL && key > qrow);
+                            if (out) s[qb][u][r] = -INFINITY;
+                        }
             }
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c, -lse2));
-                dsk[kb][r >> 1] = pack2<BF16>(p0 * (dp[r] - Dq), p1 * (dp[r + 1] - Dq));
-            }
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int r = 0; r < 4; r += 2) {
+                        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[qb][u][r], c, -lse2[qb]));
+                        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[qb][u][r + 1], c, -lse2[qb]));
+                        dsk[qb][kk][2 * u + (r >> 1)] =
+                            pack2<BF16>(p0 * (dp[qb][u][r] - Dq[qb]), p1 * (dp[qb][u][r + 1] - Dq[qb]));
+                    }
         }
         __builtin_amdgcn_sched_barrier(0);
-        // dQ^T += K^T . dS^T over the 64 keys (4 steps of 16)
+        // dQ^T += K^T . dS^T over the 64 keys (2 steps of 32); each K^T operand feeds both blocks
 #pragma unroll
-        for (int i = 0; i < 4 * DB; ++i) {
+        for (int i = 0; i < 2 * DB; ++i) {
             const int kk = i / DB, b = i % DB;
-            const int kb = kk >> 1, hf = kk & 1;
-            const u32x4 ds = {dsk[kb][4 * hf], dsk[kb][4 * hf + 1], dsk[kb][4 * hf + 2], dsk[kb][4 * hf + 3]};
-            acc[b] = mfma32<BF16>(transposed_operand<D>(kt, tlo, thi, kk, b), ds, acc[b]);
+            const u32x4 a = transposed16<D>(kt, troff, kk, b);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const u32x4 ds = {dsk[qb][kk][0], dsk[qb][kk][1], dsk[qb][kk][2], dsk[qb][kk][3]};
+                acc[qb][b] = mfma16<BF16>(a, ds, acc[qb][b]);
+            }
         }
     };
 
@@ -292,27 +381,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int T_w0s = __builtin_amdgcn_readfirstlane(T_w0);
     // BLOCKS: this wave's bit for list entry j
     auto mine = [&](int j) { return !BLOCKS || ((__builtin_amdgcn_readfirstlane(t_wm[j]) >> wave_s) & 1); };
-    stage_rows<D>(Kh, key_tile(0) * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
-    stage_rows<D>(Vh, key_tile(0) * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
+    stage_rows<D, true>(Kh, key_tile(0) * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
+    stage_rows<D, true>(Vh, key_tile(0) * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
     for (int j = 0; j < T; j += 2) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (j + 1 < T) {
-            stage_rows<D>(Kh, key_tile(j + 1) * kKeyTile, kKeyTile, N, k_lds1, wave_s, lane);
-            stage_rows<D>(Vh, key_tile(j + 1) * kKeyTile, kKeyTile, N, v_lds1, wave_s, lane);
+            stage_rows<D, true>(Kh, key_tile(j + 1) * kKeyTile, kKeyTile, N, k_lds1, wave_s, lane);
+            stage_rows<D, true>(Vh, key_tile(j + 1) * kKeyTile, kKeyTile, N, v_lds1, wave_s, lane);
         }
         if ((!MASKED || j >= T_w0s) && j < T_ws && mine(j)) tile(j, k_lds0, v_lds0);
         if (j + 1 >= T) break;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (j + 2 < T) {
-            stage_rows<D>(Kh, key_tile(j + 2) * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
-            stage_rows<D>(Vh, key_tile(j + 2) * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
+            stage_rows<D, true>(Kh, key_tile(j + 2) * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
+            stage_rows<D, true>(Vh, key_tile(j + 2) * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
         }
         if ((!MASKED || j + 1 >= T_w0s) && j + 1 < T_ws && mine(j + 1)) tile(j + 1, k_lds1, v_lds1);
     }
 
-    if (qrow < N) store_rows<D, BF16>(dQ + head + (int64_t)qrow * D, acc, scale, h);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int qrow = wq0 + 16 * qb + li;
+        if (qrow < N) store_row16<D, BF16>(dQ + head + (int64_t)qrow * D, acc[qb], scale, g);
+    }
 }
 
 template <int D, bool BF16, bool CAUSAL, bool MASKED = false, bool BLOCKS = false>
