@@ -417,8 +417,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     int bq = 0, int bk = 0, int64_t bstride_b = 0, int64_t bstride_h = 0) {
     static_assert(!(MASKED && CAUSAL), "the general mask replaces the causal one");
     static_assert(!BLOCKS || MASKED, "the block mask rides on the general mask");
-    constexpr int DK = D / 16;
-    constexpr int DB = D / 32;
+    constexpr int DT = D / 32;  // 32-column k-steps of the first two products
+    constexpr int DB = D / 16;  // 16-column blocks of dK and dV
     constexpr int TILE = kQueryTile * D;
     static_assert(kQueryTile * D / (64 * 8) % kWaves == 0, "tile loads must split evenly over the waves");
 
@@ -435,8 +435,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int h = lane >> 5;
-    const int lq = lane & 31;
+    // 16x16x32 products: lane l holds key column li = l % 16 of the S, dP, dK^T and dV^T tiles
+    // of both 16-key blocks of the wave, and row group g = l / 16 (tile rows 4g .. 4g + 3; operand
+    // k slots 8g .. 8g + 7)
+    const int g = lane >> 4;
+    const int li = lane & 15;
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const int kg = wave & 3;     // key group: keys 32 kg .. 32 kg + 31 of the workgroup
     const int half = wave >> 2;  // the 32-row half of every query tile this wave takes
@@ -453,31 +456,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const float* lse_h = LSE + (int64_t)bh * N;
     const float* del_h = DELTA + (int64_t)bh * N;
     const int kw0 = k0 + 32 * kg;
-    const int key = kw0 + lq;
 
-    stage_rows<D>(K + head, k0, kKeys, N, kv_lds, wave_s, lane);
-    stage_rows<D>(V + head, k0, kKeys, N, kv_lds + kKeys * D, wave_s, lane);
+    stage_rows<D, true>(K + head, k0, kKeys, N, kv_lds, wave_s, lane);
+    stage_rows<D, true>(V + head, k0, kKeys, N, kv_lds + kKeys * D, wave_s, lane);
 
     // Per-lane element offsets with this wave's row block folded in (the swizzle depends on
-    // row % 16 only, so moving whole 32-row blocks is a plain offset): qoff into a Q or dO tile
-    // (this wave's 32-row half), tlo/thi for the transpose reads of the same rows, and kvo into
-    // kv_lds for this lane's K chunk per k-step (its V chunk is kKeys * D elements further).
-    int qoff[DK], tlo[DB], thi[DB], kvo[DK];
-    transpose_offsets<D>(lane, tlo, thi);
+    // row % 16 only, so moving whole 16-row blocks is a plain offset): qoff into a Q or dO tile
+    // (rows 32 half + li, chunk kchunk(t, g) of k-step t), troff for the transpose reads of the
+    // same 32 rows, and kvo into kv_lds for the K row 32 kg + li (its V row is kKeys * D
+    // elements further).
+    int qoff[DT], troff[DB], kvo[DT];
+    transpose16_offsets<D>(lane, troff);
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
-        tlo[b] += 32 * half * D;
-        thi[b] += 32 * half * D;
-    }
+    for (int b = 0; b < DB; ++b) troff[b] += 32 * half * D;
 #pragma unroll
-    for (int t = 0; t < DK; ++t) {
-        qoff[t] = tile_off<D>(lq, 2 * t + h) + 32 * half * D;
-        kvo[t] = tile_off<D>(lq, 2 * t + h) + 32 * kg * D;
+    for (int t = 0; t < DT; ++t) {
+        qoff[t] = off16<D>(li, kchunk<D>(t, g)) + 32 * half * D;
+        kvo[t] = off16<D>(li, kchunk<D>(t, g)) + 32 * kg * D;
     }
 
-    f32x16 dv[DB], dk[DB];
+    // dK^T and dV^T of this wave: block (b, kb) holds columns 16b + 4g .. +3 of key kw0 + 16kb + li
+    f32x4 dv[DB][2], dk[DB][2];
 #pragma unroll
-    for (int b = 0; b < DB; ++b) dv[b] = dk[b] = (f32x16){};
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) dv[b][kb] = dk[b][kb] = (f32x4){};
 
     // query tiles j0 .. n_steps - 1 can see keys of this workgroup; rows [lo_w, hi_w) can see keys
     // of this wave (MASKED: keys past the batch's length are seen by no row)
@@ -539,7 +542,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     int skip_below = __builtin_amdgcn_readfirstlane(lo_w);
     asm volatile("" : "+s"(skip_below));
     const int skip_from = __builtin_amdgcn_readfirstlane(hi_w);  // (MASKED) rows from here see no key
-    // One 32-row half of query tile j against this wave's 32 keys: 32 MFMAs at D = 128.
+    // One 32-row half of query tile j against this wave's 32 keys: 64 MFMAs at D = 128.
     auto step = [&](int j, const uint16_t* qt_, const uint16_t* dot_, int buf) __attribute__((always_inline)) {
         const int qs = j * kQueryTile + 32 * half;  // first query row of this wave's half
         if (qs + 31 < skip_below) return;           // every key of this wave is after these rows
@@ -550,75 +553,97 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         // object to the compiler, which then waits for the tile loads in flight (vmcnt(0))
         // before reading through it.
 #pragma unroll
-        for (int t = 0; t < DK; ++t) asm volatile("" : "+v"(qoff[t]), "+v"(kvo[t]));
+        for (int t = 0; t < DT; ++t) asm volatile("" : "+v"(qoff[t]), "+v"(kvo[t]));
 #pragma unroll
-        for (int b = 0; b < DB; ++b) asm volatile("" : "+v"(tlo[b]), "+v"(thi[b]));
-        f32x16 s = {}, dp = {};
-        // The four LDS operands of k-step t + 1 are read before the two MFMAs of step t issue
-        // (sched_barrier pins the order), so their latency hides behind those MFMAs.
-        u32x4 oq[2], ok[2], od[2], ov[2];
-        auto fetch = [&](int t) __attribute__((always_inline)) {
-            const int r = t & 1;
-            oq[r] = *reinterpret_cast<const u32x4*>(qt_ + qoff[t]);
-            ok[r] = *reinterpret_cast<const u32x4*>(kv_lds + kvo[t]);
-            od[r] = *reinterpret_cast<const u32x4*>(dot_ + qoff[t]);
-            ov[r] = *reinterpret_cast<const u32x4*>(kv_lds + kKeys * D + kvo[t]);
+        for (int b = 0; b < DB; ++b) asm volatile("" : "+v"(troff[b]));
+        // S = Q . K^T, then dP = dO . V^T: at each k-step the two row operands of each side (query
+        // blocks qb, key blocks kb) feed four MFMAs. The operands of stage i + 1 are read before
+        // the MFMAs of stage i issue (sched_barrier pins the order).
+        f32x4 s[2][2], dp[2][2];  // [qb][kb]
+        u32x4 oa[2][2], ob[2][2];  // [ring][qb] row operands of Q or dO, [ring][kb] of K or V
+        auto fetch = [&](int i) __attribute__((always_inline)) {
+            const int r = i & 1, t = i % DT;
+            const uint16_t* at = i < DT ? qt_ : dot_;
+            const uint16_t* bt = i < DT ? kv_lds : kv_lds + kKeys * D;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                oa[r][u] = *reinterpret_cast<const u32x4*>(at + qoff[t] + u * 16 * D);
+                ob[r][u] = *reinterpret_cast<const u32x4*>(bt + kvo[t] + u * 16 * D);
+            }
         };
         fetch(0);
 #pragma unroll
-        for (int t = 0; t < DK; ++t) {
-            if (t + 1 < DK) fetch(t + 1);
+        for (int i = 0; i < 2 * DT; ++i) {
+            if (i + 1 < 2 * DT) fetch(i + 1);
             __builtin_amdgcn_sched_barrier(0);
-            s = mfma32<BF16>(oq[t & 1], ok[t & 1], s);
-            dp = mfma32<BF16>(od[t & 1], ov[t & 1], dp);
+            const int r = i & 1;
+            const bool first = i % DT == 0;
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    if (i < DT) s[qb][kb] = mfma16<BF16>(oa[r][qb], ob[r][kb], first ? (f32x4){} : s[qb][kb]);
+                    else dp[qb][kb] = mfma16<BF16>(oa[r][qb], ob[r][kb], first ? (f32x4){} : dp[qb][kb]);
+                }
             __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        // C layout: register r holds query row qs + 8(r/4) + 4h + r%4 of key `key`
+        // C layout: register r of (qb, kb) holds query row qs + 16qb + 4g + r of key kw0 + 16kb + li
         if (MASKED ? qs + 32 > N || kw0 + 31 >= kv_len || (wr >= 0 && kw0 + 31 > qs + wr) ||
                          (wl >= 0 && kw0 < qs + 31 - wl)
                    : qs + 32 > N || (CAUSAL && qs < kw0 + 31)) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int qrow = qs + 8 * (r >> 2) + 4 * h + (r & 3);
-                const bool out = MASKED ? key >= kv_len || (wr >= 0 && key > qrow + wr) || (wl >= 0 && key < qrow - wl)
-                                        : CAUSAL && key > qrow;
-                if (qrow >= N || out) s[r] = -INFINITY;
-            }
-        }
-        unsigned pk[8], dsk[8];
+            for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int o = 32 * half + 8 * g + 4 * h;
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int qrow = qs + 16 * qb + 4 * g + r, key = kw0 + 16 * kb + li;
+                        const bool out = MASKED ? key >= kv_len || (wr >= 0 && key > qrow + wr) ||
+                                                      (wl >= 0 && key < qrow - wl)
+                                                : CAUSAL && key > qrow;
+                        if (qrow >= N || out) s[qb][kb][r] = -INFINITY;
+                    }
+        }
+        // P and dS as B operands of the last two products: [kb][.] holds the k slots 8g .. 8g + 7,
+        // rows 4g .. 4g + 3 of query block 0 and of block 1 (the order of transposed16)
+        unsigned pk[2][4], dsk[2][4];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int o = 32 * half + 16 * qb + 4 * g;
             const float4 l4 = *reinterpret_cast<const float4*>(&st_lds[buf][0][o]);
             const float4 d4 = *reinterpret_cast<const float4*>(&st_lds[buf][1][o]);
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[4 * g + 0], c, -l4.x));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[4 * g + 1], c, -l4.y));
-            const float p2 = __builtin_amdgcn_exp2f(fmaf(s[4 * g + 2], c, -l4.z));
-            const float p3 = __builtin_amdgcn_exp2f(fmaf(s[4 * g + 3], c, -l4.w));
-            pk[2 * g] = pack2<BF16>(p0, p1);
-            pk[2 * g + 1] = pack2<BF16>(p2, p3);
-            dsk[2 * g] = pack2<BF16>(p0 * (dp[4 * g + 0] - d4.x), p1 * (dp[4 * g + 1] - d4.y));
-            dsk[2 * g + 1] = pack2<BF16>(p2 * (dp[4 * g + 2] - d4.z), p3 * (dp[4 * g + 3] - d4.w));
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][0], c, -l4.x));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][1], c, -l4.y));
+                const float p2 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][2], c, -l4.z));
+                const float p3 = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][3], c, -l4.w));
+                pk[kb][2 * qb] = pack2<BF16>(p0, p1);
+                pk[kb][2 * qb + 1] = pack2<BF16>(p2, p3);
+                dsk[kb][2 * qb] = pack2<BF16>(p0 * (dp[qb][kb][0] - d4.x), p1 * (dp[qb][kb][1] - d4.y));
+                dsk[kb][2 * qb + 1] = pack2<BF16>(p2 * (dp[qb][kb][2] - d4.z), p3 * (dp[qb][kb][3] - d4.w));
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
-        // dV^T += dO^T . P and dK^T += Q^T . dS over these 32 rows (2 steps of 16)
-        // the transposed operands of MFMA pair i + 1 are read before pair i issues
-        u32x4 ta[2], tb[2];
-        ta[0] = transposed_operand<D>(dot_, tlo, thi, 0, 0);
-        tb[0] = transposed_operand<D>(qt_, tlo, thi, 0, 0);
+        // dV^T += dO^T . P and dK^T += Q^T . dS over these 32 rows; each transposed operand feeds
+        // both key blocks, and the operands of column block b + 1 are read before block b issues
+        u32x4 ta[2], tq[2];
+        ta[0] = transposed16<D>(dot_, troff, 0, 0);
+        tq[0] = transposed16<D>(qt_, troff, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 2 * DB; ++i) {
-            const int kk = i / DB, b = i % DB;
-            if (i + 1 < 2 * DB) {
-                ta[(i + 1) & 1] = transposed_operand<D>(dot_, tlo, thi, (i + 1) / DB, (i + 1) % DB);
-                tb[(i + 1) & 1] = transposed_operand<D>(qt_, tlo, thi, (i + 1) / DB, (i + 1) % DB);
+        for (int b = 0; b < DB; ++b) {
+            if (b + 1 < DB) {
+                ta[(b + 1) & 1] = transposed16<D>(dot_, troff, 0, b + 1);
+                tq[(b + 1) & 1] = transposed16<D>(qt_, troff, 0, b + 1);
             }
-            const u32x4 pop = {pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]};
-            const u32x4 dop = {dsk[4 * kk], dsk[4 * kk + 1], dsk[4 * kk + 2], dsk[4 * kk + 3]};
             __builtin_amdgcn_sched_barrier(0);
-            dv[b] = mfma32<BF16>(ta[i & 1], pop, dv[b]);
-            dk[b] = mfma32<BF16>(tb[i & 1], dop, dk[b]);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const u32x4 pop = {pk[kb][0], pk[kb][1], pk[kb][2], pk[kb][3]};
+                const u32x4 dop = {dsk[kb][0], dsk[kb][1], dsk[kb][2], dsk[kb][3]};
+                dv[b][kb] = mfma16<BF16>(ta[b & 1], pop, dv[b][kb]);
+                dk[b][kb] = mfma16<BF16>(tq[b & 1], dop, dk[b][kb]);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -628,16 +653,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // p + 1 into registers at the same time and writes them to LDS at the end of the step (the
     // buffer they go to was last read in step p - 1, before that barrier).
     if (wave == 0) stats_load(q_tile(0));
-    stage_rows<D>(Qh, q_tile(0) * kQueryTile, kQueryTile, N, q_lds0, wave_s, lane);
-    stage_rows<D>(dOh, q_tile(0) * kQueryTile, kQueryTile, N, do_lds0, wave_s, lane);
+    stage_rows<D, true>(Qh, q_tile(0) * kQueryTile, kQueryTile, N, q_lds0, wave_s, lane);
+    stage_rows<D, true>(dOh, q_tile(0) * kQueryTile, kQueryTile, N, do_lds0, wave_s, lane);
     if (wave == 0) stats_store(0);
     for (int p = 0; p < n_list; p += 2) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (p + 1 < n_list) {
             if (wave == 0) stats_load(q_tile(p + 1));
-            stage_rows<D>(Qh, q_tile(p + 1) * kQueryTile, kQueryTile, N, q_lds1, wave_s, lane);
-            stage_rows<D>(dOh, q_tile(p + 1) * kQueryTile, kQueryTile, N, do_lds1, wave_s, lane);
+            stage_rows<D, true>(Qh, q_tile(p + 1) * kQueryTile, kQueryTile, N, q_lds1, wave_s, lane);
+            stage_rows<D, true>(dOh, q_tile(p + 1) * kQueryTile, kQueryTile, N, do_lds1, wave_s, lane);
         }
         if (mine(p)) step(q_tile(p), q_lds0, do_lds0, 0);
         if (p + 1 >= n_list) break;
@@ -646,8 +671,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         __syncthreads();
         if (p + 2 < n_list) {
             if (wave == 0) stats_load(q_tile(p + 2));
-            stage_rows<D>(Qh, q_tile(p + 2) * kQueryTile, kQueryTile, N, q_lds0, wave_s, lane);
-            stage_rows<D>(dOh, q_tile(p + 2) * kQueryTile, kQueryTile, N, do_lds0, wave_s, lane);
+            stage_rows<D, true>(Qh, q_tile(p + 2) * kQueryTile, kQueryTile, N, q_lds0, wave_s, lane);
+            stage_rows<D, true>(dOh, q_tile(p + 2) * kQueryTile, kQueryTile, N, do_lds0, wave_s, lane);
         }
         if (mine(p + 1)) step(q_tile(p + 1), q_lds1, do_lds1, 1);
         if (p + 2 < n_list && wave == 0) stats_store(0);
@@ -664,22 +689,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                dv_x[(b * 16 + r) * 64 + lane] = dv[b][r];
-                dk_x[(b * 16 + r) * 64 + lane] = dk[b][r];
-            }
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    dv_x[((b * 2 + kb) * 4 + r) * 64 + lane] = dv[b][kb][r];
+                    dk_x[((b * 2 + kb) * 4 + r) * 64 + lane] = dk[b][kb][r];
+                }
     }
     __syncthreads();
-    if (half == 0 && key < N) {
+    if (half == 0) {
 #pragma unroll
-        for (int b = 0; b < DB; ++b)
+        for (int kb = 0; kb < 2; ++kb) {
+            const int key = kw0 + 16 * kb + li;
+            if (key >= N) continue;
+            f32x4 v4[DB], k4[DB];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                dv[b][r] += dv_x[(b * 16 + r) * 64 + lane];
-                dk[b][r] += dk_x[(b * 16 + r) * 64 + lane];
-            }
-        store_rows<D, BF16>(dV + head + (int64_t)key * D, dv, 1.f, h);
-        store_rows<D, BF16>(dK + head + (int64_t)key * D, dk, scale, h);
+            for (int b = 0; b < DB; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    v4[b][r] = dv[b][kb][r] + dv_x[((b * 2 + kb) * 4 + r) * 64 + lane];
+                    k4[b][r] = dk[b][kb][r] + dk_x[((b * 2 + kb) * 4 + r) * 64 + lane];
+                }
+            store_row16<D, BF16>(dV + head + (int64_t)key * D, v4, 1.f, g);
+            store_row16<D, BF16>(dK + head + (int64_t)key * D, k4, scale, g);
+        }
     }
 }
 
