@@ -13,16 +13,19 @@
 //                    First D_i = dO_i . o_i for its rows (written to delta), then a walk over the
 //                    key tiles (64 keys, double-buffered in LDS as in the forward):
 //                      S^T  = K . Q^T,  dP^T = V . dO^T   (Q^T, dO^T held in registers)
-//                      dS^T = P^T (dP^T - D)              (one query row per lane)
+//                      dS^T = P^T (dP^T - D)              (two query rows per lane)
 //                      dQ^T += K^T . dS^T                 (K^T by the LDS transpose read)
 // fa_bwd_dkdv_kernel one workgroup = 128 keys in 4 groups of 32, each group taken by two waves
 //                    that split every query tile of 64 rows in halves; the K and V rows sit in
 //                    LDS for the whole kernel, the Q and dO tiles (with lse and D of their rows)
 //                    are double-buffered; at the end the two partial sums of each key group are
 //                    added through LDS:
-//                      S  = Q . K^T,  dP = dO . V^T       (one key per lane)
+//                      S  = Q . K^T,  dP = dO . V^T       (two keys per lane)
 //                      dS = P (dP - D)
 //                      dV^T += dO^T . P,  dK^T += Q^T . dS (dO^T, Q^T by the LDS transpose read)
+// All products are v_mfma_f32_16x16x32 on 16-row blocks (two per wave side), each operand read
+// from LDS feeding both blocks; on random operands this shape spends less energy per flop than
+// 32x32x16, and these kernels run at the power limit.
 // P and dS are rounded to f16/bf16 as operands of the second products, with fp32 accumulation;
 // masked entries (a key after the query, rows or keys past the end) get s = -inf, so p = 0 and
 // dS = 0 before they touch any sum.
@@ -49,36 +52,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 typedef __attribute__((address_space(3))) const uint16_t lds_u16;
 typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 
-// ds_read_b64_tr_b16 offsets: lane s of each 16-lane group reads 4 consecutive columns 4*(s%4).. of
-// tile row s/4 (+4h); the instruction returns, per lane, one column of 4 rows. With the second read
-// 8 rows further down, a lane holds 8 rows in the order of the C-layout registers of a 32x32 MFMA
-// result (rows 4h..4h+3, 8+4h..8+4h+3 of each 16), so a product whose B operand comes straight
-// from such registers contracts over matching rows.
-template <int D>
-__device__ __forceinline__ void transpose_offsets(int lane, int (&lo)[D / 32], int (&hi)[D / 32]) {
-    const int h = lane >> 5;
-    const int s16 = lane & 15;
-    const int tr_row = 4 * h + (s16 >> 2);
-    const int tr_chunk = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
-    const int tr_half = 4 * (s16 & 1);
-#pragma unroll
-    for (int b = 0; b < D / 32; ++b) {
-        lo[b] = tile_off<D>(tr_row, 4 * b + tr_chunk) + tr_half;
-        hi[b] = tile_off<D>(tr_row + 8, 4 * b + tr_chunk) + tr_half;
-    }
-}
-
-// A operand (32 columns of block b x 16 rows of step kk, transposed) from a row-major LDS tile.
-template <int D>
-__device__ __forceinline__ u32x4 transposed_operand(const uint16_t* tile, const int (&lo)[D / 32],
-                                                    const int (&hi)[D / 32], int kk, int b) {
-    const i16x4 l4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + lo[b] + kk * 16 * D));
-    const i16x4 h4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + hi[b] + kk * 16 * D));
-    const u32x2 a = __builtin_bit_cast(u32x2, l4);
-    const u32x2 c = __builtin_bit_cast(u32x2, h4);
-    return (u32x4){a[0], a[1], c[0], c[1]};
-}
-
 // Sum of the 8 products of two packed 8-element rows, in fp32. (Each element is copied to a
 // scalar before the bit cast: __builtin_bit_cast applied to a vector element reads element 0.)
 template <bool BF16>
@@ -95,33 +68,13 @@ __device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float acc) {
     return acc;
 }
 
-// Store rows of a transposed accumulator (lane = row, registers = 4 columns per group) times f.
-template <int D, bool BF16>
-__device__ __forceinline__ void store_rows(uint16_t* row, const f32x16 (&acc)[D / 32], float f, int h) {
-#pragma unroll
-    for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const u32x2 st = {pack2<BF16>(acc[b][4 * g + 0] * f, acc[b][4 * g + 1] * f),
-                              pack2<BF16>(acc[b][4 * g + 2] * f, acc[b][4 * g + 3] * f)};
-            *reinterpret_cast<u32x2*>(row + b * 32 + 8 * g + 4 * h) = st;
-        }
-}
-
-// Stage `rows` rows starting at r0 of one head into a swizzled LDS tile by LDS DMA (lds_load16)
-// (rows past the end repeat row N-1); each of the kWaves waves issues its share of 1 KiB loads.
-// SW16: the swizzle of the tiles read by 16x16x32 products (swz16), else that of swz.
-template <int D, bool SW16 = false>
-__device__ __forceinline__ void stage_rows(const uint16_t* src_head, int r0, int rows, int N, uint16_t* dst,
-                                           int wave_s, int lane);
-
-// ---- 16x16x32 products (the dQ kernel) ----
-// A tile read by these products is read in two patterns: as a row operand (ds_read_b128, lane
-// (li, g) reads row r0 + li, chunk kchunk(t, g) of k-step t) and, for the K tile, transposed
-// (ds_read_b64_tr_b16 over chunks 2b, 2b + 1 of 16 rows). The swizzle swz16 and the chunk order
-// kchunk keep both free of bank conflicts (by measured LDS read rates: 187-197 and 130-135 B/clk
-// per CU); the row operands of the other product (Q, dO in registers) take the same order, so
-// every column is summed once.
+// ---- tiles and operands of the 16x16x32 products ----
+// Every LDS tile is read in one or two patterns: as a row operand (ds_read_b128, lane (li, g)
+// reads row r0 + li, chunk kchunk(t, g) of k-step t) and, for the K tile of the dQ kernel and the
+// Q and dO tiles of the dK/dV kernel, transposed (ds_read_b64_tr_b16 over chunks 2b, 2b + 1 of
+// 16 rows). The swizzle swz16 and the chunk order kchunk keep both free of bank conflicts (by
+// measured LDS read rates: 187-197 and 130-135 B/clk per CU); row operands held in registers (Q,
+// dO in the dQ kernel) take the same order, so every column is summed once.
 template <int D>
 __device__ __forceinline__ int swz16(int r) {
     if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
@@ -135,7 +88,9 @@ template <int D>
 __device__ __forceinline__ int off16(int r, int c) {
     return r * D + ((c ^ swz16<D>(r)) << 3);
 }
-template <int D, bool SW16>
+// Stage `rows` rows starting at r0 of one head into a swizzled LDS tile by LDS DMA (lds_load16)
+// (rows past the end repeat row N-1); each of the kWaves waves issues its share of 1 KiB loads.
+template <int D>
 __device__ __forceinline__ void stage_rows(const uint16_t* src_head, int r0, int rows, int N, uint16_t* dst,
                                            int wave_s, int lane) {
     constexpr int CPR = D / 8;
@@ -144,7 +99,7 @@ __device__ __forceinline__ void stage_rows(const uint16_t* src_head, int r0, int
     for (int i = 0; i < per_wave; ++i) {
         const int ld = wave_s * per_wave + i;
         const int r = RPI * ld + lane / CPR;
-        const int ch = (lane % CPR) ^ (SW16 ? swz16<D>(r) : swz<D>(r));
+        const int ch = (lane % CPR) ^ swz16<D>(r);
         const unsigned src = (unsigned)min(r0 + r, N - 1) * D + 8 * ch;
         lds_load16(src_head, N * D * 2, 2 * src, (lds_void*)(dst + ld * 512));
     }
@@ -381,22 +336,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int T_w0s = __builtin_amdgcn_readfirstlane(T_w0);
     // BLOCKS: this wave's bit for list entry j
     auto mine = [&](int j) { return !BLOCKS || ((__builtin_amdgcn_readfirstlane(t_wm[j]) >> wave_s) & 1); };
-    stage_rows<D, true>(Kh, key_tile(0) * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
-    stage_rows<D, true>(Vh, key_tile(0) * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
+    stage_rows<D>(Kh, key_tile(0) * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
+    stage_rows<D>(Vh, key_tile(0) * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
     for (int j = 0; j < T; j += 2) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (j + 1 < T) {
-            stage_rows<D, true>(Kh, key_tile(j + 1) * kKeyTile, kKeyTile, N, k_lds1, wave_s, lane);
-            stage_rows<D, true>(Vh, key_tile(j + 1) * kKeyTile, kKeyTile, N, v_lds1, wave_s, lane);
+            stage_rows<D>(Kh, key_tile(j + 1) * kKeyTile, kKeyTile, N, k_lds1, wave_s, lane);
+            stage_rows<D>(Vh, key_tile(j + 1) * kKeyTile, kKeyTile, N, v_lds1, wave_s, lane);
         }
         if ((!MASKED || j >= T_w0s) && j < T_ws && mine(j)) tile(j, k_lds0, v_lds0);
         if (j + 1 >= T) break;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (j + 2 < T) {
-            stage_rows<D, true>(Kh, key_tile(j + 2) * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
-            stage_rows<D, true>(Vh, key_tile(j + 2) * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
+            stage_rows<D>(Kh, key_tile(j + 2) * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
+            stage_rows<D>(Vh, key_tile(j + 2) * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
         }
         if ((!MASKED || j + 1 >= T_w0s) && j + 1 < T_ws && mine(j + 1)) tile(j + 1, k_lds1, v_lds1);
     }
@@ -457,8 +412,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const float* del_h = DELTA + (int64_t)bh * N;
     const int kw0 = k0 + 32 * kg;
 
-    stage_rows<D, true>(K + head, k0, kKeys, N, kv_lds, wave_s, lane);
-    stage_rows<D, true>(V + head, k0, kKeys, N, kv_lds + kKeys * D, wave_s, lane);
+    stage_rows<D>(K + head, k0, kKeys, N, kv_lds, wave_s, lane);
+    stage_rows<D>(V + head, k0, kKeys, N, kv_lds + kKeys * D, wave_s, lane);
 
     // Per-lane element offsets with this wave's row block folded in (the swizzle depends on
     // row % 16 only, so moving whole 16-row blocks is a plain offset): qoff into a Q or dO tile
@@ -653,16 +608,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // p + 1 into registers at the same time and writes them to LDS at the end of the step (the
     // buffer they go to was last read in step p - 1, before that barrier).
     if (wave == 0) stats_load(q_tile(0));
-    stage_rows<D, true>(Qh, q_tile(0) * kQueryTile, kQueryTile, N, q_lds0, wave_s, lane);
-    stage_rows<D, true>(dOh, q_tile(0) * kQueryTile, kQueryTile, N, do_lds0, wave_s, lane);
+    stage_rows<D>(Qh, q_tile(0) * kQueryTile, kQueryTile, N, q_lds0, wave_s, lane);
+    stage_rows<D>(dOh, q_tile(0) * kQueryTile, kQueryTile, N, do_lds0, wave_s, lane);
     if (wave == 0) stats_store(0);
     for (int p = 0; p < n_list; p += 2) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (p + 1 < n_list) {
             if (wave == 0) stats_load(q_tile(p + 1));
-            stage_rows<D, true>(Qh, q_tile(p + 1) * kQueryTile, kQueryTile, N, q_lds1, wave_s, lane);
-            stage_rows<D, true>(dOh, q_tile(p + 1) * kQueryTile, kQueryTile, N, do_lds1, wave_s, lane);
+            stage_rows<D>(Qh, q_tile(p + 1) * kQueryTile, kQueryTile, N, q_lds1, wave_s, lane);
+            stage_rows<D>(dOh, q_tile(p + 1) * kQueryTile, kQueryTile, N, do_lds1, wave_s, lane);
         }
         if (mine(p)) step(q_tile(p), q_lds0, do_lds0, 0);
         if (p + 1 >= n_list) break;
@@ -671,8 +626,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         __syncthreads();
         if (p + 2 < n_list) {
             if (wave == 0) stats_load(q_tile(p + 2));
-            stage_rows<D, true>(Qh, q_tile(p + 2) * kQueryTile, kQueryTile, N, q_lds0, wave_s, lane);
-            stage_rows<D, true>(dOh, q_tile(p + 2) * kQueryTile, kQueryTile, N, do_lds0, wave_s, lane);
+            stage_rows<D>(Qh, q_tile(p + 2) * kQueryTile, kQueryTile, N, q_lds0, wave_s, lane);
+            stage_rows<D>(dOh, q_tile(p + 2) * kQueryTile, kQueryTile, N, do_lds0, wave_s, lane);
         }
         if (mine(p + 1)) step(q_tile(p + 1), q_lds1, do_lds1, 1);
         if (p + 2 < n_list && wave == 0) stats_store(0);
