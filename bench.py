@@ -45,6 +45,7 @@ bounded sample of the same workload (the 1024 seeded query rows per head the
 parity test checks), converted to TFLOP/s with the same flop convention.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -121,6 +122,7 @@ def cpu_baseline(w, window=None, blocks=None):
         # the conventional count halves the causal pair count; scale the sample the same way
         conv = flops * (w.flops() / (4.0 * w.d * (w.B * w.H * w.N * (w.N + 1) / 2 if w.causal
                                                    else w.B * w.H * w.N * w.N)))
+    full = w.flops() if window is None and blocks is None else None
     return {
         "value": conv / dt / 1e12,
         "unit": "TFLOP/s",
@@ -128,6 +130,9 @@ def cpu_baseline(w, window=None, blocks=None):
         "kind": "oracle",
         "sample": f"{rows.shape[1]} seeded query rows per head x {rows.shape[0]} heads of {w.name} "
                   f"({rows.size} rows, {dt:.2f} s, {what})",
+        "rows_per_s": round(rows.size / dt, 1),
+        # the whole workload at the sample's rate (plain attention only)
+        "extrapolated_full_s": round(full / (conv / dt), 1) if full else None,
     }
 
 
@@ -240,7 +245,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     w = workloads.BY_NAME[args.workload]
-    q, k, v = (t.cuda() for t in workloads.make_inputs(w))
+    host_inputs = workloads.make_inputs(w)
+    # provenance of the synthetic inputs: torch version (it draws them) and a digest of each tensor
+    inputs_record = {"torch": torch.__version__, "seed": w.seed,
+                     "sha256": {name: hashlib.sha256(t.contiguous().view(torch.uint8).numpy().tobytes()).hexdigest()[:16]
+                                for name, t in zip(("q", "k", "v"), host_inputs)}}
+    q, k, v = (t.cuda() for t in host_inputs)
+    del host_inputs
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
 
@@ -305,16 +316,17 @@ def main():
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps, on the stream the kernels run on
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for i in range(args.steps):
         step()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = e0.elapsed_time(e1) / args.steps  # average launch duration on the kernel's stream
+    kernel_ms = ev[0].elapsed_time(ev[-1]) / args.steps  # average launch duration on the kernel's stream
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
 
     flops = w.flops() * (2.5 if args.which == "bwd" else 1.0)
     if window is not None:
@@ -365,7 +377,10 @@ def main():
                        "fa_fwd_kernel (block-sparse)" if blocks is not None else
                        "fa_fwd_kernel (split) + fa_merge_kernel" if splits is not None else KERNEL_NAME),
             "kernel_ms": round(kernel_ms, 4),
+            "kernel_ms_median": round(per_step[len(per_step) // 2], 4),
+            "kernel_ms_min": round(per_step[0], 4),
         },
+        "inputs": inputs_record,
     }
     if not args.no_cpu_baseline:
         if args.which == "fwd":

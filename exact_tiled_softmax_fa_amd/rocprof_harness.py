@@ -111,6 +111,16 @@ def _find(out, name, suffix):
     raise FileNotFoundError(f"no *{suffix} under {d}")
 
 
+def _reference_copies(values):
+    """The counter values of the reference copies among a run's copy dispatches: the runtime's
+    own small copies (a block mask uploaded to the device, say) use the same copy kernel, so
+    only dispatches of at least half the largest one's size count."""
+    if not values:
+        return values
+    top = max(values)
+    return [v for v in values if v >= 0.5 * top]
+
+
 def _counter(out, name, counter, kernel):
     return [float(r["Counter_Value"]) for r in _rows(_find(out, name, "counter_collection.csv"))
             if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]]
@@ -157,8 +167,8 @@ def summarize(workload: str, out: str, steps: int, cmds=None, which: str = "fwd"
         durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in trace]
         timed = durs[-steps:]
         ms = statistics.mean(timed)
-        fetch_copy = _counter(out, "fetch", "FETCH_SIZE", "copyBuffer")
-        write_copy = _counter(out, "write", "WRITE_SIZE", "copyBuffer")
+        fetch_copy = _reference_copies(_counter(out, "fetch", "FETCH_SIZE", "copyBuffer"))
+        write_copy = _reference_copies(_counter(out, "write", "WRITE_SIZE", "copyBuffer"))
         fetch_k = _counter(out, "fetch", "FETCH_SIZE", kname)
         write_k = _counter(out, "write", "WRITE_SIZE", kname)
         f_fac = COPY_MIB * 1024.0 / statistics.mean(fetch_copy)

@@ -200,3 +200,34 @@ def test_single_hip_runtime_in_process():
     maps = open("/proc/self/maps").read()
     paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(paths) == 1, paths
+
+
+@pytest.mark.parametrize("tau", [None, 0.0, 3.0])
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_scores_rising_along_the_keys(dt, tau):
+    """Logit(i, j) = slope * j + noise: every key tile raises every row's maximum, so the kernel
+    moves its reference (and recomputes a tile's exponentials) again and again, at the default
+    threshold (None: 8), at 0 (the reference is always the running max) and at 3. The result
+    must still be the definition's."""
+    say(f"rising logits {dt} tau={tau}")
+    B, H, N, d = 1, 2, 1100, 128
+    scale = float(np.float32(1 / math.sqrt(d)))
+    g = torch.Generator().manual_seed(77)
+    # channel 0 carries the slope (q = 1, k_j = slope * j / scale), the others small noise
+    slope = 0.05
+    q = torch.randn(B, H, N, d, generator=g) * 0.1
+    k = torch.randn(B, H, N, d, generator=g) * 0.1
+    q[..., 0] = 1.0
+    k[..., 0] = torch.arange(N, dtype=torch.float32) * (slope / scale)
+    q, k = q.to(DTYPES[dt]), k.to(DTYPES[dt])
+    _, _, v = workloads.custom_inputs(B, H, N, d, dt, seed=78)
+    o, lse = fa().forward(q.cuda(), k.cuda(), v.cuda(), scale=scale, rescale_threshold_log2=tau)
+    torch.cuda.synchronize()
+    o, lse = o.float().cpu().double().numpy(), lse.cpu().double().numpy()
+    o_ref, lse_ref = ref(q, k, v, False, scale)
+    # the scores span about slope * N = 55 natural-log units: far beyond one tile's threshold
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    ok, rep = check_o(o, o_ref, dt)
+    assert ok, rep
+    ok_l, err_l = check_lse(lse, lse_ref)
+    assert ok_l, err_l

@@ -115,3 +115,9 @@ def test_clock_line_refuses_impossible_pairings():
     assert "2.10 GHz" in rh.clock_line(dict(base, clock_ghz=2.1))
     assert "not given" in rh.clock_line(dict(base, clock_ghz=2.57)) and "2.57" in rh.clock_line(dict(base, clock_ghz=2.57))
     assert "no matrix work" in rh.clock_line({"mfma_flop_per_launch": 0.0, "clock_ghz": 4.0})
+
+
+def test_reference_copies_ignore_small_copy_dispatches():
+    # three 256 MiB reference copies and one 4 KiB upload through the same copy kernel
+    assert rh._reference_copies([131092.0, 131084.0, 131084.0, 4.0]) == [131092.0, 131084.0, 131084.0]
+    assert rh._reference_copies([]) == []
