@@ -10,7 +10,8 @@ head), with q, k, v already resident in device memory. The default workload is
 B=1, H=32, N=8192, d=128, non-causal, fp16. Prints one JSON line.
 
 --splits S times fa_fwd_splitkv with S key splits (0: the library's heuristic) instead of
-fa_fwd; the roofline then covers both of its kernels (split reduction and merge).
+fa_fwd (with a window: fa_fwd_splitkv_masked); the roofline then covers both of its kernels
+(split reduction and merge).
 
 --window-left L / --window-right R time fa_fwd_masked (with --pass bwd: fa_bwd_masked) with that
 sliding window (-1 = no limit; the workload's causal flag is then ignored) and price it by the
@@ -280,8 +281,13 @@ def main():
         window = (-1 if args.window_left is None else args.window_left,
                   -1 if args.window_right is None else args.window_right)
 
-        def step():  # noqa: F811
-            fa.forward_masked(q, k, v, window[0], window[1], None, scale=w.scale, out=o, lse=lse)
+        if splits is not None:  # the masked split-KV forward
+            def step():  # noqa: F811
+                fa.forward_masked(q, k, v, window[0], window[1], None, scale=w.scale, out=o, lse=lse,
+                                  num_splits=splits, workspace=ws)
+        else:
+            def step():  # noqa: F811
+                fa.forward_masked(q, k, v, window[0], window[1], None, scale=w.scale, out=o, lse=lse)
 
     blocks = None
     if args.block_density is not None:

@@ -64,8 +64,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     int n_split = 1, float* __restrict__ PO = nullptr, float* __restrict__ PL = nullptr, int H = 1, int wl = -1,
     int wr = -1, const int* __restrict__ seqlens = nullptr, const uint8_t* __restrict__ bmask = nullptr,
     int bq = 0, int bk = 0, int64_t bstride_b = 0, int64_t bstride_h = 0) {
-    static_assert(!(MASKED && (CAUSAL || SPLIT)), "the general mask replaces the causal one and does not split");
-    static_assert(!BLOCKS || MASKED, "the block mask rides on the general mask");
+    static_assert(!(MASKED && CAUSAL), "the general mask replaces the causal one");
+    static_assert(!BLOCKS || (MASKED && !SPLIT), "the block mask rides on the general mask, unsplit");
     constexpr int DT = D / 32;                 // 32-column k-steps of the first product
     constexpr int DB = D / 16;                 // 16-column blocks of the output
     constexpr int CPR = D / 8;                 // 16-byte chunks per row
@@ -126,6 +126,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int hi = wr >= 0 ? min(kv_len, q0 + kBlockM + wr) : kv_len;
         tb = lo / kBlockN;
         T = max(0, (hi + kBlockN - 1) / kBlockN - tb);
+        if constexpr (SPLIT) {  // this split's run of the window's tiles (possibly none)
+            const int per = (T + n_split - 1) / n_split;
+            const int s0 = (vh % n_split) * per;
+            tb += s0;
+            T = max(0, min(T, s0 + per) - s0);
+        }
     }
     // BLOCKS: of the tiles tb .. tb + T - 1, those that some wave of the workgroup needs (its
     // rows' query block has a non-zero byte for the tile's key block), compacted into t_list
@@ -155,7 +161,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if constexpr (MASKED && !BLOCKS) {  // (the block-sparse schedule tests each tile's bits instead)
         const int hi_w = wr >= 0 ? min(kv_len, wq0 + 32 + wr) : kv_len;  // this wave's last key + 1
         T_w = max(0, min(T, (hi_w + kBlockN - 1) / kBlockN - tb));
-        if (wl >= 0) T_w0 = min(T_w, max(0, wq0 - wl) / kBlockN - tb);
+        // (a split may start past the wave's first tile: the wave then computes from its first)
+        if (wl >= 0) T_w0 = max(0, min(T_w, max(0, wq0 - wl) / kBlockN - tb));
     }
     if constexpr (!CAUSAL && !MASKED) asm volatile("" : "+v"(T_w));
 
@@ -949,6 +956,11 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__
         mw = fmaxf(mw, L.x);
         ml = fmaxf(ml, L.y);
     }
+    if (mw == -INFINITY) {  // (masked) no split holds a key of this row: o = 0, lse = -inf
+        *reinterpret_cast<u32x4*>(O + row * D + 8 * ch) = (u32x4){0u, 0u, 0u, 0u};
+        if (LSE != nullptr && ch == 0) LSE[row] = -INFINITY;
+        return;
+    }
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f, lsum = 0.f;
     for (int sp = 0; sp < n_split; ++sp) {
@@ -963,7 +975,7 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__
         acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
         acc[4] += w * b.x; acc[5] += w * b.y; acc[6] += w * b.z; acc[7] += w * b.w;
     }
-    const float inv = 1.f / wsum;  // split 0 holds key 0 of every row, so wsum >= 1
+    const float inv = 1.f / wsum;  // the split with the largest L.x has weight 1, so wsum >= 1
     const u32x4 st = {pack2<BF16>(acc[0] * inv, acc[1] * inv), pack2<BF16>(acc[2] * inv, acc[3] * inv),
                       pack2<BF16>(acc[4] * inv, acc[5] * inv), pack2<BF16>(acc[6] * inv, acc[7] * inv)};
     *reinterpret_cast<u32x4*>(O + row * D + 8 * ch) = st;
@@ -991,14 +1003,27 @@ hipError_t launch_blocks(const void* q, const void* k, const void* v, void* o, f
     return hipGetLastError();
 }
 
+// The general mask as the kernels take it (a window of N or more keys already turned into -1).
+struct fa_mask_args {
+    int H, wl, wr;
+    const int* seqlens;
+};
+
 template <int D, bool BF16, bool CAUSAL>
 hipError_t launch_split(const void* q, const void* k, const void* v, void* o, float* lse, int N, int n_qt, int BH,
-                        float c, float tau_raw, int n_split, float* po, float* pl, hipStream_t stream) {
+                        float c, float tau_raw, int n_split, float* po, float* pl, hipStream_t stream,
+                        const fa_mask_args* m = nullptr) {
     const int G = BH * n_split * n_qt;
-    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, true>), dim3(G), dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qt, G, c, tau_raw,
-                       n_split, po, pl);
+    if (m != nullptr)
+        hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, false, true, true>), dim3(G), dim3(kThreads), 0, stream,
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qt, G, c, tau_raw,
+                           n_split, po, pl, m->H, m->wl, m->wr, m->seqlens);
+    else
+        hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, true>), dim3(G), dim3(kThreads), 0, stream,
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qt, G, c, tau_raw,
+                           n_split, po, pl);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t total = (int64_t)BH * N * (D / 8);
@@ -1235,6 +1260,19 @@ int fa_fwd_splitkv_heuristic(int64_t B, int64_t H, int64_t N, int64_t d, int cau
     return static_cast<int>(best);
 }
 
+// A split-KV workspace: large enough, 16-byte aligned, and clear of every tensor of the call.
+static bool workspace_ok(const void* q, const void* k, const void* v, const void* o, const float* lse, int64_t B,
+                         int64_t H, int64_t N, int64_t d, int num_splits, const void* workspace,
+                         size_t workspace_bytes) {
+    const size_t need = fa_fwd_splitkv_workspace_size(B, H, N, d, num_splits);
+    const size_t nbytes = static_cast<size_t>(B * H * N * d * 2);
+    const size_t lbytes = static_cast<size_t>(B * H * N * 4);
+    return workspace && need != 0 && workspace_bytes >= need && !(reinterpret_cast<uintptr_t>(workspace) & 15) &&
+           !overlaps(workspace, need, q, nbytes) && !overlaps(workspace, need, k, nbytes) &&
+           !overlaps(workspace, need, v, nbytes) && !overlaps(workspace, need, o, nbytes) &&
+           !(lse && overlaps(workspace, need, lse, lbytes));
+}
+
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                    int64_t N, int64_t d, float scale, int causal, hipStream_t stream, int dtype, int num_splits,
                    void* workspace, size_t workspace_bytes) {
@@ -1245,14 +1283,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
     const int st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype, num_splits);
     if (st != FA_OK) return st;
     if (num_splits == 1) return fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype);
-    const size_t need = fa_fwd_splitkv_workspace_size(B, H, N, d, num_splits);
-    const size_t nbytes = static_cast<size_t>(B * H * N * d * 2);
-    const size_t lbytes = static_cast<size_t>(B * H * N * 4);
-    if (!workspace || need == 0 || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15) ||
-        overlaps(workspace, need, q, nbytes) || overlaps(workspace, need, k, nbytes) ||
-        overlaps(workspace, need, v, nbytes) || overlaps(workspace, need, o, nbytes) ||
-        (lse && overlaps(workspace, need, lse, lbytes)))
-        return FA_ERR_WORKSPACE;
+    if (!workspace_ok(q, k, v, o, lse, B, H, N, d, num_splits, workspace, workspace_bytes)) return FA_ERR_WORKSPACE;
     float* po = static_cast<float*>(workspace);
     float* pl = po + num_splits * B * H * N * d;
     const float c = scale * 1.4426950408889634f;
@@ -1272,6 +1303,47 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
         else e = causal ? launch_split<128, false, true>(q, k, v, o, lse, n, nq, bh, c, tau_raw, num_splits, po, pl, stream)
                         : launch_split<128, false, false>(q, k, v, o, lse, n, nq, bh, c, tau_raw, num_splits, po, pl, stream);
     }
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd_splitkv_masked(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                          int64_t N, int64_t d, float scale, hipStream_t stream, int dtype, const fa_mask* mask,
+                          int num_splits, void* workspace, size_t workspace_bytes) {
+    if (num_splits < 1 || num_splits > kMaxSplits) {
+        const int st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype, 1);
+        return st != FA_OK ? st : FA_ERR_OPTION;
+    }
+    const int st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype, num_splits);
+    if (st != FA_OK) return st;
+    if (!mask) return FA_ERR_NULL;
+    if (mask->window_left < -1 || mask->window_right < -1 || mask->window_left > INT32_MAX ||
+        mask->window_right > INT32_MAX)
+        return FA_ERR_OPTION;
+    if (reinterpret_cast<uintptr_t>(mask->seqlens_k) & 3) return FA_ERR_ALIGN;
+    const int64_t wl64 = mask->window_left >= N ? -1 : mask->window_left;
+    const int64_t wr64 = mask->window_right >= N ? -1 : mask->window_right;
+    // the two masks with kernels of their own, and the unsplit call
+    if (!mask->seqlens_k && wl64 == -1 && (wr64 == -1 || wr64 == 0))
+        return fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, wr64 == 0 ? 1 : 0, stream, dtype, num_splits,
+                              workspace, workspace_bytes);
+    if (num_splits == 1) return fa_fwd_masked(q, k, v, o, lse, B, H, N, d, scale, stream, dtype, mask);
+    if (!workspace_ok(q, k, v, o, lse, B, H, N, d, num_splits, workspace, workspace_bytes)) return FA_ERR_WORKSPACE;
+    float* po = static_cast<float*>(workspace);
+    float* pl = po + num_splits * B * H * N * d;
+    const float c = scale * 1.4426950408889634f;
+    const float tau_raw = kDefaultRescaleLog2 / c;
+    const int n = static_cast<int>(N), nq = static_cast<int>((N + kBlockM - 1) / kBlockM);
+    const int bh = static_cast<int>(B * H);
+    const fa_mask_args m = {static_cast<int>(H), static_cast<int>(wl64), static_cast<int>(wr64), mask->seqlens_k};
+    const bool bf = dtype == FA_BF16;
+    hipError_t e;
+#define FA_SPLIT_MASKED(DD, BB) \
+    launch_split<DD, BB, false>(q, k, v, o, lse, n, nq, bh, c, tau_raw, num_splits, po, pl, stream, &m)
+    if (d == 64)
+        e = bf ? FA_SPLIT_MASKED(64, true) : FA_SPLIT_MASKED(64, false);
+    else
+        e = bf ? FA_SPLIT_MASKED(128, true) : FA_SPLIT_MASKED(128, false);
+#undef FA_SPLIT_MASKED
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -191,7 +191,23 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    float scale, int causal, hipStream_t stream, int dtype,
                    int num_splits, void* workspace, size_t workspace_bytes);
 
-/* Bytes of workspace fa_fwd_splitkv needs: num_splits * B*H*N * (d + 2) * 4, or 0 when
+/*
+ * fa_fwd_splitkv_masked -- fa_fwd_masked with split-KV: the key tiles a query tile's window
+ * reaches (fa_mask: sliding window and per-batch key lengths) are cut into num_splits runs, each
+ * reduced by its own workgroup and merged as in fa_fwd_splitkv. A run may hold no allowed key of
+ * some row (or none at all): its partial result has weight 0 in the merge, and a row no split
+ * holds a key of gets o = 0 and lse = -inf, as in fa_fwd_masked.
+ * Arguments as for fa_fwd_masked plus num_splits, workspace and workspace_bytes as for
+ * fa_fwd_splitkv (the same workspace size). The masks -1/-1 and -1/0 without seqlens_k run
+ * fa_fwd_splitkv, and num_splits = 1 runs fa_fwd_masked. Errors: those of fa_fwd_masked and
+ * fa_fwd_splitkv.
+ */
+int fa_fwd_splitkv_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int64_t B, int64_t H, int64_t N, int64_t d,
+                          float scale, hipStream_t stream, int dtype, const fa_mask* mask,
+                          int num_splits, void* workspace, size_t workspace_bytes);
+
+/* Bytes of workspace fa_fwd_splitkv (and fa_fwd_splitkv_masked) needs: num_splits * B*H*N * (d + 2) * 4, or 0 when
  * num_splits <= 1 or an argument is out of range. */
 size_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int num_splits);
 
