@@ -140,7 +140,7 @@ __device__ __forceinline__ void store_row16(uint16_t* row, const f32x4 (&acc)[D 
 // BLOCKS (both kernels, on top of MASKED): the block mask of fa_fwd_blocksparse. Each workgroup
 // lists the tiles one of its waves needs (compact_tiles) and walks only those; a wave computes a
 // listed tile only when its own bit is set.
-template <int D, bool BF16, bool CAUSAL, bool MASKED = false, bool BLOCKS = false>
+template <int D, bool BF16, bool CAUSAL, bool MASKED = false, bool BLOCKS = false, bool CHUNKED = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
@@ -220,22 +220,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         T_w = max(0, min(T, (hi_w + kKeyTile - 1) / kKeyTile - tb));
         if (wl >= 0) T_w0 = min(T_w, max(0, wq0 - wl) / kKeyTile - tb);
     }
-    // BLOCKS: tile index j becomes a position in t_list; every wave walks the whole list
+    // BLOCKS: tile index j becomes a position in t_list; every wave walks the whole list.
+    // CHUNKED: the list is built and walked kMaxListTiles candidates at a time (below).
     __shared__ int t_list[BLOCKS ? kMaxListTiles : 1];
     __shared__ uint8_t t_wm[BLOCKS ? kMaxListTiles : 1];
     __shared__ int t_cnt[BLOCKS ? kWaves : 1];
+    const uint8_t* mb = BLOCKS ? bmask + (int64_t)(bh / H) * bstride_b + (int64_t)(bh % H) * bstride_h : nullptr;
+    const int n_kb = BLOCKS ? (N + bk - 1) / bk : 0;
+    // wave w needs key tile t when its rows and the tile's keys hold an allowed pair: the block
+    // byte is set and the offsets key - row, which run over one interval, meet the window
+    auto need = [&](int w, int t) {
+        const int r0 = q0 + 32 * w, r1 = min(r0 + 32, N) - 1;
+        const int c0 = t * kKeyTile, c1 = min(c0 + kKeyTile, kv_len) - 1;
+        return r0 < N && c0 < kv_len && (wr < 0 || c0 - r1 <= wr) && (wl < 0 || r0 - c1 <= wl) &&
+               mb[(int64_t)(r0 / bq) * n_kb + c0 / bk] != 0;
+    };
+    const int T_cand = T;
+    if constexpr (BLOCKS && !CHUNKED) T = compact_tiles<kWaves>(tb, T, need, t_list, t_wm, t_cnt, tid);
     if constexpr (BLOCKS) {
-        const uint8_t* mb = bmask + (int64_t)(bh / H) * bstride_b + (int64_t)(bh % H) * bstride_h;
-        const int n_kb = (N + bk - 1) / bk;
-        // wave w needs key tile t when its rows and the tile's keys hold an allowed pair: the
-        // block byte is set and the offsets key - row, which run over one interval, meet the window
-        auto need = [&](int w, int t) {
-            const int r0 = q0 + 32 * w, r1 = min(r0 + 32, N) - 1;
-            const int c0 = t * kKeyTile, c1 = min(c0 + kKeyTile, kv_len) - 1;
-            return r0 < N && c0 < kv_len && (wr < 0 || c0 - r1 <= wr) && (wl < 0 || r0 - c1 <= wl) &&
-                   mb[(int64_t)(r0 / bq) * n_kb + c0 / bk] != 0;
-        };
-        T = compact_tiles<kWaves>(tb, T, need, t_list, t_wm, t_cnt, tid);
         T_w0 = 0;
         T_w = T;
     }
@@ -336,24 +338,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int T_w0s = __builtin_amdgcn_readfirstlane(T_w0);
     // BLOCKS: this wave's bit for list entry j
     auto mine = [&](int j) { return !BLOCKS || ((__builtin_amdgcn_readfirstlane(t_wm[j]) >> wave_s) & 1); };
-    stage_rows<D>(Kh, key_tile(0) * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
-    stage_rows<D>(Vh, key_tile(0) * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
-    for (int j = 0; j < T; j += 2) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (j + 1 < T) {
-            stage_rows<D>(Kh, key_tile(j + 1) * kKeyTile, kKeyTile, N, k_lds1, wave_s, lane);
-            stage_rows<D>(Vh, key_tile(j + 1) * kKeyTile, kKeyTile, N, v_lds1, wave_s, lane);
+    auto walk = [&]() __attribute__((always_inline)) {
+        stage_rows<D>(Kh, key_tile(0) * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
+        stage_rows<D>(Vh, key_tile(0) * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
+        for (int j = 0; j < T; j += 2) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (j + 1 < T) {
+                stage_rows<D>(Kh, key_tile(j + 1) * kKeyTile, kKeyTile, N, k_lds1, wave_s, lane);
+                stage_rows<D>(Vh, key_tile(j + 1) * kKeyTile, kKeyTile, N, v_lds1, wave_s, lane);
+            }
+            if ((!MASKED || j >= T_w0s) && j < T_ws && mine(j)) tile(j, k_lds0, v_lds0);
+            if (j + 1 >= T) break;
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (j + 2 < T) {
+                stage_rows<D>(Kh, key_tile(j + 2) * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
+                stage_rows<D>(Vh, key_tile(j + 2) * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
+            }
+            if ((!MASKED || j + 1 >= T_w0s) && j + 1 < T_ws && mine(j + 1)) tile(j + 1, k_lds1, v_lds1);
         }
-        if ((!MASKED || j >= T_w0s) && j < T_ws && mine(j)) tile(j, k_lds0, v_lds0);
-        if (j + 1 >= T) break;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (j + 2 < T) {
-            stage_rows<D>(Kh, key_tile(j + 2) * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
-            stage_rows<D>(Vh, key_tile(j + 2) * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
+    };
+    if constexpr (CHUNKED) {
+        // acc carries over from chunk to chunk. Every wave has left the previous chunk's tiles
+        // (t_list, t_wm and both buffers read for the last time; no load in flight) before the
+        // first barrier of compact_tiles, which writes the list only after it.
+        for (int cb = 0; cb < T_cand; cb += kMaxListTiles) {
+            T = compact_tiles<kWaves>(tb + cb, min(kMaxListTiles, T_cand - cb), need, t_list, t_wm, t_cnt, tid);
+            T_ws = T;
+            if (T > 0) walk();
         }
-        if ((!MASKED || j + 1 >= T_w0s) && j + 1 < T_ws && mine(j + 1)) tile(j + 1, k_lds1, v_lds1);
+    } else {
+        walk();
     }
 
 #pragma unroll
@@ -363,7 +379,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 }
 
-template <int D, bool BF16, bool CAUSAL, bool MASKED = false, bool BLOCKS = false>
+template <int D, bool BF16, bool CAUSAL, bool MASKED = false, bool BLOCKS = false, bool CHUNKED = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ DELTA,
@@ -456,23 +472,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     // The query tiles walked: j0 + p for p < n_list, or (BLOCKS) the listed tiles t_list[p] that one
     // of the waves needs, a wave computing the ones whose bit it holds.
+    // (CHUNKED: the list is built and walked kMaxListTiles candidates at a time, below.)
     int n_list = n_steps - j0;
     __shared__ int t_list[BLOCKS ? kMaxListTiles : 1];
     __shared__ uint8_t t_wm[BLOCKS ? kMaxListTiles : 1];
     __shared__ int t_cnt[BLOCKS ? kWaves : 1];
-    if constexpr (BLOCKS) {
-        const uint8_t* mb = bmask + (int64_t)(bh / H) * bstride_b + (int64_t)(bh % H) * bstride_h;
-        const int n_kb = (N + bk - 1) / bk;
-        // wave w: row half w >> 2 of query tile t against key group w & 3 (the window test is the
-        // dQ kernel's)
-        auto need = [&](int w, int t) {
-            const int r0 = t * kQueryTile + 32 * (w >> 2), r1 = min(r0 + 32, N) - 1;
-            const int c0 = k0 + 32 * (w & 3), c1 = min(c0 + 32, kv_len) - 1;
-            return r0 < N && c0 < kv_len && (wr < 0 || c0 - r1 <= wr) && (wl < 0 || r0 - c1 <= wl) &&
-                   mb[(int64_t)(r0 / bq) * n_kb + c0 / bk] != 0;
-        };
-        n_list = compact_tiles<kWaves>(j0, n_list, need, t_list, t_wm, t_cnt, tid);
-    }
+    const uint8_t* mb = BLOCKS ? bmask + (int64_t)(bh / H) * bstride_b + (int64_t)(bh % H) * bstride_h : nullptr;
+    const int n_kb = BLOCKS ? (N + bk - 1) / bk : 0;
+    // wave w: row half w >> 2 of query tile t against key group w & 3 (the window test is the dQ
+    // kernel's)
+    auto need = [&](int w, int t) {
+        const int r0 = t * kQueryTile + 32 * (w >> 2), r1 = min(r0 + 32, N) - 1;
+        const int c0 = k0 + 32 * (w & 3), c1 = min(c0 + 32, kv_len) - 1;
+        return r0 < N && c0 < kv_len && (wr < 0 || c0 - r1 <= wr) && (wl < 0 || r0 - c1 <= wl) &&
+               mb[(int64_t)(r0 / bq) * n_kb + c0 / bk] != 0;
+    };
+    const int n_cand = n_list;
+    if constexpr (BLOCKS && !CHUNKED) n_list = compact_tiles<kWaves>(j0, n_list, need, t_list, t_wm, t_cnt, tid);
     auto q_tile = [&](int p) { return BLOCKS ? __builtin_amdgcn_readfirstlane(t_list[p]) : j0 + p; };
     auto mine = [&](int p) { return !BLOCKS || ((__builtin_amdgcn_readfirstlane(t_wm[p]) >> wave_s) & 1); };
 
@@ -607,30 +623,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // are requested right after the barrier that publishes p; wave 0 fetches the statistics of
     // p + 1 into registers at the same time and writes them to LDS at the end of the step (the
     // buffer they go to was last read in step p - 1, before that barrier).
-    if (wave == 0) stats_load(q_tile(0));
-    stage_rows<D>(Qh, q_tile(0) * kQueryTile, kQueryTile, N, q_lds0, wave_s, lane);
-    stage_rows<D>(dOh, q_tile(0) * kQueryTile, kQueryTile, N, do_lds0, wave_s, lane);
-    if (wave == 0) stats_store(0);
-    for (int p = 0; p < n_list; p += 2) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (p + 1 < n_list) {
-            if (wave == 0) stats_load(q_tile(p + 1));
-            stage_rows<D>(Qh, q_tile(p + 1) * kQueryTile, kQueryTile, N, q_lds1, wave_s, lane);
-            stage_rows<D>(dOh, q_tile(p + 1) * kQueryTile, kQueryTile, N, do_lds1, wave_s, lane);
+    auto walk = [&]() __attribute__((always_inline)) {
+        if (wave == 0) stats_load(q_tile(0));
+        stage_rows<D>(Qh, q_tile(0) * kQueryTile, kQueryTile, N, q_lds0, wave_s, lane);
+        stage_rows<D>(dOh, q_tile(0) * kQueryTile, kQueryTile, N, do_lds0, wave_s, lane);
+        if (wave == 0) stats_store(0);
+        for (int p = 0; p < n_list; p += 2) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (p + 1 < n_list) {
+                if (wave == 0) stats_load(q_tile(p + 1));
+                stage_rows<D>(Qh, q_tile(p + 1) * kQueryTile, kQueryTile, N, q_lds1, wave_s, lane);
+                stage_rows<D>(dOh, q_tile(p + 1) * kQueryTile, kQueryTile, N, do_lds1, wave_s, lane);
+            }
+            if (mine(p)) step(q_tile(p), q_lds0, do_lds0, 0);
+            if (p + 1 >= n_list) break;
+            if (wave == 0) stats_store(1);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (p + 2 < n_list) {
+                if (wave == 0) stats_load(q_tile(p + 2));
+                stage_rows<D>(Qh, q_tile(p + 2) * kQueryTile, kQueryTile, N, q_lds0, wave_s, lane);
+                stage_rows<D>(dOh, q_tile(p + 2) * kQueryTile, kQueryTile, N, do_lds0, wave_s, lane);
+            }
+            if (mine(p + 1)) step(q_tile(p + 1), q_lds1, do_lds1, 1);
+            if (p + 2 < n_list && wave == 0) stats_store(0);
         }
-        if (mine(p)) step(q_tile(p), q_lds0, do_lds0, 0);
-        if (p + 1 >= n_list) break;
-        if (wave == 0) stats_store(1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (p + 2 < n_list) {
-            if (wave == 0) stats_load(q_tile(p + 2));
-            stage_rows<D>(Qh, q_tile(p + 2) * kQueryTile, kQueryTile, N, q_lds0, wave_s, lane);
-            stage_rows<D>(dOh, q_tile(p + 2) * kQueryTile, kQueryTile, N, do_lds0, wave_s, lane);
+    };
+    if constexpr (CHUNKED) {
+        // dK and dV carry over from chunk to chunk. Every wave has left the previous chunk's
+        // steps (t_list, t_wm, the tile buffers and the statistics read for the last time; no load
+        // in flight) before the first barrier of compact_tiles, which writes the list only after it.
+        for (int cb = 0; cb < n_cand; cb += kMaxListTiles) {
+            n_list = compact_tiles<kWaves>(j0 + cb, min(kMaxListTiles, n_cand - cb), need, t_list, t_wm, t_cnt, tid);
+            if (n_list > 0) walk();
         }
-        if (mine(p + 1)) step(q_tile(p + 1), q_lds1, do_lds1, 1);
-        if (p + 2 < n_list && wave == 0) stats_store(0);
+    } else {
+        walk();
     }
 
     // The two waves of a key group summed over different query rows: the second half hands its
@@ -671,7 +700,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 }
 
-template <int D, bool BF16, bool CAUSAL, bool MASKED = false, bool BLOCKS = false>
+template <int D, bool BF16, bool CAUSAL, bool MASKED = false, bool BLOCKS = false, bool CHUNKED = false>
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                       void* dq, void* dk, void* dv, float* delta, int N, int BH, float c, float scale,
                       hipStream_t stream, int H = 1, int wl = -1, int wr = -1, const int* seqlens = nullptr,
@@ -683,12 +712,12 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
     const auto* K = static_cast<const uint16_t*>(k);
     const auto* V = static_cast<const uint16_t*>(v);
     const auto* dO = static_cast<const uint16_t*>(dout);
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, CAUSAL, MASKED, BLOCKS>), dim3(Gq), dim3(kThreads), 0, stream, Q,
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, CAUSAL, MASKED, BLOCKS, CHUNKED>), dim3(Gq), dim3(kThreads), 0, stream, Q,
                        K, V, static_cast<const uint16_t*>(o), dO, lse, delta, static_cast<uint16_t*>(dq), N, n_qt, Gq,
                        c, scale, H, wl, wr, seqlens, bmask, bq, bk, bstride_b, bstride_h);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, CAUSAL, MASKED, BLOCKS>), dim3(Gk), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, CAUSAL, MASKED, BLOCKS, CHUNKED>), dim3(Gk), dim3(kThreads), 0, stream,
                        Q, K, V, dO, lse, delta, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), N, n_kt, Gk,
                        c, scale, H, wl, wr, seqlens, bmask, bq, bk, bstride_b, bstride_h);
     return hipGetLastError();
@@ -806,9 +835,6 @@ int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* 
     if (blocks->block_q < 64 || blocks->block_k < 64 || blocks->block_q % 64 != 0 || blocks->block_k % 64 != 0 ||
         blocks->block_q > INT32_MAX || blocks->block_k > INT32_MAX || blocks->stride_b < 0 || blocks->stride_h < 0)
         return FA_ERR_OPTION;
-    // the work lists hold one entry per 64-key tile (dQ) or 64-row tile (dK, dV)
-    if (N > static_cast<int64_t>(kKeyTile) * kMaxListTiles || N > static_cast<int64_t>(kQueryTile) * kMaxListTiles)
-        return FA_ERR_SHAPE;
     int wl, wr;
     const int32_t* seqlens;
     const int ms = read_mask(mask, N, wl, wr, seqlens);
@@ -818,13 +844,25 @@ int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* 
     const int bq = static_cast<int>(blocks->block_q), bk = static_cast<int>(blocks->block_k);
     const bool bf = dtype == FA_BF16;
     hipError_t e;
-#define FA_BWD_BLOCKS(DD, BB)                                                                                     \
-    launch_bwd<DD, BB, false, true, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, n, BH, c, scale, stream, h, wl, \
-                                          wr, seqlens, blocks->mask, bq, bk, blocks->stride_b, blocks->stride_h)
-    if (d == 64)
-        e = bf ? FA_BWD_BLOCKS(64, true) : FA_BWD_BLOCKS(64, false);
-    else
-        e = bf ? FA_BWD_BLOCKS(128, true) : FA_BWD_BLOCKS(128, false);
+    // One work list holds every 64-key (dQ) or 64-row (dK, dV) tile up to 64 * kMaxListTiles;
+    // longer sequences take the kernels that build it a chunk at a time (they need more registers).
+    const bool chunked = N > static_cast<int64_t>(kKeyTile) * kMaxListTiles ||
+                         N > static_cast<int64_t>(kQueryTile) * kMaxListTiles;
+#define FA_BWD_BLOCKS(DD, BB, CH)                                                                                 \
+    launch_bwd<DD, BB, false, true, true, CH>(q, k, v, o, dout, lse, dq, dk, dv, delta, n, BH, c, scale, stream, h, \
+                                              wl, wr, seqlens, blocks->mask, bq, bk, blocks->stride_b,            \
+                                              blocks->stride_h)
+    if (d == 64) {
+        if (chunked)
+            e = bf ? FA_BWD_BLOCKS(64, true, true) : FA_BWD_BLOCKS(64, false, true);
+        else
+            e = bf ? FA_BWD_BLOCKS(64, true, false) : FA_BWD_BLOCKS(64, false, false);
+    } else {
+        if (chunked)
+            e = bf ? FA_BWD_BLOCKS(128, true, true) : FA_BWD_BLOCKS(128, false, true);
+        else
+            e = bf ? FA_BWD_BLOCKS(128, true, false) : FA_BWD_BLOCKS(128, false, false);
+    }
 #undef FA_BWD_BLOCKS
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

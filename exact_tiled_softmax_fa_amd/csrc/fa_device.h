@@ -20,7 +20,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin to 8 XCDs
-constexpr int kMaxListTiles = 1024;  // block-sparse work lists: 64-row or 64-key tiles, N <= 65536
+constexpr int kMaxListTiles = 1024;  // block-sparse work lists: 64-row or 64-key tiles (per chunk)
 
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {

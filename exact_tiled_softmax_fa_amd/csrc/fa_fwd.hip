@@ -57,7 +57,10 @@ constexpr int kDefaultVariant = 1;          // kernel fa_fwd runs: 1 = 32 rows p
 // i - wl <= j (wl >= 0), j <= i + wr (wr >= 0) and j < seqlens[b] (seqlens given). Key tiles
 // outside the workgroup's window are neither loaded nor computed; a row with no allowed key
 // gets o = 0 and lse = -inf.
-template <int D, bool BF16, bool CAUSAL, bool SPLIT = false, bool MASKED = false, bool BLOCKS = false>
+// CHUNKED (with BLOCKS): the list of needed key tiles is built and walked kMaxListTiles candidates
+// at a time, for sequences longer than one list holds (64 * kMaxListTiles keys).
+template <int D, bool BF16, bool CAUSAL, bool SPLIT = false, bool MASKED = false, bool BLOCKS = false,
+          bool CHUNKED = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qt, int G, float c, float tau_raw,
@@ -66,6 +69,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     int bq = 0, int bk = 0, int64_t bstride_b = 0, int64_t bstride_h = 0) {
     static_assert(!(MASKED && CAUSAL), "the general mask replaces the causal one");
     static_assert(!BLOCKS || (MASKED && !SPLIT), "the block mask rides on the general mask, unsplit");
+    static_assert(!CHUNKED || BLOCKS, "chunks are chunks of the block-sparse work list");
     constexpr int DT = D / 32;                 // 32-column k-steps of the first product
     constexpr int DB = D / 16;                 // 16-column blocks of the output
     constexpr int CPR = D / 8;                 // 16-byte chunks per row
@@ -137,19 +141,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // rows' query block has a non-zero byte for the tile's key block), compacted into t_list
     // (absolute tile index) with one bit per wave in t_wm; from here on a tile index j is a
     // position in that list. (Block sizes are multiples of 64: one byte decides a wave's whole
-    // 32 x 64 part of a tile.)
+    // 32 x 64 part of a tile.) CHUNKED builds the list in the schedule, a chunk at a time.
     __shared__ int t_list[BLOCKS ? kMaxListTiles : 1];
     __shared__ uint8_t t_wm[BLOCKS ? kMaxListTiles : 1];
     __shared__ int t_cnt[BLOCKS ? kWaves : 1];
-    if constexpr (BLOCKS) {
-        const uint8_t* mb = bmask + (int64_t)(bh / H) * bstride_b + (int64_t)(bh % H) * bstride_h;
-        const int n_kb = (N + bk - 1) / bk;
-        auto need = [&](int w, int t) {
-            const int r0 = q0 + 32 * w;
-            return r0 < N && mb[(int64_t)(r0 / bq) * n_kb + t * kBlockN / bk] != 0;
-        };
-        T = compact_tiles<kWaves>(tb, T, need, t_list, t_wm, t_cnt, tid);
-    }
+    const uint8_t* mb = BLOCKS ? bmask + (int64_t)(bh / H) * bstride_b + (int64_t)(bh % H) * bstride_h : nullptr;
+    const int n_kb = BLOCKS ? (N + bk - 1) / bk : 0;
+    auto need = [&](int w, int t) {
+        const int r0 = q0 + 32 * w;
+        return r0 < N && mb[(int64_t)(r0 / bq) * n_kb + t * kBlockN / bk] != 0;
+    };
+    if constexpr (BLOCKS && !CHUNKED) T = compact_tiles<kWaves>(tb, T, need, t_list, t_wm, t_cnt, tid);
     // tiles this wave computes: causal waves stop at the tile holding their last row
     // (Non-causal: T_w = T, hidden from the compiler. Folded away, the tests on it disappear and
     // the compiler keeps the output accumulators of the loop's two exit paths in two register
@@ -392,14 +394,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         // (scores, mask, max, exponentials, product with V) only when its own bit is set, so the
         // waves of a workgroup whose query blocks differ skip each other's tiles; the two waves
         // of a SIMD still overlap each other's matrix and vector work.
-        issue(Kh, 0, k_lds0, false);
-        issue(Vh, 0, v_lds0, true);
         const int wbit = 1 << wave_s;
+        int Tc = T;  // entries of the list being walked
         auto tile = [&](int j, const uint16_t* kt, const uint16_t* vt, uint16_t* kn, uint16_t* vn)
                         __attribute__((always_inline)) {
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();  // barrier j
-            if (j + 1 < T) {
+            if (j + 1 < Tc) {
                 issue(Kh, j + 1, kn, false);
                 issue(Vh, j + 1, vn, true);
             }
@@ -411,10 +412,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 pv(vt);
             }
         };
-        for (int j = 0; j < T; j += 2) {
-            tile(j, k_lds0, v_lds0, k_lds1, v_lds1);
-            if (j + 1 >= T) break;
-            tile(j + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+        auto walk = [&]() __attribute__((always_inline)) {
+            issue(Kh, 0, k_lds0, false);
+            issue(Vh, 0, v_lds0, true);
+            for (int j = 0; j < Tc; j += 2) {
+                tile(j, k_lds0, v_lds0, k_lds1, v_lds1);
+                if (j + 1 >= Tc) break;
+                tile(j + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+            }
+        };
+        if constexpr (CHUNKED) {
+            // The online state carries over from chunk to chunk. Every wave has left the previous
+            // chunk's tiles (t_list, t_wm and both tile buffers read for the last time; no load in
+            // flight) before the first barrier of compact_tiles, which writes the list only after it.
+            for (int cb = 0; cb < T; cb += kMaxListTiles) {
+                Tc = compact_tiles<kWaves>(tb + cb, min(kMaxListTiles, T - cb), need, t_list, t_wm, t_cnt, tid);
+                if (Tc > 0) walk();
+            }
+        } else {
+            walk();
         }
     } else {
         issue(Kh, 0, k_lds0, false);
@@ -996,10 +1012,18 @@ template <int D, bool BF16>
 hipError_t launch_blocks(const void* q, const void* k, const void* v, void* o, float* lse, int N, int n_qt, int G,
                          float c, float tau_raw, int H, int wl, int wr, const int* seqlens, const uint8_t* bm, int bq,
                          int bk, int64_t sb, int64_t sh, hipStream_t stream) {
-    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, false, false, true, true>), dim3(G), dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qt, G, c, tau_raw, 1,
-                       nullptr, nullptr, H, wl, wr, seqlens, bm, bq, bk, sb, sh);
+    // one list holds every key tile up to 64 * kMaxListTiles keys; longer sequences take the
+    // kernel that builds it a chunk at a time (it needs more registers)
+    if (N <= kBlockN * kMaxListTiles)
+        hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, false, false, true, true>), dim3(G), dim3(kThreads), 0, stream,
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qt, G, c, tau_raw, 1,
+                           nullptr, nullptr, H, wl, wr, seqlens, bm, bq, bk, sb, sh);
+    else
+        hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, false, false, true, true, true>), dim3(G), dim3(kThreads), 0,
+                           stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qt, G, c, tau_raw, 1,
+                           nullptr, nullptr, H, wl, wr, seqlens, bm, bq, bk, sb, sh);
     return hipGetLastError();
 }
 
@@ -1192,7 +1216,6 @@ int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, flo
     if (blocks->block_q < 64 || blocks->block_k < 64 || blocks->block_q % 64 != 0 || blocks->block_k % 64 != 0 ||
         blocks->block_q > INT32_MAX || blocks->block_k > INT32_MAX || blocks->stride_b < 0 || blocks->stride_h < 0)
         return FA_ERR_OPTION;
-    if (N > static_cast<int64_t>(kBlockN) * kMaxListTiles) return FA_ERR_SHAPE;
     int64_t wl64 = -1, wr64 = -1;
     const int32_t* seqlens = nullptr;
     if (mask) {

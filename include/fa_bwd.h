@@ -96,8 +96,8 @@ int fa_bwd_masked(const void* q, const void* k, const void* v, const void* o,
  * a key no row allows dk = dv = 0.
  * Arguments as for fa_bwd_masked, plus `blocks` (not NULL); `mask` may be NULL.
  * Errors: those of fa_bwd_masked; FA_ERR_NULL for a NULL `blocks` or blocks->mask,
- * FA_ERR_OPTION for a block size that is not a positive multiple of 64 or a negative stride,
- * FA_ERR_SHAPE for N > 65536.
+ * FA_ERR_OPTION for a block size that is not a positive multiple of 64 or a negative stride.
+ * Any N that fa_bwd takes: the work lists are built 1024 tiles at a time.
  */
 int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o,
                        const void* dout, const float* lse,

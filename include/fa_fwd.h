@@ -159,7 +159,8 @@ typedef struct fa_block_mask {
  * tiles that one of its 32-row groups needs; a row with no allowed key gets o = 0, lse = -inf.
  * Arguments as for fa_fwd_masked, plus `blocks` (not NULL). Errors: those of fa_fwd_masked;
  * FA_ERR_NULL for a NULL `blocks` or blocks->mask, FA_ERR_OPTION for a block size that is not a
- * positive multiple of 64 or a negative stride, FA_ERR_SHAPE for N > 65536.
+ * positive multiple of 64 or a negative stride. Any N that fa_fwd takes: the list of a query
+ * tile's key tiles is built 1024 candidates at a time.
  */
 int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
                        int64_t B, int64_t H, int64_t N, int64_t d,

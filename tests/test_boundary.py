@@ -226,7 +226,7 @@ FAR = dict(q=0x10000000, k=0x20000000, v=0x30000000, o=0x40000000, lse=0x5000000
     ((0xC00000, 64, 64, 0, -8), None, {}, 9), ((0xC00000, 1 << 31, 64, 0, 0), None, {}, 9),
     ((0xC00000, 64, 64, 0, 0), (-2, 0, None), {}, 9), ((0xC00000, 64, 64, 0, 0), (4, 0, 0x600002), {}, 5),
     ((0xC00000, 64, 64, 0, 0), None, dict(q=None), 1), ((0xC00000, 64, 64, 0, 0), None, dict(d=96), 3),
-    ((0xC00000, 64, 64, 0, 0), None, dict(o=QA), 7), ((0xC00000, 64, 64, 0, 0), None, dict(N=65537, **FAR), 2),
+    ((0xC00000, 64, 64, 0, 0), None, dict(o=QA), 7), ((0xC00000, 64, 64, 0, 0), None, dict(N=1 << 24, **FAR), 2),
 ])
 def test_blocksparse_argument_errors(L, blocks, mask, kw, code):
     import exact_tiled_softmax_fa_amd as fa
@@ -269,7 +269,7 @@ BWD_FAR = {name: (i + 1) << 28 for i, name in enumerate(("q", "k", "v", "o", "do
     ((0xC00000, 64, 64, 0, 0), None, dict(q=None), 1), ((0xC00000, 64, 64, 0, 0), None, dict(delta=None), 1),
     ((0xC00000, 64, 64, 0, 0), None, dict(d=96), 3), ((0xC00000, 64, 64, 0, 0), None, dict(dk=0x100000), 7),
     ((0xC00000, 64, 64, 0, 0), None, dict(scale=-1.0), 6),
-    ((0xC00000, 64, 64, 0, 0), None, dict(N=65537, **BWD_FAR), 2),
+    ((0xC00000, 64, 64, 0, 0), None, dict(N=1 << 24, **BWD_FAR), 2),
 ])
 def test_bwd_blocksparse_argument_errors(L, blocks, mask, kw, code):
     import exact_tiled_softmax_fa_amd as fa
