@@ -10,8 +10,8 @@ head), with q, k, v already resident in device memory. The default workload is
 B=1, H=32, N=8192, d=128, non-causal, fp16. Prints one JSON line.
 
 --splits S times fa_fwd_splitkv with S key splits (0: the library's heuristic) instead of
-fa_fwd (with a window: fa_fwd_splitkv_masked); the roofline then covers both of its kernels
-(split reduction and merge).
+fa_fwd (with a window: fa_fwd_splitkv_masked; with a block mask: fa_fwd_splitkv_blocksparse);
+the roofline then covers both of its kernels (split reduction and merge).
 
 --window-left L / --window-right R time fa_fwd_masked (with --pass bwd: fa_bwd_masked) with that
 sliding window (-1 = no limit; the workload's causal flag is then ignored) and price it by the
@@ -296,9 +296,14 @@ def main():
                                                                                    args.block_size))
         bmask_dev = torch.from_numpy(bmask).cuda()
 
-        def step():  # noqa: F811
-            fa.forward_blocksparse(q, k, v, bmask_dev, args.block_size, args.block_size, scale=w.scale, out=o,
-                                   lse=lse)
+        if splits is not None:  # the block-sparse split-KV forward
+            def step():  # noqa: F811
+                fa.forward_blocksparse(q, k, v, bmask_dev, args.block_size, args.block_size, scale=w.scale, out=o,
+                                       lse=lse, num_splits=splits, workspace=ws)
+        else:
+            def step():  # noqa: F811
+                fa.forward_blocksparse(q, k, v, bmask_dev, args.block_size, args.block_size, scale=w.scale, out=o,
+                                       lse=lse)
 
     if args.which == "bwd":
         step()

@@ -89,6 +89,9 @@ def lib():
         L.fa_fwd_splitkv_masked.restype = ctypes.c_int
         L.fa_fwd_splitkv_masked.argtypes = L.fa_fwd_masked.argtypes + [ctypes.c_int, ctypes.c_void_p,
                                                                         ctypes.c_size_t]
+        L.fa_fwd_splitkv_blocksparse.restype = ctypes.c_int
+        L.fa_fwd_splitkv_blocksparse.argtypes = L.fa_fwd_blocksparse.argtypes + [ctypes.c_int, ctypes.c_void_p,
+                                                                                  ctypes.c_size_t]
         L.fa_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
         L.fa_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int]
         L.fa_fwd_splitkv_heuristic.restype = ctypes.c_int
@@ -432,16 +435,28 @@ def fa_fwd_blocksparse(q, k, v, o, lse, B, H, N, d, scale, stream, dtype, mask, 
                                         ctypes.byref(blocks) if blocks is not None else None))
 
 
+def fa_fwd_splitkv_blocksparse(q, k, v, o, lse, B, H, N, d, scale, stream, dtype, mask, blocks, num_splits,
+                               workspace, workspace_bytes) -> int:
+    """Raw call of the C entry point fa_fwd_splitkv_blocksparse (mask: an FaMask or None; blocks:
+    an FaBlockMask or None); returns the status code."""
+    return int(lib().fa_fwd_splitkv_blocksparse(q, k, v, o, lse, B, H, N, d, float(scale), stream, int(dtype),
+                                                ctypes.byref(mask) if mask is not None else None,
+                                                ctypes.byref(blocks) if blocks is not None else None,
+                                                int(num_splits), workspace, int(workspace_bytes)))
+
+
 def forward_blocksparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: torch.Tensor,
                         block_q: int, block_k: int, window_left: int = -1, window_right: int = -1,
                         seqlens_k: torch.Tensor = None, scale=None, out: torch.Tensor = None,
-                        lse: torch.Tensor = None):
+                        lse: torch.Tensor = None, num_splits=None, workspace: torch.Tensor = None):
     """Block-sparse attention (include/fa_fwd.h, fa_block_mask): the pair (i, j) is allowed when
     block_mask[.., i // block_q, j // block_k] != 0 and the window / key-length mask of
     forward_masked allows it. block_mask: a contiguous uint8 (or bool) GPU tensor of shape
     [n_qb, n_kb] (all heads), [H, n_qb, n_kb] (per head) or [B, H, n_qb, n_kb], with
     n_qb = ceil(N / block_q), n_kb = ceil(N / block_k); block sizes are multiples of 64.
-    Returns (o, lse); rows with no allowed key get o = 0 and lse = -inf."""
+    Returns (o, lse); rows with no allowed key get o = 0 and lse = -inf. num_splits (an int) runs
+    fa_fwd_splitkv_blocksparse with that many key splits of each query tile's window; workspace
+    as for forward (allocated when not given)."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dim() != 4 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous GPU tensor [B, H, N, d]")
@@ -457,6 +472,22 @@ def forward_blocksparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block
     _check_like("out", out, q)
     _check_like("lse", lse, q, torch.float32, (B, H, N))
     mask = FaMask(int(window_left), int(window_right), seqlens_k.data_ptr() if seqlens_k is not None else None)
+    if num_splits is not None:
+        if num_splits < 1:
+            raise ValueError("num_splits must be at least 1")
+        need = splitkv_workspace_size(B, H, N, d, num_splits)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        elif not workspace.is_cuda or workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on q's device")
+        with torch.cuda.device(q.device):
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+            st = fa_fwd_splitkv_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                            B, H, N, d, scale, stream, _DTYPES[q.dtype], mask, blocks, num_splits,
+                                            workspace.data_ptr(), workspace.numel() * workspace.element_size())
+        if st != 0:
+            raise FaError(st, status_string(st))
+        return out, lse
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         st = fa_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,

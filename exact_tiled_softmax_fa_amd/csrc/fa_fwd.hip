@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     int wr = -1, const int* __restrict__ seqlens = nullptr, const uint8_t* __restrict__ bmask = nullptr,
     int bq = 0, int bk = 0, int64_t bstride_b = 0, int64_t bstride_h = 0) {
     static_assert(!(MASKED && CAUSAL), "the general mask replaces the causal one");
-    static_assert(!BLOCKS || (MASKED && !SPLIT), "the block mask rides on the general mask, unsplit");
+    static_assert(!BLOCKS || MASKED, "the block mask rides on the general mask");
     static_assert(!CHUNKED || BLOCKS, "chunks are chunks of the block-sparse work list");
     constexpr int DT = D / 32;                 // 32-column k-steps of the first product
     constexpr int DB = D / 16;                 // 16-column blocks of the output
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int hi = wr >= 0 ? min(kv_len, q0 + kBlockM + wr) : kv_len;
         tb = lo / kBlockN;
         T = max(0, (hi + kBlockN - 1) / kBlockN - tb);
-        if constexpr (SPLIT) {  // this split's run of the window's tiles (possibly none)
+        if constexpr (SPLIT) {  // this split's run of the window's tiles (possibly none; BLOCKS lists within it)
             const int per = (T + n_split - 1) / n_split;
             const int s0 = (vh % n_split) * per;
             tb += s0;
@@ -1032,13 +1032,30 @@ struct fa_mask_args {
     int H, wl, wr;
     const int* seqlens;
 };
+// A block mask as the kernels take it.
+struct fa_block_args {
+    const uint8_t* mask;
+    int bq, bk;
+    int64_t sb, sh;
+};
 
 template <int D, bool BF16, bool CAUSAL>
 hipError_t launch_split(const void* q, const void* k, const void* v, void* o, float* lse, int N, int n_qt, int BH,
                         float c, float tau_raw, int n_split, float* po, float* pl, hipStream_t stream,
-                        const fa_mask_args* m = nullptr) {
+                        const fa_mask_args* m = nullptr, const fa_block_args* bl = nullptr) {
     const int G = BH * n_split * n_qt;
-    if (m != nullptr)
+    // (a split's run of key tiles can exceed one block-sparse list only past 64 * kMaxListTiles keys)
+    if (bl != nullptr && N <= kBlockN * kMaxListTiles)
+        hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, false, true, true, true>), dim3(G), dim3(kThreads), 0, stream,
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qt, G, c, tau_raw,
+                           n_split, po, pl, m->H, m->wl, m->wr, m->seqlens, bl->mask, bl->bq, bl->bk, bl->sb, bl->sh);
+    else if (bl != nullptr)
+        hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, false, true, true, true, true>), dim3(G), dim3(kThreads), 0,
+                           stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qt, G, c, tau_raw,
+                           n_split, po, pl, m->H, m->wl, m->wr, m->seqlens, bl->mask, bl->bq, bl->bk, bl->sb, bl->sh);
+    else if (m != nullptr)
         hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, false, true, true>), dim3(G), dim3(kThreads), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                            static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qt, G, c, tau_raw,
@@ -1367,6 +1384,54 @@ int fa_fwd_splitkv_masked(const void* q, const void* k, const void* v, void* o, 
     else
         e = bf ? FA_SPLIT_MASKED(128, true) : FA_SPLIT_MASKED(128, false);
 #undef FA_SPLIT_MASKED
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd_splitkv_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                               int64_t H, int64_t N, int64_t d, float scale, hipStream_t stream, int dtype,
+                               const fa_mask* mask, const fa_block_mask* blocks, int num_splits, void* workspace,
+                               size_t workspace_bytes) {
+    if (num_splits < 1 || num_splits > kMaxSplits) {
+        const int st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype, 1);
+        return st != FA_OK ? st : FA_ERR_OPTION;
+    }
+    const int st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype, num_splits);
+    if (st != FA_OK) return st;
+    if (!blocks || !blocks->mask) return FA_ERR_NULL;
+    if (blocks->block_q < 64 || blocks->block_k < 64 || blocks->block_q % 64 != 0 || blocks->block_k % 64 != 0 ||
+        blocks->block_q > INT32_MAX || blocks->block_k > INT32_MAX || blocks->stride_b < 0 || blocks->stride_h < 0)
+        return FA_ERR_OPTION;
+    int64_t wl64 = -1, wr64 = -1;
+    const int32_t* seqlens = nullptr;
+    if (mask) {
+        if (mask->window_left < -1 || mask->window_right < -1 || mask->window_left > INT32_MAX ||
+            mask->window_right > INT32_MAX)
+            return FA_ERR_OPTION;
+        if (reinterpret_cast<uintptr_t>(mask->seqlens_k) & 3) return FA_ERR_ALIGN;
+        wl64 = mask->window_left >= N ? -1 : mask->window_left;
+        wr64 = mask->window_right >= N ? -1 : mask->window_right;
+        seqlens = mask->seqlens_k;
+    }
+    if (num_splits == 1) return fa_fwd_blocksparse(q, k, v, o, lse, B, H, N, d, scale, stream, dtype, mask, blocks);
+    if (!workspace_ok(q, k, v, o, lse, B, H, N, d, num_splits, workspace, workspace_bytes)) return FA_ERR_WORKSPACE;
+    float* po = static_cast<float*>(workspace);
+    float* pl = po + num_splits * B * H * N * d;
+    const float c = scale * 1.4426950408889634f;
+    const float tau_raw = kDefaultRescaleLog2 / c;
+    const int n = static_cast<int>(N), nq = static_cast<int>((N + kBlockM - 1) / kBlockM);
+    const int bh = static_cast<int>(B * H);
+    const fa_mask_args m = {static_cast<int>(H), static_cast<int>(wl64), static_cast<int>(wr64), seqlens};
+    const fa_block_args bl = {blocks->mask, static_cast<int>(blocks->block_q), static_cast<int>(blocks->block_k),
+                              blocks->stride_b, blocks->stride_h};
+    const bool bf = dtype == FA_BF16;
+    hipError_t e;
+#define FA_SPLIT_BLOCKS(DD, BB) \
+    launch_split<DD, BB, false>(q, k, v, o, lse, n, nq, bh, c, tau_raw, num_splits, po, pl, stream, &m, &bl)
+    if (d == 64)
+        e = bf ? FA_SPLIT_BLOCKS(64, true) : FA_SPLIT_BLOCKS(64, false);
+    else
+        e = bf ? FA_SPLIT_BLOCKS(128, true) : FA_SPLIT_BLOCKS(128, false);
+#undef FA_SPLIT_BLOCKS
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -208,8 +208,27 @@ int fa_fwd_splitkv_masked(const void* q, const void* k, const void* v, void* o, 
                           float scale, hipStream_t stream, int dtype, const fa_mask* mask,
                           int num_splits, void* workspace, size_t workspace_bytes);
 
-/* Bytes of workspace fa_fwd_splitkv (and fa_fwd_splitkv_masked) needs: num_splits * B*H*N * (d + 2) * 4, or 0 when
- * num_splits <= 1 or an argument is out of range. */
+/*
+ * fa_fwd_splitkv_blocksparse -- fa_fwd_blocksparse with split-KV: the key tiles a query tile's
+ * window reaches are cut into num_splits equal runs, as in fa_fwd_splitkv_masked; each run's
+ * workgroup lists and computes only the tiles of its run that the block mask (and window and key
+ * lengths) leave to one of its 32-row groups, and the runs are merged by the rescaling identity as
+ * in fa_fwd_splitkv. Splitting the keys before applying the mask, not the list of needed tiles,
+ * keeps the split of every query tile the same for one call; a run whose tiles the mask removes
+ * costs one empty workgroup and adds weight 0 in the merge. Rows with no allowed key get o = 0,
+ * lse = -inf.
+ * Arguments as for fa_fwd_blocksparse plus num_splits, workspace and workspace_bytes as for
+ * fa_fwd_splitkv (the same workspace size); num_splits = 1 runs fa_fwd_blocksparse. Errors: those
+ * of fa_fwd_blocksparse and fa_fwd_splitkv.
+ */
+int fa_fwd_splitkv_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int64_t B, int64_t H, int64_t N, int64_t d,
+                               float scale, hipStream_t stream, int dtype, const fa_mask* mask,
+                               const fa_block_mask* blocks, int num_splits, void* workspace,
+                               size_t workspace_bytes);
+
+/* Bytes of workspace fa_fwd_splitkv (and fa_fwd_splitkv_masked, fa_fwd_splitkv_blocksparse) needs:
+ * num_splits * B*H*N * (d + 2) * 4, or 0 when num_splits <= 1 or an argument is out of range. */
 size_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d, int num_splits);
 
 /* A split count for fa_fwd_splitkv from a cost model: one workgroup of 256 query rows runs per

@@ -32,8 +32,9 @@ def L():
 def test_header_declares_the_entry_points():
     assert _declared_functions() == ["fa_bwd", "fa_bwd_blocksparse", "fa_bwd_masked", "fa_fwd", "fa_fwd_blocksparse",
                                      "fa_fwd_cpu", "fa_fwd_ex", "fa_fwd_masked", "fa_fwd_splitkv",
-                                     "fa_fwd_splitkv_heuristic", "fa_fwd_splitkv_masked",
-                                     "fa_fwd_splitkv_workspace_size", "fa_status_string", "fa_version"]
+                                     "fa_fwd_splitkv_blocksparse", "fa_fwd_splitkv_heuristic",
+                                     "fa_fwd_splitkv_masked", "fa_fwd_splitkv_workspace_size", "fa_status_string",
+                                     "fa_version"]
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -300,3 +301,26 @@ def test_splitkv_masked_argument_errors(L, num_splits, ws, ws_bytes, mask, kw, c
     m = None if mask is None else fa.FaMask(*mask)
     assert fa.fa_fwd_splitkv_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
                                     a["scale"], a["stream"], a["dtype"], m, num_splits, ws, ws_bytes) == code
+
+
+@pytest.mark.parametrize("num_splits,ws,ws_bytes,blocks,mask,kw,code", [
+    (4, WS, 1 << 20, None, None, {}, 1), (4, WS, 1 << 20, (None, 64, 64, 0, 0), None, {}, 1),
+    (0, WS, 1 << 20, (0xC00000, 64, 64, 0, 0), None, {}, 9), (65, WS, 1 << 30, (0xC00000, 64, 64, 0, 0), None, {}, 9),
+    (4, WS, 1 << 20, (0xC00000, 32, 64, 0, 0), None, {}, 9), (4, WS, 1 << 20, (0xC00000, 64, 64, 0, -8), None, {}, 9),
+    (4, WS, 1 << 20, (0xC00000, 64, 64, 0, 0), (-2, 0, None), {}, 9),
+    (4, WS, 1 << 20, (0xC00000, 64, 64, 0, 0), (8, 0, 0x600002), {}, 5),
+    (4, None, 1 << 20, (0xC00000, 64, 64, 0, 0), None, {}, 10), (4, WS, 100, (0xC00000, 64, 64, 0, 0), None, {}, 10),
+    (4, WS + 8, 1 << 20, (0xC00000, 64, 64, 0, 0), None, {}, 10),
+    (4, QA, 1 << 20, (0xC00000, 64, 64, 0, 0), None, {}, 10),
+    (4, WS, 1 << 20, (0xC00000, 64, 64, 0, 0), None, dict(q=None), 1),
+    (4, WS, 1 << 20, (0xC00000, 64, 64, 0, 0), None, dict(d=96), 3),
+    (4, WS, 1 << 20, (0xC00000, 64, 64, 0, 0), None, dict(o=QA), 7),
+])
+def test_splitkv_blocksparse_argument_errors(L, num_splits, ws, ws_bytes, blocks, mask, kw, code):
+    import exact_tiled_softmax_fa_amd as fa
+    a = dict(GOOD)
+    a.update(kw)
+    b = None if blocks is None else fa.FaBlockMask(*blocks)
+    m = None if mask is None else fa.FaMask(*mask)
+    assert fa.fa_fwd_splitkv_blocksparse(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                                         a["scale"], a["stream"], a["dtype"], m, b, num_splits, ws, ws_bytes) == code
