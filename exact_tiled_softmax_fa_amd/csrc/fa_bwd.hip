@@ -765,8 +765,8 @@ int read_mask(const fa_mask* mask, int64_t N, int& wl, int& wr, const int32_t*& 
         mask->window_right > INT32_MAX)
         return FA_ERR_OPTION;
     if (reinterpret_cast<uintptr_t>(mask->seqlens_k) & 3) return FA_ERR_ALIGN;
-    wl = mask->window_left >= N ? -1 : static_cast<int>(mask->window_left);
-    wr = mask->window_right >= N ? -1 : static_cast<int>(mask->window_right);
+    wl = mask->window_left >= N - 1 ? -1 : static_cast<int>(mask->window_left);
+    wr = mask->window_right >= N - 1 ? -1 : static_cast<int>(mask->window_right);
     seqlens = mask->seqlens_k;
     return FA_OK;
 }

@@ -59,9 +59,13 @@ constexpr int kDefaultVariant = 1;          // kernel fa_fwd runs: 1 = 32 rows p
 // gets o = 0 and lse = -inf.
 // CHUNKED (with BLOCKS): the list of needed key tiles is built and walked kMaxListTiles candidates
 // at a time, for sequences longer than one list holds (64 * kMaxListTiles keys).
+// WV: waves per workgroup (query rows 32 * WV). The general mask (MASKED without BLOCKS) also
+// runs with 4 waves for narrow windows: a workgroup then spans fewer keys beyond its own rows'
+// windows, and two workgroups share a compute unit, so one's waves run while the other's wait at
+// barriers for tiles outside their window.
 template <int D, bool BF16, bool CAUSAL, bool SPLIT = false, bool MASKED = false, bool BLOCKS = false,
-          bool CHUNKED = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(
+          bool CHUNKED = false, int WV = kWaves>
+__global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qt, int G, float c, float tau_raw,
     int n_split = 1, float* __restrict__ PO = nullptr, float* __restrict__ PL = nullptr, int H = 1, int wl = -1,
@@ -70,13 +74,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     static_assert(!(MASKED && CAUSAL), "the general mask replaces the causal one");
     static_assert(!BLOCKS || MASKED, "the block mask rides on the general mask");
     static_assert(!CHUNKED || BLOCKS, "chunks are chunks of the block-sparse work list");
+    static_assert(WV == kWaves || (WV == 4 && MASKED && !BLOCKS), "4-wave workgroups: the general mask only");
+    constexpr int kBM = 32 * WV;               // query rows per workgroup
     constexpr int DT = D / 32;                 // 32-column k-steps of the first product
     constexpr int DB = D / 16;                 // 16-column blocks of the output
     constexpr int CPR = D / 8;                 // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;              // rows one wave-wide 1 KiB load covers
-    constexpr int IPW = kBlockN / RPI / kWaves;  // such loads per wave per tile (each of K, V)
+    constexpr int IPW = kBlockN / RPI / WV;    // such loads per wave per tile (each of K, V)
     constexpr int TILE = kBlockN * D;          // elements per tile
-    static_assert(IPW >= 1 && IPW * RPI * kWaves == kBlockN, "tile must split evenly over the waves");
+    static_assert(IPW >= 1 && IPW * RPI * WV == kBlockN, "tile must split evenly over the waves");
 
     // Two buffers for K and up to four for V, filled straight from global memory (LDS DMA,
     // lds_load16) in the swizzled layout. A ds_read address is a register plus an immediate below
@@ -104,14 +110,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     int vh, qt;
     map_block(blockIdx.x, G, n_qt, CAUSAL, vh, qt);
     const int bh = SPLIT ? vh / n_split : vh;
-    const int q0 = qt * kBlockM;
+    const int q0 = qt * kBM;
     const int64_t head = (int64_t)bh * N * D;
     const uint16_t* Qh = Q + head;
     const uint16_t* Kh = K + head;
     const uint16_t* Vh = V + head;
     const int wq0 = q0 + 32 * wave;  // first query row of this wave (two 16-row blocks)
 
-    const int kv_end = CAUSAL ? min(N, q0 + kBlockM) : N;
+    const int kv_end = CAUSAL ? min(N, q0 + kBM) : N;
     const int T_all = (kv_end + kBlockN - 1) / kBlockN;  // key tiles of this query tile
     // tiles tb .. tb + T - 1 are this workgroup's (all of them without SPLIT); tile indices below
     // are relative to tb
@@ -127,7 +133,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if constexpr (MASKED) {
         if (seqlens != nullptr) kv_len = min(max(seqlens[bh / H], 0), N);
         const int lo = wl >= 0 ? max(0, q0 - wl) : 0;
-        const int hi = wr >= 0 ? min(kv_len, q0 + kBlockM + wr) : kv_len;
+        const int hi = wr >= 0 ? min(kv_len, q0 + kBM + wr) : kv_len;
         tb = lo / kBlockN;
         T = max(0, (hi + kBlockN - 1) / kBlockN - tb);
         if constexpr (SPLIT) {  // this split's run of the window's tiles (possibly none; BLOCKS lists within it)
@@ -144,14 +150,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // 32 x 64 part of a tile.) CHUNKED builds the list in the schedule, a chunk at a time.
     __shared__ int t_list[BLOCKS ? kMaxListTiles : 1];
     __shared__ uint8_t t_wm[BLOCKS ? kMaxListTiles : 1];
-    __shared__ int t_cnt[BLOCKS ? kWaves : 1];
+    __shared__ int t_cnt[BLOCKS ? WV : 1];
     const uint8_t* mb = BLOCKS ? bmask + (int64_t)(bh / H) * bstride_b + (int64_t)(bh % H) * bstride_h : nullptr;
     const int n_kb = BLOCKS ? (N + bk - 1) / bk : 0;
     auto need = [&](int w, int t) {
         const int r0 = q0 + 32 * w;
         return r0 < N && mb[(int64_t)(r0 / bq) * n_kb + t * kBlockN / bk] != 0;
     };
-    if constexpr (BLOCKS && !CHUNKED) T = compact_tiles<kWaves>(tb, T, need, t_list, t_wm, t_cnt, tid);
+    if constexpr (BLOCKS && !CHUNKED) T = compact_tiles<WV>(tb, T, need, t_list, t_wm, t_cnt, tid);
     // tiles this wave computes: causal waves stop at the tile holding their last row
     // (Non-causal: T_w = T, hidden from the compiler. Folded away, the tests on it disappear and
     // the compiler keeps the output accumulators of the loop's two exit paths in two register
@@ -426,7 +432,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             // chunk's tiles (t_list, t_wm and both tile buffers read for the last time; no load in
             // flight) before the first barrier of compact_tiles, which writes the list only after it.
             for (int cb = 0; cb < T; cb += kMaxListTiles) {
-                Tc = compact_tiles<kWaves>(tb + cb, min(kMaxListTiles, T - cb), need, t_list, t_wm, t_cnt, tid);
+                Tc = compact_tiles<WV>(tb + cb, min(kMaxListTiles, T - cb), need, t_list, t_wm, t_cnt, tid);
                 if (Tc > 0) walk();
             }
         } else {
@@ -543,7 +549,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             // V(j-3)'s) at the top of the step, after barrier j in waves 0-3 and after region 2 of
             // tile j-1 in waves 4-7, and waits for them at the top of the next step: one
             // unconditional wait, so the compiler sees no path on which a read could overtake them.
-            const bool lag = wave_s >= kWaves / 2;
+            const bool lag = wave_s >= WV / 2;
             auto step = [&](int j, f32x4 (&s_cur)[2][4], f32x4 (&s_nxt)[2][4], uint16_t* k_cur, const uint16_t* k_nxt,
                             const uint16_t* v_cur, uint16_t* v_p1) __attribute__((always_inline)) {
                 __builtin_amdgcn_s_waitcnt(0);
@@ -998,11 +1004,20 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__
     if (LSE != nullptr && ch == 0) LSE[row] = ml + __log2f(lsum) * 0.69314718055994531f;
 }
 
-template <int D, bool BF16>
-hipError_t launch_masked(const void* q, const void* k, const void* v, void* o, float* lse, int N, int n_qt, int G,
-                         float c, float tau_raw, int H, int wl, int wr, const int* seqlens, hipStream_t stream) {
-    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, false, false, true>), dim3(G), dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+// The masked kernel runs with 4-wave workgroups of 128 query rows at d = 64 always, and at d = 128
+// for windows of at most this many keys (window_left + window_right + 1, both limited). Measured
+// against 8-wave workgroups on one MI355X (B1 H32 N8192 and B4 H16 N2047): d = 64 gains at every
+// window, 4% with one that masks nothing to 26% at 64 keys; d = 128 gains 3% at 2048 keys and up
+// to 17% at 64, and loses 1-2% from about 3072 keys on.
+constexpr int64_t kNarrowWindowKeys = 2048;
+
+// The masked kernel with WV waves per workgroup; B*H*ceil(N / (32 WV)) workgroups.
+template <int D, bool BF16, int WV>
+hipError_t launch_masked(const void* q, const void* k, const void* v, void* o, float* lse, int N, int BH, float c,
+                         float tau_raw, int H, int wl, int wr, const int* seqlens, hipStream_t stream) {
+    const int n_qt = (N + 32 * WV - 1) / (32 * WV), G = BH * n_qt;
+    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, false, false, true, false, false, WV>), dim3(G), dim3(64 * WV), 0,
+                       stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qt, G, c, tau_raw, 1,
                        nullptr, nullptr, H, wl, wr, seqlens);
     return hipGetLastError();
@@ -1202,25 +1217,29 @@ int fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* l
         mask->window_right > INT32_MAX)
         return FA_ERR_OPTION;
     if (reinterpret_cast<uintptr_t>(mask->seqlens_k) & 3) return FA_ERR_ALIGN;
-    // A window of N or more keys is no limit; as -1 it keeps the kernel's index sums below 2^31.
-    const int64_t wl64 = mask->window_left >= N ? -1 : mask->window_left;
-    const int64_t wr64 = mask->window_right >= N ? -1 : mask->window_right;
+    // A window of N - 1 or more keys is no limit (i - (N - 1) <= 0 <= j and j <= N - 1 <= i + N - 1);
+    // as -1 it keeps the kernel's index sums below 2^31 and sends the plain masks to fa_fwd.
+    const int64_t wl64 = mask->window_left >= N - 1 ? -1 : mask->window_left;
+    const int64_t wr64 = mask->window_right >= N - 1 ? -1 : mask->window_right;
     // the two masks with kernels of their own
     if (!mask->seqlens_k && wl64 == -1 && (wr64 == -1 || wr64 == 0))
         return fa_fwd(q, k, v, o, lse, B, H, N, d, scale, wr64 == 0 ? 1 : 0, stream, dtype);
-    const int64_t n_qt = (N + kBlockM - 1) / kBlockM;
     const float c = scale * 1.4426950408889634f;
     const float tau_raw = kDefaultRescaleLog2 / c;
-    const int n = static_cast<int>(N), nq = static_cast<int>(n_qt), g = static_cast<int>(B * H * n_qt);
+    const int n = static_cast<int>(N), bh = static_cast<int>(B * H);
     const int h = static_cast<int>(H), wl = static_cast<int>(wl64), wr = static_cast<int>(wr64);
     const bool bf = dtype == FA_BF16;
+    const bool narrow = wl64 >= 0 && wr64 >= 0 && wl64 + wr64 + 1 <= kNarrowWindowKeys;
     hipError_t e;
+#define FA_MASKED(DD, BB, WW) \
+    launch_masked<DD, BB, WW>(q, k, v, o, lse, n, bh, c, tau_raw, h, wl, wr, mask->seqlens_k, stream)
     if (d == 64)
-        e = bf ? launch_masked<64, true>(q, k, v, o, lse, n, nq, g, c, tau_raw, h, wl, wr, mask->seqlens_k, stream)
-               : launch_masked<64, false>(q, k, v, o, lse, n, nq, g, c, tau_raw, h, wl, wr, mask->seqlens_k, stream);
+        e = bf ? FA_MASKED(64, true, 4) : FA_MASKED(64, false, 4);
+    else if (narrow)
+        e = bf ? FA_MASKED(128, true, 4) : FA_MASKED(128, false, 4);
     else
-        e = bf ? launch_masked<128, true>(q, k, v, o, lse, n, nq, g, c, tau_raw, h, wl, wr, mask->seqlens_k, stream)
-               : launch_masked<128, false>(q, k, v, o, lse, n, nq, g, c, tau_raw, h, wl, wr, mask->seqlens_k, stream);
+        e = bf ? FA_MASKED(128, true, kWaves) : FA_MASKED(128, false, kWaves);
+#undef FA_MASKED
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -1240,8 +1259,8 @@ int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, flo
             mask->window_right > INT32_MAX)
             return FA_ERR_OPTION;
         if (reinterpret_cast<uintptr_t>(mask->seqlens_k) & 3) return FA_ERR_ALIGN;
-        wl64 = mask->window_left >= N ? -1 : mask->window_left;
-        wr64 = mask->window_right >= N ? -1 : mask->window_right;
+        wl64 = mask->window_left >= N - 1 ? -1 : mask->window_left;
+        wr64 = mask->window_right >= N - 1 ? -1 : mask->window_right;
         seqlens = mask->seqlens_k;
     }
     const int64_t n_qt = (N + kBlockM - 1) / kBlockM;
@@ -1360,8 +1379,8 @@ int fa_fwd_splitkv_masked(const void* q, const void* k, const void* v, void* o, 
         mask->window_right > INT32_MAX)
         return FA_ERR_OPTION;
     if (reinterpret_cast<uintptr_t>(mask->seqlens_k) & 3) return FA_ERR_ALIGN;
-    const int64_t wl64 = mask->window_left >= N ? -1 : mask->window_left;
-    const int64_t wr64 = mask->window_right >= N ? -1 : mask->window_right;
+    const int64_t wl64 = mask->window_left >= N - 1 ? -1 : mask->window_left;
+    const int64_t wr64 = mask->window_right >= N - 1 ? -1 : mask->window_right;
     // the two masks with kernels of their own, and the unsplit call
     if (!mask->seqlens_k && wl64 == -1 && (wr64 == -1 || wr64 == 0))
         return fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, wr64 == 0 ? 1 : 0, stream, dtype, num_splits,
@@ -1408,8 +1427,8 @@ int fa_fwd_splitkv_blocksparse(const void* q, const void* k, const void* v, void
             mask->window_right > INT32_MAX)
             return FA_ERR_OPTION;
         if (reinterpret_cast<uintptr_t>(mask->seqlens_k) & 3) return FA_ERR_ALIGN;
-        wl64 = mask->window_left >= N ? -1 : mask->window_left;
-        wr64 = mask->window_right >= N ? -1 : mask->window_right;
+        wl64 = mask->window_left >= N - 1 ? -1 : mask->window_left;
+        wr64 = mask->window_right >= N - 1 ? -1 : mask->window_right;
         seqlens = mask->seqlens_k;
     }
     if (num_splits == 1) return fa_fwd_blocksparse(q, k, v, o, lse, B, H, N, d, scale, stream, dtype, mask, blocks);

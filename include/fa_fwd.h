@@ -127,9 +127,12 @@ typedef struct fa_mask {
 /*
  * fa_fwd_masked -- fa_fwd under a general mask (see fa_mask). Key tiles outside a query tile's
  * window are neither loaded nor computed, so a window of w keys costs O(N w), not O(N^2).
- * Arguments as for fa_fwd, with `causal` replaced by `mask` (not NULL). The masks -1/-1 and -1/0
- * without seqlens_k run fa_fwd's own kernels. Errors: those of fa_fwd; FA_ERR_NULL for a NULL
- * mask, FA_ERR_OPTION for a window out of range, FA_ERR_ALIGN for a misaligned seqlens_k.
+ * Arguments as for fa_fwd, with `causal` replaced by `mask` (not NULL). A window of N - 1 or more
+ * keys excludes nothing and is taken as -1; the masks -1/-1 and -1/0 without seqlens_k then run
+ * fa_fwd's own kernels. The masked kernel runs with 128-row workgroups at d = 64 and for windows
+ * of at most 2048 keys (window_left + window_right + 1), else with 256-row ones (the same
+ * results). Errors: those of fa_fwd; FA_ERR_NULL for a NULL mask, FA_ERR_OPTION for a window out
+ * of range, FA_ERR_ALIGN for a misaligned seqlens_k.
  */
 int fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
                   int64_t B, int64_t H, int64_t N, int64_t d,

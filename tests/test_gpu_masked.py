@@ -79,3 +79,35 @@ def test_general_kernel_agrees_with_the_causal_one():
     torch.cuda.synchronize()
     assert (o_c.float() - o_m.float()).abs().max().item() <= 1e-2
     assert (l_c - l_m).abs().max().item() <= 1e-4
+
+
+@pytest.mark.parametrize("wl,wr", [(2047, 0), (2048, 0), (1023, 1024), (1024, 1024), (0, 2047)])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_windows_around_the_four_wave_limit(wl, wr, dt):
+    # at d = 128, windows of up to 2048 keys run 128-row workgroups, wider ones 256-row workgroups
+    q, k, v = workloads.custom_inputs(1, 2, 3000, 128, dt, 960 + wl + wr)
+    scale = float(np.float32(1 / np.sqrt(128)))
+    o, lse = _run(q, k, v, wl, wr, None, scale)
+    _compare(o, lse, q, k, v, wl, wr, None, scale, dt)
+
+
+def test_narrow_window_on_the_headline_shape():
+    w = workloads.HEADLINE
+    q, k, v = workloads.make_inputs(w)
+    o, lse = _run(q, k, v, 255, 0, None, w.scale)
+    _compare(o, lse, q, k, v, 255, 0, None, w.scale, w.dtype, workloads.sample_rows(w))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_windows_of_n_minus_one_keys_are_no_limit(d):
+    # a window of N - 1 keys back (or ahead) excludes no key: the call is plain or causal fa_fwd
+    import exact_tiled_softmax_fa_amd as fa
+    N = 777
+    q, k, v = (t.cuda() for t in workloads.custom_inputs(1, 2, N, d, "f16", 970 + d))
+    for (wl, wr), causal in (((N - 1, 0), True), ((N - 1, N - 1), False), ((-1, N - 1), False)):
+        o_m, l_m = fa.forward_masked(q, k, v, wl, wr)
+        o_f, l_f = fa.forward(q, k, v, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o_m, o_f) and torch.equal(l_m, l_f), (wl, wr)
+    o, lse = _run(q.cpu(), k.cpu(), v.cpu(), N - 2, 0, None, None)  # one key short of causal
+    _compare(o, lse, q.cpu(), k.cpu(), v.cpu(), N - 2, 0, None, float(np.float32(1 / np.sqrt(d))), "f16")
