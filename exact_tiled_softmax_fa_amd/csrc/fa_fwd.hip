@@ -1,19 +1,23 @@
 // Exact tiled-softmax attention forward for gfx950 (CDNA4), behind the C ABI of fa_fwd.h.
 //
-// One workgroup = 8 waves = 256 query rows of one (batch, head); each wave owns 32 rows, held
-// in registers (one row per lane) for the whole kernel. The workgroup walks the keys in tiles
-// of 64 (ascending), staging each K and V tile in LDS with coalesced 16-byte global loads that
-// are issued one tile ahead. Per tile and wave:
+// One workgroup = 8 waves = 256 query rows of one (batch, head) (4 waves = 128 rows for the
+// masked kernel's narrow-window form); each wave owns 32 rows, as two 16-row blocks whose Q
+// operands stay in registers for the whole kernel. The workgroup walks the keys in tiles of 64
+// (ascending), staging each K and V tile in LDS with coalesced 16-byte loads (LDS DMA) issued
+// ahead of use. Per tile and wave:
 //
-//   S^T = K_tile . Q^T          v_mfma_f32_32x32x16_{f16,bf16}, fp32 accumulate.
-//                               Computing the transpose puts one query row in each lane
-//                               (lanes l and l+32 hold the same row, different keys), so
-//                               the row max and row sum are in-lane work plus one
-//                               cross-half exchange (v_permlane32_swap).
-//   mask                        only on tiles that cross the causal diagonal or the end of
-//                               the sequence; masked scores become -inf before the max.
-//   m, alpha, p, l              online softmax in log2 units: p = exp2(s*c - m*c), with
-//                               c = scale*log2(e) folded into one fma.
+//   S^T = K_tile . Q^T          v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulate; each K operand
+//                               read from LDS feeds both query blocks. Computing the transpose
+//                               puts one query row in each lane column (the four 16-lane rows
+//                               of a wave hold different keys of the same query rows), so the
+//                               row sum and max are in-lane work plus two cross-row exchanges
+//                               (v_permlane16_swap, v_permlane32_swap).
+//   mask                        only on tiles that cross the causal diagonal, a window edge or
+//                               the end of the sequence; masked scores become -inf first.
+//   p, l                        online softmax in log2 units: p = exp2(s*c - m*c), with
+//                               c = scale*log2(e) folded into one fma, against a reference m
+//                               that moves (with the alpha rescale of l and o~) only when a
+//                               tile's sums show a p above 2^tau.
 //   O^T += V_tile^T . P^T       P converted to f16/bf16 (round to nearest even) straight
 //                               from the S^T accumulator registers, which already have the
 //                               operand layout; V^T comes from ds_read_b64_tr_b16 on the

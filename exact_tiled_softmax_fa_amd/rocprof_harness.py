@@ -274,7 +274,8 @@ def main():
     ap.add_argument("--block-size", type=int, default=128, help="block-sparse: rows and keys per block")
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "rocprof"))
     ap.add_argument("--summary-dir", default=os.path.join(ROOT, "gpurun_out", "rocprof"))
-    ap.add_argument("--steps", type=int, default=20)
+    # the kernel-trace pass times the same 10 warm-up and 50 timed calls as a default bench.py line
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--timeout", type=int, default=240, help="seconds per rocprofv3 pass")
     ap.add_argument("--parse-only", action="store_true", help="summarise existing outputs under --out")
