@@ -88,6 +88,18 @@ def _window_keys(i, N, window):
     return np.maximum(hi - lo, 0)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, window=None, blocks=None):
     """The fp64 oracle on 1024 seeded rows per head (every row of the small workloads), in the GPU
     line's unit: conventional TFLOP/s, or 4 d flops per allowed pair under a window (the masked
@@ -128,6 +140,7 @@ def cpu_baseline(w, window=None, blocks=None):
         "value": conv / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": core.threads(),
+        "cpu": cpu_model(),
         "kind": "oracle",
         "sample": f"{rows.shape[1]} seeded query rows per head x {rows.shape[0]} heads of {w.name} "
                   f"({rows.size} rows, {dt:.2f} s, {what})",
@@ -174,6 +187,7 @@ def cpu_baseline_bwd(w, window=None, blocks=None):
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": core.threads(),
+        "cpu": cpu_model(),
         "kind": "oracle",
         "sample": f"one head of {w.name}: every row's softmax statistics and D, dq of "
                   f"{'all' if rows is None else rows.shape[1]} rows, dk and dv of "
