@@ -236,7 +236,7 @@ def write_summary(rec: dict, summary_dir: str):
                   + (f" --splits {rec['splits']}" if rec.get("splits") else "")
                   + (f" --block-size {rec['blocks'][0]} --block-density {rec['blocks'][1]}" if rec.get("blocks")
                      else "")
-                  + "` (repository root, GPU box), which ran:", "", "```",
+                  + "` (repository root, on the GPU), which ran:", "", "```",
                   *rec["commands"], "```", ""]
     d = rec["dispatch_ms"]
     lines += [
@@ -272,8 +272,8 @@ def main():
     ap.add_argument("--block-density", type=float, default=None,
                     help="profile fa_fwd_blocksparse (fa_bwd_blocksparse with --pass bwd) at this density")
     ap.add_argument("--block-size", type=int, default=128, help="block-sparse: rows and keys per block")
-    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "rocprof"))
-    ap.add_argument("--summary-dir", default=os.path.join(ROOT, "gpurun_out", "rocprof"))
+    ap.add_argument("--out", default=os.path.join(ROOT, "rocprof_out"))
+    ap.add_argument("--summary-dir", default=os.path.join(ROOT, "rocprof_out"))
     # the kernel-trace pass times the same 10 warm-up and 50 timed calls as a default bench.py line
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
