@@ -90,12 +90,12 @@ __device__ __forceinline__ int off16(int r, int c) {
 }
 // Stage `rows` rows starting at r0 of one head into a swizzled LDS tile by LDS DMA (lds_load16)
 // (rows past the end repeat row N-1); each of the kWaves waves issues its share of 1 KiB loads.
-template <int D>
+template <int D, int W = kWaves>
 __device__ __forceinline__ void stage_rows(const uint16_t* src_head, int r0, int rows, int N, uint16_t* dst,
                                            int wave_s, int lane) {
     constexpr int CPR = D / 8;
     constexpr int RPI = 64 / CPR;
-    const int per_wave = rows / RPI / kWaves;
+    const int per_wave = rows / RPI / W;
     for (int i = 0; i < per_wave; ++i) {
         const int ld = wave_s * per_wave + i;
         const int r = RPI * ld + lane / CPR;
@@ -140,8 +140,9 @@ __device__ __forceinline__ void store_row16(uint16_t* row, const f32x4 (&acc)[D 
 // BLOCKS (both kernels, on top of MASKED): the block mask of fa_fwd_blocksparse. Each workgroup
 // lists the tiles one of its waves needs (compact_tiles) and walks only those; a wave computes a
 // listed tile only when its own bit is set.
-template <int D, bool BF16, bool CAUSAL, bool MASKED = false, bool BLOCKS = false, bool CHUNKED = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dq_kernel(
+template <int D, bool BF16, bool CAUSAL, bool MASKED = false, bool BLOCKS = false, bool CHUNKED = false,
+          int WV = kWaves>
+__global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
     float* __restrict__ DELTA, uint16_t* __restrict__ dQ, int N, int n_qt, int G, float c, float scale, int H = 1,
@@ -152,7 +153,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     constexpr int DT = D / 32;  // 32-column k-steps of the first two products
     constexpr int DB = D / 16;  // 16-column blocks of dQ
     constexpr int TILE = kKeyTile * D;
-    static_assert(kKeyTile * D / (64 * 8) % kWaves == 0, "tile loads must split evenly over the waves");
+    static_assert(kKeyTile * D / (64 * 8) % WV == 0, "tile loads must split evenly over the waves");
+    static_assert(WV == kWaves || (WV == 4 && MASKED && !BLOCKS), "4-wave workgroups: the general mask only");
 
     __shared__ __attribute__((aligned(4096))) uint16_t k_lds0[TILE];
     __shared__ __attribute__((aligned(4096))) uint16_t k_lds1[TILE];
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     int bh, qt;
     map_block(blockIdx.x, G, n_qt, CAUSAL, bh, qt);
-    const int q0 = qt * kRows;
+    const int q0 = qt * (32 * WV);
     const int64_t head = (int64_t)bh * N * D;
     const uint16_t* Kh = K + head;
     const uint16_t* Vh = V + head;
@@ -203,7 +205,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         lse2[qb] = (MASKED && lse_raw == -INFINITY) ? 0.f : lse_raw * kLog2e;  // lse in log2 units
     }
 
-    const int kv_end = CAUSAL ? min(N, q0 + kRows) : N;
+    const int kv_end = CAUSAL ? min(N, q0 + 32 * WV) : N;
     // key tiles tb .. tb + T - 1 (tile indices below are relative to tb); this wave computes
     // T_w0 .. T_w - 1 of them
     int tb = 0, kv_len = N;
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if constexpr (MASKED) {
         if (seqlens != nullptr) kv_len = min(max(seqlens[bh / H], 0), N);
         const int lo = wl >= 0 ? max(0, q0 - wl) : 0;
-        const int hi = wr >= 0 ? min(kv_len, q0 + kRows + wr) : kv_len;
+        const int hi = wr >= 0 ? min(kv_len, q0 + 32 * WV + wr) : kv_len;
         tb = lo / kKeyTile;
         T = max(0, (hi + kKeyTile - 1) / kKeyTile - tb);
         const int hi_w = wr >= 0 ? min(kv_len, wq0 + 32 + wr) : kv_len;  // this wave's last key + 1
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // CHUNKED: the list is built and walked kMaxListTiles candidates at a time (below).
     __shared__ int t_list[BLOCKS ? kMaxListTiles : 1];
     __shared__ uint8_t t_wm[BLOCKS ? kMaxListTiles : 1];
-    __shared__ int t_cnt[BLOCKS ? kWaves : 1];
+    __shared__ int t_cnt[BLOCKS ? WV : 1];
     const uint8_t* mb = BLOCKS ? bmask + (int64_t)(bh / H) * bstride_b + (int64_t)(bh % H) * bstride_h : nullptr;
     const int n_kb = BLOCKS ? (N + bk - 1) / bk : 0;
     // wave w needs key tile t when its rows and the tile's keys hold an allowed pair: the block
@@ -236,7 +238,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                mb[(int64_t)(r0 / bq) * n_kb + c0 / bk] != 0;
     };
     const int T_cand = T;
-    if constexpr (BLOCKS && !CHUNKED) T = compact_tiles<kWaves>(tb, T, need, t_list, t_wm, t_cnt, tid);
+    if constexpr (BLOCKS && !CHUNKED) T = compact_tiles<WV>(tb, T, need, t_list, t_wm, t_cnt, tid);
     if constexpr (BLOCKS) {
         T_w0 = 0;
         T_w = T;
@@ -339,22 +341,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // BLOCKS: this wave's bit for list entry j
     auto mine = [&](int j) { return !BLOCKS || ((__builtin_amdgcn_readfirstlane(t_wm[j]) >> wave_s) & 1); };
     auto walk = [&]() __attribute__((always_inline)) {
-        stage_rows<D>(Kh, key_tile(0) * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
-        stage_rows<D>(Vh, key_tile(0) * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
+        stage_rows<D, WV>(Kh, key_tile(0) * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
+        stage_rows<D, WV>(Vh, key_tile(0) * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
         for (int j = 0; j < T; j += 2) {
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             if (j + 1 < T) {
-                stage_rows<D>(Kh, key_tile(j + 1) * kKeyTile, kKeyTile, N, k_lds1, wave_s, lane);
-                stage_rows<D>(Vh, key_tile(j + 1) * kKeyTile, kKeyTile, N, v_lds1, wave_s, lane);
+                stage_rows<D, WV>(Kh, key_tile(j + 1) * kKeyTile, kKeyTile, N, k_lds1, wave_s, lane);
+                stage_rows<D, WV>(Vh, key_tile(j + 1) * kKeyTile, kKeyTile, N, v_lds1, wave_s, lane);
             }
             if ((!MASKED || j >= T_w0s) && j < T_ws && mine(j)) tile(j, k_lds0, v_lds0);
             if (j + 1 >= T) break;
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             if (j + 2 < T) {
-                stage_rows<D>(Kh, key_tile(j + 2) * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
-                stage_rows<D>(Vh, key_tile(j + 2) * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
+                stage_rows<D, WV>(Kh, key_tile(j + 2) * kKeyTile, kKeyTile, N, k_lds0, wave_s, lane);
+                stage_rows<D, WV>(Vh, key_tile(j + 2) * kKeyTile, kKeyTile, N, v_lds0, wave_s, lane);
             }
             if ((!MASKED || j + 1 >= T_w0s) && j + 1 < T_ws && mine(j + 1)) tile(j + 1, k_lds1, v_lds1);
         }
@@ -364,7 +366,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         // (t_list, t_wm and both buffers read for the last time; no load in flight) before the
         // first barrier of compact_tiles, which writes the list only after it.
         for (int cb = 0; cb < T_cand; cb += kMaxListTiles) {
-            T = compact_tiles<kWaves>(tb + cb, min(kMaxListTiles, T_cand - cb), need, t_list, t_wm, t_cnt, tid);
+            T = compact_tiles<WV>(tb + cb, min(kMaxListTiles, T_cand - cb), need, t_list, t_wm, t_cnt, tid);
             T_ws = T;
             if (T > 0) walk();
         }
@@ -700,19 +702,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 }
 
-template <int D, bool BF16, bool CAUSAL, bool MASKED = false, bool BLOCKS = false, bool CHUNKED = false>
+// WQ: waves per dQ workgroup (query rows 32 * WQ); 4 only under the general mask.
+template <int D, bool BF16, bool CAUSAL, bool MASKED = false, bool BLOCKS = false, bool CHUNKED = false,
+          int WQ = kWaves>
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                       void* dq, void* dk, void* dv, float* delta, int N, int BH, float c, float scale,
                       hipStream_t stream, int H = 1, int wl = -1, int wr = -1, const int* seqlens = nullptr,
                       const uint8_t* bmask = nullptr, int bq = 0, int bk = 0, int64_t bstride_b = 0,
                       int64_t bstride_h = 0) {
-    const int n_qt = (N + kRows - 1) / kRows, n_kt = (N + kKeys - 1) / kKeys;
+    const int n_qt = (N + 32 * WQ - 1) / (32 * WQ), n_kt = (N + kKeys - 1) / kKeys;
     const int Gq = BH * n_qt, Gk = BH * n_kt;
     const auto* Q = static_cast<const uint16_t*>(q);
     const auto* K = static_cast<const uint16_t*>(k);
     const auto* V = static_cast<const uint16_t*>(v);
     const auto* dO = static_cast<const uint16_t*>(dout);
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, CAUSAL, MASKED, BLOCKS, CHUNKED>), dim3(Gq), dim3(kThreads), 0, stream, Q,
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, CAUSAL, MASKED, BLOCKS, CHUNKED, WQ>), dim3(Gq), dim3(64 * WQ), 0, stream, Q,
                        K, V, static_cast<const uint16_t*>(o), dO, lse, delta, static_cast<uint16_t*>(dq), N, n_qt, Gq,
                        c, scale, H, wl, wr, seqlens, bmask, bq, bk, bstride_b, bstride_h);
     hipError_t e = hipGetLastError();
@@ -757,6 +761,13 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
 
 // The window of a fa_mask (NULL: none) as the kernels take it; a window of N or more keys is no
 // limit (as in fa_fwd_masked).
+// The dQ kernel of fa_bwd_masked runs with 4-wave workgroups of 128 query rows at d = 64 always,
+// and at d = 128 for windows of at most kNarrowDqKeys keys (window_left + window_right + 1, both
+// limited): a workgroup spans fewer keys beyond its rows' windows, and two share a compute unit.
+// Measured on the whole fa_bwd_masked call on one MI355X (B1 H32 N8192): d = 64 gains 0.5-12%
+// at every window tried; d = 128 gains 2.5-7% up to 2048 keys and loses 1% at 4096 (both sides).
+constexpr int64_t kNarrowDqKeys = 2048;
+
 int read_mask(const fa_mask* mask, int64_t N, int& wl, int& wr, const int32_t*& seqlens) {
     wl = wr = -1;
     seqlens = nullptr;
@@ -813,14 +824,16 @@ int fa_bwd_masked(const void* q, const void* k, const void* v, const void* o, co
     const float c = scale * kLog2e;
     const int n = static_cast<int>(N), BH = static_cast<int>(B * H), h = static_cast<int>(H);
     const bool bf = dtype == FA_BF16;
+    const bool narrow = d == 64 || (wl >= 0 && wr >= 0 && (int64_t)wl + wr + 1 <= kNarrowDqKeys);
     hipError_t e;
-#define FA_BWD_MASKED(DD, BB)                                                                                  \
-    launch_bwd<DD, BB, false, true>(q, k, v, o, dout, lse, dq, dk, dv, delta, n, BH, c, scale, stream, h, wl, wr, \
-                                    seqlens)
+#define FA_BWD_MASKED(DD, BB, WQ)                                                                              \
+    launch_bwd<DD, BB, false, true, false, false, WQ>(q, k, v, o, dout, lse, dq, dk, dv, delta, n, BH, c, scale, \
+                                                      stream, h, wl, wr, seqlens)
     if (d == 64)
-        e = bf ? FA_BWD_MASKED(64, true) : FA_BWD_MASKED(64, false);
+        e = bf ? FA_BWD_MASKED(64, true, 4) : FA_BWD_MASKED(64, false, 4);
     else
-        e = bf ? FA_BWD_MASKED(128, true) : FA_BWD_MASKED(128, false);
+        e = narrow ? (bf ? FA_BWD_MASKED(128, true, 4) : FA_BWD_MASKED(128, false, 4))
+                   : (bf ? FA_BWD_MASKED(128, true, kWaves) : FA_BWD_MASKED(128, false, kWaves));
 #undef FA_BWD_MASKED
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

@@ -116,3 +116,31 @@ def test_general_kernel_agrees_with_the_causal_one():
     for x, y in zip(a, b):
         scale = x.float().abs().max().item()
         assert (x.float() - y.float()).abs().max().item() <= 4 * U["bf16"] * scale
+
+
+@pytest.mark.parametrize("wl,wr", [(2047, 0), (2048, 0), (1023, 1024), (1024, 1024)])
+def test_windows_around_the_four_wave_limit(wl, wr):
+    # at d = 128 the dq kernel runs 128-row workgroups for windows of up to 2048 keys, 256-row ones
+    # beyond
+    N, d, dt = 2600, 128, "bf16"
+    q, k, v = workloads.custom_inputs(1, 1, N, d, dt, 2200 + wl + wr)
+    dout = workloads.custom_inputs(1, 1, N, d, dt, 2201 + wl + wr)[0]
+    scale = float(np.float32(1 / np.sqrt(d)))
+    got = _run(q, k, v, dout, wl, wr, None, scale)
+    _compare(got, q, k, v, dout, wl, wr, None, scale, dt)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_windows_of_n_minus_one_keys_are_no_limit(d):
+    # a window of N - 1 keys back (or ahead) excludes no key: the call is plain or causal fa_bwd
+    import exact_tiled_softmax_fa_amd as fa
+    N = 777
+    q, k, v, dout = (t.cuda() for t in workloads.custom_inputs(1, 2, N, d, "f16", 2300 + d) +
+                     (workloads.custom_inputs(1, 2, N, d, "f16", 2301 + d)[0],))
+    for (wl, wr), causal in (((N - 1, 0), True), ((N - 1, N - 1), False)):
+        o, lse = fa.forward(q, k, v, causal=causal)
+        a = fa.backward(q, k, v, o, lse, dout, causal=causal)
+        b = fa.backward_masked(q, k, v, o, lse, dout, wl, wr)
+        torch.cuda.synchronize()
+        for x, y in zip(a, b):
+            assert torch.equal(x, y), (wl, wr)
