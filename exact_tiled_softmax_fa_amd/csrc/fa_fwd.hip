@@ -80,8 +80,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
     static_assert(!(MASKED && CAUSAL), "the general mask replaces the causal one");
     static_assert(!BLOCKS || MASKED, "the block mask rides on the general mask");
     static_assert(!CHUNKED || BLOCKS, "chunks are chunks of the block-sparse work list");
-    static_assert(WV == kWaves || (WV == 4 && MASKED && (BLOCKS || !SPLIT)),
-                  "4-wave workgroups: the masked and block-sparse kernels");
+    static_assert(WV == kWaves || (WV == 4 && MASKED), "4-wave workgroups: the masked and block-sparse kernels");
     constexpr int kBM = 32 * WV;               // query rows per workgroup
     constexpr int DT = D / 32;                 // 32-column k-steps of the first product
     constexpr int DB = D / 16;                 // 16-column blocks of the output
@@ -1060,6 +1059,7 @@ hipError_t launch_blocks(const void* q, const void* k, const void* v, void* o, f
 struct fa_mask_args {
     int H, wl, wr;
     const int* seqlens;
+    bool narrow = false;  // run 4-wave workgroups
 };
 // A block mask as the kernels take it.
 struct fa_block_args {
@@ -1073,8 +1073,9 @@ hipError_t launch_split(const void* q, const void* k, const void* v, void* o, fl
                         float c, float tau_raw, int n_split, float* po, float* pl, hipStream_t stream,
                         const fa_mask_args* m = nullptr, const fa_block_args* bl = nullptr) {
     const int G = BH * n_split * n_qt;
-    // the block-sparse kernel's query tiles have 32 * kBlocksWaves rows
-    const int n_qb = (N + 32 * kBlocksWaves - 1) / (32 * kBlocksWaves), Gb = BH * n_split * n_qb;
+    // the 4-wave kernels' query tiles (block-sparse, narrow windows) have 128 rows
+    static_assert(kBlocksWaves == 4, "one grid for the 4-wave kernels");
+    const int n_qb = (N + 127) / 128, Gb = BH * n_split * n_qb;
     // (a split's run of key tiles can exceed one block-sparse list only past 64 * kMaxListTiles keys)
     if (bl != nullptr && N <= kBlockN * kMaxListTiles)
         hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, false, true, true, true, false, kBlocksWaves>), dim3(Gb),
@@ -1088,6 +1089,11 @@ hipError_t launch_split(const void* q, const void* k, const void* v, void* o, fl
                            static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o),
                            lse, N, n_qb, Gb, c, tau_raw, n_split, po, pl, m->H, m->wl, m->wr, m->seqlens, bl->mask,
                            bl->bq, bl->bk, bl->sb, bl->sh);
+    else if (m != nullptr && m->narrow)
+        hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, false, true, true, false, false, 4>), dim3(Gb), dim3(256), 0,
+                           stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qb, Gb, c, tau_raw,
+                           n_split, po, pl, m->H, m->wl, m->wr, m->seqlens);
     else if (m != nullptr)
         hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, false, true, true>), dim3(G), dim3(kThreads), 0, stream,
                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
@@ -1413,7 +1419,11 @@ int fa_fwd_splitkv_masked(const void* q, const void* k, const void* v, void* o, 
     const float tau_raw = kDefaultRescaleLog2 / c;
     const int n = static_cast<int>(N), nq = static_cast<int>((N + kBlockM - 1) / kBlockM);
     const int bh = static_cast<int>(B * H);
-    const fa_mask_args m = {static_cast<int>(H), static_cast<int>(wl64), static_cast<int>(wr64), mask->seqlens_k};
+    // 4-wave workgroups at d = 64: on the thin grid B1 H2 N16384 (one MI355X) +2% .. +12% there, but
+    // -3% .. -5% at d = 128 even for windows of 1024 keys (the split already fills the grid)
+    const bool narrow = d == 64;
+    const fa_mask_args m = {static_cast<int>(H), static_cast<int>(wl64), static_cast<int>(wr64), mask->seqlens_k,
+                            narrow};
     const bool bf = dtype == FA_BF16;
     hipError_t e;
 #define FA_SPLIT_MASKED(DD, BB) \
