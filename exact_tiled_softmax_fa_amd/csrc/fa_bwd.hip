@@ -43,7 +43,6 @@ using namespace fa_detail;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRows = 32 * kWaves;  // query rows per workgroup in the dq kernel
 constexpr int kKeyTile = 64;        // keys per tile in the dq kernel
 constexpr int kKeys = 128;          // keys per workgroup in the dkdv kernel (4 groups of 32)
 constexpr int kQueryTile = 64;      // query rows per tile in the dkdv kernel (two halves of 32)
