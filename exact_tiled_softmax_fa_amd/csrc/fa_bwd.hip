@@ -792,7 +792,7 @@ extern "C" {
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
            void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
-           int causal, hipStream_t stream, int dtype) {
+           int causal, hipStream_t stream, fa_dtype dtype) {
     const int st = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, dtype);
     if (st != FA_OK) return st;
     const float c = scale * kLog2e;
@@ -815,7 +815,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
 
 int fa_bwd_masked(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                   void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
-                  hipStream_t stream, int dtype, const fa_mask* mask) {
+                  hipStream_t stream, fa_dtype dtype, const fa_mask* mask) {
     const int st = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, dtype);
     if (st != FA_OK) return st;
     if (!mask) return FA_ERR_NULL;
@@ -844,7 +844,7 @@ int fa_bwd_masked(const void* q, const void* k, const void* v, const void* o, co
 
 int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const void* dout,
                        const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t N,
-                       int64_t d, float scale, hipStream_t stream, int dtype, const fa_mask* mask,
+                       int64_t d, float scale, hipStream_t stream, fa_dtype dtype, const fa_mask* mask,
                        const fa_block_mask* blocks) {
     const int st = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, scale, dtype);
     if (st != FA_OK) return st;

@@ -427,7 +427,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }  // namespace
 
 extern "C" int fa_fwd_cpu(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                          int64_t N, int64_t d, float scale, int causal, int dtype, int num_threads) {
+                          int64_t N, int64_t d, float scale, int causal, fa_dtype dtype, int num_threads) {
     if (!q || !k || !v || !o) return FA_ERR_NULL;
     if (B < 1 || H < 1 || N < 1 || N > INT32_MAX / 2) return FA_ERR_SHAPE;
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;

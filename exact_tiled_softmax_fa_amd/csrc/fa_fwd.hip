@@ -15,9 +15,10 @@
 //   mask                        only on tiles that cross the causal diagonal, a window edge or
 //                               the end of the sequence; masked scores become -inf first.
 //   p, l                        online softmax in log2 units: p = exp2(s*c - m*c), with
-//                               c = scale*log2(e) folded into one fma, against a reference m
-//                               that moves (with the alpha rescale of l and o~) only when a
-//                               tile's sums show a p above 2^tau.
+//                               c = scale*log2(e) folded into one fma, against a reference m.
+//                               f16: m moves (with the alpha rescale of l and o~) only when a
+//                               tile's sums show a p above 2^tau. bf16: m is the exact running
+//                               maximum, from a row max taken while the other product runs.
 //   O^T += V_tile^T . P^T       P converted to f16/bf16 (round to nearest even) straight
 //                               from the S^T accumulator registers, which already have the
 //                               operand layout; V^T comes from ds_read_b64_tr_b16 on the
@@ -31,8 +32,14 @@
 // Fewer rescales (a wave skips the alpha multiply when no row's max moved) follow the
 // FlashAttention-2 remark on "Decoding flash attention" (bibekananda.in), "Later versions". The
 // rescaling identity holds for any reference value, so the reference need not be the running
-// max: the default kernel keeps every unnormalised p within 2^tau and tests that on the tile
-// sums it forms anyway, instead of taking a max over every tile.
+// max: the f16 kernels keep every unnormalised p within 2^tau and test that on the tile sums they
+// form anyway, instead of taking a max over every tile. The bf16 kernels keep the exact running
+// maximum, the recurrence as "transformer math: flash attention math" writes it: bf16 keeps 8
+// significant bits, so a probability rounded to it is off by up to 2^-8 of itself, and with a
+// lazy reference the largest weights of a row all carry that error; against the exact maximum
+// the largest one is exactly 1. (With the lazy reference a peaked bf16 row, logits of standard
+// deviation 9, measured 1.02e-2 from the fp64 result, above the 1e-2 bound; an emulation of these
+// roundings reproduces that value and gives 5.6e-3 for the exact maximum.)
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -52,7 +59,6 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBlockM = 32 * kWaves;  // query rows per workgroup (32 per wave)
 constexpr int kBlockN = 64;           // keys per tile
 constexpr float kDefaultRescaleLog2 = 8.f;  // default reference-max threshold (log2 units)
-constexpr int kDefaultVariant = 1;          // kernel fa_fwd runs: 1 = 32 rows per wave, 2 = 64
 
 // SPLIT: the key range of every query tile is cut into n_split equal runs of tiles, one per
 // workgroup; each writes its partial result (O normalised over its own keys, in fp32, and the
@@ -228,11 +234,15 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // the current tile's part of l_run and l_f32, added once the tile is accepted (settle)
     float l_tile[2] = {0.f, 0.f};
     float lf_tile[2] = {0.f, 0.f};
+    // EXACT (bf16): the reference is the exact running maximum of each row, moved whenever a
+    // tile's max exceeds it (tau is not used). Otherwise (f16) the lazy reference below.
+    constexpr bool EXACT = BF16;
     // bound on every unnormalised p: 2^tau_log2 (tau_raw is tau_log2 in raw score units)
     const float p_cap = __builtin_amdgcn_exp2f(tau_raw * c);
     // a moved reference sits this far above the maximum that moved it (0 for tau = 0, where it is
     // the exact running maximum), so later scores must rise by more before it moves again
-    const float headroom = 0.5f * tau_raw;
+    const float headroom = EXACT ? 0.f : 0.5f * tau_raw;
+    const float move_above = EXACT ? 0.f : tau_raw;  // a row moves when its max exceeds m + this
 
     // LDS operand addresses (elements). Both swizzles depend on row & 15 only, so moving 16 rows
     // down a tile is the constant offset 16*D: one address per k-step serves the four 16-key
@@ -327,7 +337,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // otherwise p stays <= 2^tau_log2. mx0, mx1: the rows' maxima over the tile (reduced over the
     // four lane rows). The new reference is the larger of the old one and max + headroom.
     auto rebase = [&](float mx0, float mx1, bool force) __attribute__((always_inline)) {
-        if (force || __builtin_amdgcn_ballot_w64(mx0 > m_run[0] + tau_raw || mx1 > m_run[1] + tau_raw)) {
+        if (force || __builtin_amdgcn_ballot_w64(mx0 > m_run[0] + move_above || mx1 > m_run[1] + move_above)) {
             const float mx[2] = {mx0, mx1};
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
@@ -377,11 +387,14 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // max exists to keep. Otherwise (rare: the scores rose past the reference, or a row has no
     // reference yet) move the reference to the running max and take them again. This replaces a
     // max over every tile by a test on sums the softmax forms anyway.
+    // (EXACT: the reference already is the row's maximum over this tile, so every p <= 1.)
     auto settle = [&](const f32x4 (&sd)[2][4]) __attribute__((always_inline)) {
-        if (__builtin_amdgcn_ballot_w64(l_tile[0] > p_cap || l_tile[1] > p_cap || m_run[0] == -INFINITY ||
-                                        m_run[1] == -INFINITY)) {
-            rebase_from(sd, true);
-            expo(sd);
+        if constexpr (!EXACT) {
+            if (__builtin_amdgcn_ballot_w64(l_tile[0] > p_cap || l_tile[1] > p_cap || m_run[0] == -INFINITY ||
+                                            m_run[1] == -INFINITY)) {
+                rebase_from(sd, true);
+                expo(sd);
+            }
         }
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
@@ -419,6 +432,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
             if (__builtin_amdgcn_readfirstlane(t_wm[j]) & wbit) {
                 qk(kt, s0);
                 mask(j, s0);
+                if constexpr (EXACT) rebase_from(s0, false);
                 expo(s0);
                 settle(s0);
                 pv(vt);
@@ -493,11 +507,15 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 if constexpr (BF16) asm volatile("" : "+v"(lf_tile[qb]));
             }
         };
-        // region 2 of tile j: O^T += V(j)^T . P^T(j).
-        auto region2 = [&](const uint16_t* v_cur) __attribute__((always_inline)) {
+        // region 2 of tile j: O^T += V(j)^T . P^T(j). EXACT: the row maxima of S^T(j+1) (s_nxt,
+        // already masked) are formed between the MFMAs, on the vector ALU this region leaves idle,
+        // and the reference moves after the product, once P(j) (taken against the old one) is in.
+        auto region2 = [&](const uint16_t* v_cur, const f32x4 (&s_nxt)[2][4]) __attribute__((always_inline)) {
             // V^T operands read two steps ahead.
             constexpr int NV = 2 * DB;  // V^T operands: 16 for D = 128, 8 for D = 64
+            constexpr int EPS = 32 / NV;  // scores of S^T(j+1) folded into the maxima per step
             u32x4 va[NV];
+            float pm[2] = {-INFINITY, -INFINITY};  // this lane's maxima of the two rows
             va[0] = v_operand(v_cur, 0, 0);
             va[1] = v_operand(v_cur, 1 / DB, 1 % DB);
 #pragma unroll
@@ -510,7 +528,16 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
                     oacc[qb][b] = mfma16<BF16>(va[i], p_operand(qb, kk), oacc[qb][b]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                if constexpr (EXACT) {
+#pragma unroll
+                    for (int u = 0; u < EPS; ++u) {
+                        const int e = i * EPS + u, qb = e >> 4, kb = (e >> 2) & 3, r = e & 3;
+                        pm[qb] = fmaxf(pm[qb], s_nxt[qb][kb][r]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
+            if constexpr (EXACT) rebase(max_over_rows(pm[0]), max_over_rows(pm[1]), false);
         };
         if constexpr (MASKED) {
             // every wave: barrier, loads, region 1, region 2 (V in two buffers)
@@ -531,7 +558,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
                     region1(s_cur, s_nxt, k_nxt);
                     settle(s_cur);
                     mask(j + 1, s_nxt);
-                    region2(v_cur);
+                    region2(v_cur, s_nxt);
                 } else if (j < T_w) {
                     expo(s_cur);
                     settle(s_cur);
@@ -575,7 +602,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
                     __syncthreads();  // barrier j + 1
                 }
                 if (j + 1 < T_w) {
-                    region2(v_cur);
+                    region2(v_cur, s_nxt);
                 } else if (j < T_w) {
                     pv(v_cur);
                 }
@@ -635,326 +662,6 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
             if (LSE != nullptr && g == 0)
                 LSE[(int64_t)bh * N + qrow] = (!MASKED || l_lse > 0.f) ? (mcf + __log2f(l_lse)) * 0.69314718055994531f
                                                                        : -INFINITY;
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------------------------
-// Kernel B: 64 query rows per wave. A workgroup is 4 waves = 256 rows (the same query tile as
-// above) and runs alone on its CU with one wave per SIMD, so a wave may use 512 registers: the
-// output accumulators and the score tile live in AGPRs (the MFMAs accumulate there directly) and
-// the rest in VGPRs, Q included. Each K operand and each V^T operand read from LDS now feeds two
-// MFMAs (one per 32-row block), which halves the LDS traffic per flop; the schedule is the same
-// two-region software pipeline.
-constexpr int kWavesB = 4;
-constexpr int kThreadsB = 64 * kWavesB;
-constexpr int kBlockMB = 64 * kWavesB;
-static_assert(kBlockMB == kBlockM, "both kernels use the same query tiles and grid");
-
-template <int D, bool BF16, bool CAUSAL>
-__global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(1, 1))) void fa_fwd_kernel_w64(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qt, int G, float c, float tau_raw) {
-    constexpr int DK = D / 16;
-    constexpr int DB = D / 32;
-    constexpr int CPR = D / 8;
-    constexpr int RPI = 64 / CPR;
-    constexpr int IPW = kBlockN / RPI / kWavesB;
-    constexpr int TILE = kBlockN * D;
-    static_assert(IPW >= 1 && IPW * RPI * kWavesB == kBlockN, "tile must split evenly over the waves");
-
-    __shared__ __attribute__((aligned(4096))) uint16_t k_lds0[TILE];
-    __shared__ __attribute__((aligned(4096))) uint16_t k_lds1[TILE];
-    __shared__ __attribute__((aligned(4096))) uint16_t v_lds0[TILE];
-    __shared__ __attribute__((aligned(4096))) uint16_t v_lds1[TILE];
-
-    // Let the register allocator use AGPRs (it infers "none" for a kernel without AGPR asm).
-    {
-        float z = 0.f;
-        asm volatile("" : "+a"(z));
-    }
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int h = lane >> 5;
-    const int lq = lane & 31;
-
-    int bh, qt;
-    map_block(blockIdx.x, G, n_qt, CAUSAL, bh, qt);
-    const int q0 = qt * kBlockMB;
-    const int64_t head = (int64_t)bh * N * D;
-    const uint16_t* Qh = Q + head;
-    const uint16_t* Kh = K + head;
-    const uint16_t* Vh = V + head;
-    const int wq0 = q0 + 64 * wave;              // first query row of this wave
-    const int qrow[2] = {wq0 + lq, wq0 + 32 + lq};  // this lane's two query rows
-
-    const int kv_end = CAUSAL ? min(N, q0 + kBlockMB) : N;
-    const int T = (kv_end + kBlockN - 1) / kBlockN;
-    int T_w = CAUSAL ? min(T, (min(wq0 + 64, N) + kBlockN - 1) / kBlockN) : T;
-    if constexpr (!CAUSAL) asm volatile("" : "+v"(T_w));  // as in the first kernel
-
-    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-    auto issue = [&](const uint16_t* src_head, int j, uint16_t* dst) __attribute__((always_inline)) {
-        const int k0 = j * kBlockN;
-#pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-            const int g = wave_s * IPW + i;
-            const int r = RPI * g + lane / CPR;
-            const int ch = (lane % CPR) ^ swz<D>(r);
-            const unsigned src = (unsigned)min(k0 + r, N - 1) * D + 8 * ch;
-            lds_load16(src_head, N * D * 2, 2 * src, (lds_void*)(dst + g * 512));
-        }
-    };
-
-    // Q^T fragments of both 32-row blocks in registers; rows past N are zero.
-    u32x4 qf[2][DK];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int t = 0; t < DK; ++t) {
-            qf[qb][t] = (u32x4){0u, 0u, 0u, 0u};
-            if (qrow[qb] < N)
-                qf[qb][t] = *reinterpret_cast<const u32x4*>(Qh + (int64_t)qrow[qb] * D + 16 * t + 8 * h);
-        }
-
-    int koff[DK];
-#pragma unroll
-    for (int t = 0; t < DK; ++t) koff[t] = tile_off<D>(lq, 2 * t + h);
-    int voff_lo[DB], voff_hi[DB];
-    {
-        const int s16 = lane & 15;
-        const int tr_row = 4 * h + (s16 >> 2);
-        const int tr_chunk = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
-        const int tr_half = 4 * (s16 & 1);
-#pragma unroll
-        for (int b = 0; b < DB; ++b) {
-            voff_lo[b] = tile_off<D>(tr_row, 4 * b + tr_chunk) + tr_half;
-            voff_hi[b] = tile_off<D>(tr_row + 8, 4 * b + tr_chunk) + tr_half;
-        }
-    }
-    auto k_operand = [&](const uint16_t* kt, int t, int kb) __attribute__((always_inline)) {
-        return *reinterpret_cast<const u32x4*>(kt + koff[t] + kb * 32 * D);
-    };
-    auto v_operand = [&](const uint16_t* vt, int kk, int b) __attribute__((always_inline)) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + voff_lo[b] + kk * 16 * D));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + voff_hi[b] + kk * 16 * D));
-        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
-        const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
-        return (u32x4){lo2[0], lo2[1], hi2[0], hi2[1]};
-    };
-
-    f32x16 oacc[2][DB];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int b = 0; b < DB; ++b) oacc[qb][b] = (f32x16){};
-    f32x16 sacc[2][2];      // S^T of the tile being produced (per query block, key block)
-    float sv[2][2][16];     // VGPR copy of the previous S^T, consumed by the exponentials
-    unsigned pk[2][2][8];   // P^T per query block and key block
-    float m_run[2] = {-INFINITY, -INFINITY};
-    float l_run[2] = {0.f, 0.f};
-    float l_f32[2] = {0.f, 0.f};
-    float mc[2] = {0.f, 0.f};
-
-    auto p_operand = [&](int qb, int kk) __attribute__((always_inline)) {
-        const int kb = kk >> 1, hf = kk & 1;
-        return (u32x4){pk[qb][kb][4 * hf + 0], pk[qb][kb][4 * hf + 1], pk[qb][kb][4 * hf + 2], pk[qb][kb][4 * hf + 3]};
-    };
-    auto needs_mask = [&](int t) __attribute__((always_inline)) {
-        const int k0 = t * kBlockN;
-        return (k0 + kBlockN > N) || (CAUSAL && k0 + kBlockN - 1 > wq0);
-    };
-    auto mask_sv = [&](int t) __attribute__((always_inline)) {
-        const int k0 = t * kBlockN;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    if (key >= N || (CAUSAL && key > qrow[qb])) sv[qb][kb][r] = -INFINITY;
-                }
-    };
-    auto max_of_sv = [&](int qb) __attribute__((always_inline)) {
-        float mx = fmaxf(sv[qb][0][0], sv[qb][0][1]);
-#pragma unroll
-        for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sv[qb][0][r]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[qb][1][r]);
-        return mx;
-    };
-    auto rebase = [&](float mx0, float mx1) __attribute__((always_inline)) {
-        mx0 = max_with_partner(mx0);
-        mx1 = max_with_partner(mx1);
-        if (__builtin_amdgcn_ballot_w64(mx0 > m_run[0] + tau_raw || mx1 > m_run[1] + tau_raw)) {
-            const float mx[2] = {mx0, mx1};
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const float m_new = fmaxf(m_run[qb], mx[qb]);
-                const float alpha = (m_new == m_run[qb]) ? 1.f : __builtin_amdgcn_exp2f((m_run[qb] - m_new) * c);
-                l_run[qb] *= alpha;
-                if constexpr (BF16) l_f32[qb] *= alpha;
-#pragma unroll
-                for (int b = 0; b < DB; ++b)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[qb][b][r] *= alpha;
-                m_run[qb] = m_new;
-                mc[qb] = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb] * c;
-            }
-        }
-    };
-    auto exp_pair = [&](int q) __attribute__((always_inline)) {  // pair q of 32: (qb, kb, r)
-        const int qb = q >> 4, kb = (q >> 3) & 1, r = 2 * (q & 7);
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[qb][kb][r], c, -mc[qb]));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[qb][kb][r + 1], c, -mc[qb]));
-        pk[qb][kb][r >> 1] = pack2<BF16>(p0, p1);
-        l_run[qb] = add_pair<BF16>(pk[qb][kb][r >> 1], l_run[qb]);
-        if constexpr (BF16) l_f32[qb] += p0 + p1;
-    };
-    // S^T(t) for both query blocks: 4 * DK MFMAs, each K operand used twice
-    auto qk_plain = [&](const uint16_t* kt) __attribute__((always_inline)) {
-#pragma unroll
-        for (int pi = 0; pi < 2 * DK; ++pi) {
-            const int t = pi >> 1, kb = pi & 1;
-            const u32x4 a = k_operand(kt, t, kb);
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-                sacc[qb][kb] = mfma32<BF16>(a, qf[qb][t], t == 0 ? (f32x16){} : sacc[qb][kb]);
-        }
-    };
-    auto pv_plain = [&](const uint16_t* vt) __attribute__((always_inline)) {
-#pragma unroll
-        for (int pi = 0; pi < 4 * DB; ++pi) {
-            const int kk = pi / DB, b = pi % DB;
-            const u32x4 a = v_operand(vt, kk, b);
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) oacc[qb][b] = mfma32<BF16>(a, p_operand(qb, kk), oacc[qb][b]);
-        }
-    };
-    auto copy_sv = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sv[qb][kb][r] = sacc[qb][kb][r];
-    };
-
-    issue(Kh, 0, k_lds0);
-    issue(Vh, 0, v_lds0);
-    if (T > 1) issue(Kh, 1, k_lds1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (0 < T_w) {
-        qk_plain(k_lds0);
-        copy_sv();
-        if (needs_mask(0)) mask_sv(0);
-        rebase(max_of_sv(0), max_of_sv(1));
-    }
-    auto iteration = [&](int j, const uint16_t* k_nxt, const uint16_t* v_cur, uint16_t* k_load,
-                         uint16_t* v_load) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (j + 2 < T) issue(Kh, j + 2, k_load);
-        if (j + 1 < T) issue(Vh, j + 1, v_load);
-        if (j + 1 < T_w) {
-            // region 1: S^T(j+1) for both query blocks (4*DK MFMAs, K operands two pairs ahead)
-            // with the 32 pairs of exponentials of tile j in between
-            constexpr int NPR = 2 * DK;  // K operand reads (pairs of MFMAs)
-            constexpr int EPM = 32 / (2 * NPR);  // exponential pairs per MFMA: 1 (D=128), 2 (D=64)
-            u32x4 ka[NPR];
-            ka[0] = k_operand(k_nxt, 0, 0);
-            ka[1] = k_operand(k_nxt, 0, 1);
-#pragma unroll
-            for (int i = 0; i < 2 * NPR; ++i) {
-                const int pi = i >> 1, qb = i & 1, t = pi >> 1, kb = pi & 1;
-                if (qb == 0 && pi + 2 < NPR) ka[pi + 2] = k_operand(k_nxt, (pi + 2) >> 1, (pi + 2) & 1);
-                __builtin_amdgcn_sched_barrier(0);
-                sacc[qb][kb] = mfma32<BF16>(ka[pi], qf[qb][t], t == 0 ? (f32x16){} : sacc[qb][kb]);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int u = 0; u < EPM; ++u) exp_pair(i * EPM + u);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 8; ++r) asm volatile("" : "+v"(pk[qb][kb][r]));
-            asm volatile("" : "+v"(l_run[0]), "+v"(l_run[1]));
-            if constexpr (BF16) asm volatile("" : "+v"(l_f32[0]), "+v"(l_f32[1]));
-            // region 2: O^T += V(j)^T . P^T(j) for both query blocks (4*DB*2 MFMAs, V^T operands two
-            // pairs ahead) with S^T(j+1) copied to VGPRs and its row maxima in between
-            constexpr int NPV = 4 * DB;
-            float mx0, mx1;
-            if (!needs_mask(j + 1)) {
-                constexpr int CPM = 64 / (2 * NPV);  // scores copied per MFMA: 2 (D=128), 4 (D=64)
-                u32x4 va[NPV];
-                va[0] = v_operand(v_cur, 0, 0);
-                va[1] = v_operand(v_cur, 1 / DB, 1 % DB);
-                mx0 = -INFINITY;
-                mx1 = -INFINITY;
-#pragma unroll
-                for (int i = 0; i < 2 * NPV; ++i) {
-                    const int pi = i >> 1, qb = i & 1, kk = pi / DB, b = pi % DB;
-                    if (qb == 0 && pi + 2 < NPV) va[pi + 2] = v_operand(v_cur, (pi + 2) / DB, (pi + 2) % DB);
-                    __builtin_amdgcn_sched_barrier(0);
-                    oacc[qb][b] = mfma32<BF16>(va[pi], p_operand(qb, kk), oacc[qb][b]);
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int u = 0; u < CPM; ++u) {
-                        const int e = i * CPM + u;  // score e of 64: (qb, kb, r)
-                        const int eq = e >> 5, ek = (e >> 4) & 1, er = e & 15;
-                        sv[eq][ek][er] = sacc[eq][ek][er];
-                        if (eq == 0) mx0 = fmaxf(mx0, sv[eq][ek][er]);
-                        else mx1 = fmaxf(mx1, sv[eq][ek][er]);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            } else {
-                pv_plain(v_cur);
-                copy_sv();
-                mask_sv(j + 1);
-                mx0 = max_of_sv(0);
-                mx1 = max_of_sv(1);
-            }
-            rebase(mx0, mx1);
-        } else if (j < T_w) {
-#pragma unroll
-            for (int q = 0; q < 32; ++q) exp_pair(q);
-            pv_plain(v_cur);
-        }
-    };
-    for (int j = 0; j < T; j += 2) {
-        iteration(j, k_lds1, v_lds0, k_lds0, v_lds1);
-        if (j + 1 >= T) break;
-        iteration(j + 1, k_lds0, v_lds1, k_lds1, v_lds0);
-    }
-
-    // ---- epilogue ----
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const float l_tot = sum_with_partner(l_run[qb]);
-        const float l_lse = BF16 ? sum_with_partner(l_f32[qb]) : l_tot;
-        if (qrow[qb] < N) {
-            const float inv = 1.f / l_tot;
-            uint16_t* orow = O + head + (int64_t)qrow[qb] * D;
-#pragma unroll
-            for (int b = 0; b < DB; ++b)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const u32x2 st = {pack2<BF16>(oacc[qb][b][4 * g + 0] * inv, oacc[qb][b][4 * g + 1] * inv),
-                                      pack2<BF16>(oacc[qb][b][4 * g + 2] * inv, oacc[qb][b][4 * g + 3] * inv)};
-                    *reinterpret_cast<u32x2*>(orow + b * 32 + 8 * g + 4 * h) = st;
-                }
-            if (LSE != nullptr && h == 0) {
-                const float mcf = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb] * c;
-                LSE[(int64_t)bh * N + qrow[qb]] = (mcf + __log2f(l_lse)) * 0.69314718055994531f;
-            }
         }
     }
 }
@@ -1121,15 +828,6 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
     return hipGetLastError();
 }
 
-template <int D, bool BF16, bool CAUSAL>
-hipError_t launch_w64(const void* q, const void* k, const void* v, void* o, float* lse, int N, int n_qt, int G,
-                      float c, float tau_raw, hipStream_t stream) {
-    hipLaunchKernelGGL((fa_fwd_kernel_w64<D, BF16, CAUSAL>), dim3(G), dim3(kThreadsB), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qt, G, c, tau_raw);
-    return hipGetLastError();
-}
-
 // Checks shared by the forward entry points (everything but options and workspace). n_split
 // multiplies the grid.
 int validate(const void* q, const void* k, const void* v, const void* o, const float* lse, int64_t B, int64_t H,
@@ -1176,14 +874,14 @@ const char* fa_status_string(int status) {
         case FA_ERR_SCALE: return "scale must be finite and > 0";
         case FA_ERR_ALIAS: return "o and lse must not overlap the inputs or each other";
         case FA_ERR_LAUNCH: return "kernel launch failed";
-        case FA_ERR_OPTION: return "option out of range (rescale threshold 0..15, variant 0..2, splits 1..64)";
+        case FA_ERR_OPTION: return "option out of range (rescale threshold 0..15, variant 0..1, splits 1..64)";
         case FA_ERR_WORKSPACE: return "workspace is NULL, misaligned, too small or overlaps an argument";
         default: return "unknown status";
     }
 }
 
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
-              int64_t d, float scale, int causal, hipStream_t stream, int dtype, const fa_fwd_options* opts) {
+              int64_t d, float scale, int causal, hipStream_t stream, fa_dtype dtype, const fa_fwd_options* opts) {
     const int st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype, 1);
     if (st != FA_OK) return st;
     const int64_t n_qt = (N + kBlockM - 1) / kBlockM;
@@ -1192,19 +890,16 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
     // unnormalised p stay <= 2^tau and most tiles skip the rescale; tau = 0 moves it on every
     // increase, the loop exactly as the pages write it.
     float tau = kDefaultRescaleLog2;
-    int variant = 0;
     if (opts) {
         if (!(opts->rescale_threshold_log2 >= 0.f && opts->rescale_threshold_log2 <= 15.f)) return FA_ERR_OPTION;
-        if (opts->variant < 0 || opts->variant > 2) return FA_ERR_OPTION;
+        if (opts->variant < 0 || opts->variant > 1) return FA_ERR_OPTION;
         tau = opts->rescale_threshold_log2;
-        variant = opts->variant;
     }
 
     const float c = scale * 1.4426950408889634f;  // scale * log2(e)
     const float tau_raw = tau / c;
     const int n = static_cast<int>(N), nq = static_cast<int>(n_qt), g = static_cast<int>(G);
     const bool bf = dtype == FA_BF16;
-    const bool w64 = variant == 2 || (variant == 0 && kDefaultVariant == 2);
     hipError_t e;
 #define FA_DISPATCH(L)                                                                                \
     if (d == 64) {                                                                                    \
@@ -1218,22 +913,18 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
         else e = causal ? L<128, false, true>(q, k, v, o, lse, n, nq, g, c, tau_raw, stream)           \
                         : L<128, false, false>(q, k, v, o, lse, n, nq, g, c, tau_raw, stream);         \
     }
-    if (w64) {
-        FA_DISPATCH(launch_w64)
-    } else {
-        FA_DISPATCH(launch)
-    }
+    FA_DISPATCH(launch)
 #undef FA_DISPATCH
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
-           int64_t d, float scale, int causal, hipStream_t stream, int dtype) {
+           int64_t d, float scale, int causal, hipStream_t stream, fa_dtype dtype) {
     return fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype, nullptr);
 }
 
 int fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                  int64_t N, int64_t d, float scale, hipStream_t stream, int dtype, const fa_mask* mask) {
+                  int64_t N, int64_t d, float scale, hipStream_t stream, fa_dtype dtype, const fa_mask* mask) {
     const int st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype, 1);
     if (st != FA_OK) return st;
     if (!mask) return FA_ERR_NULL;
@@ -1268,7 +959,7 @@ int fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* l
 }
 
 int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                       int64_t N, int64_t d, float scale, hipStream_t stream, int dtype, const fa_mask* mask,
+                       int64_t N, int64_t d, float scale, hipStream_t stream, fa_dtype dtype, const fa_mask* mask,
                        const fa_block_mask* blocks) {
     const int st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype, 1);
     if (st != FA_OK) return st;
@@ -1359,7 +1050,7 @@ static bool workspace_ok(const void* q, const void* k, const void* v, const void
 }
 
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                   int64_t N, int64_t d, float scale, int causal, hipStream_t stream, int dtype, int num_splits,
+                   int64_t N, int64_t d, float scale, int causal, hipStream_t stream, fa_dtype dtype, int num_splits,
                    void* workspace, size_t workspace_bytes) {
     if (num_splits < 1 || num_splits > kMaxSplits) {
         const int st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype, 1);
@@ -1392,7 +1083,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 }
 
 int fa_fwd_splitkv_masked(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                          int64_t N, int64_t d, float scale, hipStream_t stream, int dtype, const fa_mask* mask,
+                          int64_t N, int64_t d, float scale, hipStream_t stream, fa_dtype dtype, const fa_mask* mask,
                           int num_splits, void* workspace, size_t workspace_bytes) {
     if (num_splits < 1 || num_splits > kMaxSplits) {
         const int st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype, 1);
@@ -1437,7 +1128,7 @@ int fa_fwd_splitkv_masked(const void* q, const void* k, const void* v, void* o, 
 }
 
 int fa_fwd_splitkv_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
-                               int64_t H, int64_t N, int64_t d, float scale, hipStream_t stream, int dtype,
+                               int64_t H, int64_t N, int64_t d, float scale, hipStream_t stream, fa_dtype dtype,
                                const fa_mask* mask, const fa_block_mask* blocks, int num_splits, void* workspace,
                                size_t workspace_bytes) {
     if (num_splits < 1 || num_splits > kMaxSplits) {

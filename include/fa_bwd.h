@@ -64,7 +64,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dout, const float* lse,
            void* dq, void* dk, void* dv, float* delta,
            int64_t B, int64_t H, int64_t N, int64_t d,
-           float scale, int causal, hipStream_t stream, int dtype);
+           float scale, int causal, hipStream_t stream, fa_dtype dtype);
 
 /*
  * fa_bwd_masked -- fa_bwd under the general mask of fa_fwd_masked (fa_mask in fa_fwd.h: a
@@ -82,7 +82,7 @@ int fa_bwd_masked(const void* q, const void* k, const void* v, const void* o,
                   const void* dout, const float* lse,
                   void* dq, void* dk, void* dv, float* delta,
                   int64_t B, int64_t H, int64_t N, int64_t d,
-                  float scale, hipStream_t stream, int dtype, const fa_mask* mask);
+                  float scale, hipStream_t stream, fa_dtype dtype, const fa_mask* mask);
 
 /*
  * fa_bwd_blocksparse -- fa_bwd under the block mask of fa_fwd_blocksparse (fa_block_mask in
@@ -103,7 +103,7 @@ int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const void* 
                        const void* dout, const float* lse,
                        void* dq, void* dk, void* dv, float* delta,
                        int64_t B, int64_t H, int64_t N, int64_t d,
-                       float scale, hipStream_t stream, int dtype, const fa_mask* mask,
+                       float scale, hipStream_t stream, fa_dtype dtype, const fa_mask* mask,
                        const fa_block_mask* blocks);
 
 #ifdef __cplusplus

@@ -42,7 +42,7 @@ extern "C" {
  */
 int fa_fwd_cpu(const void* q, const void* k, const void* v, void* o, float* lse,
                int64_t B, int64_t H, int64_t N, int64_t d,
-               float scale, int causal, int dtype, int num_threads);
+               float scale, int causal, fa_dtype dtype, int num_threads);
 
 #ifdef __cplusplus
 }

@@ -38,8 +38,8 @@ extern "C" {
  * Tuning options for fa_fwd_ex. They change how the result is reached, never
  * what it is (the same exact softmax attention, up to rounding).
  *
- * rescale_threshold_log2: the online recurrence keeps every partial sum
- *   relative to a reference maximum m and rescales them by
+ * rescale_threshold_log2 (f16 only): the online recurrence keeps every partial
+ *   sum relative to a reference maximum m and rescales them by
  *   alpha = exp(m_old - m_new) when m moves ("transformer math: flash
  *   attention math", aicassindra.com, "The rescaling identity, derived").
  *   With 0 the reference is the running maximum at every step, the loop
@@ -48,15 +48,16 @@ extern "C" {
  *   unnormalised probability <= 2^t, and then to t/2 above the running
  *   maximum, so most tiles skip the rescale ("fewer rescaling operations",
  *   "Decoding flash attention", bibekananda.in, "Later versions"). The
- *   default kernel tests this on the sums of each tile's probabilities that
- *   the recurrence forms anyway: when a sum exceeds 2^t (which any score
- *   more than t above the reference makes happen) the wave moves the
- *   reference and recomputes that tile. Range [0, 15]; fa_fwd uses 8.
- * variant: which kernel evaluates it. 0 = the default (variant 1);
- *   1 = 32 query rows per wave, two waves per SIMD (the fast one);
- *   2 = 64 query rows per wave, one wave per SIMD (fewer shared-memory reads
- *   per product, slower; kept as an independently blocked check).
- *   Both give the same result to rounding; range [0, 2].
+ *   kernel tests this on the sums of each tile's probabilities that the
+ *   recurrence forms anyway: when a sum exceeds 2^t (which any score more
+ *   than t above the reference makes happen) the wave moves the reference
+ *   and recomputes that tile. Range [0, 15]; fa_fwd uses 8. bf16 ignores
+ *   it and always keeps the exact running maximum: a probability rounded to
+ *   bf16 (8 significant bits) is off by up to 2^-8 of itself, and only
+ *   against the exact maximum is a row's largest weight exactly 1.
+ * variant: which kernel evaluates it; 0 = the default, 1 = the same kernel
+ *   named explicitly (32 query rows per wave, two waves per SIMD). Range
+ *   [0, 1].
  */
 typedef struct fa_fwd_options {
     float rescale_threshold_log2;
@@ -92,7 +93,7 @@ typedef struct fa_fwd_options {
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int64_t B, int64_t H, int64_t N, int64_t d,
-           float scale, int causal, hipStream_t stream, int dtype);
+           float scale, int causal, hipStream_t stream, fa_dtype dtype);
 
 /*
  * fa_fwd_ex -- fa_fwd with tuning options (see fa_fwd_options). opts == NULL
@@ -101,7 +102,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  */
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               int64_t B, int64_t H, int64_t N, int64_t d,
-              float scale, int causal, hipStream_t stream, int dtype,
+              float scale, int causal, hipStream_t stream, fa_dtype dtype,
               const fa_fwd_options* opts);
 
 /*
@@ -136,7 +137,7 @@ typedef struct fa_mask {
  */
 int fa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
                   int64_t B, int64_t H, int64_t N, int64_t d,
-                  float scale, hipStream_t stream, int dtype, const fa_mask* mask);
+                  float scale, hipStream_t stream, fa_dtype dtype, const fa_mask* mask);
 
 /*
  * A mask over blocks of the score matrix (block-sparse attention) for fa_fwd_blocksparse. Query i
@@ -167,7 +168,7 @@ typedef struct fa_block_mask {
  */
 int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
                        int64_t B, int64_t H, int64_t N, int64_t d,
-                       float scale, hipStream_t stream, int dtype, const fa_mask* mask,
+                       float scale, hipStream_t stream, fa_dtype dtype, const fa_mask* mask,
                        const fa_block_mask* blocks);
 
 /*
@@ -192,7 +193,7 @@ int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, flo
  */
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                    int64_t B, int64_t H, int64_t N, int64_t d,
-                   float scale, int causal, hipStream_t stream, int dtype,
+                   float scale, int causal, hipStream_t stream, fa_dtype dtype,
                    int num_splits, void* workspace, size_t workspace_bytes);
 
 /*
@@ -208,7 +209,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
  */
 int fa_fwd_splitkv_masked(const void* q, const void* k, const void* v, void* o, float* lse,
                           int64_t B, int64_t H, int64_t N, int64_t d,
-                          float scale, hipStream_t stream, int dtype, const fa_mask* mask,
+                          float scale, hipStream_t stream, fa_dtype dtype, const fa_mask* mask,
                           int num_splits, void* workspace, size_t workspace_bytes);
 
 /*
@@ -226,7 +227,7 @@ int fa_fwd_splitkv_masked(const void* q, const void* k, const void* v, void* o, 
  */
 int fa_fwd_splitkv_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
                                int64_t B, int64_t H, int64_t N, int64_t d,
-                               float scale, hipStream_t stream, int dtype, const fa_mask* mask,
+                               float scale, hipStream_t stream, fa_dtype dtype, const fa_mask* mask,
                                const fa_block_mask* blocks, int num_splits, void* workspace,
                                size_t workspace_bytes);
 

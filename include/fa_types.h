@@ -25,8 +25,8 @@ typedef enum fa_status {
     FA_ERR_DTYPE = 4,     /* dtype is not FA_F16 or FA_BF16 */
     FA_ERR_ALIGN = 5,     /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
     FA_ERR_SCALE = 6,     /* scale is not finite and > 0 */
-    FA_ERR_ALIAS = 7,     /* o or lse overlaps an input, or o overlaps lse */
-    FA_ERR_LAUNCH = 8,    /* a kernel launch (hipGetLastError) or a host thread failed */
+    FA_ERR_LAUNCH = 7,    /* a kernel launch (hipGetLastError) or a host thread failed */
+    FA_ERR_ALIAS = 8,     /* o or lse overlaps an input, or o overlaps lse */
     FA_ERR_OPTION = 9,    /* an fa_fwd_options field or num_splits is out of range */
     FA_ERR_WORKSPACE = 10 /* fa_fwd_splitkv: workspace NULL, not 16-byte aligned, smaller than
                              fa_fwd_splitkv_workspace_size, or overlapping an argument */

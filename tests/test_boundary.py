@@ -51,6 +51,33 @@ def test_exported_symbols_match_with_nm():
     assert set(_declared_functions()) <= exported
 
 
+def test_status_codes_are_pinned():
+    """The numeric values of fa_dtype and fa_status are part of the ABI: FA_OK .. FA_ERR_LAUNCH
+    are 0 .. 7 in the order of the interface's definition, then the codes this library adds."""
+    text = open(os.path.join(INCLUDE, "fa_types.h")).read()
+    vals = {m.group(1): int(m.group(2)) for m in re.finditer(r"\b(FA_\w+)\s*=\s*(\d+)", text)}
+    assert vals == {"FA_F16": 0, "FA_BF16": 1, "FA_OK": 0, "FA_ERR_NULL": 1, "FA_ERR_SHAPE": 2,
+                    "FA_ERR_HEAD_DIM": 3, "FA_ERR_DTYPE": 4, "FA_ERR_ALIGN": 5, "FA_ERR_SCALE": 6,
+                    "FA_ERR_LAUNCH": 7, "FA_ERR_ALIAS": 8, "FA_ERR_OPTION": 9, "FA_ERR_WORKSPACE": 10}
+
+
+def test_status_strings_match_codes(L):
+    assert L.fa_status_string(7) == b"kernel launch failed"
+    assert b"overlap" in L.fa_status_string(8)
+    assert b"option" in L.fa_status_string(9)
+    assert b"workspace" in L.fa_status_string(10)
+
+
+def test_entry_points_take_fa_dtype():
+    """Every entry point with an element type declares it as fa_dtype, never a bare int."""
+    for f in sorted(os.listdir(INCLUDE)):
+        if f.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(INCLUDE, f)).read(), flags=re.S)
+            assert not re.search(r"\bint\s+dtype\b", text), f
+            if f != "fa_types.h":
+                assert "fa_dtype dtype" in text, f
+
+
 def test_status_strings(L):
     for st in range(0, 11):
         s = L.fa_status_string(st)
@@ -81,7 +108,7 @@ def _call(L, **kw):
     (dict(dtype=2), 4), (dict(dtype=-1), 4),
     (dict(q=QA + 8), 5), (dict(k=KA + 2), 5), (dict(v=VA + 4), 5), (dict(o=OA + 12), 5), (dict(lse=LA + 2), 5),
     (dict(scale=0.0), 6), (dict(scale=-0.125), 6), (dict(scale=float("inf")), 6), (dict(scale=float("nan")), 6),
-    (dict(o=QA), 7), (dict(o=KA + 16), 7), (dict(lse=VA + 64), 7), (dict(lse=OA), 7),
+    (dict(o=QA), 8), (dict(o=KA + 16), 8), (dict(lse=VA + 64), 8), (dict(lse=OA), 8),
 ])
 def test_argument_errors(L, kw, code):
     assert _call(L, **kw) == code
@@ -110,7 +137,7 @@ def test_binding_fails_loudly_without_gpu_tensors():
         fa.forward(q, q, q)
 
 
-@pytest.mark.parametrize("thr,variant", [(-1.0, 0), (15.5, 0), (float("nan"), 0), (float("inf"), 0), (8.0, 3), (8.0, -1)])
+@pytest.mark.parametrize("thr,variant", [(-1.0, 0), (15.5, 0), (float("nan"), 0), (float("inf"), 0), (8.0, 2), (8.0, 3), (8.0, -1)])
 def test_option_errors(L, thr, variant):
     import exact_tiled_softmax_fa_amd as fa
     a = dict(GOOD)
@@ -148,8 +175,8 @@ def _bwd(**kw):
     (dict(q=0x100008), 5), (dict(dout=0x500004), 5), (dict(dq=0x700002), 5), (dict(lse=0x600002), 5),
     (dict(delta=0xA00001), 5),
     (dict(scale=0.0), 6), (dict(scale=float("nan")), 6),
-    (dict(dq=0x100000), 7), (dict(dk=0x500000 + 64), 7), (dict(dv=0x700000), 7), (dict(delta=0x600000), 7),
-    (dict(delta=0x900000), 7), (dict(dk=0x700000 + 16), 7),
+    (dict(dq=0x100000), 8), (dict(dk=0x500000 + 64), 8), (dict(dv=0x700000), 8), (dict(delta=0x600000), 8),
+    (dict(delta=0x900000), 8), (dict(dk=0x700000 + 16), 8),
 ])
 def test_backward_argument_errors(L, kw, code):
     assert _bwd(**kw) == code
@@ -196,7 +223,7 @@ WS = 0xB00000
     (0, WS, 1 << 20, {}, 9), (65, WS, 1 << 30, {}, 9), (-1, WS, 1 << 20, {}, 9),
     (4, None, 1 << 20, {}, 10), (4, WS, 100, {}, 10), (4, WS + 8, 1 << 20, {}, 10),
     (4, QA, 1 << 20, {}, 10), (4, OA - 64, 1 << 20, {}, 10), (4, LA, 1 << 20, {}, 10),
-    (4, WS, 1 << 20, dict(q=None), 1), (4, WS, 1 << 20, dict(d=96), 3), (4, WS, 1 << 20, dict(o=QA), 7),
+    (4, WS, 1 << 20, dict(q=None), 1), (4, WS, 1 << 20, dict(d=96), 3), (4, WS, 1 << 20, dict(o=QA), 8),
     (0, WS, 1 << 20, dict(q=None), 1),
 ])
 def test_splitkv_argument_errors(L, num_splits, ws, ws_bytes, kw, code):
@@ -206,7 +233,7 @@ def test_splitkv_argument_errors(L, num_splits, ws, ws_bytes, kw, code):
 @pytest.mark.parametrize("mask,kw,code", [
     (None, {}, 1), ((-2, 0, None), {}, 9), ((0, -2, None), {}, 9), ((1 << 31, 0, None), {}, 9),
     ((4, 0, 0x600002), {}, 5), ((4, 0, None), dict(q=None), 1), ((4, 0, None), dict(d=96), 3),
-    ((4, 0, None), dict(o=QA), 7),
+    ((4, 0, None), dict(o=QA), 8),
 ])
 def test_masked_argument_errors(L, mask, kw, code):
     import exact_tiled_softmax_fa_amd as fa
@@ -227,7 +254,7 @@ FAR = dict(q=0x10000000, k=0x20000000, v=0x30000000, o=0x40000000, lse=0x5000000
     ((0xC00000, 64, 64, 0, -8), None, {}, 9), ((0xC00000, 1 << 31, 64, 0, 0), None, {}, 9),
     ((0xC00000, 64, 64, 0, 0), (-2, 0, None), {}, 9), ((0xC00000, 64, 64, 0, 0), (4, 0, 0x600002), {}, 5),
     ((0xC00000, 64, 64, 0, 0), None, dict(q=None), 1), ((0xC00000, 64, 64, 0, 0), None, dict(d=96), 3),
-    ((0xC00000, 64, 64, 0, 0), None, dict(o=QA), 7), ((0xC00000, 64, 64, 0, 0), None, dict(N=1 << 24, **FAR), 2),
+    ((0xC00000, 64, 64, 0, 0), None, dict(o=QA), 8), ((0xC00000, 64, 64, 0, 0), None, dict(N=1 << 24, **FAR), 2),
 ])
 def test_blocksparse_argument_errors(L, blocks, mask, kw, code):
     import exact_tiled_softmax_fa_amd as fa
@@ -251,7 +278,7 @@ def _bwd_masked(mask, **kw):
 @pytest.mark.parametrize("mask,kw,code", [
     (None, {}, 1), ((-2, 0, None), {}, 9), ((0, -2, None), {}, 9), ((1 << 31, 0, None), {}, 9),
     ((4, 0, 0x600002), {}, 5), ((4, 0, None), dict(q=None), 1), ((4, 0, None), dict(delta=None), 1),
-    ((4, 0, None), dict(d=96), 3), ((4, 0, None), dict(dq=0x100000), 7), ((4, 0, None), dict(scale=0.0), 6),
+    ((4, 0, None), dict(d=96), 3), ((4, 0, None), dict(dq=0x100000), 8), ((4, 0, None), dict(scale=0.0), 6),
 ])
 def test_bwd_masked_argument_errors(L, mask, kw, code):
     assert _bwd_masked(mask, **kw) == code
@@ -268,7 +295,7 @@ BWD_FAR = {name: (i + 1) << 28 for i, name in enumerate(("q", "k", "v", "o", "do
     ((0xC00000, 64, 64, 0, -8), None, {}, 9), ((0xC00000, 64, 1 << 31, 0, 0), None, {}, 9),
     ((0xC00000, 64, 64, 0, 0), (-2, 0, None), {}, 9), ((0xC00000, 64, 64, 0, 0), (4, 0, 0x600002), {}, 5),
     ((0xC00000, 64, 64, 0, 0), None, dict(q=None), 1), ((0xC00000, 64, 64, 0, 0), None, dict(delta=None), 1),
-    ((0xC00000, 64, 64, 0, 0), None, dict(d=96), 3), ((0xC00000, 64, 64, 0, 0), None, dict(dk=0x100000), 7),
+    ((0xC00000, 64, 64, 0, 0), None, dict(d=96), 3), ((0xC00000, 64, 64, 0, 0), None, dict(dk=0x100000), 8),
     ((0xC00000, 64, 64, 0, 0), None, dict(scale=-1.0), 6),
     ((0xC00000, 64, 64, 0, 0), None, dict(N=1 << 24, **BWD_FAR), 2),
 ])
@@ -290,7 +317,7 @@ def test_bwd_blocksparse_argument_errors(L, blocks, mask, kw, code):
     (4, None, 1 << 20, (8, 0, None), {}, 10), (4, WS, 100, (8, 0, None), {}, 10),
     (4, WS + 8, 1 << 20, (8, 0, None), {}, 10), (4, QA, 1 << 20, (8, 0, None), {}, 10),
     (4, WS, 1 << 20, (8, 0, None), dict(q=None), 1), (4, WS, 1 << 20, (8, 0, None), dict(d=96), 3),
-    (4, WS, 1 << 20, (8, 0, None), dict(o=QA), 7),
+    (4, WS, 1 << 20, (8, 0, None), dict(o=QA), 8),
     # the trivial masks go to fa_fwd_splitkv, which checks the same workspace
     (4, None, 1 << 20, (-1, -1, None), {}, 10),
 ])
@@ -314,7 +341,7 @@ def test_splitkv_masked_argument_errors(L, num_splits, ws, ws_bytes, mask, kw, c
     (4, QA, 1 << 20, (0xC00000, 64, 64, 0, 0), None, {}, 10),
     (4, WS, 1 << 20, (0xC00000, 64, 64, 0, 0), None, dict(q=None), 1),
     (4, WS, 1 << 20, (0xC00000, 64, 64, 0, 0), None, dict(d=96), 3),
-    (4, WS, 1 << 20, (0xC00000, 64, 64, 0, 0), None, dict(o=QA), 7),
+    (4, WS, 1 << 20, (0xC00000, 64, 64, 0, 0), None, dict(o=QA), 8),
 ])
 def test_splitkv_blocksparse_argument_errors(L, num_splits, ws, ws_bytes, blocks, mask, kw, code):
     import exact_tiled_softmax_fa_amd as fa

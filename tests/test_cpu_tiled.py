@@ -81,7 +81,7 @@ def test_cpu_tiled_rejects_bad_arguments():
     assert fa.fa_fwd_cpu(None, z.data_ptr(), z.data_ptr(), z.data_ptr(), None, 1, 1, 8, 64, 0.1, 0, 0, 1) == 1
     o = torch.empty_like(z)
     assert fa.fa_fwd_cpu(z.data_ptr(), z.data_ptr(), z.data_ptr(), o.data_ptr(), None, 1, 1, 8, 96, 0.1, 0, 0, 1) == 3
-    assert fa.fa_fwd_cpu(z.data_ptr(), z.data_ptr(), z.data_ptr(), z.data_ptr(), None, 1, 1, 8, 64, 0.1, 0, 0, 1) == 7
+    assert fa.fa_fwd_cpu(z.data_ptr(), z.data_ptr(), z.data_ptr(), z.data_ptr(), None, 1, 1, 8, 64, 0.1, 0, 0, 1) == 8  # FA_ERR_ALIAS
     assert fa.fa_fwd_cpu(z.data_ptr(), z.data_ptr(), z.data_ptr(), o.data_ptr(), None, 1, 1, 8, 64, -1.0, 0, 0, 1) == 6
 
 
