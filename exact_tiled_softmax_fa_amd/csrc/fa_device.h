@@ -172,9 +172,11 @@ inline bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
-// 16 bytes at byte offset `off` of one head's n_bytes into LDS, lane l's at dst + 16 l
-// (buffer_load_dwordx4 ... lds). Offsets past n_bytes read zero; the callers clamp their rows so
-// none are. This is the MUBUF form of the LDS DMA on purpose: the compiler's wait-count pass
+// 16 bytes at byte offset `off` of the n_bytes at `head` into LDS, lane l's at dst + 16 l
+// (buffer_load_dwordx4 ... lds). Offsets past n_bytes read zero (the buffer's range check; no
+// memory beyond them is touched): the forward kernels pass a base at the tile's first row and the
+// bytes up to the head's end, so rows past the sequence read as zero; the backward kernels clamp
+// their rows instead. This is the MUBUF form of the LDS DMA on purpose: the compiler's wait-count pass
 // takes the FLAT-encoded global_load_lds for an access that may touch LDS and finish out of
 // order, and while one is in flight it waits for every LDS read (lgkmcnt(0)), also for those a
 // register ring issued ahead; the MUBUF form counts only against vmcnt and leaves those waits

@@ -188,19 +188,27 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
     // Load g of a tile covers rows RPI*g .. RPI*g+RPI-1; lane l writes LDS bytes [1024 g + 16 l,
     // +16), i.e. row RPI*g + l/CPR at chunk position l % CPR, which holds global chunk
-    // (l % CPR) ^ swz_k(row) (K tiles) or ^ swz_v(row) (V tiles). Rows past the end of the sequence
-    // repeat row N-1 (finite data; those keys are masked before they can carry weight).
+    // (l % CPR) ^ swz_k(row) (K tiles) or ^ swz_v(row) (V tiles). Those per-lane byte offsets
+    // within a tile are fixed (koffs, voffs); a tile moves only the buffer descriptor's base (a
+    // scalar add), and the descriptor's size ends at the head's last row, so rows past the end of
+    // the sequence read as zero (those keys are masked to -inf before they can carry weight).
     // Offsets inside one head fit in 32 bits (the host limits N * d * 2 bytes to < 2^31).
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // scalar copy for LDS destinations
+    unsigned koffs[IPW], voffs[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int ld = wave_s * IPW + i;
+        const int r = RPI * ld + lane / CPR;
+        koffs[i] = 2u * (unsigned)(r * D + 8 * ((lane % CPR) ^ swz_k<D>(r)));
+        voffs[i] = 2u * (unsigned)(r * D + 8 * ((lane % CPR) ^ swz_v<D>(r)));
+    }
     auto issue = [&](const uint16_t* src_head, int j, uint16_t* dst, bool v_tile) __attribute__((always_inline)) {
-        const int k0 = (BLOCKS ? t_list[j] : tb + j) * kBlockN;
+        const int k0 = __builtin_amdgcn_readfirstlane((BLOCKS ? t_list[j] : tb + j) * kBlockN);
+        const int nb = (N - k0) * D * 2;
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
             const int ld = wave_s * IPW + i;
-            const int r = RPI * ld + lane / CPR;
-            const int ch = (lane % CPR) ^ (v_tile ? swz_v<D>(r) : swz_k<D>(r));
-            const unsigned src = (unsigned)min(k0 + r, N - 1) * D + 8 * ch;
-            lds_load16(src_head, N * D * 2, 2 * src, (lds_void*)(dst + ld * 512));
+            lds_load16(src_head + (int64_t)k0 * D, nb, v_tile ? voffs[i] : koffs[i], (lds_void*)(dst + ld * 512));
         }
     };
 
@@ -384,14 +392,16 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
     };
     // Accept the exponentials of a tile (taken against the current reference) when no lane's sum
     // of a row's values exceeds 2^tau_log2: then no single p does either, the bound the reference
-    // max exists to keep. Otherwise (rare: the scores rose past the reference, or a row has no
-    // reference yet) move the reference to the running max and take them again. This replaces a
-    // max over every tile by a test on sums the softmax forms anyway.
+    // max exists to keep. Otherwise (rare: the scores rose past the reference, or -- masked kernels
+    // only -- a row has no reference yet) move the reference to the running max and take them
+    // again. This replaces a max over every tile by a test on sums the softmax forms anyway. (In the
+    // other kernels the first tile sets every row's reference: it holds key 0, or under split-KV a
+    // key every row that has any key in the split can see.)
     // (EXACT: the reference already is the row's maximum over this tile, so every p <= 1.)
     auto settle = [&](const f32x4 (&sd)[2][4]) __attribute__((always_inline)) {
         if constexpr (!EXACT) {
-            if (__builtin_amdgcn_ballot_w64(l_tile[0] > p_cap || l_tile[1] > p_cap || m_run[0] == -INFINITY ||
-                                            m_run[1] == -INFINITY)) {
+            if (__builtin_amdgcn_ballot_w64(l_tile[0] > p_cap || l_tile[1] > p_cap ||
+                                            (MASKED && (m_run[0] == -INFINITY || m_run[1] == -INFINITY)))) {
                 rebase_from(sd, true);
                 expo(sd);
             }
