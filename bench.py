@@ -236,6 +236,8 @@ def main():
     ap.add_argument("--block-density", type=float, default=None, help="block-sparse: fraction of blocks kept")
     ap.add_argument("--block-size", type=int, default=128, help="block-sparse: rows and keys per block")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--no-steady-state", action="store_true",
+                    help="skip the steady-state figure (profiled runs: only the warm-up and timed steps)")
     ap.add_argument("--cpu-variant", action="store_true", help="time fa_fwd_cpu on host cores instead")
     ap.add_argument("--heads", type=int, default=4, help="--cpu-variant: heads of the workload to run")
     ap.add_argument("--threads", type=int, default=0, help="--cpu-variant: worker threads (0: all)")
@@ -351,7 +353,30 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kernel_ms = ev[0].elapsed_time(ev[-1]) / args.steps  # average launch duration on the kernel's stream
-    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    in_order = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    per_step = sorted(in_order)
+
+    # Reported alongside, never in place of the line above: the same step once the clock has
+    # settled. Leaving idle, the chip first clocks high, then its power limit pulls the clock down
+    # and lets it recover over some tens of milliseconds (the cycles per launch stay constant; the
+    # rocprof summaries give the clock of each timed dispatch), so the K steps after W warm-up
+    # steps can run slower than the same steps later on.
+    steady_ms = t_steady = None
+    if not args.no_steady_state:
+        settle_s = 0.3
+        t1 = time.perf_counter()
+        while time.perf_counter() - t1 < settle_s:
+            for _ in range(5):
+                step()
+            torch.cuda.synchronize()
+        ev2 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        t_steady = time.perf_counter() - t0  # seconds from the start of the timed steps
+        ev2[0].record(stream)
+        for _ in range(args.steps):
+            step()
+        ev2[1].record(stream)
+        torch.cuda.synchronize()
+        steady_ms = ev2[0].elapsed_time(ev2[1]) / args.steps
 
     flops = w.flops() * (2.5 if args.which == "bwd" else 1.0)
     if window is not None:
@@ -404,6 +429,16 @@ def main():
             "kernel_ms": round(kernel_ms, 4),
             "kernel_ms_median": round(per_step[len(per_step) // 2], 4),
             "kernel_ms_min": round(per_step[0], 4),
+            "kernel_ms_first_last": [round(in_order[0], 4), round(in_order[-1], 4)],
+        },
+        "steady_state": None if steady_ms is None else {
+            "value": round(flops / (steady_ms * 1e-3) / 1e12, 2),
+            "pct_mfma_peak": round(100.0 * flops / (steady_ms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 2),
+            "kernel_ms": round(steady_ms, 4),
+            "steps": args.steps,
+            "after_s": round(t_steady, 2),
+            "note": "the same steps after the timed ones and another 0.3 s of them (clock settled); "
+                    "context for value, not the value",
         },
         "inputs": inputs_record,
     }

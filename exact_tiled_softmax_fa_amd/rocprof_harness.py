@@ -1,6 +1,8 @@
-"""rocprofv3 harness: kernel time, matrix-core utilisation and device-memory traffic.
+"""rocprofv3 harness: kernel time, matrix-core utilisation, clock, instruction mix and device-memory
+traffic, all measured on the same timed dispatches.
 
     python -m exact_tiled_softmax_fa_amd.rocprof_harness [--workload NAME] [--pass fwd|bwd]
+                                                         [--steps K] [--warmup W]
                                                          [--out DIR] [--summary-dir DIR] [--parse-only]
 
 --pass fwd (default) profiles fa_fwd's kernel; --pass bwd profiles the two kernels of fa_bwd
@@ -9,27 +11,37 @@ profiles fa_fwd_splitkv's split kernel and its merge kernel; --block-density P [
 (with --pass fwd) profiles fa_fwd_blocksparse on bench.py's seeded block mask, priced by the
 allowed (row, key) pairs.
 
-Runs four rocprofv3 passes over ``bench.py`` as child processes (this process
-never touches the GPU, so the profiler's preload stays in its own process):
+Every pass runs the same command, ``bench.py --steps K --warmup W`` (default K = 20, W = 5: the
+command a default benchmark line is measured with), as a child process (this process never touches
+the GPU, so the profiler's preload stays in its own process):
 
-1. ``--kernel-trace --stats``: per-dispatch kernel durations.
-2. ``--pmc FETCH_SIZE`` and 3. ``--pmc WRITE_SIZE``, one counter per pass, with a
-   plain 256 MiB device copy run first (``bench.py --copy-ref-mib 256``). The copy's
-   known size calibrates both counters (bytes read and written by a copy of known
-   size / counter value), and the same factors scale the kernel's counts.
-4. ``--pmc SQ_INSTS_VALU_MFMA_MOPS_{F16,BF16} SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES
+1. ``--kernel-trace --stats``: per-dispatch kernel durations, no counters.
+2. ``--kernel-trace --pmc FETCH_SIZE`` and 3. ``--kernel-trace --pmc WRITE_SIZE``, one counter per
+   pass, with a plain 256 MiB device copy run first (``bench.py --copy-ref-mib 256``). The copy's
+   known size calibrates both counters (bytes read and written by a copy of known size / counter
+   value), and the same factors scale the kernel's counts.
+4. ``--kernel-trace --pmc SQ_INSTS_VALU_MFMA_MOPS_{F16,BF16} SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES
    GRBM_GUI_ACTIVE``: matrix-core work and busy cycles against elapsed cycles.
+5. ``--kernel-trace --pmc SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_SALU SQ_INSTS_LDS
+   SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_COEXEC_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY GRBM_GUI_ACTIVE``:
+   the instruction mix and where the waves' cycles go.
 
-It then writes a Markdown summary (``<summary-dir>/fa_fwd_kernel_<workload>.md``)
-and ``traffic_fa_fwd_kernel_<workload>.json``. The JSON holds the bytes per launch
-and the SHA-256 of the kernel source it was measured on; ``bench.py`` reports
-the traffic only while that hash matches. Reported figures:
-- the mean kernel time over the timed dispatches;
+In every pass the timed dispatches are the kernel's dispatches W+1 .. W+K in dispatch-id order: the
+same K calls the benchmark times, after its W warm-up calls (the profiled command skips the
+benchmark's steady-state block). Each counter is averaged over those
+dispatches of its own pass, and the clock is each dispatch's GUI-active cycles per XCD over that
+same dispatch's duration in the same pass (a counter pass serialises dispatches, so its durations
+are not the benchmark's; they only pair cycles with time). It then writes a Markdown summary
+(``<summary-dir>/fa_fwd_kernel_<workload>.md``) and ``traffic_fa_fwd_kernel_<workload>.json``. The
+JSON holds the bytes per launch and the SHA-256 of the kernel source it was measured on;
+``bench.py`` reports the traffic only while that hash matches. Reported figures:
+- the per-dispatch durations of the trace pass and their mean over the timed dispatches;
 - MFMA busy fraction = busy cycles / SIMDs / (GUI-active cycles / XCDs);
+- the clock of the timed dispatches, and the dense MFMA peak scaled to it;
+- vector, matrix, scalar and LDS instructions per launch, and the fractions of wave cycles spent
+  issuing vector work, waiting for issue and waiting on counters or barriers;
 - device-memory bytes per launch and the achieved GB/s (bytes / mean kernel time);
-- the ratio of measured to unavoidable bytes (Q, K, V read once; O, lse written once);
-- the sustained clock, GUI-active cycles per XCD over the mean kernel time, and the dense MFMA
-  peak scaled to it (the counters and the trace come from separate runs of the same command).
+- the ratio of measured to unavoidable bytes (Q, K, V read once; O, lse written once).
 """
 import argparse
 import csv
@@ -63,22 +75,27 @@ def kernel_sha(which: str = "fwd") -> str:
     return h.hexdigest()
 
 
+MIX_COUNTERS = ["SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_ACTIVE_INST_VALU",
+                "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "GRBM_GUI_ACTIVE"]
+
+
 def passes(workload: str, out: str, steps: int, warmup: int, which: str = "fwd", splits=None, blocks=None):
     bench = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload, "--pass", which,
-             "--no-cpu-baseline"]
+             "--no-cpu-baseline", "--no-steady-state"]
     if splits is not None:
         bench += ["--splits", str(splits)]
     if blocks is not None:
         bench += ["--block-size", str(blocks[0]), "--block-density", str(blocks[1])]
     timed = bench + ["--steps", str(steps), "--warmup", str(warmup)]
-    short = bench + ["--steps", "2", "--warmup", "1"]
     copy = ["--copy-ref-mib", str(COPY_MIB)]
     dtype_mops = "SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU_MFMA_MOPS_BF16".split()
+    kt = ["--kernel-trace"]
     return [
         ("kt", ["--kernel-trace", "--stats"], timed),
-        ("fetch", ["--pmc", "FETCH_SIZE"], short + copy),
-        ("write", ["--pmc", "WRITE_SIZE"], short + copy),
-        ("mfma", ["--pmc", *dtype_mops, "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"], short),
+        ("fetch", kt + ["--pmc", "FETCH_SIZE"], timed + copy),
+        ("write", kt + ["--pmc", "WRITE_SIZE"], timed + copy),
+        ("mfma", kt + ["--pmc", *dtype_mops, "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"], timed),
+        ("mix", kt + ["--pmc", *MIX_COUNTERS], timed),
     ]
 
 
@@ -121,9 +138,34 @@ def _reference_copies(values):
     return [v for v in values if v >= 0.5 * top]
 
 
-def _counter(out, name, counter, kernel):
-    return [float(r["Counter_Value"]) for r in _rows(_find(out, name, "counter_collection.csv"))
-            if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]]
+def timed_dispatches(rows, kernel: str, steps: int, warmup: int):
+    """Dispatch ids of a pass's timed calls of `kernel`: in id order, the `steps` dispatches after its
+    first `warmup` ones (the benchmark's warm-up calls come first). Works on kernel-trace and
+    counter-collection rows."""
+    ids = sorted({int(r["Dispatch_Id"]) for r in rows if kernel in r["Kernel_Name"]})
+    return ids[warmup:warmup + steps]
+
+
+def _durations_ms(out, name):
+    """Dispatch id -> duration (ms) from a pass's kernel trace."""
+    return {int(r["Dispatch_Id"]): (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
+            for r in _rows(_find(out, name, "kernel_trace.csv"))}
+
+
+def _counter(out, name, counter, kernel, steps=None, warmup=0):
+    """Per-dispatch values of `counter` for `kernel` in pass `name`: {dispatch id: value}, restricted
+    to the timed dispatches when `steps` is given."""
+    rows = [r for r in _rows(_find(out, name, "counter_collection.csv")) if kernel in r["Kernel_Name"]]
+    keep = set(timed_dispatches(rows, kernel, steps, warmup)) if steps else None
+    vals = {}
+    for r in rows:
+        if r["Counter_Name"] == counter and (keep is None or int(r["Dispatch_Id"]) in keep):
+            vals[int(r["Dispatch_Id"])] = vals.get(int(r["Dispatch_Id"]), 0.0) + float(r["Counter_Value"])
+    return vals
+
+
+def _mean(d):
+    return statistics.mean(d.values()) if d else 0.0
 
 
 def kernels(workload: str, which: str = "fwd", splits=None, blocks=None):
@@ -159,31 +201,44 @@ def kernels(workload: str, which: str = "fwd", splits=None, blocks=None):
             ("fa_bwd_dkdv_kernel", 4 * per_product, BH * (6 * t + 8 * N))]  # q k v dO lse delta -> dk dv
 
 
-def summarize(workload: str, out: str, steps: int, cmds=None, which: str = "fwd", splits=None, blocks=None) -> list:
+def summarize(workload: str, out: str, steps: int, cmds=None, which: str = "fwd", splits=None, blocks=None,
+              warmup: int = 0) -> list:
     """One record per kernel of the pass (see ``kernels``)."""
     recs = []
     for kname, flops, unavoidable in kernels(workload, which, splits, blocks):
-        trace = [r for r in _rows(_find(out, "kt", "kernel_trace.csv")) if kname in r["Kernel_Name"]]
-        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in trace]
-        timed = durs[-steps:]
+        trace = _rows(_find(out, "kt", "kernel_trace.csv"))
+        dur = _durations_ms(out, "kt")
+        all_ids = sorted({int(r["Dispatch_Id"]) for r in trace if kname in r["Kernel_Name"]})
+        durs = [dur[i] for i in all_ids]
+        timed = [dur[i] for i in timed_dispatches(trace, kname, steps, warmup)]
         ms = statistics.mean(timed)
-        fetch_copy = _reference_copies(_counter(out, "fetch", "FETCH_SIZE", "copyBuffer"))
-        write_copy = _reference_copies(_counter(out, "write", "WRITE_SIZE", "copyBuffer"))
-        fetch_k = _counter(out, "fetch", "FETCH_SIZE", kname)
-        write_k = _counter(out, "write", "WRITE_SIZE", kname)
+        fetch_copy = _reference_copies(list(_counter(out, "fetch", "FETCH_SIZE", "copyBuffer").values()))
+        write_copy = _reference_copies(list(_counter(out, "write", "WRITE_SIZE", "copyBuffer").values()))
         f_fac = COPY_MIB * 1024.0 / statistics.mean(fetch_copy)
         w_fac = COPY_MIB * 1024.0 / statistics.mean(write_copy)
-        fetch_b = statistics.mean(fetch_k) * f_fac * 1024
-        write_b = statistics.mean(write_k) * w_fac * 1024
-        gui = statistics.mean(_counter(out, "mfma", "GRBM_GUI_ACTIVE", kname))
-        busy = statistics.mean(_counter(out, "mfma", "SQ_VALU_MFMA_BUSY_CYCLES", kname))
-        mops = sum(statistics.mean(v) for v in (_counter(out, "mfma", "SQ_INSTS_VALU_MFMA_MOPS_F16", kname),
-                                                _counter(out, "mfma", "SQ_INSTS_VALU_MFMA_MOPS_BF16", kname)) if v)
-        util = busy / N_SIMD / (gui / N_XCD)
+        fetch_b = _mean(_counter(out, "fetch", "FETCH_SIZE", kname, steps, warmup)) * f_fac * 1024
+        write_b = _mean(_counter(out, "write", "WRITE_SIZE", kname, steps, warmup)) * w_fac * 1024
+        gui_d = _counter(out, "mfma", "GRBM_GUI_ACTIVE", kname, steps, warmup)
+        gui = _mean(gui_d)
+        busy = _mean(_counter(out, "mfma", "SQ_VALU_MFMA_BUSY_CYCLES", kname, steps, warmup))
+        mops = sum(_mean(_counter(out, "mfma", c, kname, steps, warmup))
+                   for c in ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_BF16"))
+        util = busy / N_SIMD / (gui / N_XCD) if gui else 0.0
+        # clock: each timed dispatch's cycles over its own duration, in the same (counter) pass
+        dur_mfma = _durations_ms(out, "mfma")
+        clocks = [gui_d[i] / N_XCD / (dur_mfma[i] * 1e-3) / 1e9 for i in gui_d if dur_mfma.get(i)]
+        mix = {}
+        try:
+            for c in MIX_COUNTERS:
+                mix[c] = _mean(_counter(out, "mix", c, kname, steps, warmup))
+        except FileNotFoundError:
+            mix = {}
         recs.append({
             "kernel": kname,
             "kernel_sha256": kernel_sha(which),
             "workload": workload,
+            "steps": steps,
+            "warmup": warmup,
             "kernel_ms_mean_timed": ms,
             "dispatch_ms": durs,
             "bytes_per_launch": fetch_b + write_b,
@@ -197,7 +252,8 @@ def summarize(workload: str, out: str, steps: int, cmds=None, which: str = "fwd"
             "mfma_flop_per_launch": mops * 512,
             "mfma_busy_fraction": util,
             "tflops_from_trace": flops / (ms * 1e-3) / 1e12,
-            "clock_ghz": gui / N_XCD / (ms * 1e-3) / 1e9,
+            "clock_ghz": statistics.mean(clocks) if clocks else 0.0,
+            "instruction_mix": mix,
             "commands": cmds or [],
             "pass": which,
             "splits": splits,
@@ -212,18 +268,34 @@ def variant_tag(splits=None, blocks=None) -> str:
 
 
 def clock_line(rec: dict) -> str:
-    """The sustained-clock line of a summary. The cycle count comes from the short counter run and
-    the time from the trace run; when they cannot belong together (no matrix work, or a clock
-    above the part's maximum) the line says so instead of giving a number."""
+    """The clock line of a summary: the timed dispatches' GUI-active cycles per XCD over their own
+    durations, both from the matrix-core counter pass."""
     ghz = rec["clock_ghz"]
-    if rec["mfma_flop_per_launch"] <= 0:
-        return ("- sustained clock: not given (no matrix work; for a kernel this short the cycle count of a "
-                "separate run does not pair with the trace)")
-    if ghz > 1.02 * PEAK_CLOCK_GHZ:
-        return (f"- sustained clock: not given (the counter run's cycles over the trace's time give {ghz:.2f} GHz, "
-                f"above the {PEAK_CLOCK_GHZ} GHz maximum: the two runs do not pair for this kernel)")
-    return (f"- sustained clock: {ghz:.2f} GHz; dense MFMA peak at that clock: "
-            f"{PEAK_TFLOPS * ghz / PEAK_CLOCK_GHZ:.0f} TFLOP/s (of {PEAK_TFLOPS} at {PEAK_CLOCK_GHZ} GHz)")
+    if rec["mfma_flop_per_launch"] <= 0 or ghz <= 0:
+        return "- clock of the timed dispatches: not given (no matrix work or no cycle count)"
+    return (f"- clock of the timed dispatches: {ghz:.2f} GHz (cycles and durations of the same dispatches); "
+            f"dense MFMA peak at that clock: {PEAK_TFLOPS * ghz / PEAK_CLOCK_GHZ:.0f} TFLOP/s "
+            f"(of {PEAK_TFLOPS} at {PEAK_CLOCK_GHZ} GHz)")
+
+
+def mix_lines(rec: dict) -> list:
+    """Instruction mix per launch and the split of wave cycles (from the mix counter pass)."""
+    m = rec.get("instruction_mix") or {}
+    if not m or not m.get("SQ_INSTS_VALU"):
+        return []
+    lines = ["## Instruction mix (SQ_INSTS_*, SQ_ACTIVE_INST_VALU, SQ_WAIT_*; per launch)", "",
+             f"- vector instructions {m['SQ_INSTS_VALU']:.4g} (of which MFMA {m['SQ_INSTS_MFMA']:.4g}), "
+             f"scalar {m['SQ_INSTS_SALU']:.4g}, LDS {m['SQ_INSTS_LDS']:.4g}"]
+    gui = m.get("GRBM_GUI_ACTIVE", 0.0)
+    if gui:
+        simd_cycles = gui / N_XCD * N_SIMD
+        lines.append(f"- vector issue busy (incl. MFMA issue) {100 * 4 * m['SQ_ACTIVE_INST_VALU'] / simd_cycles:.1f} % "
+                     f"of SIMD cycles; MFMA busy while a vector instruction issued (co-execution) "
+                     f"{100 * m['SQ_VALU_MFMA_COEXEC_CYCLES'] / simd_cycles:.1f} %")
+        lines.append(f"- wave cycles waiting on counters or barriers {4 * m['SQ_WAIT_ANY'] / simd_cycles:.2f}, "
+                     f"waiting to issue {4 * m['SQ_WAIT_INST_ANY'] / simd_cycles:.2f} (wave-cycles per SIMD cycle)")
+    lines.append("")
+    return lines
 
 
 def write_summary(rec: dict, summary_dir: str):
@@ -242,7 +314,7 @@ def write_summary(rec: dict, summary_dir: str):
     lines += [
         "## Kernel time (rocprofv3 --kernel-trace --stats)", "",
         f"- dispatches (ms): {', '.join(f'{x:.3f}' for x in d)}",
-        f"- mean of the timed dispatches: **{rec['kernel_ms_mean_timed']:.4f} ms** "
+        f"- mean of the timed dispatches ({rec.get('warmup', 0) + 1} .. {rec.get('warmup', 0) + rec.get('steps', len(d))}): **{rec['kernel_ms_mean_timed']:.4f} ms** "
         f"= {rec['tflops_from_trace']:.1f} TFLOP/s (the matrix products this kernel executes)", "",
         "## Device-memory traffic (FETCH_SIZE, WRITE_SIZE; one counter per pass)", "",
         f"- scale factors from a {COPY_MIB} MiB device copy: fetch x{rec['fetch_scale']:.3f}, "
@@ -255,7 +327,7 @@ def write_summary(rec: dict, summary_dir: str):
         f"- MFMA work per launch: {rec['mfma_flop_per_launch']:.4e} flop",
         f"- MFMA busy: **{100 * rec['mfma_busy_fraction']:.1f} %** of elapsed cycles",
         clock_line(rec), "",
-    ]
+    ] + mix_lines(rec)
     with open(os.path.join(summary_dir, name + ".md"), "w") as f:
         f.write("\n".join(lines))
     slim = {k: v for k, v in rec.items() if k != "dispatch_ms"}
@@ -274,9 +346,9 @@ def main():
     ap.add_argument("--block-size", type=int, default=128, help="block-sparse: rows and keys per block")
     ap.add_argument("--out", default=os.path.join(ROOT, "rocprof_out"))
     ap.add_argument("--summary-dir", default=os.path.join(ROOT, "rocprof_out"))
-    # the kernel-trace pass times the same 10 warm-up and 50 timed calls as a default bench.py line
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # every pass runs the calls of the benchmark command the headline line is measured with
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--timeout", type=int, default=240, help="seconds per rocprofv3 pass")
     ap.add_argument("--parse-only", action="store_true", help="summarise existing outputs under --out")
     args = ap.parse_args()
@@ -286,7 +358,7 @@ def main():
     cmds = None
     if not args.parse_only:
         cmds = run(args.workload, out, args.steps, args.warmup, args.timeout, args.which, args.splits, blocks)
-    for rec in summarize(args.workload, out, args.steps, cmds, args.which, args.splits, blocks):
+    for rec in summarize(args.workload, out, args.steps, cmds, args.which, args.splits, blocks, args.warmup):
         if args.parse_only:  # keep the commands an earlier summary of the same run recorded
             name = f"{rec['kernel']}_{rec['workload']}" + variant_tag(rec.get("splits"), rec.get("blocks"))
             prev = os.path.join(args.summary_dir, "traffic_" + name + ".json")
