@@ -86,6 +86,8 @@ def lib():
             ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(FaMask), ctypes.POINTER(FaBlockMask)]
         L.fa_fwd_splitkv.restype = ctypes.c_int
         L.fa_fwd_splitkv.argtypes = L.fa_fwd.argtypes + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t]
+        L.fa_fwd_splitkv_noalloc.restype = ctypes.c_int
+        L.fa_fwd_splitkv_noalloc.argtypes = L.fa_fwd.argtypes + [ctypes.c_int]
         L.fa_fwd_splitkv_masked.restype = ctypes.c_int
         L.fa_fwd_splitkv_masked.argtypes = L.fa_fwd_masked.argtypes + [ctypes.c_int, ctypes.c_void_p,
                                                                         ctypes.c_size_t]
@@ -140,6 +142,13 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype, nu
     """Raw call of the C entry point fa_fwd_splitkv; returns the status code."""
     return int(lib().fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, float(scale), int(causal), stream, int(dtype),
                                     int(num_splits), workspace, int(workspace_bytes)))
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype, num_splits) -> int:
+    """Raw call of the C entry point fa_fwd_splitkv_noalloc (no workspace: the library's fixed
+    scratch); returns the status code."""
+    return int(lib().fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, N, d, float(scale), int(causal), stream,
+                                            int(dtype), int(num_splits)))
 
 
 def splitkv_workspace_size(B, H, N, d, num_splits) -> int:

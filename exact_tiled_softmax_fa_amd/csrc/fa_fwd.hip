@@ -46,6 +46,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "fa_fwd.h"
 #include "fa_device.h"
@@ -869,6 +870,37 @@ constexpr int kMaxSplits = 64;
 
 }  // namespace
 
+// Fixed device scratch of fa_fwd_splitkv_noalloc: the split-KV partial results (O_s in fp32 and two
+// log-sum-exps per row and split) for callers that cannot allocate. Each GPU the library runs on
+// holds its own copy from the library's first use there until the process ends. Calls on one GPU
+// share it, so calls that overlap on one GPU race; every split writes all of its rows' partials
+// before the merge reads them, so nothing needs clearing between calls.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's copy of `scratch`, looked up once per device with that device
+// current (in host code the array's name is a host-side stand-in, not a device address); nullptr
+// when the lookup fails.
+void* scratch_for_current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
 extern "C" {
 
 int fa_version(void) { return 200; }
@@ -886,6 +918,7 @@ const char* fa_status_string(int status) {
         case FA_ERR_LAUNCH: return "kernel launch failed";
         case FA_ERR_OPTION: return "option out of range (rescale threshold 0..15, variant 0..1, splits 1..64)";
         case FA_ERR_WORKSPACE: return "workspace is NULL, misaligned, too small or overlaps an argument";
+        case FA_ERR_SCRATCH: return "split-KV partials exceed the library's fixed 64 MiB scratch (use fa_fwd_splitkv)";
         default: return "unknown status";
     }
 }
@@ -1090,6 +1123,23 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                         : launch_split<128, false, false>(q, k, v, o, lse, n, nq, bh, c, tau_raw, num_splits, po, pl, stream);
     }
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                           int64_t N, int64_t d, float scale, int causal, hipStream_t stream, fa_dtype dtype,
+                           int num_splits) {
+    if (num_splits < 1 || num_splits > kMaxSplits) {
+        const int st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype, 1);
+        return st != FA_OK ? st : FA_ERR_OPTION;
+    }
+    const int st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype, num_splits);
+    if (st != FA_OK) return st;
+    if (num_splits == 1) return fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype);
+    const size_t need = fa_fwd_splitkv_workspace_size(B, H, N, d, num_splits);
+    if (need == 0 || need > kScratchBytes) return FA_ERR_SCRATCH;  // before any device call
+    void* ws = scratch_for_current_device();
+    if (ws == nullptr) return FA_ERR_LAUNCH;
+    return fa_fwd_splitkv(q, k, v, o, lse, B, H, N, d, scale, causal, stream, dtype, num_splits, ws, need);
 }
 
 int fa_fwd_splitkv_masked(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,

@@ -197,6 +197,28 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int num_splits, void* workspace, size_t workspace_bytes);
 
 /*
+ * fa_fwd_splitkv_noalloc -- fa_fwd_splitkv for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the same kernels, with
+ * the partial results kept in a fixed scratch array of the library instead of a caller workspace.
+ * It calls no hipMalloc, hipFree or other allocating routine.
+ *
+ * Arguments, layouts and results as for fa_fwd_splitkv without the workspace arguments; num_splits
+ * 1 .. 64 (1 is exactly fa_fwd). The partials must fit the scratch:
+ * fa_fwd_splitkv_workspace_size(B, H, N, d, num_splits) <= 64 MiB, i.e. B*H*N*(d+2)*num_splits
+ * <= 2^24 (at 2 splits: 64 527 rows B*H*N of d = 128, 127 100 of d = 64); larger problems return
+ * FA_ERR_SCRATCH before any device work. Each GPU holds its own 64 MiB array from the library's
+ * first use there until the process ends (its address is looked up once per device, on the first
+ * call with that device current). All calls on one GPU share that array: calls that overlap on
+ * one GPU (two streams, two threads) race and give wrong results; serialise them. Its contents
+ * between calls are unspecified.
+ * Errors: those of fa_fwd_splitkv except FA_ERR_WORKSPACE, plus FA_ERR_SCRATCH.
+ */
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t B, int64_t H, int64_t N, int64_t d,
+                           float scale, int causal, hipStream_t stream, fa_dtype dtype,
+                           int num_splits);
+
+/*
  * fa_fwd_splitkv_masked -- fa_fwd_masked with split-KV: the key tiles a query tile's window
  * reaches (fa_mask: sliding window and per-batch key lengths) are cut into num_splits runs, each
  * reduced by its own workgroup and merged as in fa_fwd_splitkv. A run may hold no allowed key of

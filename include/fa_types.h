@@ -28,8 +28,9 @@ typedef enum fa_status {
     FA_ERR_LAUNCH = 7,    /* a kernel launch (hipGetLastError) or a host thread failed */
     FA_ERR_ALIAS = 8,     /* o or lse overlaps an input, or o overlaps lse */
     FA_ERR_OPTION = 9,    /* an fa_fwd_options field or num_splits is out of range */
-    FA_ERR_WORKSPACE = 10 /* fa_fwd_splitkv: workspace NULL, not 16-byte aligned, smaller than
-                             fa_fwd_splitkv_workspace_size, or overlapping an argument */
+    FA_ERR_WORKSPACE = 10, /* fa_fwd_splitkv: workspace NULL, not 16-byte aligned, smaller than
+                              fa_fwd_splitkv_workspace_size, or overlapping an argument */
+    FA_ERR_SCRATCH = 11    /* fa_fwd_splitkv_noalloc: the partials exceed the fixed 64 MiB scratch */
 } fa_status;
 
 #ifdef __cplusplus

@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
     assert _declared_functions() == ["fa_bwd", "fa_bwd_blocksparse", "fa_bwd_masked", "fa_fwd", "fa_fwd_blocksparse",
                                      "fa_fwd_cpu", "fa_fwd_ex", "fa_fwd_masked", "fa_fwd_splitkv",
                                      "fa_fwd_splitkv_blocksparse", "fa_fwd_splitkv_heuristic",
-                                     "fa_fwd_splitkv_masked", "fa_fwd_splitkv_workspace_size", "fa_status_string",
+                                     "fa_fwd_splitkv_masked", "fa_fwd_splitkv_noalloc",
+                                     "fa_fwd_splitkv_workspace_size", "fa_status_string",
                                      "fa_version"]
 
 
@@ -58,7 +59,8 @@ def test_status_codes_are_pinned():
     vals = {m.group(1): int(m.group(2)) for m in re.finditer(r"\b(FA_\w+)\s*=\s*(\d+)", text)}
     assert vals == {"FA_F16": 0, "FA_BF16": 1, "FA_OK": 0, "FA_ERR_NULL": 1, "FA_ERR_SHAPE": 2,
                     "FA_ERR_HEAD_DIM": 3, "FA_ERR_DTYPE": 4, "FA_ERR_ALIGN": 5, "FA_ERR_SCALE": 6,
-                    "FA_ERR_LAUNCH": 7, "FA_ERR_ALIAS": 8, "FA_ERR_OPTION": 9, "FA_ERR_WORKSPACE": 10}
+                    "FA_ERR_LAUNCH": 7, "FA_ERR_ALIAS": 8, "FA_ERR_OPTION": 9, "FA_ERR_WORKSPACE": 10,
+                    "FA_ERR_SCRATCH": 11}
 
 
 def test_status_strings_match_codes(L):
@@ -66,6 +68,7 @@ def test_status_strings_match_codes(L):
     assert b"overlap" in L.fa_status_string(8)
     assert b"option" in L.fa_status_string(9)
     assert b"workspace" in L.fa_status_string(10)
+    assert b"scratch" in L.fa_status_string(11)
 
 
 def test_entry_points_take_fa_dtype():
@@ -79,7 +82,7 @@ def test_entry_points_take_fa_dtype():
 
 
 def test_status_strings(L):
-    for st in range(0, 11):
+    for st in range(0, 12):
         s = L.fa_status_string(st)
         assert s and s != b"unknown status"
     assert L.fa_status_string(99) == b"unknown status"
@@ -351,3 +354,19 @@ def test_splitkv_blocksparse_argument_errors(L, num_splits, ws, ws_bytes, blocks
     m = None if mask is None else fa.FaMask(*mask)
     assert fa.fa_fwd_splitkv_blocksparse(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
                                          a["scale"], a["stream"], a["dtype"], m, b, num_splits, ws, ws_bytes) == code
+
+
+def test_noalloc_rejects_before_device_work():
+    """fa_fwd_splitkv_noalloc checks its arguments and the scratch limit on the host, before any
+    device call (the pointers here are never dereferenced)."""
+    import exact_tiled_softmax_fa_amd as fa
+    q, k, v, o, lse = (i << 32 for i in range(1, 6))  # far apart: no overlap
+    # 2 splits of B*H*N = 65536 rows of d = 128 need 2 * 65536 * 130 * 4 bytes > 64 MiB
+    assert fa.fa_fwd_splitkv_noalloc(q, k, v, o, lse, 1, 8, 8192, 128, 0.088, 0, 0, 0, 2) == 11
+    assert fa.fa_fwd_splitkv_noalloc(q, k, v, o, lse, 1, 8, 8192, 128, 0.088, 0, 0, 0, 0) == 9
+    assert fa.fa_fwd_splitkv_noalloc(q, k, v, o, lse, 1, 8, 8192, 128, 0.088, 0, 0, 0, 65) == 9
+    assert fa.fa_fwd_splitkv_noalloc(q, k, v, o, lse, 1, 8, 8192, 96, 0.088, 0, 0, 0, 2) == 3
+    assert fa.fa_fwd_splitkv_noalloc(None, k, v, o, lse, 1, 8, 8192, 128, 0.088, 0, 0, 0, 2) == 1
+    assert fa.fa_fwd_splitkv_noalloc(q, k, v, q, lse, 1, 8, 8192, 128, 0.088, 0, 0, 0, 2) == 8
+    # the largest problem that fits: B*H*N*(d+2)*splits <= 2^24
+    assert fa.splitkv_workspace_size(1, 1, 64527, 128, 2) <= 64 << 20 < fa.splitkv_workspace_size(1, 1, 64528, 128, 2)
