@@ -59,10 +59,13 @@ __device__ __forceinline__ float add_pair(unsigned packed, float acc) {
 }
 
 // Value held by the lane 32 positions away (same query row, other half of the keys).
+// (IEEE maximum, v_maximum3_f32: unlike fmaxf it needs no quieting of the swapped-in operands,
+// which the compiler cannot see to be canonical; the scores it is used on are never NaN.)
+__device__ __forceinline__ float fmax_ieee(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float max_with_partner(float x) {
     unsigned u = __float_as_uint(x);
     auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return fmax_ieee(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_with_partner(float x) {
     unsigned u = __float_as_uint(x);
@@ -115,9 +118,9 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ float max_over_rows(float x) {
     unsigned u = __float_as_uint(x);
     auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    u = __float_as_uint(fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1])));
+    u = __float_as_uint(fmax_ieee(__uint_as_float(a[0]), __uint_as_float(a[1])));
     auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return fmax_ieee(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float sum_over_rows(float x) {
     unsigned u = __float_as_uint(x);

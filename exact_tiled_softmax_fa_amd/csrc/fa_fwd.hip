@@ -234,15 +234,15 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
         for (int b = 0; b < DB; ++b) oacc[qb][b] = (f32x4){};
     unsigned pk[2][2][4];  // P^T of the tile between its softmax and its product with V: [qb][kk][.]
-    // per query row (qb): reference max of raw dot products for l and oacc, this lane's quarter of
-    // the running denominator (rounded p), and the same sum of unrounded p (bf16 keeps 8 mantissa
-    // bits, too few for lse to 1e-3 on rows with few keys, so lse uses that one)
+    // per query row (qb): reference max of raw dot products for l and oacc, and this lane's quarter
+    // of the running denominator: f16 sums the rounded p (the weights the second product uses);
+    // bf16 sums the unrounded p in fp32 (8 mantissa bits would leave lse short of 1e-3 on rows with
+    // few keys; against the exact running maximum, normalising by this sum is as accurate as by
+    // the rounded one, and one sum serves O and lse)
     float m_run[2] = {-INFINITY, -INFINITY};
     float l_run[2] = {0.f, 0.f};
-    float l_f32[2] = {0.f, 0.f};
-    // the current tile's part of l_run and l_f32, added once the tile is accepted (settle)
+    // the current tile's part of l_run, added once the tile is accepted (settle)
     float l_tile[2] = {0.f, 0.f};
-    float lf_tile[2] = {0.f, 0.f};
     // EXACT (bf16): the reference is the exact running maximum of each row, moved whenever a
     // tile's max exceeds it (tau is not used). Otherwise (f16) the lazy reference below.
     constexpr bool EXACT = BF16;
@@ -342,18 +342,19 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
         }
     };
     // Move the reference max of each row (and rescale l, o~ by alpha = exp(m_old - m_new)) when
-    // `force`, or when some row of the wave has a score more than tau above its reference;
-    // otherwise p stays <= 2^tau_log2. mx0, mx1: the rows' maxima over the tile (reduced over the
-    // four lane rows). The new reference is the larger of the old one and max + headroom.
+    // `force`, or when some row of the wave's 16-row block has a score more than tau above its
+    // reference; otherwise p stays <= 2^tau_log2. mx0, mx1: the rows' maxima over the tile
+    // (reduced over the four lane rows). The new reference is the larger of the old one and
+    // max + headroom. (The two row blocks decide apart: under the exact running maximum a block
+    // whose rows all keep their maximum skips the rescale, which is then the identity.)
     auto rebase = [&](float mx0, float mx1, bool force) __attribute__((always_inline)) {
-        if (force || __builtin_amdgcn_ballot_w64(mx0 > m_run[0] + move_above || mx1 > m_run[1] + move_above)) {
-            const float mx[2] = {mx0, mx1};
+        const float mx[2] = {mx0, mx1};
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const float m_new = fmaxf(m_run[qb], mx[qb] + headroom);
+        for (int qb = 0; qb < 2; ++qb) {
+            if (force || __builtin_amdgcn_ballot_w64(mx[qb] > m_run[qb] + move_above)) {
+                const float m_new = fmax_ieee(m_run[qb], EXACT ? mx[qb] : mx[qb] + headroom);
                 const float alpha = (m_new == m_run[qb]) ? 1.f : __builtin_amdgcn_exp2f((m_run[qb] - m_new) * c);
                 l_run[qb] *= alpha;
-                if constexpr (BF16) l_f32[qb] *= alpha;
 #pragma unroll
                 for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -382,12 +383,14 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const float p1 = __builtin_amdgcn_exp2f(fmaf(sd[qb][kb][r + 1], c, -mc[qb]));
         unsigned& dst = pk[qb][kb >> 1][2 * (kb & 1) + (r >> 1)];
         dst = pack2<BF16>(p0, p1);
-        l_tile[qb] = add_pair<BF16>(dst, l_tile[qb]);
-        if constexpr (BF16) lf_tile[qb] += p0 + p1;
+        // a row block's first pair (pr = 0, 8) starts the tile's sums (from -0, which folds away)
+        const bool first = (pr & 7) == 0;
+        if constexpr (BF16)
+            l_tile[qb] = (first ? -0.f : l_tile[qb]) + (p0 + p1);
+        else
+            l_tile[qb] = add_pair<BF16>(dst, first ? -0.f : l_tile[qb]);
     };
     auto expo = [&](const f32x4 (&sd)[2][4]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) l_tile[qb] = lf_tile[qb] = 0.f;
 #pragma unroll
         for (int pr = 0; pr < 16; ++pr) exp_pair(sd, pr);
     };
@@ -410,7 +413,6 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             l_run[qb] += l_tile[qb];
-            if constexpr (BF16) l_f32[qb] += lf_tile[qb];
         }
     };
 
@@ -492,8 +494,6 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
             ka[0] = k_operand(k_nxt, 0, 0);
             ka[1] = k_operand(k_nxt, 0, 1);
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) l_tile[qb] = lf_tile[qb] = 0.f;
-#pragma unroll
             for (int i = 0; i < NK; ++i) {
                 const int t = i >> 2, kb = i & 3;
                 if (i + 2 < NK) ka[i + 2] = k_operand(k_nxt, (i + 2) >> 2, (i + 2) & 3);
@@ -515,7 +515,6 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
                     for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(pk[qb][kk][r]));
                 asm volatile("" : "+v"(l_tile[qb]));
-                if constexpr (BF16) asm volatile("" : "+v"(lf_tile[qb]));
             }
         };
         // region 2 of tile j: O^T += V(j)^T . P^T(j). EXACT: the row maxima of S^T(j+1) (s_nxt,
@@ -638,7 +637,6 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int qb = 0; qb < 2; ++qb) {
         const int qrow = wq0 + 16 * qb + li;
         const float l_tot = sum_over_rows(l_run[qb]);
-        const float l_lse = BF16 ? sum_over_rows(l_f32[qb]) : l_tot;  // every lane active here
         const float mcf = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb] * c;
         if constexpr (SPLIT) {
             // partial result over this split's keys; a row none of whose keys fall in the split
@@ -653,10 +651,10 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
                     *reinterpret_cast<float4*>(prow + 16 * b + 4 * g) = st;
                 }
                 if (g == 0) {
-                    // [0]: log-sum-exp of the denominator O was normalised by (the merge weights);
-                    // [1]: of the unrounded sum (the final lse; the same value in f16)
-                    const float2 ls = {l_tot > 0.f ? (mcf + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY,
-                                       l_lse > 0.f ? (mcf + __log2f(l_lse)) * 0.69314718055994531f : -INFINITY};
+                    // log-sum-exp of the denominator O was normalised by, in both slots: [0] weighs
+                    // the merge, [1] forms the final lse (one sum serves both in this kernel)
+                    const float ll = l_tot > 0.f ? (mcf + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+                    const float2 ls = {ll, ll};
                     *reinterpret_cast<float2*>(PL + 2 * ((int64_t)vh * N + qrow)) = ls;
                 }
             }
@@ -671,7 +669,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 *reinterpret_cast<u32x2*>(orow + 16 * b + 4 * g) = st;
             }
             if (LSE != nullptr && g == 0)
-                LSE[(int64_t)bh * N + qrow] = (!MASKED || l_lse > 0.f) ? (mcf + __log2f(l_lse)) * 0.69314718055994531f
+                LSE[(int64_t)bh * N + qrow] = (!MASKED || l_tot > 0.f) ? (mcf + __log2f(l_tot)) * 0.69314718055994531f
                                                                        : -INFINITY;
         }
     }

@@ -87,7 +87,9 @@ typedef struct fa_fwd_options {
  * calls are re-entrant and thread-safe. o and lse must not overlap q, k, v
  * or each other. Numerics: products accumulate in fp32 on the matrix cores;
  * the probabilities are rounded to `dtype` as the second product's operand;
- * the running statistics are fp32.
+ * the running statistics are fp32. The denominator (O's normaliser and the
+ * argument of lse's logarithm) sums the rounded probabilities in f16 and the
+ * unrounded fp32 ones in bf16.
  * Errors: see fa_status. Device faults surface at the caller's next
  * synchronisation.
  */

@@ -5,8 +5,8 @@ The model follows the arithmetic the kernels are built to do ("Decoding flash at
 bibekananda.in, "The backward pass": recompute p from the saved statistic, then the chain rule
 through softmax), with each rounding placed where the kernels place it:
   forward  p = exp(s - m) in fp32, rounded to the input dtype as the second product's operand;
-           O = (sum_j p~_j v_j) / (sum_j p~_j) in fp32, stored rounded to the dtype; lse in fp32
-           (from the unrounded sum in bf16, the rounded one in f16);
+           O = (sum_j p~_j v_j) / l in fp32, stored rounded to the dtype, and lse = m + ln l in
+           fp32, with l the sum of the rounded p in f16 and of the unrounded p in bf16;
   backward D_i = dO_i . O_i from the stored O (fp32 sum); p_ij = exp(s_ij - lse_i) in fp32;
            dP = dO V^T and dS = p (dP - D) in fp32; dV = p~^T dO, dK = scale dS~^T Q and
            dQ = scale dS~ K with p~, dS~ rounded to the dtype as operands, fp32 sums; each
@@ -55,11 +55,10 @@ def model_backward(q, k, v, dout, scale, wl, wr, seqlens, dt, stored=True):
         m = np.where(np.isfinite(m), m, np.float32(0))
         p = _f32(np.exp(s.astype(np.float64) - m))
         pt = _round(p, dt)
-        l_r = _f32(pt.astype(np.float64).sum(axis=1, keepdims=True))
-        l_u = _f32(p.astype(np.float64).sum(axis=1, keepdims=True))
-        o = _round(_f32(_f32(pt.astype(np.float64) @ V) / np.where(l_r > 0, l_r, 1)), dt)
-        l_lse = l_u if dt == "bf16" else l_r
-        lse = np.where(l_lse > 0, _f32(m + np.log(np.where(l_lse > 0, l_lse, 1).astype(np.float64))), -np.inf)
+        summed = p if dt == "bf16" else pt
+        l = _f32(summed.astype(np.float64).sum(axis=1, keepdims=True))
+        o = _round(_f32(_f32(pt.astype(np.float64) @ V) / np.where(l > 0, l, 1)), dt)
+        lse = np.where(l > 0, _f32(m + np.log(np.where(l > 0, l, 1).astype(np.float64))), -np.inf)
         # backward
         D = _f32((dO * o.astype(np.float64)).sum(axis=1, keepdims=True))
         with np.errstate(invalid="ignore"):  # rows with no allowed key: lse = -inf, p = 0

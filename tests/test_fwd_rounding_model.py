@@ -3,9 +3,10 @@ running maximum ("transformer math: flash attention math", aicassindra.com, "The
 and the full algorithm") while the f16 kernels may move the reference lazily.
 
 The model follows the kernel per 64-key tile: scores in fp32; p = exp2(s c - m c) with
-c = scale log2(e); p rounded to the input dtype as the second product's operand; the row sum of
-the rounded p (by the four 16-key groups a lane holds); O = (sum p~ v) / (sum p~) in fp32, stored
-rounded to the dtype. Reference policies:
+c = scale log2(e); p rounded to the input dtype as the second product's operand; the row sums
+(by the four 16-key groups a lane holds) of the rounded p, which also normalise O under the lazy
+reference (the f16 kernels), and of the unrounded p, which normalise O under the exact maximum
+(the bf16 kernels); O = (sum p~ v) / l in fp32, stored rounded to the dtype. Reference policies:
   lazy   the wave's 32 rows keep a reference m that moves only when some group sum of some row
          exceeds 2^tau (tau = 8), and then to the tile max + tau/2 (all rows of the wave move);
   exact  m is each row's running maximum, moved whenever a tile's max exceeds it.
@@ -61,7 +62,8 @@ def model_forward_wave(Q, K, V, scale, dt, policy, tau=8.0):
     def exps(s):
         p = np.exp2((s.astype(np.float64) * c - mc[:, None].astype(np.float64)).astype(np.float32))
         pr = _round(p.astype(np.float32), dt)
-        sums = np.stack([pr[:, group == g].astype(np.float64).sum(1) for g in range(4)], 1).astype(np.float32)
+        summed = pr if policy == "lazy" else p.astype(np.float32)
+        sums = np.stack([summed[:, group == g].astype(np.float64).sum(1) for g in range(4)], 1).astype(np.float32)
         return pr, sums
 
     for k0 in range(0, N, 64):
