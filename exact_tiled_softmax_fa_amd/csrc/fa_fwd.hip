@@ -87,7 +87,8 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
     static_assert(!(MASKED && CAUSAL), "the general mask replaces the causal one");
     static_assert(!BLOCKS || MASKED, "the block mask rides on the general mask");
     static_assert(!CHUNKED || BLOCKS, "chunks are chunks of the block-sparse work list");
-    static_assert(WV == kWaves || (WV == 4 && MASKED), "4-wave workgroups: the masked and block-sparse kernels");
+    static_assert(WV == kWaves || (WV == 4 && (MASKED || D == 64)),
+                  "4-wave workgroups: the masked and block-sparse kernels, and d = 64");
     constexpr int kBM = 32 * WV;               // query rows per workgroup
     constexpr int DT = D / 32;                 // 32-column k-steps of the first product
     constexpr int DB = D / 16;                 // 16-column blocks of the output
@@ -828,12 +829,23 @@ hipError_t launch_split(const void* q, const void* k, const void* v, void* o, fl
     return hipGetLastError();
 }
 
+// n_qt, G: 256-row query tiles and workgroups. d = 64 runs 4-wave (128-row) workgroups, two per
+// CU: with half the matrix work per score of d = 128 the vector ALU bounds it, and two workgroups
+// that do not share barriers keep it busier than one 8-wave workgroup's lock-stepped pairs.
 template <int D, bool BF16, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int N, int n_qt, int G,
                   float c, float tau_raw, hipStream_t stream) {
-    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL>), dim3(G), dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qt, G, c, tau_raw);
+    if constexpr (D == 64) {
+        const int n_qt4 = (N + 127) / 128, G4 = (G / n_qt) * n_qt4;
+        hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, false, false, false, false, 4>), dim3(G4), dim3(256), 0,
+                           stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qt4, G4, c,
+                           tau_raw);
+    } else {
+        hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL>), dim3(G), dim3(kThreads), 0, stream,
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, N, n_qt, G, c, tau_raw);
+    }
     return hipGetLastError();
 }
 
