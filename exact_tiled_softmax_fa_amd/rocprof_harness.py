@@ -99,13 +99,28 @@ def passes(workload: str, out: str, steps: int, warmup: int, which: str = "fwd",
     ]
 
 
+def display_command(cmd: str) -> str:
+    """A recorded command as run from the repository root: the interpreter as python3 and the
+    benchmark and output paths relative to the root (the absolute ones name one machine's copy)."""
+    words = []
+    for w in shlex.split(cmd):
+        if w == sys.executable or (os.path.isabs(w) and os.path.basename(w).startswith("python")):
+            w = "python3"
+        elif os.path.isabs(w) and w.endswith("/bench.py"):
+            w = "bench.py"
+        elif os.path.isabs(w) and os.path.commonpath([w, ROOT]) == ROOT:
+            w = os.path.relpath(w, ROOT)
+        words.append(w)
+    return " ".join(shlex.quote(w) for w in words)
+
+
 def run(workload: str, out: str, steps: int, warmup: int, timeout: int, which: str = "fwd", splits=None,
         blocks=None) -> list:
     cmds = []
     for name, prof_args, prog in passes(workload, out, steps, warmup, which, splits, blocks):
         cmd = ["rocprofv3", *prof_args, "--output-format", "csv", "-d", os.path.join(out, name), "-o", name,
                "--", *prog]
-        cmds.append(" ".join(shlex.quote(c) for c in cmd))
+        cmds.append(display_command(" ".join(shlex.quote(c) for c in cmd)))
         print(f"[rocprof] {name}: {cmds[-1]}", flush=True)
         env = dict(os.environ, TMPDIR=os.environ.get("TMPDIR", "/tmp"))
         res = subprocess.run(cmd, env=env, timeout=timeout)
@@ -308,12 +323,21 @@ def write_summary(rec: dict, summary_dir: str):
                   + (f" --splits {rec['splits']}" if rec.get("splits") else "")
                   + (f" --block-size {rec['blocks'][0]} --block-density {rec['blocks'][1]}" if rec.get("blocks")
                      else "")
+                  + f" --steps {rec.get('steps')} --warmup {rec.get('warmup', 0)}"
                   + "` (repository root, on the GPU), which ran:", "", "```",
-                  *rec["commands"], "```", ""]
+                  *[display_command(c) for c in rec["commands"]], "```", ""]
     d = rec["dispatch_ms"]
+    w0 = rec.get("warmup", 0)
+    if len(d) <= 40:
+        disp = [f"- dispatches (ms): {', '.join(f'{x:.3f}' for x in d)}"]
+    else:  # long warm-ups: their range, then the timed dispatches
+        warm = d[:w0]
+        disp = [f"- warm-up dispatches 1 .. {w0} (ms): first {warm[0]:.3f}, min {min(warm):.3f}, "
+                f"max {max(warm):.3f}, last {warm[-1]:.3f}" if warm else "- no warm-up dispatches",
+                f"- timed dispatches (ms): {', '.join(f'{x:.3f}' for x in d[w0:])}"]
     lines += [
         "## Kernel time (rocprofv3 --kernel-trace --stats)", "",
-        f"- dispatches (ms): {', '.join(f'{x:.3f}' for x in d)}",
+        *disp,
         f"- mean of the timed dispatches ({rec.get('warmup', 0) + 1} .. {rec.get('warmup', 0) + rec.get('steps', len(d))}): **{rec['kernel_ms_mean_timed']:.4f} ms** "
         f"= {rec['tflops_from_trace']:.1f} TFLOP/s (the matrix products this kernel executes)", "",
         "## Device-memory traffic (FETCH_SIZE, WRITE_SIZE; one counter per pass)", "",
@@ -331,6 +355,7 @@ def write_summary(rec: dict, summary_dir: str):
     with open(os.path.join(summary_dir, name + ".md"), "w") as f:
         f.write("\n".join(lines))
     slim = {k: v for k, v in rec.items() if k != "dispatch_ms"}
+    slim["commands"] = [display_command(c) for c in rec["commands"]]
     with open(os.path.join(summary_dir, "traffic_" + name + ".json"), "w") as f:
         json.dump(slim, f, indent=1)
     print("\n".join(lines), flush=True)

@@ -176,3 +176,15 @@ def test_reference_copies_ignore_small_copy_dispatches():
     # three 256 MiB reference copies and one 4 KiB upload through the same copy kernel
     assert rh._reference_copies([131092.0, 131084.0, 131084.0, 4.0]) == [131092.0, 131084.0, 131084.0]
     assert rh._reference_copies([]) == []
+
+
+def test_recorded_commands_run_from_the_repository_root():
+    # an absolute interpreter and benchmark path (another machine's copy) become python3 and bench.py
+    cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/p/kt -o kt -- "
+           "/usr/local/bin/python3 /some/where/repo/bench.py --workload W --steps 20 --warmup 5")
+    assert rh.display_command(cmd) == ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/p/kt "
+                                       "-o kt -- python3 bench.py --workload W --steps 20 --warmup 5")
+    # paths under this repository become relative to it
+    import os
+    inside = os.path.join(rh.ROOT, "gpurun_out", "x")
+    assert rh.display_command(f"rocprofv3 -d {inside} -- python3 bench.py") == "rocprofv3 -d gpurun_out/x -- python3 bench.py"
