@@ -160,7 +160,20 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
     __shared__ __attribute__((aligned(4096))) uint16_t v_lds0[TILE];
     __shared__ __attribute__((aligned(4096))) uint16_t v_lds1[TILE];
 
-    const int tid = threadIdx.x;
+    // PAIRED (plain causal): workgroup p of a head takes query tile n_qt - 1 - p and then tile p,
+    // as the causal forward does: equal work per workgroup, and the workgroups that run together
+    // read one head's K/V in step.
+    constexpr bool PAIRED = CAUSAL && !MASKED;
+    int bh, qt_first;
+    map_block(blockIdx.x, G, PAIRED ? (n_qt + 1) / 2 : n_qt, CAUSAL && !PAIRED, bh, qt_first);
+    const int n_pass = PAIRED && n_qt - 1 - qt_first != qt_first ? 2 : 1;
+#pragma nounroll
+    for (int pass = 0; pass < n_pass; ++pass) {
+    if (pass) __syncthreads();  // every wave is done with the first tile's LDS buffers
+    // (the thread index is hidden from the compiler in each pass, so it does not keep every
+    // per-lane address of the tile loop live across both passes)
+    int tid = threadIdx.x;
+    if constexpr (PAIRED) asm volatile("" : "+v"(tid));
     const int lane = tid & 63;
     const int wave = tid >> 6;
     // 16x16x32 products: lane l holds query column li = l % 16 of the S^T, dP^T and dQ^T tiles of
@@ -169,9 +182,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int g = lane >> 4;
     const int li = lane & 15;
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-
-    int bh, qt;
-    map_block(blockIdx.x, G, n_qt, CAUSAL, bh, qt);
+    const int qt = PAIRED ? (pass == 0 ? n_qt - 1 - qt_first : qt_first) : qt_first;
     const int q0 = qt * (32 * WV);
     const int64_t head = (int64_t)bh * N * D;
     const uint16_t* Kh = K + head;
@@ -378,6 +389,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const int qrow = wq0 + 16 * qb + li;
         if (qrow < N) store_row16<D, BF16>(dQ + head + (int64_t)qrow * D, acc[qb], scale, g);
     }
+    }  // pass
 }
 
 template <int D, bool BF16, bool CAUSAL, bool MASKED = false, bool BLOCKS = false, bool CHUNKED = false>
@@ -404,7 +416,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __shared__ __attribute__((aligned(4096))) uint16_t kv_lds[2 * kKeys * D];  // K rows, then V rows
     __shared__ __attribute__((aligned(16))) float st_lds[2][2][kQueryTile];    // [buffer][lse2, D][row]
 
-    const int tid = threadIdx.x;
+    // Causal: key tile 0 meets every query row. PAIRED (plain causal): workgroup p of a head takes
+    // key tile p and then key tile n_kt - 1 - p, so every workgroup meets the same number of query
+    // tiles.
+    constexpr bool PAIRED = CAUSAL && !MASKED;
+    int bh, kt_first;
+    map_block(blockIdx.x, G, PAIRED ? (n_kt + 1) / 2 : n_kt, CAUSAL && !PAIRED, bh, kt_first);
+    const int n_pass = PAIRED && n_kt - 1 - kt_first != kt_first ? 2 : 1;
+#pragma nounroll
+    for (int pass = 0; pass < n_pass; ++pass) {
+    if (pass) __syncthreads();  // every wave is done with the first key tile's LDS (the sums too)
+    int tid = threadIdx.x;
+    if constexpr (PAIRED) asm volatile("" : "+v"(tid));
     const int lane = tid & 63;
     const int wave = tid >> 6;
     // 16x16x32 products: lane l holds key column li = l % 16 of the S, dP, dK^T and dV^T tiles
@@ -416,11 +439,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int kg = wave & 3;     // key group: keys 32 kg .. 32 kg + 31 of the workgroup
     const int half = wave >> 2;  // the 32-row half of every query tile this wave takes
 
-    // Causal: key tile 0 meets every query row, so the reversed order of map_block puts the
-    // longest key tiles first.
-    int bh, kt;
-    map_block(blockIdx.x, G, n_kt, CAUSAL, bh, kt);
-    if (CAUSAL) kt = n_kt - 1 - kt;
+    const int kt = PAIRED ? (pass == 0 ? kt_first : n_kt - 1 - kt_first) : kt_first;
     const int k0 = kt * kKeys;
     const int64_t head = (int64_t)bh * N * D;
     const uint16_t* Qh = Q + head;
@@ -699,6 +718,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             store_row16<D, BF16>(dK + head + (int64_t)key * D, k4, scale, g);
         }
     }
+    }  // pass
 }
 
 // WQ: waves per dQ workgroup (query rows 32 * WQ); 4 only under the general mask.
@@ -710,7 +730,9 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
                       const uint8_t* bmask = nullptr, int bq = 0, int bk = 0, int64_t bstride_b = 0,
                       int64_t bstride_h = 0) {
     const int n_qt = (N + 32 * WQ - 1) / (32 * WQ), n_kt = (N + kKeys - 1) / kKeys;
-    const int Gq = BH * n_qt, Gk = BH * n_kt;
+    // (plain causal: one workgroup per pair of tiles in both kernels, see PAIRED)
+    constexpr bool paired = CAUSAL && !MASKED;
+    const int Gq = BH * (paired ? (n_qt + 1) / 2 : n_qt), Gk = BH * (paired ? (n_kt + 1) / 2 : n_kt);
     const auto* Q = static_cast<const uint16_t*>(q);
     const auto* K = static_cast<const uint16_t*>(k);
     const auto* V = static_cast<const uint16_t*>(v);
