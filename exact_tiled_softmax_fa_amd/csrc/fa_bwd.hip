@@ -23,6 +23,8 @@
 //                      S  = Q . K^T,  dP = dO . V^T       (two keys per lane)
 //                      dS = P (dP - D)
 //                      dV^T += dO^T . P,  dK^T += Q^T . dS (dO^T, Q^T by the LDS transpose read)
+// Plain causal workgroups of both kernels take two tiles in turn, a long and a short one, so all
+// meet the same number of tiles and the ones running together read a head's tiles in step.
 // All products are v_mfma_f32_16x16x32 on 16-row blocks (two per wave side), each operand read
 // from LDS feeding both blocks; on random operands this shape spends less energy per flop than
 // 32x32x16, and these kernels run at the power limit.

@@ -1,10 +1,11 @@
 // Exact tiled-softmax attention forward for gfx950 (CDNA4), behind the C ABI of fa_fwd.h.
 //
-// One workgroup = 8 waves = 256 query rows of one (batch, head) (4 waves = 128 rows for the
-// masked kernel's narrow-window form); each wave owns 32 rows, as two 16-row blocks whose Q
-// operands stay in registers for the whole kernel. The workgroup walks the keys in tiles of 64
-// (ascending), staging each K and V tile in LDS with coalesced 16-byte loads (LDS DMA) issued
-// ahead of use. Per tile and wave:
+// One workgroup = 8 waves = 256 query rows of one (batch, head) (4 waves = 128 rows at d = 64,
+// for the masked kernel's narrow-window form and for the block-sparse kernels); each wave owns
+// 32 rows, as two 16-row blocks whose Q operands stay in registers for the whole kernel. A plain
+// causal workgroup takes two query tiles in turn, a long and a short one. The workgroup walks the
+// keys in tiles of 64 (ascending), staging each K and V tile in LDS with coalesced 16-byte loads
+// (LDS DMA) issued ahead of use. Per tile and wave:
 //
 //   S^T = K_tile . Q^T          v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulate; each K operand
 //                               read from LDS feeds both query blocks. Computing the transpose
@@ -533,8 +534,9 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
         };
         // region 2 of tile j: O^T += V(j)^T . P^T(j). EXACT: the row maxima of S^T(j+1) (s_nxt,
         // already masked) are formed between the MFMAs, on the vector ALU this region leaves idle,
-        // and the reference moves after the product, once P(j) (taken against the old one) is in.
-        auto region2 = [&](const uint16_t* v_cur, const f32x4 (&s_nxt)[2][4]) __attribute__((always_inline)) {
+        // and the reference moves after the product, once P(j) (taken against the old one) is in;
+        // `next` is false when there is no tile j+1.
+        auto region2 = [&](const uint16_t* v_cur, const f32x4 (&s_nxt)[2][4], bool next) __attribute__((always_inline)) {
             // V^T operands read two steps ahead.
             constexpr int NV = 2 * DB;  // V^T operands: 16 for D = 128, 8 for D = 64
             constexpr int EPS = 32 / NV;  // scores of S^T(j+1) folded into the maxima per step
@@ -561,7 +563,9 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            if constexpr (EXACT) rebase(max_over_rows(pm[0]), max_over_rows(pm[1]), false);
+            if constexpr (EXACT) {
+                if (next) rebase(max_over_rows(pm[0]), max_over_rows(pm[1]), false);
+            }
         };
         if constexpr (MASKED) {
             // every wave: barrier, loads, region 1, region 2 (V in two buffers)
@@ -582,7 +586,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
                     region1(s_cur, s_nxt, k_nxt);
                     settle(s_cur);
                     mask(j + 1, s_nxt);
-                    region2(v_cur, s_nxt);
+                    region2(v_cur, s_nxt, true);
                 } else if (j < T_w) {
                     expo(s_cur);
                     settle(s_cur);
@@ -606,6 +610,12 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
             // V(j-3)'s) at the top of the step, after barrier j in waves 0-3 and after region 2 of
             // tile j-1 in waves 4-7, and waits for them at the top of the next step: one
             // unconditional wait, so the compiler sees no path on which a read could overtake them.
+            // Without a causal mask every wave runs both regions in every step: the last step's
+            // region 1 also forms an S^T(T) that nothing uses (from a stale K buffer, no load in
+            // flight into it; masked, and kept out of the bf16 maximum), which costs one tile of
+            // the first product but leaves a step one path, with no second set of per-step tests.
+            // (The test on the opaque T_w stays: the compiler keeps the same registers for the
+            // loop's exits only while the branches around the regions are per-lane ones.)
             const bool lag = wave_s >= WV / 2;
             auto step = [&](int j, f32x4 (&s_cur)[2][4], f32x4 (&s_nxt)[2][4], uint16_t* k_cur, const uint16_t* k_nxt,
                             const uint16_t* v_cur, uint16_t* v_p1) __attribute__((always_inline)) {
@@ -613,11 +623,11 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 if (!lag) __syncthreads();  // barrier j
                 if (j + 2 < T) issue(Kh, j + 2, k_cur, false);
                 if (j + 1 < T) issue(Vh, j + 1, v_p1, true);
-                if (j + 1 < T_w) {
+                if (CAUSAL ? j + 1 < T_w : j < T_w) {
                     region1(s_cur, s_nxt, k_nxt);
                     settle(s_cur);
                     mask(j + 1, s_nxt);
-                } else if (j < T_w) {
+                } else if (CAUSAL && j < T_w) {
                     expo(s_cur);
                     settle(s_cur);
                 }
@@ -625,9 +635,9 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
                     __builtin_amdgcn_s_waitcnt(0);
                     __syncthreads();  // barrier j + 1
                 }
-                if (j + 1 < T_w) {
-                    region2(v_cur, s_nxt);
-                } else if (j < T_w) {
+                if (CAUSAL ? j + 1 < T_w : j < T_w) {
+                    region2(v_cur, s_nxt, j + 1 < T);
+                } else if (CAUSAL && j < T_w) {
                     pv(v_cur);
                 }
             };
