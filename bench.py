@@ -100,15 +100,18 @@ def cpu_model() -> str:
     return "unknown"
 
 
+CPU_SAMPLE_ROWS = 3072  # query rows per head the CPU baseline times (about 10 s of the oracle)
+
+
 def cpu_baseline(w, window=None, blocks=None):
-    """The fp64 oracle on 1024 seeded rows per head (every row of the small workloads), in the GPU
-    line's unit: conventional TFLOP/s, or 4 d flops per allowed pair under a window (the masked
-    oracle) or a block mask (the block-sparse oracle; blocks = (block size, mask))."""
+    """The fp64 oracle on CPU_SAMPLE_ROWS seeded rows per head (every row of the small workloads),
+    in the GPU line's unit: conventional TFLOP/s, or 4 d flops per allowed pair under a window (the
+    masked oracle) or a block mask (the block-sparse oracle; blocks = (block size, mask))."""
     import numpy as np
     from oracle import core
 
     q, k, v = workloads.make_inputs(w)
-    rows = workloads.sample_rows(w)
+    rows = workloads.sample_rows(w, CPU_SAMPLE_ROWS) if w.rows_per_head is not None else None
     if rows is None:
         rows = np.tile(np.arange(w.N, dtype=np.int64), (w.B * w.H, 1))
     qd, kd, vd = q.double().numpy(), k.double().numpy(), v.double().numpy()

@@ -96,12 +96,13 @@ def custom_inputs(B, H, N, d, dtype, seed, sigma_qk=1.0):
     return make_inputs(w)
 
 
-def sample_rows(w: Workload):
-    """int64 array [B*H, R] of query rows to check, or None for every row."""
-    if w.rows_per_head is None or w.rows_per_head >= w.N:
+def sample_rows(w: Workload, rows_per_head: int = None):
+    """int64 array [B*H, R] of query rows to check (R = the workload's rows_per_head, or the given
+    count), or None for every row."""
+    r = w.rows_per_head if rows_per_head is None else rows_per_head
+    if r is None or r >= w.N:
         return None
     g = torch.Generator(device="cpu").manual_seed(w.seed + 1000)
-    r = w.rows_per_head
     out = np.empty((w.B * w.H, r), dtype=np.int64)
     for bh in range(w.B * w.H):
         rows = torch.randperm(w.N, generator=g)[:r].numpy().copy()
