@@ -125,212 +125,226 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int n_pass = PAIRED && n_qt - 1 - qt_first != qt_first ? 2 : 1;
 #pragma nounroll
     for (int pass = 0; pass < n_pass; ++pass) {
-    if (pass) __syncthreads();  // every wave is done with the first tile's LDS buffers
-    // (the thread index is hidden from the compiler in each pass, so it does not keep every
-    // per-lane address of the tile loops live across both passes, which spills)
-    int tid = threadIdx.x;
-    if constexpr (PAIRED) asm volatile("" : "+v"(tid));
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    // 16x16x32 products: lane l holds query column li = l % 16 of the S^T and O^T tiles, and row
-    // group g = l / 16 (tile rows 4g .. 4g + 3; operand k slots 8g .. 8g + 7)
-    const int g = lane >> 4;
-    const int li = lane & 15;
-    const int qt = PAIRED ? (pass == 0 ? n_qt - 1 - qt_first : qt_first) : qt_first;
-    const int bh = SPLIT ? vh / n_split : vh;
-    const int q0 = qt * kBM;
-    const int64_t head = (int64_t)bh * N * D;
-    const uint16_t* Qh = Q + head;
-    const uint16_t* Kh = K + head;
-    const uint16_t* Vh = V + head;
-    const int wq0 = q0 + 32 * wave;  // first query row of this wave (two 16-row blocks)
+        if (pass) __syncthreads();  // every wave is done with the first tile's LDS buffers
+        // (the thread index is hidden from the compiler in each pass, so it does not keep every
+        // per-lane address of the tile loops live across both passes, which spills)
+        int tid = threadIdx.x;
+        if constexpr (PAIRED) asm volatile("" : "+v"(tid));
+        const int lane = tid & 63;
+        const int wave = tid >> 6;
+        // 16x16x32 products: lane l holds query column li = l % 16 of the S^T and O^T tiles, and row
+        // group g = l / 16 (tile rows 4g .. 4g + 3; operand k slots 8g .. 8g + 7)
+        const int g = lane >> 4;
+        const int li = lane & 15;
+        const int qt = PAIRED ? (pass == 0 ? n_qt - 1 - qt_first : qt_first) : qt_first;
+        const int bh = SPLIT ? vh / n_split : vh;
+        const int q0 = qt * kBM;
+        const int64_t head = (int64_t)bh * N * D;
+        const uint16_t* Qh = Q + head;
+        const uint16_t* Kh = K + head;
+        const uint16_t* Vh = V + head;
+        const int wq0 = q0 + 32 * wave;  // first query row of this wave (two 16-row blocks)
 
-    const int kv_end = CAUSAL ? min(N, q0 + kBM) : N;
-    const int T_all = (kv_end + kBlockN - 1) / kBlockN;  // key tiles of this query tile
-    // tiles tb .. tb + T - 1 are this workgroup's (all of them without SPLIT); tile indices below
-    // are relative to tb
-    int tb = 0, T = T_all;
-    if constexpr (SPLIT) {
-        const int per = (T_all + n_split - 1) / n_split;
-        tb = (vh % n_split) * per;
-        T = max(0, min(T_all, tb + per) - tb);
-    }
-    // MASKED: kv_len keys exist for this batch; the workgroup's rows q0 .. q0 + 255 need keys
-    // [lo, hi), a range of whole tiles from tb
-    int kv_len = N;
-    if constexpr (MASKED) {
-        if (seqlens != nullptr) kv_len = min(max(seqlens[bh / H], 0), N);
-        const int lo = wl >= 0 ? max(0, q0 - wl) : 0;
-        const int hi = wr >= 0 ? min(kv_len, q0 + kBM + wr) : kv_len;
-        tb = lo / kBlockN;
-        T = max(0, (hi + kBlockN - 1) / kBlockN - tb);
-        if constexpr (SPLIT) {  // this split's run of the window's tiles (possibly none; BLOCKS lists within it)
-            const int per = (T + n_split - 1) / n_split;
-            const int s0 = (vh % n_split) * per;
-            tb += s0;
-            T = max(0, min(T, s0 + per) - s0);
+        const int kv_end = CAUSAL ? min(N, q0 + kBM) : N;
+        const int T_all = (kv_end + kBlockN - 1) / kBlockN;  // key tiles of this query tile
+        // tiles tb .. tb + T - 1 are this workgroup's (all of them without SPLIT); tile indices below
+        // are relative to tb
+        int tb = 0, T = T_all;
+        if constexpr (SPLIT) {
+            const int per = (T_all + n_split - 1) / n_split;
+            tb = (vh % n_split) * per;
+            T = max(0, min(T_all, tb + per) - tb);
         }
-    }
-    // BLOCKS: of the tiles tb .. tb + T - 1, those that some wave of the workgroup needs (its
-    // rows' query block has a non-zero byte for the tile's key block), compacted into t_list
-    // (absolute tile index) with one bit per wave in t_wm; from here on a tile index j is a
-    // position in that list. (Block sizes are multiples of 64: one byte decides a wave's whole
-    // 32 x 64 part of a tile.) CHUNKED builds the list in the schedule, a chunk at a time.
-    __shared__ int t_list[BLOCKS ? kMaxListTiles : 1];
-    __shared__ uint8_t t_wm[BLOCKS ? kMaxListTiles : 1];
-    __shared__ int t_cnt[BLOCKS ? WV : 1];
-    const uint8_t* mb = BLOCKS ? bmask + (int64_t)(bh / H) * bstride_b + (int64_t)(bh % H) * bstride_h : nullptr;
-    const int n_kb = BLOCKS ? (N + bk - 1) / bk : 0;
-    auto need = [&](int w, int t) {
-        const int r0 = q0 + 32 * w;
-        return r0 < N && mb[(int64_t)(r0 / bq) * n_kb + t * kBlockN / bk] != 0;
-    };
-    if constexpr (BLOCKS && !CHUNKED) T = compact_tiles<WV>(tb, T, need, t_list, t_wm, t_cnt, tid);
-    // tiles this wave computes: causal waves stop at the tile holding their last row
-    // (Non-causal: T_w = T, hidden from the compiler. Folded away, the tests on it disappear and
-    // the compiler keeps the output accumulators of the loop's two exit paths in two register
-    // sets, which spills; a per-lane opaque value keeps the control flow of the causal kernel.)
-    int T_w = CAUSAL ? max(0, min(T, (min(wq0 + 32, N) + kBlockN - 1) / kBlockN - tb)) : T;
-    // MASKED: this wave's key tiles are T_w0 .. T_w - 1 (a window leaves the first ones to the
-    // workgroup's earlier rows); the wave joins every barrier and load but computes only those
-    int T_w0 = 0;
-    if constexpr (MASKED && !BLOCKS) {  // (the block-sparse schedule tests each tile's bits instead)
-        const int hi_w = wr >= 0 ? min(kv_len, wq0 + 32 + wr) : kv_len;  // this wave's last key + 1
-        T_w = max(0, min(T, (hi_w + kBlockN - 1) / kBlockN - tb));
-        // (a split may start past the wave's first tile: the wave then computes from its first)
-        if (wl >= 0) T_w0 = max(0, min(T_w, max(0, wq0 - wl) / kBlockN - tb));
-    }
-    if constexpr (!CAUSAL && !MASKED) asm volatile("" : "+v"(T_w));
+        // MASKED: kv_len keys exist for this batch; the workgroup's rows q0 .. q0 + 255 need keys
+        // [lo, hi), a range of whole tiles from tb
+        int kv_len = N;
+        if constexpr (MASKED) {
+            if (seqlens != nullptr) kv_len = min(max(seqlens[bh / H], 0), N);
+            const int lo = wl >= 0 ? max(0, q0 - wl) : 0;
+            const int hi = wr >= 0 ? min(kv_len, q0 + kBM + wr) : kv_len;
+            tb = lo / kBlockN;
+            T = max(0, (hi + kBlockN - 1) / kBlockN - tb);
+            if constexpr (SPLIT) {  // this split's run of the window's tiles (possibly none; BLOCKS lists within it)
+                const int per = (T + n_split - 1) / n_split;
+                const int s0 = (vh % n_split) * per;
+                tb += s0;
+                T = max(0, min(T, s0 + per) - s0);
+            }
+        }
+        // BLOCKS: of the tiles tb .. tb + T - 1, those that some wave of the workgroup needs (its
+        // rows' query block has a non-zero byte for the tile's key block), compacted into t_list
+        // (absolute tile index) with one bit per wave in t_wm; from here on a tile index j is a
+        // position in that list. (Block sizes are multiples of 64: one byte decides a wave's whole
+        // 32 x 64 part of a tile.) CHUNKED builds the list in the schedule, a chunk at a time.
+        __shared__ int t_list[BLOCKS ? kMaxListTiles : 1];
+        __shared__ uint8_t t_wm[BLOCKS ? kMaxListTiles : 1];
+        __shared__ int t_cnt[BLOCKS ? WV : 1];
+        const uint8_t* mb = BLOCKS ? bmask + (int64_t)(bh / H) * bstride_b + (int64_t)(bh % H) * bstride_h : nullptr;
+        const int n_kb = BLOCKS ? (N + bk - 1) / bk : 0;
+        auto need = [&](int w, int t) {
+            const int r0 = q0 + 32 * w;
+            return r0 < N && mb[(int64_t)(r0 / bq) * n_kb + t * kBlockN / bk] != 0;
+        };
+        if constexpr (BLOCKS && !CHUNKED) T = compact_tiles<WV>(tb, T, need, t_list, t_wm, t_cnt, tid);
+        // tiles this wave computes: causal waves stop at the tile holding their last row
+        // (Non-causal: T_w = T, hidden from the compiler. Folded away, the tests on it disappear and
+        // the compiler keeps the output accumulators of the loop's two exit paths in two register
+        // sets, which spills; a per-lane opaque value keeps the control flow of the causal kernel.)
+        int T_w = CAUSAL ? max(0, min(T, (min(wq0 + 32, N) + kBlockN - 1) / kBlockN - tb)) : T;
+        // MASKED: this wave's key tiles are T_w0 .. T_w - 1 (a window leaves the first ones to the
+        // workgroup's earlier rows); the wave joins every barrier and load but computes only those
+        int T_w0 = 0;
+        if constexpr (MASKED && !BLOCKS) {  // (the block-sparse schedule tests each tile's bits instead)
+            const int hi_w = wr >= 0 ? min(kv_len, wq0 + 32 + wr) : kv_len;  // this wave's last key + 1
+            T_w = max(0, min(T, (hi_w + kBlockN - 1) / kBlockN - tb));
+            // (a split may start past the wave's first tile: the wave then computes from its first)
+            if (wl >= 0) T_w0 = max(0, min(T_w, max(0, wq0 - wl) / kBlockN - tb));
+        }
+        if constexpr (!CAUSAL && !MASKED) asm volatile("" : "+v"(T_w));
 
-    // Load g of a tile covers rows RPI*g .. RPI*g+RPI-1; lane l writes LDS bytes [1024 g + 16 l,
-    // +16), i.e. row RPI*g + l/CPR at chunk position l % CPR, which holds global chunk
-    // (l % CPR) ^ swz_k(row) (K tiles) or ^ swz_v(row) (V tiles). Those per-lane byte offsets
-    // within a tile are fixed (koffs, voffs); a tile moves only the buffer descriptor's base (a
-    // scalar add), and the descriptor's size ends at the head's last row, so rows past the end of
-    // the sequence read as zero (those keys are masked to -inf before they can carry weight).
-    // Offsets inside one head fit in 32 bits (the host limits N * d * 2 bytes to < 2^31).
-    const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // scalar copy for LDS destinations
-    unsigned koffs[IPW], voffs[IPW];
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-        const int ld = wave_s * IPW + i;
-        const int r = RPI * ld + lane / CPR;
-        koffs[i] = 2u * (unsigned)(r * D + 8 * ((lane % CPR) ^ swz_k<D>(r)));
-        voffs[i] = 2u * (unsigned)(r * D + 8 * ((lane % CPR) ^ swz_v<D>(r)));
-    }
-    auto issue = [&](const uint16_t* src_head, int j, uint16_t* dst, bool v_tile) __attribute__((always_inline)) {
-        const int k0 = __builtin_amdgcn_readfirstlane((BLOCKS ? t_list[j] : tb + j) * kBlockN);
-        const int nb = (N - k0) * D * 2;
+        // Load g of a tile covers rows RPI*g .. RPI*g+RPI-1; lane l writes LDS bytes [1024 g + 16 l,
+        // +16), i.e. row RPI*g + l/CPR at chunk position l % CPR, which holds global chunk
+        // (l % CPR) ^ swz_k(row) (K tiles) or ^ swz_v(row) (V tiles). Those per-lane byte offsets
+        // within a tile are fixed (koffs, voffs); a tile moves only the buffer descriptor's base (a
+        // scalar add), and the descriptor's size ends at the head's last row, so rows past the end of
+        // the sequence read as zero (those keys are masked to -inf before they can carry weight).
+        // Offsets inside one head fit in 32 bits (the host limits N * d * 2 bytes to < 2^31).
+        const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // scalar copy for LDS destinations
+        unsigned koffs[IPW], voffs[IPW];
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
             const int ld = wave_s * IPW + i;
-            lds_load16(src_head + (int64_t)k0 * D, nb, v_tile ? voffs[i] : koffs[i], (lds_void*)(dst + ld * 512));
+            const int r = RPI * ld + lane / CPR;
+            koffs[i] = 2u * (unsigned)(r * D + 8 * ((lane % CPR) ^ swz_k<D>(r)));
+            voffs[i] = 2u * (unsigned)(r * D + 8 * ((lane % CPR) ^ swz_v<D>(r)));
         }
-    };
+        auto issue = [&](const uint16_t* src_head, int j, uint16_t* dst, bool v_tile) __attribute__((always_inline)) {
+            const int k0 = __builtin_amdgcn_readfirstlane((BLOCKS ? t_list[j] : tb + j) * kBlockN);
+            const int nb = (N - k0) * D * 2;
+#pragma unroll
+            for (int i = 0; i < IPW; ++i) {
+                const int ld = wave_s * IPW + i;
+                lds_load16(src_head + (int64_t)k0 * D, nb, v_tile ? voffs[i] : koffs[i], (lds_void*)(dst + ld * 512));
+            }
+        };
 
-    // The k slots 8g .. 8g + 7 of k-step t of the first product are the columns of 16-byte chunk
-    // t + DT*g (any one-to-one map of (t, g) to chunks sums every column once; with this one the
-    // K operand reads, one chunk per lane group, are free of bank conflicts).
-    // This lane's two query rows (wq0 + li and wq0 + 16 + li, query blocks qb = 0, 1) as B
-    // operands of the first product, held in registers for the whole kernel. Rows past N repeat
-    // row N-1 (never stored).
-    u32x4 qf[2][DT];
+        // The k slots 8g .. 8g + 7 of k-step t of the first product are the columns of 16-byte chunk
+        // t + DT*g (any one-to-one map of (t, g) to chunks sums every column once; with this one the
+        // K operand reads, one chunk per lane group, are free of bank conflicts).
+        // This lane's two query rows (wq0 + li and wq0 + 16 + li, query blocks qb = 0, 1) as B
+        // operands of the first product, held in registers for the whole kernel. Rows past N repeat
+        // row N-1 (never stored).
+        u32x4 qf[2][DT];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const uint16_t* qrp = Qh + (int64_t)min(wq0 + 16 * qb + li, N - 1) * D + 8 * DT * g;
+        for (int qb = 0; qb < 2; ++qb) {
+            const uint16_t* qrp = Qh + (int64_t)min(wq0 + 16 * qb + li, N - 1) * D + 8 * DT * g;
 #pragma unroll
-        for (int t = 0; t < DT; ++t) qf[qb][t] = *reinterpret_cast<const u32x4*>(qrp + 8 * t);
-    }
-
-    // O^T of this wave: block (qb, b) holds columns d = 16b + 4g .. +3 of query row wq0 + 16qb + li
-    f32x4 oacc[2][DB];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int b = 0; b < DB; ++b) oacc[qb][b] = (f32x4){};
-    unsigned pk[2][2][4];  // P^T of the tile between its softmax and its product with V: [qb][kk][.]
-    // per query row (qb): reference max of raw dot products for l and oacc, and this lane's quarter
-    // of the running denominator: f16 sums the rounded p (the weights the second product uses);
-    // bf16 sums the unrounded p in fp32 (8 mantissa bits would leave lse short of 1e-3 on rows with
-    // few keys; against the exact running maximum, normalising by this sum is as accurate as by
-    // the rounded one, and one sum serves O and lse)
-    float m_run[2] = {-INFINITY, -INFINITY};
-    float l_run[2] = {0.f, 0.f};
-    // the current tile's part of l_run, added once the tile is accepted (settle)
-    float l_tile[2] = {0.f, 0.f};
-    // EXACT (bf16): the reference is the exact running maximum of each row, moved whenever a
-    // tile's max exceeds it (tau is not used). Otherwise (f16) the lazy reference below.
-    constexpr bool EXACT = BF16;
-    // bound on every unnormalised p: 2^tau_log2 (tau_raw is tau_log2 in raw score units)
-    const float p_cap = __builtin_amdgcn_exp2f(tau_raw * c);
-    // a moved reference sits this far above the maximum that moved it (0 for tau = 0, where it is
-    // the exact running maximum), so later scores must rise by more before it moves again
-    const float headroom = EXACT ? 0.f : 0.5f * tau_raw;
-    const float move_above = EXACT ? 0.f : tau_raw;  // a row moves when its max exceeds m + this
-
-    // LDS operand addresses (elements). Both swizzles depend on row & 15 only, so moving 16 rows
-    // down a tile is the constant offset 16*D: one address per k-step serves the four 16-key
-    // blocks of the K tile, and one per column block serves both 32-key steps of the V tile.
-    int koff[DT];
-#pragma unroll
-    for (int t = 0; t < DT; ++t) koff[t] = tile_off_k<D>(li, t + DT * g);
-    // ds_read_b64_tr_b16: within each 16-lane group, lane i receives element e from the 4 values
-    // lane 4e + i/4 points at, position i % 4. Lane s of group g points at key row 4g + s/4,
-    // columns 16b + 4(s % 4) .. +3, so lane i receives V[4g + e][16b + i] for e = 0..3: one V^T
-    // row (column d = 16b + i) over 4 keys. The second read takes keys 16 + 4g .. +3.
-    int voff[DB];
-#pragma unroll
-    for (int b = 0; b < DB; ++b) voff[b] = tile_off_v<D>(4 * g + (li >> 2), 2 * b + ((li & 3) >> 1)) + 4 * (li & 1);
-    // A operand of S^T: keys 16kb + li, chunk t + DT*g
-    auto k_operand = [&](const uint16_t* kt, int t, int kb) __attribute__((always_inline)) {
-        return *reinterpret_cast<const u32x4*>(kt + koff[t] + kb * 16 * D);
-    };
-    // A operand of O^T: V^T rows d = 16b + li; its k slots 8g + s are keys 32kk + 4g + s (s < 4)
-    // and 32kk + 16 + 4g + s - 4 (s >= 4), the order in which this lane holds P^T
-    auto v_operand = [&](const uint16_t* vt, int kk, int b) __attribute__((always_inline)) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + voff[b] + kk * 32 * D));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + voff[b] + kk * 32 * D + 16 * D));
-        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
-        const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
-        return (u32x4){lo2[0], lo2[1], hi2[0], hi2[1]};
-    };
-    // B operand of O^T: P^T of query block qb over the 32 keys of step kk
-    auto p_operand = [&](int qb, int kk) __attribute__((always_inline)) {
-        return (u32x4){pk[qb][kk][0], pk[qb][kk][1], pk[qb][kk][2], pk[qb][kk][3]};
-    };
-
-    // ---- the pieces of one tile's work ----
-    // S^T of two consecutive tiles (one being produced, one being consumed): [qb][kb] holds keys
-    // 16kb + 4g .. +3 of query row wq0 + 16qb + li
-    f32x4 s0[2][4], s1[2][4];
-    float mc[2] = {0.f, 0.f};  // m_run * c with m_run the current reference (0 while m_run = -inf)
-
-    // S^T(t) = K(t) . Q^T into s (32 MFMAs for D = 128; each K operand feeds both query blocks)
-    auto qk = [&](const uint16_t* kt, f32x4 (&sd)[2][4]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < 4 * DT; ++i) {
-            const int t = i >> 2, kb = i & 3;
-            const u32x4 a = k_operand(kt, t, kb);
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) sd[qb][kb] = mfma16<BF16>(a, qf[qb][t], t == 0 ? (f32x4){} : sd[qb][kb]);
+            for (int t = 0; t < DT; ++t) qf[qb][t] = *reinterpret_cast<const u32x4*>(qrp + 8 * t);
         }
-    };
-    // O^T += V(t)^T . P^T (32 MFMAs for D = 128; each V^T operand feeds both query blocks)
-    auto pv = [&](const uint16_t* vt) __attribute__((always_inline)) {
+
+        // O^T of this wave: block (qb, b) holds columns d = 16b + 4g .. +3 of query row wq0 + 16qb + li
+        f32x4 oacc[2][DB];
 #pragma unroll
-        for (int i = 0; i < 2 * DB; ++i) {
-            const int kk = i / DB, b = i % DB;
-            const u32x4 a = v_operand(vt, kk, b);
+        for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) oacc[qb][b] = mfma16<BF16>(a, p_operand(qb, kk), oacc[qb][b]);
-        }
-    };
-    // keys past the end, and (causal) keys after the query, become -inf before the max
-    auto mask = [&](int t, f32x4 (&sd)[2][4]) __attribute__((always_inline)) {
-        const int k0 = (BLOCKS ? t_list[t] : tb + t) * kBlockN;
-        if constexpr (MASKED) {
-            if ((k0 + kBlockN > kv_len) || (wr >= 0 && k0 + kBlockN - 1 > wq0 + wr) ||
-                (wl >= 0 && k0 < wq0 + 31 - wl)) {
+            for (int b = 0; b < DB; ++b) oacc[qb][b] = (f32x4){};
+        unsigned pk[2][2][4];  // P^T of the tile between its softmax and its product with V: [qb][kk][.]
+        // per query row (qb): reference max of raw dot products for l and oacc, and this lane's quarter
+        // of the running denominator: f16 sums the rounded p (the weights the second product uses);
+        // bf16 sums the unrounded p in fp32 (8 mantissa bits would leave lse short of 1e-3 on rows with
+        // few keys; against the exact running maximum, normalising by this sum is as accurate as by
+        // the rounded one, and one sum serves O and lse)
+        float m_run[2] = {-INFINITY, -INFINITY};
+        float l_run[2] = {0.f, 0.f};
+        // the current tile's part of l_run, added once the tile is accepted (settle)
+        float l_tile[2] = {0.f, 0.f};
+        // EXACT (bf16): the reference is the exact running maximum of each row, moved whenever a
+        // tile's max exceeds it (tau is not used). Otherwise (f16) the lazy reference below.
+        constexpr bool EXACT = BF16;
+        // bound on every unnormalised p: 2^tau_log2 (tau_raw is tau_log2 in raw score units)
+        const float p_cap = __builtin_amdgcn_exp2f(tau_raw * c);
+        // a moved reference sits this far above the maximum that moved it (0 for tau = 0, where it is
+        // the exact running maximum), so later scores must rise by more before it moves again
+        const float headroom = EXACT ? 0.f : 0.5f * tau_raw;
+        const float move_above = EXACT ? 0.f : tau_raw;  // a row moves when its max exceeds m + this
+
+        // LDS operand addresses (elements). Both swizzles depend on row & 15 only, so moving 16 rows
+        // down a tile is the constant offset 16*D: one address per k-step serves the four 16-key
+        // blocks of the K tile, and one per column block serves both 32-key steps of the V tile.
+        int koff[DT];
+#pragma unroll
+        for (int t = 0; t < DT; ++t) koff[t] = tile_off_k<D>(li, t + DT * g);
+        // ds_read_b64_tr_b16: within each 16-lane group, lane i receives element e from the 4 values
+        // lane 4e + i/4 points at, position i % 4. Lane s of group g points at key row 4g + s/4,
+        // columns 16b + 4(s % 4) .. +3, so lane i receives V[4g + e][16b + i] for e = 0..3: one V^T
+        // row (column d = 16b + i) over 4 keys. The second read takes keys 16 + 4g .. +3.
+        int voff[DB];
+#pragma unroll
+        for (int b = 0; b < DB; ++b) voff[b] = tile_off_v<D>(4 * g + (li >> 2), 2 * b + ((li & 3) >> 1)) + 4 * (li & 1);
+        // A operand of S^T: keys 16kb + li, chunk t + DT*g
+        auto k_operand = [&](const uint16_t* kt, int t, int kb) __attribute__((always_inline)) {
+            return *reinterpret_cast<const u32x4*>(kt + koff[t] + kb * 16 * D);
+        };
+        // A operand of O^T: V^T rows d = 16b + li; its k slots 8g + s are keys 32kk + 4g + s (s < 4)
+        // and 32kk + 16 + 4g + s - 4 (s >= 4), the order in which this lane holds P^T
+        auto v_operand = [&](const uint16_t* vt, int kk, int b) __attribute__((always_inline)) {
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + voff[b] + kk * 32 * D));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + voff[b] + kk * 32 * D + 16 * D));
+            const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+            const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+            return (u32x4){lo2[0], lo2[1], hi2[0], hi2[1]};
+        };
+        // B operand of O^T: P^T of query block qb over the 32 keys of step kk
+        auto p_operand = [&](int qb, int kk) __attribute__((always_inline)) {
+            return (u32x4){pk[qb][kk][0], pk[qb][kk][1], pk[qb][kk][2], pk[qb][kk][3]};
+        };
+
+        // ---- the pieces of one tile's work ----
+        // S^T of two consecutive tiles (one being produced, one being consumed): [qb][kb] holds keys
+        // 16kb + 4g .. +3 of query row wq0 + 16qb + li
+        f32x4 s0[2][4], s1[2][4];
+        float mc[2] = {0.f, 0.f};  // m_run * c with m_run the current reference (0 while m_run = -inf)
+
+        // S^T(t) = K(t) . Q^T into s (32 MFMAs for D = 128; each K operand feeds both query blocks)
+        auto qk = [&](const uint16_t* kt, f32x4 (&sd)[2][4]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 4 * DT; ++i) {
+                const int t = i >> 2, kb = i & 3;
+                const u32x4 a = k_operand(kt, t, kb);
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) sd[qb][kb] = mfma16<BF16>(a, qf[qb][t], t == 0 ? (f32x4){} : sd[qb][kb]);
+            }
+        };
+        // O^T += V(t)^T . P^T (32 MFMAs for D = 128; each V^T operand feeds both query blocks)
+        auto pv = [&](const uint16_t* vt) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 2 * DB; ++i) {
+                const int kk = i / DB, b = i % DB;
+                const u32x4 a = v_operand(vt, kk, b);
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) oacc[qb][b] = mfma16<BF16>(a, p_operand(qb, kk), oacc[qb][b]);
+            }
+        };
+        // keys past the end, and (causal) keys after the query, become -inf before the max
+        auto mask = [&](int t, f32x4 (&sd)[2][4]) __attribute__((always_inline)) {
+            const int k0 = (BLOCKS ? t_list[t] : tb + t) * kBlockN;
+            if constexpr (MASKED) {
+                if ((k0 + kBlockN > kv_len) || (wr >= 0 && k0 + kBlockN - 1 > wq0 + wr) ||
+                    (wl >= 0 && k0 < wq0 + 31 - wl)) {
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const int key = k0 + 16 * kb + 4 * g + r, qrow = wq0 + 16 * qb + li;
+                                if (key >= kv_len || (wr >= 0 && key > qrow + wr) || (wl >= 0 && key < qrow - wl))
+                                    sd[qb][kb][r] = -INFINITY;
+                            }
+                }
+                return;
+            }
+            if ((k0 + kBlockN > N) || (CAUSAL && k0 + kBlockN - 1 > wq0)) {
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -338,365 +352,351 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int key = k0 + 16 * kb + 4 * g + r, qrow = wq0 + 16 * qb + li;
-                            if (key >= kv_len || (wr >= 0 && key > qrow + wr) || (wl >= 0 && key < qrow - wl))
-                                sd[qb][kb][r] = -INFINITY;
+                            if (key >= N || (CAUSAL && key > qrow)) sd[qb][kb][r] = -INFINITY;
                         }
             }
-            return;
-        }
-        if ((k0 + kBlockN > N) || (CAUSAL && k0 + kBlockN - 1 > wq0)) {
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int key = k0 + 16 * kb + 4 * g + r, qrow = wq0 + 16 * qb + li;
-                        if (key >= N || (CAUSAL && key > qrow)) sd[qb][kb][r] = -INFINITY;
-                    }
-        }
-    };
-    // Move the reference max of each row (and rescale l, o~ by alpha = exp(m_old - m_new)) when
-    // `force`, or when some row of the wave's 16-row block has a score more than tau above its
-    // reference; otherwise p stays <= 2^tau_log2. mx0, mx1: the rows' maxima over the tile
-    // (reduced over the four lane rows). The new reference is the larger of the old one and
-    // max + headroom. (The two row blocks decide apart: under the exact running maximum a block
-    // whose rows all keep their maximum skips the rescale, which is then the identity.)
-    auto rebase = [&](float mx0, float mx1, bool force) __attribute__((always_inline)) {
-        const float mx[2] = {mx0, mx1};
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            if (force || __builtin_amdgcn_ballot_w64(mx[qb] > m_run[qb] + move_above)) {
-                const float m_new = fmax_ieee(m_run[qb], EXACT ? mx[qb] : mx[qb] + headroom);
-                const float alpha = (m_new == m_run[qb]) ? 1.f : __builtin_amdgcn_exp2f((m_run[qb] - m_new) * c);
-                l_run[qb] *= alpha;
-#pragma unroll
-                for (int b = 0; b < DB; ++b)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) oacc[qb][b][r] *= alpha;
-                m_run[qb] = m_new;
-                mc[qb] = (m_new == -INFINITY) ? 0.f : m_new * c;
-            }
-        }
-    };
-    auto rebase_from = [&](const f32x4 (&sd)[2][4], bool force) __attribute__((always_inline)) {
-        float mx[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            float m = fmaxf(sd[qb][0][0], sd[qb][0][1]);
-#pragma unroll
-            for (int e = 2; e < 16; ++e) m = fmaxf(m, sd[qb][e >> 2][e & 3]);
-            mx[qb] = max_over_rows(m);
-        }
-        rebase(mx[0], mx[1], force);
-    };
-    // exponential pair pr (0..15) of S^T: p = exp2(s*c - m*c), rounded to the operand type, and the
-    // row sum of the rounded values. Pair pr = 8qb + 2kb + r/2 lands in pk[qb][kb/2][2(kb%2) + r/2].
-    auto exp_pair = [&](const f32x4 (&sd)[2][4], int pr) __attribute__((always_inline)) {
-        const int qb = pr >> 3, kb = (pr >> 1) & 3, r = 2 * (pr & 1);
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sd[qb][kb][r], c, -mc[qb]));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sd[qb][kb][r + 1], c, -mc[qb]));
-        unsigned& dst = pk[qb][kb >> 1][2 * (kb & 1) + (r >> 1)];
-        dst = pack2<BF16>(p0, p1);
-        // a row block's first pair (pr = 0, 8) starts the tile's sums (from -0, which folds away)
-        const bool first = (pr & 7) == 0;
-        if constexpr (BF16)
-            l_tile[qb] = (first ? -0.f : l_tile[qb]) + (p0 + p1);
-        else
-            l_tile[qb] = add_pair<BF16>(dst, first ? -0.f : l_tile[qb]);
-    };
-    auto expo = [&](const f32x4 (&sd)[2][4]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int pr = 0; pr < 16; ++pr) exp_pair(sd, pr);
-    };
-    // Accept the exponentials of a tile (taken against the current reference) when no lane's sum
-    // of a row's values exceeds 2^tau_log2: then no single p does either, the bound the reference
-    // max exists to keep. Otherwise (rare: the scores rose past the reference, or -- masked kernels
-    // only -- a row has no reference yet) move the reference to the running max and take them
-    // again. This replaces a max over every tile by a test on sums the softmax forms anyway. (In the
-    // other kernels the first tile sets every row's reference: it holds key 0, or under split-KV a
-    // key every row that has any key in the split can see.)
-    // (EXACT: the reference already is the row's maximum over this tile, so every p <= 1.)
-    auto settle = [&](const f32x4 (&sd)[2][4]) __attribute__((always_inline)) {
-        if constexpr (!EXACT) {
-            if (__builtin_amdgcn_ballot_w64(l_tile[0] > p_cap || l_tile[1] > p_cap ||
-                                            (MASKED && (m_run[0] == -INFINITY || m_run[1] == -INFINITY)))) {
-                rebase_from(sd, true);
-                expo(sd);
-            }
-        }
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            l_run[qb] += l_tile[qb];
-        }
-    };
-
-    // ---- schedule ----
-    // Tile t's K sits in buffer t % 2. Iteration j runs, in each wave:
-    //   region 1: S^T(j+1) = K(j+1) . Q^T on the matrix cores, with the exponentials of tile j
-    //             (S^T(j) -> P^T(j)) interleaved between the MFMAs on the vector ALU;
-    //   region 2: O^T += V(j)^T . P^T(j), with the row max of S^T(j+1) interleaved;
-    //   then the (rare) move of the reference max for tile j+1, after P(j) has been used.
-    // So each wave overlaps its own softmax with its own products, one tile apart. Barrier j
-    // makes K(j+1) and V(j) visible (loaded after barrier j - 1) and frees the buffer of K(j) for
-    // K(j+2) and one V buffer for V(j+1): V(j-1)'s when V alternates between two buffers (the
-    // masked kernel), V(j-3)'s when it rotates through four (the ping-pong below).
-    if constexpr (BLOCKS) {
-        // Block-sparse schedule. Barrier j makes K(j) and V(j) visible (buffer j % 2) and frees
-        // the other pair, which takes K(j+1) and V(j+1). A wave computes tile j start to finish
-        // (scores, mask, max, exponentials, product with V) only when its own bit is set, so the
-        // waves of a workgroup whose query blocks differ skip each other's tiles; the two waves
-        // of a SIMD still overlap each other's matrix and vector work.
-        const int wbit = 1 << wave_s;
-        int Tc = T;  // entries of the list being walked
-        auto tile = [&](int j, const uint16_t* kt, const uint16_t* vt, uint16_t* kn, uint16_t* vn)
-                        __attribute__((always_inline)) {
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();  // barrier j
-            if (j + 1 < Tc) {
-                issue(Kh, j + 1, kn, false);
-                issue(Vh, j + 1, vn, true);
-            }
-            if (__builtin_amdgcn_readfirstlane(t_wm[j]) & wbit) {
-                qk(kt, s0);
-                mask(j, s0);
-                if constexpr (EXACT) rebase_from(s0, false);
-                expo(s0);
-                settle(s0);
-                pv(vt);
-            }
         };
-        auto walk = [&]() __attribute__((always_inline)) {
-            issue(Kh, 0, k_lds0, false);
-            issue(Vh, 0, v_lds0, true);
-            for (int j = 0; j < Tc; j += 2) {
-                tile(j, k_lds0, v_lds0, k_lds1, v_lds1);
-                if (j + 1 >= Tc) break;
-                tile(j + 1, k_lds1, v_lds1, k_lds0, v_lds0);
-            }
-        };
-        if constexpr (CHUNKED) {
-            // The online state carries over from chunk to chunk. Every wave has left the previous
-            // chunk's tiles (t_list, t_wm and both tile buffers read for the last time; no load in
-            // flight) before the first barrier of compact_tiles, which writes the list only after it.
-            for (int cb = 0; cb < T; cb += kMaxListTiles) {
-                Tc = compact_tiles<WV>(tb + cb, min(kMaxListTiles, T - cb), need, t_list, t_wm, t_cnt, tid);
-                if (Tc > 0) walk();
-            }
-        } else {
-            walk();
-        }
-    } else {
-        issue(Kh, 0, k_lds0, false);
-        issue(Vh, 0, v_lds0, true);
-        if (T > 1) issue(Kh, 1, k_lds1, false);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (T_w0 < T_w && T_w0 == 0) {  // the first tile sets the reference (m_run = -inf until then)
-            qk(k_lds0, s0);
-            mask(0, s0);
-            rebase_from(s0, false);
-        }
-        // region 1 of tile j: S^T(j+1) = K(j+1) . Q^T with the exponentials of tile j in between.
-        auto region1 = [&](f32x4 (&s_cur)[2][4], f32x4 (&s_nxt)[2][4], const uint16_t* k_nxt) __attribute__((always_inline)) {
-            // Explicit software pipeline: the LDS operand of K step i + 2 is read before the two
-            // MFMAs of step i issue, and the 16 pairs of exponentials are spread over the steps;
-            // sched_barrier(0) pins that order so the LDS latency stays behind the MFMAs.
-            constexpr int NK = 4 * DT;  // K operands: 16 for D = 128, 8 for D = 64
-            constexpr int PPS = 16 / NK;  // exponential pairs per step: 1 (after the first MFMA) or 2
-            static_assert(PPS == 1 || PPS == 2, "one or two pairs of exponentials per step");
-            u32x4 ka[NK];
-            ka[0] = k_operand(k_nxt, 0, 0);
-            ka[1] = k_operand(k_nxt, 0, 1);
-#pragma unroll
-            for (int i = 0; i < NK; ++i) {
-                const int t = i >> 2, kb = i & 3;
-                if (i + 2 < NK) ka[i + 2] = k_operand(k_nxt, (i + 2) >> 2, (i + 2) & 3);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    s_nxt[qb][kb] = mfma16<BF16>(ka[i], qf[qb][t], t == 0 ? (f32x4){} : s_nxt[qb][kb]);
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (PPS == 2 || qb == 0) exp_pair(s_cur, i * PPS + qb);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-            // Keep the exponentials in region 1: without this the compiler sinks them past the
-            // mask branch into region 2, next to their only consumer.
+        // Move the reference max of each row (and rescale l, o~ by alpha = exp(m_old - m_new)) when
+        // `force`, or when some row of the wave's 16-row block has a score more than tau above its
+        // reference; otherwise p stays <= 2^tau_log2. mx0, mx1: the rows' maxima over the tile
+        // (reduced over the four lane rows). The new reference is the larger of the old one and
+        // max + headroom. (The two row blocks decide apart: under the exact running maximum a block
+        // whose rows all keep their maximum skips the rescale, which is then the identity.)
+        auto rebase = [&](float mx0, float mx1, bool force) __attribute__((always_inline)) {
+            const float mx[2] = {mx0, mx1};
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
+                if (force || __builtin_amdgcn_ballot_w64(mx[qb] > m_run[qb] + move_above)) {
+                    const float m_new = fmax_ieee(m_run[qb], EXACT ? mx[qb] : mx[qb] + headroom);
+                    const float alpha = (m_new == m_run[qb]) ? 1.f : __builtin_amdgcn_exp2f((m_run[qb] - m_new) * c);
+                    l_run[qb] *= alpha;
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
+                    for (int b = 0; b < DB; ++b)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(pk[qb][kk][r]));
-                asm volatile("" : "+v"(l_tile[qb]));
-            }
-        };
-        // region 2 of tile j: O^T += V(j)^T . P^T(j). EXACT: the row maxima of S^T(j+1) (s_nxt,
-        // already masked) are formed between the MFMAs, on the vector ALU this region leaves idle,
-        // and the reference moves after the product, once P(j) (taken against the old one) is in;
-        // `next` is false when there is no tile j+1.
-        auto region2 = [&](const uint16_t* v_cur, const f32x4 (&s_nxt)[2][4], bool next) __attribute__((always_inline)) {
-            // V^T operands read two steps ahead.
-            constexpr int NV = 2 * DB;  // V^T operands: 16 for D = 128, 8 for D = 64
-            constexpr int EPS = 32 / NV;  // scores of S^T(j+1) folded into the maxima per step
-            u32x4 va[NV];
-            float pm[2] = {-INFINITY, -INFINITY};  // this lane's maxima of the two rows
-            va[0] = v_operand(v_cur, 0, 0);
-            va[1] = v_operand(v_cur, 1 / DB, 1 % DB);
-#pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const int kk = i / DB, b = i % DB;
-                if (i + 2 < NV) va[i + 2] = v_operand(v_cur, (i + 2) / DB, (i + 2) % DB);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    oacc[qb][b] = mfma16<BF16>(va[i], p_operand(qb, kk), oacc[qb][b]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                if constexpr (EXACT) {
-#pragma unroll
-                    for (int u = 0; u < EPS; ++u) {
-                        const int e = i * EPS + u, qb = e >> 4, kb = (e >> 2) & 3, r = e & 3;
-                        pm[qb] = fmaxf(pm[qb], s_nxt[qb][kb][r]);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
+                        for (int r = 0; r < 4; ++r) oacc[qb][b][r] *= alpha;
+                    m_run[qb] = m_new;
+                    mc[qb] = (m_new == -INFINITY) ? 0.f : m_new * c;
                 }
             }
-            if constexpr (EXACT) {
-                if (next) rebase(max_over_rows(pm[0]), max_over_rows(pm[1]), false);
+        };
+        auto rebase_from = [&](const f32x4 (&sd)[2][4], bool force) __attribute__((always_inline)) {
+            float mx[2];
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                float m = fmaxf(sd[qb][0][0], sd[qb][0][1]);
+#pragma unroll
+                for (int e = 2; e < 16; ++e) m = fmaxf(m, sd[qb][e >> 2][e & 3]);
+                mx[qb] = max_over_rows(m);
+            }
+            rebase(mx[0], mx[1], force);
+        };
+        // exponential pair pr (0..15) of S^T: p = exp2(s*c - m*c), rounded to the operand type, and the
+        // row sum of the rounded values. Pair pr = 8qb + 2kb + r/2 lands in pk[qb][kb/2][2(kb%2) + r/2].
+        auto exp_pair = [&](const f32x4 (&sd)[2][4], int pr) __attribute__((always_inline)) {
+            const int qb = pr >> 3, kb = (pr >> 1) & 3, r = 2 * (pr & 1);
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sd[qb][kb][r], c, -mc[qb]));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sd[qb][kb][r + 1], c, -mc[qb]));
+            unsigned& dst = pk[qb][kb >> 1][2 * (kb & 1) + (r >> 1)];
+            dst = pack2<BF16>(p0, p1);
+            // a row block's first pair (pr = 0, 8) starts the tile's sums (from -0, which folds away)
+            const bool first = (pr & 7) == 0;
+            if constexpr (BF16)
+                l_tile[qb] = (first ? -0.f : l_tile[qb]) + (p0 + p1);
+            else
+                l_tile[qb] = add_pair<BF16>(dst, first ? -0.f : l_tile[qb]);
+        };
+        auto expo = [&](const f32x4 (&sd)[2][4]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int pr = 0; pr < 16; ++pr) exp_pair(sd, pr);
+        };
+        // Accept the exponentials of a tile (taken against the current reference) when no lane's sum
+        // of a row's values exceeds 2^tau_log2: then no single p does either, the bound the reference
+        // max exists to keep. Otherwise (rare: the scores rose past the reference, or -- masked kernels
+        // only -- a row has no reference yet) move the reference to the running max and take them
+        // again. This replaces a max over every tile by a test on sums the softmax forms anyway. (In the
+        // other kernels the first tile sets every row's reference: it holds key 0, or under split-KV a
+        // key every row that has any key in the split can see.)
+        // (EXACT: the reference already is the row's maximum over this tile, so every p <= 1.)
+        auto settle = [&](const f32x4 (&sd)[2][4]) __attribute__((always_inline)) {
+            if constexpr (!EXACT) {
+                if (__builtin_amdgcn_ballot_w64(l_tile[0] > p_cap || l_tile[1] > p_cap ||
+                                                (MASKED && (m_run[0] == -INFINITY || m_run[1] == -INFINITY)))) {
+                    rebase_from(sd, true);
+                    expo(sd);
+                }
+            }
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                l_run[qb] += l_tile[qb];
             }
         };
-        if constexpr (MASKED) {
-            // every wave: barrier, loads, region 1, region 2 (V in two buffers)
-            auto iteration = [&](int j, f32x4 (&s_cur)[2][4], f32x4 (&s_nxt)[2][4], const uint16_t* k_nxt,
-                                 const uint16_t* v_cur, uint16_t* k_load, uint16_t* v_load) __attribute__((always_inline)) {
+
+        // ---- schedule ----
+        // Tile t's K sits in buffer t % 2. Iteration j runs, in each wave:
+        //   region 1: S^T(j+1) = K(j+1) . Q^T on the matrix cores, with the exponentials of tile j
+        //             (S^T(j) -> P^T(j)) interleaved between the MFMAs on the vector ALU;
+        //   region 2: O^T += V(j)^T . P^T(j), with the row max of S^T(j+1) interleaved;
+        //   then the (rare) move of the reference max for tile j+1, after P(j) has been used.
+        // So each wave overlaps its own softmax with its own products, one tile apart. Barrier j
+        // makes K(j+1) and V(j) visible (loaded after barrier j - 1) and frees the buffer of K(j) for
+        // K(j+2) and one V buffer for V(j+1): V(j-1)'s when V alternates between two buffers (the
+        // masked kernel), V(j-3)'s when it rotates through four (the ping-pong below).
+        if constexpr (BLOCKS) {
+            // Block-sparse schedule. Barrier j makes K(j) and V(j) visible (buffer j % 2) and frees
+            // the other pair, which takes K(j+1) and V(j+1). A wave computes tile j start to finish
+            // (scores, mask, max, exponentials, product with V) only when its own bit is set, so the
+            // waves of a workgroup whose query blocks differ skip each other's tiles; the two waves
+            // of a SIMD still overlap each other's matrix and vector work.
+            const int wbit = 1 << wave_s;
+            int Tc = T;  // entries of the list being walked
+            auto tile = [&](int j, const uint16_t* kt, const uint16_t* vt, uint16_t* kn, uint16_t* vn)
+                            __attribute__((always_inline)) {
                 __builtin_amdgcn_s_waitcnt(0);
-                __syncthreads();
-                if (j + 2 < T) issue(Kh, j + 2, k_load, false);
-                if (j + 1 < T) issue(Vh, j + 1, v_load, true);
-                if (j < T_w0) {
-                    // before this wave's first tile: at most start the pipeline with S^T(j+1)
-                    if (j + 1 == T_w0 && j + 1 < T_w) {
-                        qk(k_nxt, s_nxt);
-                        mask(j + 1, s_nxt);
-                        rebase_from(s_nxt, false);
-                    }
-                } else if (j + 1 < T_w) {
-                    region1(s_cur, s_nxt, k_nxt);
-                    settle(s_cur);
-                    mask(j + 1, s_nxt);
-                    region2(v_cur, s_nxt, true);
-                } else if (j < T_w) {
-                    expo(s_cur);
-                    settle(s_cur);
-                    pv(v_cur);
+                __syncthreads();  // barrier j
+                if (j + 1 < Tc) {
+                    issue(Kh, j + 1, kn, false);
+                    issue(Vh, j + 1, vn, true);
+                }
+                if (__builtin_amdgcn_readfirstlane(t_wm[j]) & wbit) {
+                    qk(kt, s0);
+                    mask(j, s0);
+                    if constexpr (EXACT) rebase_from(s0, false);
+                    expo(s0);
+                    settle(s0);
+                    pv(vt);
                 }
             };
-            for (int j = 0; j < T; j += 2) {
-                // even j: K(j+1) in buffer 1, V(j) in buffer 0; K(j+2) -> buffer 0, V(j+1) -> buffer 1
-                iteration(j, s0, s1, k_lds1, v_lds0, k_lds0, v_lds1);
-                if (j + 1 >= T) break;
-                iteration(j + 1, s1, s0, k_lds0, v_lds1, k_lds1, v_lds0);
+            auto walk = [&]() __attribute__((always_inline)) {
+                issue(Kh, 0, k_lds0, false);
+                issue(Vh, 0, v_lds0, true);
+                for (int j = 0; j < Tc; j += 2) {
+                    tile(j, k_lds0, v_lds0, k_lds1, v_lds1);
+                    if (j + 1 >= Tc) break;
+                    tile(j + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+                }
+            };
+            if constexpr (CHUNKED) {
+                // The online state carries over from chunk to chunk. Every wave has left the previous
+                // chunk's tiles (t_list, t_wm and both tile buffers read for the last time; no load in
+                // flight) before the first barrier of compact_tiles, which writes the list only after it.
+                for (int cb = 0; cb < T; cb += kMaxListTiles) {
+                    Tc = compact_tiles<WV>(tb + cb, min(kMaxListTiles, T - cb), need, t_list, t_wm, t_cnt, tid);
+                    if (Tc > 0) walk();
+                }
+            } else {
+                walk();
             }
         } else {
-            // Ping-pong. The two waves on a SIMD run the same sequence of regions half an iteration
-            // apart: waves 0-3 pass barrier j before region 1 of tile j, waves 4-7 ("lag") before
-            // region 2 of tile j-1. While one wave of the pair runs the exponentials of region 1 on
-            // the vector ALU, the other runs the MFMA-only region 2, instead of both contending for
-            // the vector ALU and then both for the matrix core. A lagging wave still reads V(j-1)
-            // after barrier j, so V rotates through four buffers (V(t) in buffer t % 4). Every wave
-            // issues its share of the loads of step j (K(j+2) into K(j)'s buffer, V(j+1) into
-            // V(j-3)'s) at the top of the step, after barrier j in waves 0-3 and after region 2 of
-            // tile j-1 in waves 4-7, and waits for them at the top of the next step: one
-            // unconditional wait, so the compiler sees no path on which a read could overtake them.
-            // Without a causal mask every wave runs both regions in every step: the last step's
-            // region 1 also forms an S^T(T) that nothing uses (from a stale K buffer, no load in
-            // flight into it; masked, and kept out of the bf16 maximum), which costs one tile of
-            // the first product but leaves a step one path, with no second set of per-step tests.
-            // (The test on the opaque T_w stays: the compiler keeps the same registers for the
-            // loop's exits only while the branches around the regions are per-lane ones.)
-            const bool lag = wave_s >= WV / 2;
-            auto step = [&](int j, f32x4 (&s_cur)[2][4], f32x4 (&s_nxt)[2][4], uint16_t* k_cur, const uint16_t* k_nxt,
-                            const uint16_t* v_cur, uint16_t* v_p1) __attribute__((always_inline)) {
-                __builtin_amdgcn_s_waitcnt(0);
-                if (!lag) __syncthreads();  // barrier j
-                if (j + 2 < T) issue(Kh, j + 2, k_cur, false);
-                if (j + 1 < T) issue(Vh, j + 1, v_p1, true);
-                if (CAUSAL ? j + 1 < T_w : j < T_w) {
-                    region1(s_cur, s_nxt, k_nxt);
-                    settle(s_cur);
-                    mask(j + 1, s_nxt);
-                } else if (CAUSAL && j < T_w) {
-                    expo(s_cur);
-                    settle(s_cur);
+            issue(Kh, 0, k_lds0, false);
+            issue(Vh, 0, v_lds0, true);
+            if (T > 1) issue(Kh, 1, k_lds1, false);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (T_w0 < T_w && T_w0 == 0) {  // the first tile sets the reference (m_run = -inf until then)
+                qk(k_lds0, s0);
+                mask(0, s0);
+                rebase_from(s0, false);
+            }
+            // region 1 of tile j: S^T(j+1) = K(j+1) . Q^T with the exponentials of tile j in between.
+            auto region1 = [&](f32x4 (&s_cur)[2][4], f32x4 (&s_nxt)[2][4], const uint16_t* k_nxt) __attribute__((always_inline)) {
+                // Explicit software pipeline: the LDS operand of K step i + 2 is read before the two
+                // MFMAs of step i issue, and the 16 pairs of exponentials are spread over the steps;
+                // sched_barrier(0) pins that order so the LDS latency stays behind the MFMAs.
+                constexpr int NK = 4 * DT;  // K operands: 16 for D = 128, 8 for D = 64
+                constexpr int PPS = 16 / NK;  // exponential pairs per step: 1 (after the first MFMA) or 2
+                static_assert(PPS == 1 || PPS == 2, "one or two pairs of exponentials per step");
+                u32x4 ka[NK];
+                ka[0] = k_operand(k_nxt, 0, 0);
+                ka[1] = k_operand(k_nxt, 0, 1);
+#pragma unroll
+                for (int i = 0; i < NK; ++i) {
+                    const int t = i >> 2, kb = i & 3;
+                    if (i + 2 < NK) ka[i + 2] = k_operand(k_nxt, (i + 2) >> 2, (i + 2) & 3);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb) {
+                        s_nxt[qb][kb] = mfma16<BF16>(ka[i], qf[qb][t], t == 0 ? (f32x4){} : s_nxt[qb][kb]);
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (PPS == 2 || qb == 0) exp_pair(s_cur, i * PPS + qb);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
-                if (lag && j + 1 < T) {
-                    __builtin_amdgcn_s_waitcnt(0);
-                    __syncthreads();  // barrier j + 1
-                }
-                if (CAUSAL ? j + 1 < T_w : j < T_w) {
-                    region2(v_cur, s_nxt, j + 1 < T);
-                } else if (CAUSAL && j < T_w) {
-                    pv(v_cur);
+                // Keep the exponentials in region 1: without this the compiler sinks them past the
+                // mask branch into region 2, next to their only consumer.
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(pk[qb][kk][r]));
+                    asm volatile("" : "+v"(l_tile[qb]));
                 }
             };
-            if (lag && T > 0) __syncthreads();  // barrier 0
-            // T barriers in every wave: waves 0-3 one per step; waves 4-7 barrier 0 above and one
-            // per step but the last
-            for (int j = 0; j < T; j += 4) {
-                step(j, s0, s1, k_lds0, k_lds1, v_lds0, v_lds1);
-                if (j + 1 >= T) break;
-                step(j + 1, s1, s0, k_lds1, k_lds0, v_lds1, v_lds2);
-                if (j + 2 >= T) break;
-                step(j + 2, s0, s1, k_lds0, k_lds1, v_lds2, v_lds3);
-                if (j + 3 >= T) break;
-                step(j + 3, s1, s0, k_lds1, k_lds0, v_lds3, v_lds0);
+            // region 2 of tile j: O^T += V(j)^T . P^T(j). EXACT: the row maxima of S^T(j+1) (s_nxt,
+            // already masked) are formed between the MFMAs, on the vector ALU this region leaves idle,
+            // and the reference moves after the product, once P(j) (taken against the old one) is in;
+            // `next` is false when there is no tile j+1.
+            auto region2 = [&](const uint16_t* v_cur, const f32x4 (&s_nxt)[2][4], bool next) __attribute__((always_inline)) {
+                // V^T operands read two steps ahead.
+                constexpr int NV = 2 * DB;  // V^T operands: 16 for D = 128, 8 for D = 64
+                constexpr int EPS = 32 / NV;  // scores of S^T(j+1) folded into the maxima per step
+                u32x4 va[NV];
+                float pm[2] = {-INFINITY, -INFINITY};  // this lane's maxima of the two rows
+                va[0] = v_operand(v_cur, 0, 0);
+                va[1] = v_operand(v_cur, 1 / DB, 1 % DB);
+#pragma unroll
+                for (int i = 0; i < NV; ++i) {
+                    const int kk = i / DB, b = i % DB;
+                    if (i + 2 < NV) va[i + 2] = v_operand(v_cur, (i + 2) / DB, (i + 2) % DB);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb) {
+                        oacc[qb][b] = mfma16<BF16>(va[i], p_operand(qb, kk), oacc[qb][b]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if constexpr (EXACT) {
+#pragma unroll
+                        for (int u = 0; u < EPS; ++u) {
+                            const int e = i * EPS + u, qb = e >> 4, kb = (e >> 2) & 3, r = e & 3;
+                            pm[qb] = fmaxf(pm[qb], s_nxt[qb][kb][r]);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                if constexpr (EXACT) {
+                    if (next) rebase(max_over_rows(pm[0]), max_over_rows(pm[1]), false);
+                }
+            };
+            if constexpr (MASKED) {
+                // every wave: barrier, loads, region 1, region 2 (V in two buffers)
+                auto iteration = [&](int j, f32x4 (&s_cur)[2][4], f32x4 (&s_nxt)[2][4], const uint16_t* k_nxt,
+                                     const uint16_t* v_cur, uint16_t* k_load, uint16_t* v_load) __attribute__((always_inline)) {
+                    __builtin_amdgcn_s_waitcnt(0);
+                    __syncthreads();
+                    if (j + 2 < T) issue(Kh, j + 2, k_load, false);
+                    if (j + 1 < T) issue(Vh, j + 1, v_load, true);
+                    if (j < T_w0) {
+                        // before this wave's first tile: at most start the pipeline with S^T(j+1)
+                        if (j + 1 == T_w0 && j + 1 < T_w) {
+                            qk(k_nxt, s_nxt);
+                            mask(j + 1, s_nxt);
+                            rebase_from(s_nxt, false);
+                        }
+                    } else if (j + 1 < T_w) {
+                        region1(s_cur, s_nxt, k_nxt);
+                        settle(s_cur);
+                        mask(j + 1, s_nxt);
+                        region2(v_cur, s_nxt, true);
+                    } else if (j < T_w) {
+                        expo(s_cur);
+                        settle(s_cur);
+                        pv(v_cur);
+                    }
+                };
+                for (int j = 0; j < T; j += 2) {
+                    // even j: K(j+1) in buffer 1, V(j) in buffer 0; K(j+2) -> buffer 0, V(j+1) -> buffer 1
+                    iteration(j, s0, s1, k_lds1, v_lds0, k_lds0, v_lds1);
+                    if (j + 1 >= T) break;
+                    iteration(j + 1, s1, s0, k_lds0, v_lds1, k_lds1, v_lds0);
+                }
+            } else {
+                // Ping-pong. The two waves on a SIMD run the same sequence of regions half an iteration
+                // apart: waves 0-3 pass barrier j before region 1 of tile j, waves 4-7 ("lag") before
+                // region 2 of tile j-1. While one wave of the pair runs the exponentials of region 1 on
+                // the vector ALU, the other runs the MFMA-only region 2, instead of both contending for
+                // the vector ALU and then both for the matrix core. A lagging wave still reads V(j-1)
+                // after barrier j, so V rotates through four buffers (V(t) in buffer t % 4). Every wave
+                // issues its share of the loads of step j (K(j+2) into K(j)'s buffer, V(j+1) into
+                // V(j-3)'s) at the top of the step, after barrier j in waves 0-3 and after region 2 of
+                // tile j-1 in waves 4-7, and waits for them at the top of the next step: one
+                // unconditional wait, so the compiler sees no path on which a read could overtake them.
+                // Without a causal mask every wave runs both regions in every step: the last step's
+                // region 1 also forms an S^T(T) that nothing uses (from a stale K buffer, no load in
+                // flight into it; masked, and kept out of the bf16 maximum), which costs one tile of
+                // the first product but leaves a step one path, with no second set of per-step tests.
+                // (The test on the opaque T_w stays: the compiler keeps the same registers for the
+                // loop's exits only while the branches around the regions are per-lane ones.)
+                const bool lag = wave_s >= WV / 2;
+                auto step = [&](int j, f32x4 (&s_cur)[2][4], f32x4 (&s_nxt)[2][4], uint16_t* k_cur, const uint16_t* k_nxt,
+                                const uint16_t* v_cur, uint16_t* v_p1) __attribute__((always_inline)) {
+                    __builtin_amdgcn_s_waitcnt(0);
+                    if (!lag) __syncthreads();  // barrier j
+                    if (j + 2 < T) issue(Kh, j + 2, k_cur, false);
+                    if (j + 1 < T) issue(Vh, j + 1, v_p1, true);
+                    if (CAUSAL ? j + 1 < T_w : j < T_w) {
+                        region1(s_cur, s_nxt, k_nxt);
+                        settle(s_cur);
+                        mask(j + 1, s_nxt);
+                    } else if (CAUSAL && j < T_w) {
+                        expo(s_cur);
+                        settle(s_cur);
+                    }
+                    if (lag && j + 1 < T) {
+                        __builtin_amdgcn_s_waitcnt(0);
+                        __syncthreads();  // barrier j + 1
+                    }
+                    if (CAUSAL ? j + 1 < T_w : j < T_w) {
+                        region2(v_cur, s_nxt, j + 1 < T);
+                    } else if (CAUSAL && j < T_w) {
+                        pv(v_cur);
+                    }
+                };
+                if (lag && T > 0) __syncthreads();  // barrier 0
+                // T barriers in every wave: waves 0-3 one per step; waves 4-7 barrier 0 above and one
+                // per step but the last
+                for (int j = 0; j < T; j += 4) {
+                    step(j, s0, s1, k_lds0, k_lds1, v_lds0, v_lds1);
+                    if (j + 1 >= T) break;
+                    step(j + 1, s1, s0, k_lds1, k_lds0, v_lds1, v_lds2);
+                    if (j + 2 >= T) break;
+                    step(j + 2, s0, s1, k_lds0, k_lds1, v_lds2, v_lds3);
+                    if (j + 3 >= T) break;
+                    step(j + 3, s1, s0, k_lds1, k_lds0, v_lds3, v_lds0);
+                }
             }
         }
-    }
 
-    // ---- epilogue: O = o~ / l, lse = m*scale + ln l, per query row (qb) ----
+        // ---- epilogue: O = o~ / l, lse = m*scale + ln l, per query row (qb) ----
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int qrow = wq0 + 16 * qb + li;
-        const float l_tot = sum_over_rows(l_run[qb]);
-        const float mcf = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb] * c;
-        if constexpr (SPLIT) {
-            // partial result over this split's keys; a row none of whose keys fall in the split
-            // (l = 0) gets O = 0 and lse = -inf, i.e. zero weight in the merge
-            if (qrow < N) {
-                const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-                float* prow = PO + ((int64_t)vh * N + qrow) * D;
+        for (int qb = 0; qb < 2; ++qb) {
+            const int qrow = wq0 + 16 * qb + li;
+            const float l_tot = sum_over_rows(l_run[qb]);
+            const float mcf = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb] * c;
+            if constexpr (SPLIT) {
+                // partial result over this split's keys; a row none of whose keys fall in the split
+                // (l = 0) gets O = 0 and lse = -inf, i.e. zero weight in the merge
+                if (qrow < N) {
+                    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+                    float* prow = PO + ((int64_t)vh * N + qrow) * D;
+#pragma unroll
+                    for (int b = 0; b < DB; ++b) {
+                        const float4 st = {oacc[qb][b][0] * inv, oacc[qb][b][1] * inv, oacc[qb][b][2] * inv,
+                                           oacc[qb][b][3] * inv};
+                        *reinterpret_cast<float4*>(prow + 16 * b + 4 * g) = st;
+                    }
+                    if (g == 0) {
+                        // log-sum-exp of the denominator O was normalised by, in both slots: [0] weighs
+                        // the merge, [1] forms the final lse (one sum serves both in this kernel)
+                        const float ll = l_tot > 0.f ? (mcf + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+                        const float2 ls = {ll, ll};
+                        *reinterpret_cast<float2*>(PL + 2 * ((int64_t)vh * N + qrow)) = ls;
+                    }
+                }
+            } else if (qrow < N) {
+                // (MASKED: a row with no allowed key has l = 0: o = 0, lse = -inf)
+                const float inv = (!MASKED || l_tot > 0.f) ? 1.f / l_tot : 0.f;
+                uint16_t* orow = O + head + (int64_t)qrow * D;
 #pragma unroll
                 for (int b = 0; b < DB; ++b) {
-                    const float4 st = {oacc[qb][b][0] * inv, oacc[qb][b][1] * inv, oacc[qb][b][2] * inv,
-                                       oacc[qb][b][3] * inv};
-                    *reinterpret_cast<float4*>(prow + 16 * b + 4 * g) = st;
+                    const u32x2 st = {pack2<BF16>(oacc[qb][b][0] * inv, oacc[qb][b][1] * inv),
+                                      pack2<BF16>(oacc[qb][b][2] * inv, oacc[qb][b][3] * inv)};
+                    *reinterpret_cast<u32x2*>(orow + 16 * b + 4 * g) = st;
                 }
-                if (g == 0) {
-                    // log-sum-exp of the denominator O was normalised by, in both slots: [0] weighs
-                    // the merge, [1] forms the final lse (one sum serves both in this kernel)
-                    const float ll = l_tot > 0.f ? (mcf + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-                    const float2 ls = {ll, ll};
-                    *reinterpret_cast<float2*>(PL + 2 * ((int64_t)vh * N + qrow)) = ls;
-                }
+                if (LSE != nullptr && g == 0)
+                    LSE[(int64_t)bh * N + qrow] = (!MASKED || l_tot > 0.f) ? (mcf + __log2f(l_tot)) * 0.69314718055994531f
+                                                                           : -INFINITY;
             }
-        } else if (qrow < N) {
-            // (MASKED: a row with no allowed key has l = 0: o = 0, lse = -inf)
-            const float inv = (!MASKED || l_tot > 0.f) ? 1.f / l_tot : 0.f;
-            uint16_t* orow = O + head + (int64_t)qrow * D;
-#pragma unroll
-            for (int b = 0; b < DB; ++b) {
-                const u32x2 st = {pack2<BF16>(oacc[qb][b][0] * inv, oacc[qb][b][1] * inv),
-                                  pack2<BF16>(oacc[qb][b][2] * inv, oacc[qb][b][3] * inv)};
-                *reinterpret_cast<u32x2*>(orow + 16 * b + 4 * g) = st;
-            }
-            if (LSE != nullptr && g == 0)
-                LSE[(int64_t)bh * N + qrow] = (!MASKED || l_tot > 0.f) ? (mcf + __log2f(l_tot)) * 0.69314718055994531f
-                                                                       : -INFINITY;
         }
-    }
     }  // pass
 }
 
