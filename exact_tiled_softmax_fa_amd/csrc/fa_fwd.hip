@@ -208,6 +208,10 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
         // within a tile are fixed (koffs, voffs); a tile moves only the buffer descriptor's base (a
         // scalar add), and the descriptor's size ends at the head's last row, so rows past the end of
         // the sequence read as zero (those keys are masked to -inf before they can carry weight).
+        // A tile that starts at or past the end (the first tile of an empty split-KV run or
+        // block-sparse list, loaded before the loop whatever the run's length) gets size 0, so every
+        // lane reads zero and nothing past the tensor is touched: a negative size would be taken as
+        // a huge unsigned one and the loads would run past the end of the tensor.
         // Offsets inside one head fit in 32 bits (the host limits N * d * 2 bytes to < 2^31).
         const int wave_s = __builtin_amdgcn_readfirstlane(wave);  // scalar copy for LDS destinations
         unsigned koffs[IPW], voffs[IPW];
@@ -220,7 +224,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2, 2)))
         }
         auto issue = [&](const uint16_t* src_head, int j, uint16_t* dst, bool v_tile) __attribute__((always_inline)) {
             const int k0 = __builtin_amdgcn_readfirstlane((BLOCKS ? t_list[j] : tb + j) * kBlockN);
-            const int nb = (N - k0) * D * 2;
+            const int nb = max(0, N - k0) * D * 2;
 #pragma unroll
             for (int i = 0; i < IPW; ++i) {
                 const int ld = wave_s * IPW + i;
