@@ -86,6 +86,8 @@ CASES = [
     (1, 3, 7, 128, "f16", 3.0, -1, -1, None),
     (2, 2, 40, 64, "bf16", 3.0, 0, 0, [40, 17]),
     (1, 2, 300, 128, "f16", 3.0, 1, 1, None),
+    (1, 2, 2, 64, "bf16", 3.0, 1, 2, None),
+    (1, 2, 35, 128, "bf16", 3.0, 2, 0, None),
 ]
 
 
